@@ -1,0 +1,198 @@
+/*
+ * zebra.h -- C ABI of libzebra: the global multi-view attention stage of a
+ * Zebra3D-style hybrid 3D reconstruction model, for AMD MI355X (gfx950).
+ *
+ * Source pages: "How Hybrid Attention Lets Feed-Forward 3D Models Scale to
+ * Many Views" (wispaper.ai) and its translations. A global stage is either
+ *   (a) tile-sparse softmax attention ("Linear-centered stages plus
+ *       tile-sparse stages"): 8x8-patch key tiles, a selector keeping a
+ *       key-tile fraction 1 - y per query tile, mean-K/V landmarks for the
+ *       omitted tiles, special keys always visible, special query rows
+ *       dense, every patch query keeps its self key; or
+ *   (b) linear attention ("Speedup scales with the number of input views"):
+ *       fused Q/K normalisation, 2D rotary and channel-softmax feature map,
+ *       then the centred affine output correction ("A closed-form fit avoids
+ *       retraining from scratch").
+ *
+ * Conventions for every entry point
+ *   - Sequence layout: F frames; each frame holds S special tokens then an
+ *     R x C patch grid in row-major order; N = F*(S+R*C) tokens. Q, K, V and
+ *     the output are contiguous bfloat16 arrays [N][H][64] (token, head,
+ *     channel). Head dim d must be 64; 1 <= R, C <= 128; H >= 1.
+ *   - Tiles: tile u = f*tpf + a*ceil(C/8) + b (tpf = ceil(R/8)*ceil(C/8))
+ *     covers patch rows [8a, min(8a+8,R)) and columns [8b, min(8b+8,C));
+ *     n_u = its patch count; T = F*tpf tiles. Lower index wins score ties.
+ *   - Kept tiles per query tile: k = round-half-even((1-y)*T), 0 <= y <= 1.
+ *   - All pointers in zebra_args are DEVICE pointers owned by the caller,
+ *     except where a field says "host". Buffer sizes come from
+ *     zebra_buffer_bytes(). The library allocates no device memory, keeps
+ *     no global state and is re-entrant across streams.
+ *   - Every call validates its arguments on the host before any launch and
+ *     then enqueues kernels on `stream` (asynchronous, no implicit sync).
+ *     Errors: a non-zero zebra_status; zebra_last_error() returns a
+ *     thread-local message. No C++ exception crosses this ABI.
+ */
+#ifndef ZEBRA_H
+#define ZEBRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZEBRA_OK = 0,
+  ZEBRA_ERR_INVALID_ARG = 1, /* null pointer, bad size, y outside [0,1] ... */
+  ZEBRA_ERR_UNSUPPORTED = 2, /* head_dim != 64, grid larger than 128x128 */
+  ZEBRA_ERR_WORKSPACE = 3,   /* workspace smaller than zebra_buffer_bytes */
+  ZEBRA_ERR_HIP = 4          /* a HIP launch reported an error */
+} zebra_status;
+
+typedef struct {
+  int32_t frames;    /* F >= 1 */
+  int32_t specials;  /* S >= 0 special tokens per frame */
+  int32_t rows;      /* R, patch grid rows, 1..128 */
+  int32_t cols;      /* C, patch grid columns, 1..128 */
+  int32_t heads;     /* H >= 1 */
+  int32_t head_dim;  /* d, must be 64 */
+} zebra_layout;
+
+/* Opaque stream handle: a hipStream_t (NULL = the default stream). */
+typedef void* zebra_stream;
+
+typedef struct {
+  zebra_layout L;
+  double y;            /* sparsity of a tile-sparse stage, 0 <= y <= 1 */
+
+  const void* q;       /* bf16 [N][H][64] */
+  const void* k;       /* bf16 [N][H][64] */
+  const void* v;       /* bf16 [N][H][64] */
+  void* out;           /* bf16 [N][H][64], written by the attention calls */
+
+  /* Linear stage parameters (float32, may be NULL):
+   * W [H][64][64] acting on column vectors (NULL: identity), b [H][64]
+   * (NULL: 0), mu [H][64] (NULL: 0), RMSNorm gains gq, gk [H][64]
+   * (NULL: 1). The correction is y_i = mu + W (o_i - mu) + b. */
+  const float* W;
+  const float* b;
+  const float* mu;
+  const float* gq;
+  const float* gk;
+  float rms_eps;       /* RMSNorm epsilon; <= 0 selects 1e-6 */
+  float rope_base;     /* rotary base; <= 0 selects 100 */
+
+  /* Tile-sparse stage buffers (sizes: zebra_buffer_bytes). */
+  void* kt;            /* packed keys, tile-major (ZEBRA_BUF_KT) */
+  void* vt;            /* packed values, tile-major (ZEBRA_BUF_VT) */
+  void* ks;            /* packed special-token keys (ZEBRA_BUF_KS) */
+  void* vs;            /* packed special-token values (ZEBRA_BUF_VS) */
+  double* kbar;        /* mean key of every tile, fp64 [H][T][64] */
+  float* vbar;         /* mean value of every tile, fp32 [H][T][64] */
+  float* logn;         /* ln n_u, fp32 [T] */
+  void* lm;            /* landmarks repacked for attention (ZEBRA_BUF_LM) */
+  int32_t* sel;        /* kept key tiles of every query tile, ascending,
+                          int32 [H][T][k] */
+  uint32_t* selmask;   /* the same as a bitmap, [H][T][ceil(T/32)] */
+  double* gap;         /* optional (NULL ok): relative gap between the k-th
+                          and (k+1)-th ranked tile score, fp64 [H][T];
+                          +inf when k = 0 or k = T */
+
+  void* workspace;     /* scratch (ZEBRA_BUF_WORKSPACE bytes) */
+  size_t workspace_bytes;
+} zebra_args;
+
+/* Which buffer zebra_buffer_bytes sizes. */
+enum {
+  ZEBRA_BUF_KT = 0,
+  ZEBRA_BUF_VT = 1,
+  ZEBRA_BUF_KS = 2,
+  ZEBRA_BUF_VS = 3,
+  ZEBRA_BUF_KBAR = 4,
+  ZEBRA_BUF_VBAR = 5,
+  ZEBRA_BUF_LOGN = 6,
+  ZEBRA_BUF_LM = 7,
+  ZEBRA_BUF_SEL = 8,
+  ZEBRA_BUF_SELMASK = 9,
+  ZEBRA_BUF_GAP = 10,
+  ZEBRA_BUF_WORKSPACE = 11  /* enough for every entry point below */
+};
+
+/* Operation codes for zebra_validate. */
+enum {
+  ZEBRA_OP_PACK = 0,
+  ZEBRA_OP_LANDMARKS = 1,
+  ZEBRA_OP_SELECT = 2,
+  ZEBRA_OP_SPARSE = 3,
+  ZEBRA_OP_LINEAR = 4,
+  ZEBRA_OP_DENSE = 5
+};
+
+/* Pack K and V into tile-major order ("Speedup scales with the number of
+ * input views": the sparse-stage kernels pack the key/value sequence into
+ * tile-major order). Reads k, v; writes kt, vt (each tile's tokens
+ * row-major, zero-padded to a multiple of 32 slots) and ks, vs (all special
+ * tokens in frame order, zero-padded to a multiple of 32). */
+zebra_status zebra_pack_tiles(const zebra_args* a, zebra_stream stream);
+
+/* Mean key/value landmark of every tile ("Linear-centered stages plus
+ * tile-sparse stages": omitted tiles are summarised as mean key/value
+ * landmarks). Reads kt, vt; writes kbar (exact fp64 mean of the bf16 keys),
+ * vbar, logn = ln n_u and lm (the landmark keys split into bf16 high and low
+ * parts and the values in bf16, in the attention kernel's layout). */
+zebra_status zebra_landmarks(const zebra_args* a, zebra_stream stream);
+
+/* Tile selector ("Linear-centered stages plus tile-sparse stages": keep a
+ * key-tile fraction 1 - y per query tile). For every head and query tile t:
+ * qbar_t = mean of its patch queries (fp64), score s_{t,u} = qbar_t . kbar_u
+ * / 8 in fp64 for every key tile u of every frame, keep the top k by
+ * (score descending, tile index ascending). Reads q, kbar; writes sel
+ * (ascending), selmask and gap (if non-NULL). Uses the workspace. */
+zebra_status zebra_select_tiles(const zebra_args* a, zebra_stream stream);
+
+/* Tile-sparse attention ("Linear-centered stages plus tile-sparse stages").
+ * Patch row i of query tile t: softmax over (1/8 scaling) the real tokens
+ * of every kept tile, the landmark of every omitted tile (logit
+ * q.kbar_u/8 + ln n_u, value vbar_u), every special key, and its own key
+ * when tile t itself is not kept. Special rows: dense over all N keys.
+ * Reads q, kt, vt, ks, vs, lm, logn, selmask; writes out. */
+zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream);
+
+/* Linear attention with the centred affine correction. For each head:
+ * phi(x) = softmax over the 64 channels of RoPE2D(RMSNorm(x)) (channels
+ * [0,32) turn by the patch row, [32,64) by the column, pair (j, j+16)
+ * by p * base^(-j/16); specials at (0,0)); S = sum_j phi(k_j) v_j^T,
+ * z = sum_j phi(k_j) over all N tokens (fp32); o_i = phi(q_i)^T S /
+ * phi(q_i)^T z; out_i = mu + W (o_i - mu) + b. Reads q, k, v, W, b, mu,
+ * gq, gk; writes out. Uses the workspace. */
+zebra_status zebra_linear_attn(const zebra_args* a, zebra_stream stream);
+
+/* Dense softmax attention of every token over all N keys ("Global attention
+ * dominates runtime as views grow"): the measurement baseline. Reads q, k,
+ * v; writes kt, vt, ks, vs (it packs first) and out. */
+zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream);
+
+/* Host-only argument check of operation `op` (ZEBRA_OP_*); no GPU call. */
+zebra_status zebra_validate(const zebra_args* a, int op);
+
+/* Bytes needed for buffer `which` (ZEBRA_BUF_*) at layout L and sparsity y;
+ * 0 for an invalid layout. */
+size_t zebra_buffer_bytes(const zebra_layout* L, double y, int which);
+
+/* k = round-half-even((1-y)*T) clamped to [0,T]; -1 if invalid. */
+int64_t zebra_keep_count(const zebra_layout* L, double y);
+
+/* Number of tiles T; -1 if the layout is invalid. */
+int64_t zebra_num_tiles(const zebra_layout* L);
+
+/* Message of the last error on this thread ("" if none). */
+const char* zebra_last_error(void);
+
+/* Library version string. */
+const char* zebra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZEBRA_H */

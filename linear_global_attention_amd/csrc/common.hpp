@@ -1,0 +1,78 @@
+// Shared definitions of libzebra's host code and gfx950 kernels: the tile
+// geometry of a multi-view sequence, the packed buffer layouts, bf16 helpers
+// and MFMA vector types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zebra {
+
+constexpr int D = 64;          // head dim (fixed)
+constexpr int TILE = 8;        // 8x8 patches per complete tile
+constexpr int MAX_GRID = 128;  // R, C <= 128
+constexpr int MAX_TPF = (MAX_GRID / TILE) * (MAX_GRID / TILE);  // tiles per frame
+constexpr int KBLK = 32;       // key-slot granularity of the packed layouts
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+
+// Geometry of one (F, S, R, C, H) layout, passed to kernels by value.
+//   token of patch (f, r, c) = f*tok_pf + S + r*C + c
+//   special s of frame f     = f*tok_pf + s
+//   tile u = f*tpf + a*tc + b, patch rows [8a, 8a+th), cols [8b, 8b+tw)
+// Packed key/value slots: tile (f, tl) starts at slot f*slots_pf +
+// slot_off[tl] and owns pad32(n) slots (n = th*tw real tokens, rest zero).
+struct Geom {
+  int F, S, R, C, H;
+  int tr, tc, tpf;     // tile rows/cols per frame, tiles per frame
+  int T;               // tiles
+  int tok_pf;          // tokens per frame, S + R*C
+  long long N;         // tokens
+  int slots_pf;        // packed slots per frame
+  long long slots;     // F*slots_pf
+  int nspec;           // F*S special tokens
+  int spec_pad;        // nspec rounded up to KBLK
+  int T_pad;           // T rounded up to KBLK
+  int slot_off[MAX_TPF];
+  unsigned char th[MAX_TPF];
+  unsigned char tw[MAX_TPF];
+};
+
+// Buffer layouts (element counts are per head unless stated):
+//   Kt  bf16 [H][slots][64]                    key of slot s, row-major
+//   Vt  bf16 [H][slots/32][64][32]             value, d-major per 32 slots
+//   Ks  bf16 [H][spec_pad][64]
+//   Vs  bf16 [H][spec_pad/32][64][32]
+//   LM  bf16 [H][3][T_pad*64]: kbar high part [T_pad][64], kbar low part
+//       [T_pad][64] (kbar - high, rounded), vbar [T_pad/32][64][32]
+
+// Arguments of the attention kernel (tile-sparse or dense).
+struct AttnArgs {
+  const u16* Q;
+  u16* O;
+  const u16* Kt;
+  const u16* Vt;
+  const u16* Ks;
+  const u16* Vs;
+  const u16* LM;
+  const float* logn;
+  const unsigned* selmask;  // nullptr: every tile kept (dense)
+  int nwords;               // ceil(T/32)
+  int sparse;               // 1: landmarks + self key for patch groups
+};
+
+__host__ __device__ inline int pad32(int n) { return (n + KBLK - 1) / KBLK * KBLK; }
+
+__device__ inline float bf2f(u16 b) { return __uint_as_float(((unsigned)b) << 16); }
+
+// float -> bf16 bits, round to nearest even (inputs are finite here)
+__device__ inline u16 f2bf(float f) {
+  unsigned u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+
+}  // namespace zebra

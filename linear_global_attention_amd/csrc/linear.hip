@@ -1,0 +1,386 @@
+// Linear global attention for gfx950: fused RMSNorm, 2D rotary and
+// channel-softmax feature map, a per-head KV state on MFMA, and the centred
+// affine output correction folded into that state.
+//
+// Zebra3D pages, "Speedup scales with the number of input views": the linear
+// stages fuse Q/K normalisation, positional rotation and a channel-softmax
+// feature map. "A closed-form fit avoids retraining from scratch": a centred
+// affine correction y = mu + W (o - mu) + b is applied to the output.
+//
+// Three kernels:
+//   linear_state  stream K and V once: phi(k) for 16 tokens per wave pass,
+//                 staged with V in LDS, then S += phi(K)^T V (bf16 MFMA,
+//                 fp32 accumulators) and z += phi(k); one partial per wave.
+//   linear_reduce fixed-order sum of the partials (fp64), then
+//                 S' = S W^T split into bf16 high/low parts and
+//                 b' = mu - W mu + b, because W o = phi(q)^T S W^T / den.
+//   linear_apply  stream Q once: phi(q), y^T = S'^T phi(q)^T on MFMA,
+//                 divide by phi(q).z, add b', store bf16.
+//
+// Lane layout of the feature map: lane l holds token l%16 of a 16-token
+// pass and, with g = l/16, the 16 channels ch(g,i) = (i/4)*16 + 4g + i%4.
+// Each rotary pair (j, j+16) therefore sits in one lane; channel sums need
+// two cross-lane steps. For the apply MFMA the reduction index a runs over
+// these channels in lane order, so S'^T is stored column-permuted to match.
+#include "common.hpp"
+
+namespace zebra {
+
+constexpr int LIN_THREADS = 256;
+constexpr int LIN_WAVES = LIN_THREADS / 64;
+constexpr int LIN_TOKENS_PER_WG = 8192;
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct LinParams {
+  float eps;
+  float base;
+};
+
+__device__ inline int lane_channel(int g, int i) { return (i >> 2) * 16 + 4 * g + (i & 3); }
+
+// cos/sin of p * base^(-j/16) for p < npos, j < 16, in LDS: tab[p][j] = {c, s}
+__device__ inline void build_rope_table(float2* tab, int npos, float base) {
+  for (int i = threadIdx.x; i < npos * 16; i += blockDim.x) {
+    const int p = i >> 4, j = i & 15;
+    const double ang = (double)p * pow((double)base, -(double)j / 16.0);
+    double s, c;
+    sincos(ang, &s, &c);
+    tab[i] = make_float2((float)c, (float)s);
+  }
+}
+
+__device__ inline void token_pos(const Geom& g, long long tok, int& pr, int& pc) {
+  const long long f = tok / g.tok_pf;
+  const int loc = (int)(tok - f * g.tok_pf);
+  if (loc < g.S) {
+    pr = 0;
+    pc = 0;
+  } else {
+    const int p = loc - g.S;
+    pr = p / g.C;
+    pc = p - pr * g.C;
+  }
+}
+
+// Feature map of one token's 16 lane channels (x holds them, fp32, in
+// lane order). On return x holds phi(x) for those channels.
+__device__ inline void featurize16(float x[16], const float gain[16], const float2* tab, int pr,
+                                   int pc, int g, float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ss += x[i] * x[i];
+  ss += __shfl_xor(ss, 16, 64);
+  ss += __shfl_xor(ss, 32, 64);
+  const float r = 1.0f / sqrtf(ss * (1.0f / 64.0f) + eps);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] *= gain[i];
+  // rotary: pairs (i, i+4) for i in 0..3 (row) and 8..11 (column)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = 4 * g + i;
+    const float2 cr = tab[pr * 16 + j];
+    const float2 cc = tab[pc * 16 + j];
+    const float a = x[i], b = x[i + 4];
+    x[i] = a * cr.x - b * cr.y;
+    x[i + 4] = b * cr.x + a * cr.y;
+    const float a2 = x[i + 8], b2 = x[i + 12];
+    x[i + 8] = a2 * cc.x - b2 * cc.y;
+    x[i + 12] = b2 * cc.x + a2 * cc.y;
+  }
+  float m = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) m = fmaxf(m, x[i]);
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  const float sc = r * LOG2E;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[i] = __builtin_amdgcn_exp2f((x[i] - m) * sc);
+    s += x[i];
+  }
+  s += __shfl_xor(s, 16, 64);
+  s += __shfl_xor(s, 32, 64);
+  const float inv = 1.0f / s;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] *= inv;
+}
+
+__device__ inline void load16(const u16* row, int g, float x[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint2 w = *(const uint2*)(row + q * 16 + 4 * g);
+    x[q * 4 + 0] = __uint_as_float(w.x << 16);
+    x[q * 4 + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+    x[q * 4 + 2] = __uint_as_float(w.y << 16);
+    x[q * 4 + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+  }
+}
+
+// grid (nchunks, H), block 256. partial p = chunk*4 + wave holds
+// S [64][64] (row a = phi channel, column c = value channel) then z [64].
+__global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
+    Geom g, LinParams P, const u16* __restrict__ K, const u16* __restrict__ V,
+    const float* __restrict__ gk, float* __restrict__ partials, int nchunks) {
+  __shared__ float2 tab[MAX_GRID * 16];
+  __shared__ u16 phis[LIN_WAVES][32][D + 8];
+  __shared__ u16 vals[LIN_WAVES][32][D + 8];
+  const int h = blockIdx.y, chunk = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane >> 4, tl = lane & 15;
+  build_rope_table(tab, max(g.R, g.C), P.base);
+  float gain[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) gain[i] = gk ? gk[h * D + lane_channel(grp, i)] : 1.0f;
+  __syncthreads();
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float zacc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) zacc[i] = 0.f;
+
+  const long long t_begin = (long long)chunk * LIN_TOKENS_PER_WG;
+  const long long t_end = min((long long)g.N, t_begin + LIN_TOKENS_PER_WG);
+  const long long rs = (long long)g.H * D;
+  for (long long t0 = t_begin + wave * 32; t0 < t_end; t0 += 32 * LIN_WAVES) {
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int slot = pass * 16 + tl;
+      const long long tok = t0 + slot;
+      float x[16], vv[16];
+      if (tok < t_end) {
+        load16(K + tok * rs + h * D, grp, x);
+        load16(V + tok * rs + h * D, grp, vv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = vv[i] = 0.f;
+      }
+      int pr = 0, pc = 0;
+      if (tok < t_end) token_pos(g, tok, pr, pc);
+      featurize16(x, gain, tab, pr, pc, grp, P.eps);
+      if (tok >= t_end) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const u16 pb = f2bf(x[i]);
+        zacc[i] += bf2f(pb);
+        phis[wave][slot][lane_channel(grp, i)] = pb;
+        vals[wave][slot][lane_channel(grp, i)] = f2bf(vv[i]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS writes done (single wave)
+    __builtin_amdgcn_wave_barrier();
+    // S[a][c] += sum_tok phi[tok][a] * v[tok][c]; k index = token
+    bf16x8 A[4], B[4];
+#pragma unroll
+    for (int ab = 0; ab < 4; ++ab) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const u16 pa = phis[wave][8 * grp + m][ab * 16 + tl];
+        const u16 vb = vals[wave][8 * grp + m][ab * 16 + tl];
+        A[ab][m] = __builtin_bit_cast(__bf16, pa);
+        B[ab][m] = __builtin_bit_cast(__bf16, vb);
+      }
+    }
+#pragma unroll
+    for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        acc[ab][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ab], B[cb], acc[ab][cb], 0, 0, 0);
+    __builtin_amdgcn_wave_barrier();
+  }
+  // z: sum the 16 lanes of each channel group
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float v = zacc[i];
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
+    zacc[i] = v;
+  }
+  float* out = partials + ((long long)h * nchunks * LIN_WAVES + chunk * LIN_WAVES + wave) * (D * D + D);
+  // MFMA 16x16 output: lane holds column tl, rows 4*grp + 0..3
+#pragma unroll
+  for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[(ab * 16 + 4 * grp + r) * D + cb * 16 + tl] = acc[ab][cb][r];
+  if (tl == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[D * D + lane_channel(grp, i)] = zacc[i];
+  }
+}
+
+// grid (H), block 256. Writes per head: Sp_hi, Sp_lo bf16 [64][64] holding
+// (S W^T)^T with columns in lane-channel order, z fp32 [64], bp fp32 [64].
+__global__ void __launch_bounds__(256) linear_reduce_kernel(
+    Geom g, const float* __restrict__ partials, int nparts, const float* __restrict__ W,
+    const float* __restrict__ b, const float* __restrict__ mu, u16* __restrict__ sp,
+    float* __restrict__ zb) {
+  __shared__ double S[D][D + 1];
+  __shared__ double z[D];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const float* base = partials + (long long)h * nparts * (D * D + D);
+  for (int e = tid; e < D * D + D; e += 256) {
+    double s = 0.0;
+    for (int p = 0; p < nparts; ++p) s += (double)base[(long long)p * (D * D + D) + e];
+    if (e < D * D) S[e / D][e % D] = s;
+    else z[e - D * D] = s;
+  }
+  __syncthreads();
+  const float* Wh = W ? W + (long long)h * D * D : nullptr;
+  u16* hi = sp + (long long)h * 2 * D * D;
+  u16* lo = hi + D * D;
+  // Sp^T[e][p] = sum_c S[ch(p)][c] W[e][c], p = ks*32 + 8g + m -> channel
+  for (int idx = tid; idx < D * D; idx += 256) {
+    const int e = idx / D, p = idx % D;
+    const int ks = p >> 5, gg = (p & 31) >> 3, m = p & 7;
+    const int a = lane_channel(gg, ks * 8 + m);
+    double s;
+    if (Wh) {
+      s = 0.0;
+      for (int c = 0; c < D; ++c) s += S[a][c] * (double)Wh[e * D + c];
+    } else {
+      s = S[a][e];
+    }
+    const float sf = (float)s;
+    const u16 hb = f2bf(sf);
+    hi[idx] = hb;
+    lo[idx] = f2bf((float)(s - (double)bf2f(hb)));
+  }
+  float* zo = zb + (long long)h * 2 * D;
+  if (tid < D) {
+    zo[tid] = (float)z[tid];
+    // b' = mu - W mu + b
+    double wm = 0.0, m_e = mu ? (double)mu[h * D + tid] : 0.0;
+    if (mu) {
+      for (int c = 0; c < D; ++c)
+        wm += (Wh ? (double)Wh[tid * D + c] : (c == tid ? 1.0 : 0.0)) * (double)mu[h * D + c];
+    }
+    zo[D + tid] = (float)(m_e - wm + (b ? (double)b[h * D + tid] : 0.0));
+  }
+}
+
+// grid (nchunks, H), block 256.
+__global__ void __launch_bounds__(LIN_THREADS) linear_apply_kernel(
+    Geom g, LinParams P, const u16* __restrict__ Q, const float* __restrict__ gq,
+    const u16* __restrict__ sp, const float* __restrict__ zb, u16* __restrict__ out) {
+  __shared__ float2 tab[MAX_GRID * 16];
+  const int h = blockIdx.y, chunk = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane >> 4, tl = lane & 15;
+  build_rope_table(tab, max(g.R, g.C), P.base);
+  float gain[16], zl[16], bp[16];
+  const float* zo = zb + (long long)h * 2 * D;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int ch = lane_channel(grp, i);
+    gain[i] = gq ? gq[h * D + ch] : 1.0f;
+    zl[i] = zo[ch];
+  }
+#pragma unroll
+  for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bp[eb * 4 + r] = zo[D + eb * 16 + 4 * grp + r];
+  // A operands: Sp^T rows e = eb*16 + tl, k slots ks*32 + 8*grp + 0..7
+  bf16x8 Ahi[4][2], Alo[4][2];
+  const u16* hi = sp + (long long)h * 2 * D * D;
+  const u16* lo = hi + D * D;
+#pragma unroll
+  for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int off = (eb * 16 + tl) * D + ks * 32 + 8 * grp;
+      Ahi[eb][ks] = *(const bf16x8*)(hi + off);
+      Alo[eb][ks] = *(const bf16x8*)(lo + off);
+    }
+  __syncthreads();
+  const long long t_begin = (long long)chunk * LIN_TOKENS_PER_WG;
+  const long long t_end = min((long long)g.N, t_begin + LIN_TOKENS_PER_WG);
+  const long long rs = (long long)g.H * D;
+  for (long long t0 = t_begin + wave * 16; t0 < t_end; t0 += 16 * LIN_WAVES) {
+    const long long tok = t0 + tl;
+    float x[16];
+    if (tok < t_end) load16(Q + tok * rs + h * D, grp, x);
+    else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = 0.f;
+    }
+    int pr = 0, pc = 0;
+    if (tok < t_end) token_pos(g, tok, pr, pc);
+    featurize16(x, gain, tab, pr, pc, grp, P.eps);
+    bf16x8 Bk[2];
+    float den = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const u16 pb = f2bf(x[i]);
+      den += bf2f(pb) * zl[i];
+      Bk[i >> 3][i & 7] = __builtin_bit_cast(__bf16, pb);
+    }
+    den += __shfl_xor(den, 16, 64);
+    den += __shfl_xor(den, 32, 64);
+    const float inv = 1.0f / den;
+    f32x4 y[4];
+#pragma unroll
+    for (int eb = 0; eb < 4; ++eb) {
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi[eb][ks], Bk[ks], a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo[eb][ks], Bk[ks], a, 0, 0, 0);
+      }
+      y[eb] = a;
+    }
+    // output token = t0 + tl (MFMA column), channels eb*16 + 4*grp + r
+    if (tok < t_end) {
+      u16* orow = out + tok * rs + h * D;
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb) {
+        uint2 w;
+        const u16 b0 = f2bf(y[eb][0] * inv + bp[eb * 4 + 0]);
+        const u16 b1 = f2bf(y[eb][1] * inv + bp[eb * 4 + 1]);
+        const u16 b2 = f2bf(y[eb][2] * inv + bp[eb * 4 + 2]);
+        const u16 b3 = f2bf(y[eb][3] * inv + bp[eb * 4 + 3]);
+        w.x = (unsigned)b0 | ((unsigned)b1 << 16);
+        w.y = (unsigned)b2 | ((unsigned)b3 << 16);
+        *(uint2*)(orow + eb * 16 + 4 * grp) = w;
+      }
+    }
+  }
+}
+
+int linear_chunks(const Geom& g) { return (int)((g.N + LIN_TOKENS_PER_WG - 1) / LIN_TOKENS_PER_WG); }
+
+size_t linear_workspace_bytes(const Geom& g) {
+  const size_t parts = (size_t)g.H * linear_chunks(g) * LIN_WAVES * (D * D + D) * sizeof(float);
+  const size_t red = (size_t)g.H * (2 * D * D * sizeof(u16) + 2 * D * sizeof(float));
+  return parts + red;
+}
+
+// Workspace: partials, then Sp [H][2][64][64] bf16, then zb [H][2][64] fp32.
+hipError_t launch_linear(const Geom& g, float eps, float base, const u16* Q, const u16* K,
+                         const u16* V, const float* W, const float* b, const float* mu,
+                         const float* gq, const float* gk, u16* out, void* ws, hipStream_t s) {
+  const int nch = linear_chunks(g);
+  float* parts = (float*)ws;
+  u16* sp = (u16*)(parts + (size_t)g.H * nch * LIN_WAVES * (D * D + D));
+  float* zb = (float*)(sp + (size_t)g.H * 2 * D * D);
+  LinParams P{eps, base};
+  hipLaunchKernelGGL(linear_state_kernel, dim3(nch, g.H), dim3(LIN_THREADS), 0, s, g, P, K, V, gk,
+                     parts, nch);
+  hipLaunchKernelGGL(linear_reduce_kernel, dim3(g.H), dim3(256), 0, s, g, parts, nch * LIN_WAVES,
+                     W, b, mu, sp, zb);
+  hipLaunchKernelGGL(linear_apply_kernel, dim3(nch, g.H), dim3(LIN_THREADS), 0, s, g, P, Q, gq, sp,
+                     zb, out);
+  return hipGetLastError();
+}
+
+}  // namespace zebra

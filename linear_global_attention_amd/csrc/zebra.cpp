@@ -1,0 +1,305 @@
+// libzebra host side: argument validation, tile geometry, buffer sizing and
+// kernel launches behind the C ABI declared in include/zebra.h.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/zebra.h"
+#include "common.hpp"
+
+namespace zebra {
+hipError_t launch_pack(const Geom&, const u16*, const u16*, u16*, u16*, u16*, u16*, hipStream_t);
+hipError_t launch_landmarks(const Geom&, const u16*, const u16*, double*, float*, float*, u16*,
+                            hipStream_t);
+size_t select_workspace_bytes(const Geom&);
+hipError_t launch_select(const Geom&, int, const u16*, const double*, int*, unsigned*, double*,
+                         void*, hipStream_t);
+hipError_t launch_attn(const Geom&, const AttnArgs&, hipStream_t);
+size_t linear_workspace_bytes(const Geom&);
+hipError_t launch_linear(const Geom&, float, float, const u16*, const u16*, const u16*,
+                         const float*, const float*, const float*, const float*, const float*,
+                         u16*, void*, hipStream_t);
+}  // namespace zebra
+
+using namespace zebra;
+
+namespace {
+
+thread_local std::string g_err;
+
+zebra_status fail(zebra_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+// Fills g from L; returns ZEBRA_OK or an error (message set).
+zebra_status make_geom(const zebra_layout* L, Geom& g) {
+  if (!L) return fail(ZEBRA_ERR_INVALID_ARG, "layout is NULL");
+  if (L->head_dim != D) return fail(ZEBRA_ERR_UNSUPPORTED, "head_dim must be 64");
+  if (L->frames < 1 || L->heads < 1 || L->specials < 0 || L->rows < 1 || L->cols < 1)
+    return fail(ZEBRA_ERR_INVALID_ARG, "frames, heads, rows, cols must be >= 1, specials >= 0");
+  if (L->rows > MAX_GRID || L->cols > MAX_GRID)
+    return fail(ZEBRA_ERR_UNSUPPORTED, "patch grid larger than 128 x 128");
+  if (L->heads > 65535) return fail(ZEBRA_ERR_UNSUPPORTED, "more than 65535 heads");
+  memset(&g, 0, sizeof(g));
+  g.F = L->frames;
+  g.S = L->specials;
+  g.R = L->rows;
+  g.C = L->cols;
+  g.H = L->heads;
+  g.tr = (g.R + TILE - 1) / TILE;
+  g.tc = (g.C + TILE - 1) / TILE;
+  g.tpf = g.tr * g.tc;
+  const long long T = (long long)g.F * g.tpf;
+  g.tok_pf = g.S + g.R * g.C;
+  g.N = (long long)g.F * g.tok_pf;
+  if (T > (1LL << 30) || g.N > (1LL << 40))
+    return fail(ZEBRA_ERR_UNSUPPORTED, "sequence too long");
+  g.T = (int)T;
+  int off = 0;
+  for (int a = 0; a < g.tr; ++a)
+    for (int b = 0; b < g.tc; ++b) {
+      const int tl = a * g.tc + b;
+      const int th = (g.R - TILE * a) < TILE ? (g.R - TILE * a) : TILE;
+      const int tw = (g.C - TILE * b) < TILE ? (g.C - TILE * b) : TILE;
+      g.th[tl] = (unsigned char)th;
+      g.tw[tl] = (unsigned char)tw;
+      g.slot_off[tl] = off;
+      off += pad32(th * tw);
+    }
+  g.slots_pf = off;
+  g.slots = (long long)g.F * g.slots_pf;
+  const long long nspec = (long long)g.F * g.S;
+  if (nspec > (1LL << 30)) return fail(ZEBRA_ERR_UNSUPPORTED, "too many special tokens");
+  g.nspec = (int)nspec;
+  g.spec_pad = pad32(g.nspec);
+  g.T_pad = pad32(g.T);
+  return ZEBRA_OK;
+}
+
+int64_t keep_count(const Geom& g, double y) {
+  if (!(y >= 0.0 && y <= 1.0)) return -1;
+  double k = nearbyint((1.0 - y) * (double)g.T);  // round half to even (default mode)
+  if (k < 0) k = 0;
+  if (k > g.T) k = g.T;
+  return (int64_t)k;
+}
+
+size_t buf_bytes(const Geom& g, int64_t k, int which) {
+  const size_t H = (size_t)g.H, T = (size_t)g.T;
+  switch (which) {
+    case ZEBRA_BUF_KT:
+    case ZEBRA_BUF_VT: return H * (size_t)g.slots * D * sizeof(u16);
+    case ZEBRA_BUF_KS:
+    case ZEBRA_BUF_VS: return H * (size_t)(g.spec_pad ? g.spec_pad : KBLK) * D * sizeof(u16);
+    case ZEBRA_BUF_KBAR: return H * T * D * sizeof(double);
+    case ZEBRA_BUF_VBAR: return H * T * D * sizeof(float);
+    case ZEBRA_BUF_LOGN: return T * sizeof(float);
+    case ZEBRA_BUF_LM: return H * 3 * (size_t)g.T_pad * D * sizeof(u16);
+    case ZEBRA_BUF_SEL: return H * T * (size_t)(k > 0 ? k : 1) * sizeof(int32_t);
+    case ZEBRA_BUF_SELMASK: return H * T * ((T + 31) / 32) * sizeof(uint32_t);
+    case ZEBRA_BUF_GAP: return H * T * sizeof(double);
+    case ZEBRA_BUF_WORKSPACE: {
+      const size_t a = select_workspace_bytes(g), b = linear_workspace_bytes(g);
+      return a > b ? a : b;
+    }
+    default: return 0;
+  }
+}
+
+zebra_status check_common(const zebra_args* a, Geom& g) {
+  if (!a) return fail(ZEBRA_ERR_INVALID_ARG, "args is NULL");
+  return make_geom(&a->L, g);
+}
+
+#define NEED(ptr, name) \
+  if (!(ptr)) return fail(ZEBRA_ERR_INVALID_ARG, std::string(name) + " is NULL")
+
+zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
+  zebra_status s = check_common(a, g);
+  if (s != ZEBRA_OK) return s;
+  k = keep_count(g, a->y);
+  switch (op) {
+    case ZEBRA_OP_PACK:
+      NEED(a->k, "k");
+      NEED(a->v, "v");
+      NEED(a->kt, "kt");
+      NEED(a->vt, "vt");
+      NEED(a->ks, "ks");
+      NEED(a->vs, "vs");
+      break;
+    case ZEBRA_OP_LANDMARKS:
+      NEED(a->kt, "kt");
+      NEED(a->vt, "vt");
+      NEED(a->kbar, "kbar");
+      NEED(a->vbar, "vbar");
+      NEED(a->logn, "logn");
+      NEED(a->lm, "lm");
+      break;
+    case ZEBRA_OP_SELECT:
+      if (k < 0) return fail(ZEBRA_ERR_INVALID_ARG, "y must lie in [0, 1]");
+      if (g.T > 32768) return fail(ZEBRA_ERR_UNSUPPORTED, "selection supports at most 32768 tiles");
+      NEED(a->q, "q");
+      NEED(a->kbar, "kbar");
+      NEED(a->sel, "sel");
+      NEED(a->selmask, "selmask");
+      NEED(a->workspace, "workspace");
+      if (a->workspace_bytes < select_workspace_bytes(g))
+        return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_select_tiles");
+      break;
+    case ZEBRA_OP_SPARSE:
+      if (k < 0) return fail(ZEBRA_ERR_INVALID_ARG, "y must lie in [0, 1]");
+      NEED(a->q, "q");
+      NEED(a->out, "out");
+      NEED(a->kt, "kt");
+      NEED(a->vt, "vt");
+      NEED(a->ks, "ks");
+      NEED(a->vs, "vs");
+      NEED(a->lm, "lm");
+      NEED(a->logn, "logn");
+      NEED(a->selmask, "selmask");
+      break;
+    case ZEBRA_OP_LINEAR:
+      NEED(a->q, "q");
+      NEED(a->k, "k");
+      NEED(a->v, "v");
+      NEED(a->out, "out");
+      NEED(a->workspace, "workspace");
+      if (a->workspace_bytes < linear_workspace_bytes(g))
+        return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_linear_attn");
+      if (a->mu && !a->W) {
+        /* allowed: W = I makes mu cancel */
+      }
+      break;
+    case ZEBRA_OP_DENSE:
+      NEED(a->q, "q");
+      NEED(a->k, "k");
+      NEED(a->v, "v");
+      NEED(a->out, "out");
+      NEED(a->kt, "kt");
+      NEED(a->vt, "vt");
+      NEED(a->ks, "ks");
+      NEED(a->vs, "vs");
+      break;
+    default:
+      return fail(ZEBRA_ERR_INVALID_ARG, "unknown operation");
+  }
+  g_err.clear();
+  return ZEBRA_OK;
+}
+
+zebra_status hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) {
+    char buf[256];
+    snprintf(buf, sizeof buf, "%s: %s", what, hipGetErrorString(e));
+    return fail(ZEBRA_ERR_HIP, buf);
+  }
+  return ZEBRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+zebra_status zebra_validate(const zebra_args* a, int op) {
+  Geom g;
+  int64_t k;
+  return validate(a, op, g, k);
+}
+
+size_t zebra_buffer_bytes(const zebra_layout* L, double y, int which) {
+  Geom g;
+  if (make_geom(L, g) != ZEBRA_OK) return 0;
+  const int64_t k = keep_count(g, y);
+  if (k < 0 && which == ZEBRA_BUF_SEL) return 0;
+  return buf_bytes(g, k, which);
+}
+
+int64_t zebra_keep_count(const zebra_layout* L, double y) {
+  Geom g;
+  if (make_geom(L, g) != ZEBRA_OK) return -1;
+  return keep_count(g, y);
+}
+
+int64_t zebra_num_tiles(const zebra_layout* L) {
+  Geom g;
+  if (make_geom(L, g) != ZEBRA_OK) return -1;
+  return g.T;
+}
+
+const char* zebra_last_error(void) { return g_err.c_str(); }
+
+const char* zebra_version(void) { return "zebra-mi355x 0.1 (gfx950)"; }
+
+zebra_status zebra_pack_tiles(const zebra_args* a, zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_PACK, g, k);
+  if (s != ZEBRA_OK) return s;
+  return hip_result(launch_pack(g, (const u16*)a->k, (const u16*)a->v, (u16*)a->kt, (u16*)a->vt,
+                                (u16*)a->ks, (u16*)a->vs, (hipStream_t)stream),
+                    "zebra_pack_tiles");
+}
+
+zebra_status zebra_landmarks(const zebra_args* a, zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_LANDMARKS, g, k);
+  if (s != ZEBRA_OK) return s;
+  return hip_result(launch_landmarks(g, (const u16*)a->kt, (const u16*)a->vt, a->kbar, a->vbar,
+                                     a->logn, (u16*)a->lm, (hipStream_t)stream),
+                    "zebra_landmarks");
+}
+
+zebra_status zebra_select_tiles(const zebra_args* a, zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_SELECT, g, k);
+  if (s != ZEBRA_OK) return s;
+  return hip_result(launch_select(g, (int)k, (const u16*)a->q, a->kbar, (int*)a->sel,
+                                  (unsigned*)a->selmask, a->gap, a->workspace,
+                                  (hipStream_t)stream),
+                    "zebra_select_tiles");
+}
+
+zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_SPARSE, g, k);
+  if (s != ZEBRA_OK) return s;
+  AttnArgs A{(const u16*)a->q, (u16*)a->out, (const u16*)a->kt, (const u16*)a->vt,
+             (const u16*)a->ks, (const u16*)a->vs, (const u16*)a->lm, a->logn,
+             (const unsigned*)a->selmask, (g.T + 31) / 32, 1};
+  return hip_result(launch_attn(g, A, (hipStream_t)stream), "zebra_sparse_attn");
+}
+
+zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_DENSE, g, k);
+  if (s != ZEBRA_OK) return s;
+  s = hip_result(launch_pack(g, (const u16*)a->k, (const u16*)a->v, (u16*)a->kt, (u16*)a->vt,
+                             (u16*)a->ks, (u16*)a->vs, (hipStream_t)stream),
+                 "zebra_dense_attn (pack)");
+  if (s != ZEBRA_OK) return s;
+  AttnArgs A{(const u16*)a->q, (u16*)a->out, (const u16*)a->kt, (const u16*)a->vt,
+             (const u16*)a->ks, (const u16*)a->vs, nullptr, nullptr, nullptr, (g.T + 31) / 32, 0};
+  return hip_result(launch_attn(g, A, (hipStream_t)stream), "zebra_dense_attn");
+}
+
+zebra_status zebra_linear_attn(const zebra_args* a, zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_LINEAR, g, k);
+  if (s != ZEBRA_OK) return s;
+  const float eps = a->rms_eps > 0.f ? a->rms_eps : 1e-6f;
+  const float base = a->rope_base > 0.f ? a->rope_base : 100.0f;
+  return hip_result(launch_linear(g, eps, base, (const u16*)a->q, (const u16*)a->k,
+                                  (const u16*)a->v, a->W, a->b, a->mu, a->gq, a->gk,
+                                  (u16*)a->out, a->workspace, (hipStream_t)stream),
+                    "zebra_linear_attn");
+}
+
+}  // extern "C"

@@ -1,0 +1,218 @@
+"""GPU parity of every hot-path entry point against the fp64 oracle, through
+the C ABI, on seeded synthetic inputs (tile-centroid model).
+
+Bars: packing, landmark means and tile selection bit-exact (selection except
+rows whose k-th/(k+1)-th score gap is below 1e-6 relative, which are
+counted and reported); attention outputs within max-abs 2e-2 and mean-abs
+2e-3 of the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import zebra_synth as zs
+from oracle import linear as olin
+from oracle import sparse as osp
+from oracle.layout import TileMap, keep_count
+
+from gpu_helpers import Stage, bf16_host, close, compare_selection, log, widen
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(L, seed=0, stage=0):
+    q, k, v = zs.stage_inputs(L, seed=seed, stage=stage)
+    return q, k, v
+
+
+def _sel_ref(Q, K, tm, y):
+    H = Q.shape[1]
+    sels, ties = [], []
+    for h in range(H):
+        kbar, _, _ = osp.landmarks(K[:, h], K[:, h], tm)
+        s, t, _ = osp.select_tiles(Q[:, h], kbar, tm, y)
+        sels.append(s)
+        ties.append(t)
+    return np.stack(sels), np.stack(ties)
+
+
+# ------------------------------------------------------------- small, full
+EDGE = [
+    ("c0", zs.CONFIGS["c0"], 0.5),
+    ("partial-no-specials", zs.Layout(3, 0, 11, 13, heads=2), 0.3),
+    ("partial-y0", zs.Layout(2, 3, 9, 17, heads=2), 0.0),
+    ("partial-y1", zs.Layout(2, 3, 9, 17, heads=2), 1.0),
+    ("one-tile", zs.Layout(1, 2, 8, 8, heads=1), 0.5),
+    ("one-small-tile", zs.Layout(1, 1, 3, 5, heads=1), 0.7),
+    ("vggt-2view", zs.Layout(2, 5, 37, 37, heads=2), 0.8),
+]
+
+
+@pytest.mark.parametrize("name,L,y", EDGE, ids=[e[0] for e in EDGE])
+def test_sparse_stage_full(name, L, y):
+    log(f"sparse full {name} {L} y={y}")
+    q, k, v = _inputs(L, seed=1)
+    Q, K, V = widen(q), widen(k), widen(v)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    st = Stage(L, q, k, v, y)
+    out = bf16_host(st.sparse()).reshape(L.tokens, L.heads, 64)
+    O_ref, sel_ref, tie_ref = osp.sparse_attention(Q, K, V, tm, y)
+    kk = keep_count(y, tm.T)
+    if kk > 0:
+        sel = st.bufs.sel().cpu().numpy()
+        compare_selection(sel, sel_ref, tie_ref, f"{name} selection")
+        # the bitmap agrees with the lists
+        mask = st.bufs.selmask().cpu().numpy().view(np.uint32)
+        for h in range(L.heads):
+            for t in range(tm.T):
+                bits = [u for u in range(tm.T) if (mask[h, t, u // 32] >> (u % 32)) & 1]
+                assert bits == sel[h, t].tolist()
+    close(out, O_ref, f"{name} sparse output")
+
+
+@pytest.mark.parametrize("name,L,y", EDGE[:3] + EDGE[4:5], ids=[e[0] for e in EDGE[:3] + EDGE[4:5]])
+def test_pack_and_landmarks_exact(name, L, y):
+    q, k, v = _inputs(L, seed=2)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    st = Stage(L, q, k, v, y)
+    st.sparse()
+    H = L.heads
+    kt = st.bufs.t["KT"].cpu().numpy().view(np.uint16)
+    vt = st.bufs.t["VT"].cpu().numpy().view(np.uint16)
+    slots = []
+    off = 0
+    for u in range(tm.T):
+        slots.append(off)
+        off += -(-int(tm.n[u]) // 32) * 32
+    kt = kt[: H * off * 64].reshape(H, off, 64)
+    vt = vt[: H * off * 64].reshape(H, off // 32, 64, 32)
+    for u in range(tm.T):
+        toks = tm.tokens[u]
+        s0 = slots[u]
+        n = len(toks)
+        assert np.array_equal(kt[:, s0:s0 + n, :], k[toks].transpose(1, 0, 2)), u
+        pad = -(-n // 32) * 32
+        assert not kt[:, s0 + n:s0 + pad].any()
+        for j, tok in enumerate(toks):
+            blk, col = (s0 + j) // 32, (s0 + j) % 32
+            assert np.array_equal(vt[:, blk, :, col], v[tok]), (u, j)
+    kbar = st.bufs.kbar().cpu().numpy()
+    for h in range(H):
+        kb, _, _ = osp.landmarks(widen(k)[:, h], widen(v)[:, h], tm)
+        assert np.array_equal(kbar[h], kb), h  # exact fp64 sums, one rounding
+
+
+def test_landmark_of_identical_tile_equals_tile():
+    L = zs.Layout(2, 2, 11, 9, heads=2)
+    q, k, v = _inputs(L, seed=3)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    for u in range(tm.T):
+        k[tm.tokens[u]] = k[tm.tokens[u][0]]
+        v[tm.tokens[u]] = v[tm.tokens[u][0]]
+    st = Stage(L, q, k, v, 0.5)
+    st.sparse()
+    kbar = st.bufs.kbar().cpu().numpy()
+    vbar = st.bufs.t["VBAR"][: L.heads * tm.T * 64 * 4].view(torch.float32).cpu().numpy()
+    vbar = vbar.reshape(L.heads, tm.T, 64)
+    for u in range(tm.T):
+        assert np.array_equal(kbar[:, u], widen(k[tm.tokens[u][0]]))
+        assert np.array_equal(vbar[:, u], widen(v[tm.tokens[u][0]]).astype(np.float32))
+
+
+@pytest.mark.parametrize("name,L", [("c0", zs.CONFIGS["c0"]), ("partial", zs.Layout(3, 2, 11, 13, heads=2)),
+                                    ("vggt-2view", zs.Layout(2, 5, 37, 37, heads=2))])
+def test_dense_full(name, L):
+    q, k, v = _inputs(L, seed=4)
+    st = Stage(L, q, k, v, 0.0)
+    out = bf16_host(st.dense()).reshape(L.tokens, L.heads, 64)
+    ref = osp.dense_attention(widen(q), widen(k), widen(v))
+    close(out, ref, f"{name} dense")
+
+
+def test_y0_sparse_equals_dense_on_gpu():
+    L = zs.Layout(2, 5, 16, 24, heads=2)
+    q, k, v = _inputs(L, seed=5)
+    st = Stage(L, q, k, v, 0.0)
+    a = bf16_host(st.sparse())
+    b = bf16_host(st.dense())
+    close(a, b, "y=0 sparse vs dense (GPU)")
+
+
+LIN = [("c0-identity", zs.CONFIGS["c0"], False),
+       ("partial-affine", zs.Layout(3, 2, 11, 13, heads=2), True),
+       ("vggt-2view-affine", zs.Layout(2, 5, 37, 37, heads=3), True)]
+
+
+@pytest.mark.parametrize("name,L,affine", LIN, ids=[x[0] for x in LIN])
+def test_linear_full(name, L, affine):
+    q, k, v = _inputs(L, seed=6)
+    Q, K, V = widen(q), widen(k), widen(v)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    W = b = mu = None
+    if affine:
+        W, b = zs.affine_params(L, seed=6)
+        mu = np.stack([olin.mean_output(Q[:, h], K[:, h], V[:, h], tm)
+                       for h in range(L.heads)]).astype(np.float32)
+    st = Stage(L, q, k, v, 0.0, sparse=False)
+    out = bf16_host(st.linear(W, b, mu)).reshape(L.tokens, L.heads, 64)
+    ref = olin.linear_attention(Q, K, V, tm, W, b, mu)
+    close(out, ref, f"{name} linear")
+
+
+# ------------------------------------------------------------- 32 views
+def test_c1_sparse_selection_and_rows():
+    L = zs.CONFIGS["c1"]
+    y = 0.8
+    log("c1: drawing inputs")
+    q, k, v = _inputs(L, seed=0)
+    Q, K, V = widen(q), widen(k), widen(v)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    st = Stage(L, q, k, v, y)
+    log("c1: GPU sparse stage")
+    st.sparse()
+    sel = st.bufs.sel().cpu().numpy()
+    sel_ref, tie_ref = _sel_ref(Q, K, tm, y)
+    compare_selection(sel, sel_ref, tie_ref, "c1 selection (all 16x800 query tiles)")
+    # every row of 40 seeded (head, query tile) pairs plus all special rows of 2 heads
+    g = np.random.default_rng(0)
+    rows = []
+    for h, t in zip(g.integers(0, 16, 40), g.integers(0, tm.T, 40)):
+        rows += [(int(h), int(tok)) for tok in tm.tokens[t]]
+    rows += [(h, int(s)) for h in (0, 9) for s in tm.specials]
+    rows = np.array(sorted(set(rows)), dtype=np.int64)
+    log(f"c1: oracle on {len(rows)} rows")
+    ref, _ = osp.sparse_rows(Q, K, V, tm, y, rows)
+    close(st.rows(rows), ref, "c1 sparse rows")
+
+
+def test_c1_dense_and_linear_rows():
+    L = zs.CONFIGS["c1"]
+    q, k, v = _inputs(L, seed=0)
+    Q, K, V = widen(q), widen(k), widen(v)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    rows = zs.sample_rows(L, 512, seed=0, special_frames=2)
+    st = Stage(L, q, k, v, 0.0)
+    st.dense()
+    ref = np.stack([osp.dense_rows(Q[:, h], K[:, h], V[:, h], [t])[0] for h, t in rows])
+    close(st.rows(rows), ref, "c1 dense rows")
+    W, b = zs.affine_params(L, seed=0)
+    mu = (0.01 * np.random.default_rng(1).standard_normal((L.heads, 64))).astype(np.float32)
+    st.linear(W, b, mu)
+    ref = olin.linear_rows(Q, K, V, tm, rows, W, b, mu)
+    close(st.rows(rows), ref, "c1 linear rows")
+
+
+def test_c2_linear_full():
+    L = zs.CONFIGS["c2"]
+    log("c2: drawing inputs")
+    q, k, v = _inputs(L, seed=0)
+    Q, K, V = widen(q), widen(k), widen(v)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    W, b = zs.affine_params(L, seed=0)
+    log("c2: oracle mean output")
+    mu = np.stack([olin.mean_output(Q[:, h], K[:, h], V[:, h], tm)
+                   for h in range(L.heads)]).astype(np.float32)
+    st = Stage(L, q, k, v, 0.0, sparse=False)
+    out = bf16_host(st.linear(W, b, mu)).reshape(L.tokens, L.heads, 64)
+    log("c2: oracle linear stage")
+    ref = olin.linear_attention(Q, K, V, tm, W, b, mu)
+    close(out, ref, "c2 linear (all 175,872 x 16 rows)")

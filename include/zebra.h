@@ -139,8 +139,8 @@ zebra_status zebra_pack_tiles(const zebra_args* a, zebra_stream stream);
 /* Mean key/value landmark of every tile ("Linear-centered stages plus
  * tile-sparse stages": omitted tiles are summarised as mean key/value
  * landmarks). Reads kt, vt; writes kbar (exact fp64 mean of the bf16 keys),
- * vbar, logn = ln n_u and lm (the landmark keys split into bf16 high and low
- * parts and the values in bf16, in the attention kernel's layout). */
+ * vbar, logn = ln n_u and lm (landmark keys and values rounded to bf16, in
+ * the attention kernel's layout). */
 zebra_status zebra_landmarks(const zebra_args* a, zebra_stream stream);
 
 /* Tile selector ("Linear-centered stages plus tile-sparse stages": keep a
@@ -156,7 +156,9 @@ zebra_status zebra_select_tiles(const zebra_args* a, zebra_stream stream);
  * of every kept tile, the landmark of every omitted tile (logit
  * q.kbar_u/8 + ln n_u, value vbar_u), every special key, and its own key
  * when tile t itself is not kept. Special rows: dense over all N keys.
- * Reads q, kt, vt, ks, vs, lm, logn, selmask; writes out. */
+ * Reads q, kt, vt, ks, vs, lm, logn, selmask; writes out. Uses the workspace
+ * (one flag per work item: rows whose cheap logit bound is too loose are
+ * recomputed with an exact online softmax). */
 zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream);
 
 /* Linear attention with the centred affine correction. For each head:
@@ -170,7 +172,8 @@ zebra_status zebra_linear_attn(const zebra_args* a, zebra_stream stream);
 
 /* Dense softmax attention of every token over all N keys ("Global attention
  * dominates runtime as views grow"): the measurement baseline. Reads q, k,
- * v; writes kt, vt, ks, vs (it packs first) and out. */
+ * v; writes kt, vt, ks, vs, kbar, vbar, logn, lm (it packs and builds the
+ * per-tile key bounds first) and out; uses the workspace. */
 zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream);
 
 /* Host-only argument check of operation `op` (ZEBRA_OP_*); no GPU call. */

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzebra.so")
-SOURCES = ["zebra.cpp", "pack.hip", "select.hip", "attn.hip", "linear.hip"]
+SOURCES = ["zebra.cpp", "pack.hip", "select.hip", "attn.hip", "attn_exact.hip", "linear.hip"]
 ARCH = os.environ.get("ZEBRA_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

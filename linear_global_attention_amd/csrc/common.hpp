@@ -13,6 +13,10 @@ constexpr int TILE = 8;        // 8x8 patches per complete tile
 constexpr int MAX_GRID = 128;  // R, C <= 128
 constexpr int MAX_TPF = (MAX_GRID / TILE) * (MAX_GRID / TILE);  // tiles per frame
 constexpr int KBLK = 32;       // key-slot granularity of the packed layouts
+constexpr int LM_KEY_BLOCK = 8192;                      // bytes per landmark key block
+constexpr int LM_LOG2N_ROW = 32;                        // row of log2(n_u) in a key block
+constexpr int LM_RADIUS_ROW = 40;                       // row of the key radii r_u
+constexpr int LM_BYTES_PER_TILE = (LM_KEY_BLOCK + KBLK * D * 2) / KBLK;  // 384
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -24,7 +28,7 @@ typedef unsigned short u16;
 //   special s of frame f     = f*tok_pf + s
 //   tile u = f*tpf + a*tc + b, patch rows [8a, 8a+th), cols [8b, 8b+tw)
 // Packed key/value slots: tile (f, tl) starts at slot f*slots_pf +
-// slot_off[tl] and owns pad32(n) slots (n = th*tw real tokens, rest zero).
+// tile_off(tl) and owns pad32(n) slots (n = th*tw real tokens, rest zero).
 struct Geom {
   int F, S, R, C, H;
   int tr, tc, tpf;     // tile rows/cols per frame, tiles per frame
@@ -36,18 +40,30 @@ struct Geom {
   int nspec;           // F*S special tokens
   int spec_pad;        // nspec rounded up to KBLK
   int T_pad;           // T rounded up to KBLK
-  int slot_off[MAX_TPF];
-  unsigned char th[MAX_TPF];
-  unsigned char tw[MAX_TPF];
+  // per tile of a frame: bits 0..19 first packed slot (within the frame),
+  // bits 20..23 patch rows th, bits 24..27 patch columns tw. One 32-bit word
+  // per tile so that uniform lookups are scalar loads.
+  int tile[MAX_TPF];
 };
+
+__host__ __device__ inline int tile_off(const Geom& g, int tl) { return g.tile[tl] & 0xFFFFF; }
+__host__ __device__ inline int tile_h(const Geom& g, int tl) { return (g.tile[tl] >> 20) & 15; }
+__host__ __device__ inline int tile_w(const Geom& g, int tl) { return (g.tile[tl] >> 24) & 15; }
+__host__ __device__ inline int tile_n(const Geom& g, int tl) { return tile_h(g, tl) * tile_w(g, tl); }
 
 // Buffer layouts (element counts are per head unless stated):
 //   Kt  bf16 [H][slots][64]                    key of slot s, row-major
-//   Vt  bf16 [H][slots/32][64][32]             value, d-major per 32 slots
+//   Vt  bf16 [H][slots/32][64][32]             value, d-major per 32 slots,
+//                                              key k of a block at position
+//                                              value_pos(k) (see below)
 //   Ks  bf16 [H][spec_pad][64]
 //   Vs  bf16 [H][spec_pad/32][64][32]
-//   LM  bf16 [H][3][T_pad*64]: kbar high part [T_pad][64], kbar low part
-//       [T_pad][64] (kbar - high, rounded), vbar [T_pad/32][64][32]
+//   LM  per head: T_pad/32 landmark key blocks of LM_KEY_BLOCK bytes (rows
+//       0..31: kbar of the block's tiles, bf16 [32][64]; row 32: 32 fp32
+//       log2(n_u), -inf past the last tile; row 40: 32 fp32 key radii r_u,
+//       an upper bound of |k_j - kbar_u| over the tile's keys that also
+//       covers the bf16 rounding of kbar; other rows zero), then T_pad/32
+//       value blocks [64][32] bf16 of vbar (keys permuted by value_pos)
 
 // Arguments of the attention kernel (tile-sparse or dense).
 struct AttnArgs {
@@ -63,6 +79,13 @@ struct AttnArgs {
   int nwords;               // ceil(T/32)
   int sparse;               // 1: landmarks + self key for patch groups
 };
+
+// Position of key k (0..31) inside a 32-key value block: the 8 keys
+// {4g..4g+3, 16+4g..16+4g+3} of lane group g are contiguous, matching the
+// k-slot order of the probabilities fed to the P.V MFMA.
+__host__ __device__ inline int value_pos(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
+// Inverse of value_pos.
+__host__ __device__ inline int value_key(int p) { return ((p & 7) >> 2) * 16 + (p >> 3) * 4 + (p & 3); }
 
 __host__ __device__ inline int pad32(int n) { return (n + KBLK - 1) / KBLK * KBLK; }
 

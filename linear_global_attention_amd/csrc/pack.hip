@@ -8,14 +8,15 @@
 // Both kernels are pure HBM streams: one workgroup per (tile or 32 special
 // tokens, head). Keys keep their row-major [slot][64] layout so the attention
 // kernel reads 16-byte key fragments; values are transposed per 32-slot block
-// to [64][32] so the attention kernel reads 8-byte runs of consecutive keys.
+// to [64][32] with the keys of a block permuted (value_pos) so the attention
+// kernel reads each lane's 8 keys of a channel as one 16-byte run.
 #include "common.hpp"
 
 namespace zebra {
 
 __device__ inline long long tile_token(const Geom& g, int f, int tl, int s) {
   const int a = tl / g.tc, b = tl - a * g.tc;
-  const int tw = g.tw[tl];
+  const int tw = tile_w(g, tl);
   const int r = TILE * a + s / tw, c = TILE * b + s % tw;
   return (long long)f * g.tok_pf + g.S + (long long)r * g.C + c;
 }
@@ -40,9 +41,9 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
     const int u = blockIdx.x;
     f = u / g.tpf;
     tl = u - f * g.tpf;
-    nreal = g.th[tl] * g.tw[tl];
+    nreal = tile_n(g, tl);
     nslots = pad32(nreal);
-    base_slot = (long long)f * g.slots_pf + g.slot_off[tl];
+    base_slot = (long long)f * g.slots_pf + tile_off(g, tl);
     Kdst = Kt + (long long)h * g.slots * D;
     Vdst = Vt + (long long)h * g.slots * D;
   } else {
@@ -77,7 +78,7 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
       const int d = tid >> 2, k0 = (tid & 3) * 8;
       u16 w[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = vstage[k0 + i][d];
+      for (int i = 0; i < 8; ++i) w[i] = vstage[value_key(k0 + i)][d];
       const long long vblk = (base_slot / KBLK) + blk;
       *(uint4*)(Vdst + (vblk * D + d) * KBLK + k0) = *(const uint4*)w;
     }
@@ -85,45 +86,69 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
   }
 }
 
-// grid (T_pad, H), block 64 (thread = channel).
+// grid (T_pad, H), block 64 (thread = channel). Also writes, per tile, a
+// key radius r_u >= max_j |k_j - kbar_u| (per-channel max deviations, their
+// Euclidean norm, inflated to also cover the bf16 rounding of kbar), which
+// the attention kernel uses to bound the logits of the tile's keys.
 __global__ void __launch_bounds__(64) landmark_kernel(Geom g, const u16* __restrict__ Kt,
                                                       const u16* __restrict__ Vt,
                                                       double* __restrict__ kbar,
                                                       float* __restrict__ vbar,
                                                       float* __restrict__ logn,
-                                                      u16* __restrict__ LM) {
+                                                      char* __restrict__ LM) {
   const int u = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-  u16* lmk_hi = LM + (long long)h * 3 * g.T_pad * D;
-  u16* lmk_lo = lmk_hi + (long long)g.T_pad * D;
-  u16* lmv = lmk_lo + (long long)g.T_pad * D;
-  const long long vpos = ((long long)(u / KBLK) * D + d) * KBLK + (u % KBLK);
-  if (u >= g.T) {  // padding landmarks: zero key and value
-    lmk_hi[(long long)u * D + d] = 0;
-    lmk_lo[(long long)u * D + d] = 0;
-    lmv[vpos] = 0;
+  const int lb = u / KBLK, r = u % KBLK;
+  char* lmh = LM + (long long)h * g.T_pad * LM_BYTES_PER_TILE;
+  char* kblk = lmh + (long long)lb * LM_KEY_BLOCK;
+  u16* krow = (u16*)(kblk + r * D * 2);
+  float* log2n_row = (float*)(kblk + LM_LOG2N_ROW * D * 2);
+  float* rad_row = (float*)(kblk + LM_RADIUS_ROW * D * 2);
+  u16* vblk = (u16*)(lmh + (long long)(g.T_pad / KBLK) * LM_KEY_BLOCK + (long long)lb * KBLK * D * 2);
+  // rows 32..63 beyond the two table rows are zero
+  if (r < KBLK && KBLK + r != LM_LOG2N_ROW && KBLK + r != LM_RADIUS_ROW)
+    ((u16*)(kblk + (KBLK + r) * D * 2))[d] = 0;
+  if (u >= g.T) {  // padding landmarks: zero key and value, log2 n = -inf
+    krow[d] = 0;
+    vblk[d * KBLK + value_pos(r)] = 0;
+    if (d == 0) {
+      log2n_row[r] = -INFINITY;
+      rad_row[r] = 0.f;
+    }
     return;
   }
   const int f = u / g.tpf, tl = u - f * g.tpf;
-  const int n = g.th[tl] * g.tw[tl];
-  const long long base = (long long)f * g.slots_pf + g.slot_off[tl];
+  const int n = tile_n(g, tl);
+  const long long base = (long long)f * g.slots_pf + tile_off(g, tl);
   const u16* kp = Kt + ((long long)h * g.slots + base) * D + d;
   const u16* vp = Vt + (long long)h * g.slots * D;
   double sk = 0.0, sv = 0.0;  // exact: sums of <= 64 bf16 values
   for (int s = 0; s < n; ++s) {
     sk += (double)bf2f(kp[(long long)s * D]);
     const long long vb = base / KBLK + s / KBLK;
-    sv += (double)bf2f(vp[(vb * D + d) * KBLK + (s % KBLK)]);
+    sv += (double)bf2f(vp[(vb * D + d) * KBLK + value_pos(s % KBLK)]);
   }
   const double mk = sk / n;
   const float mv = (float)(sv / n);
   kbar[((long long)h * g.T + u) * D + d] = mk;
   vbar[((long long)h * g.T + u) * D + d] = mv;
-  const float hi = (float)mk;
-  const u16 hb = f2bf(hi);
-  const u16 lb = f2bf((float)(mk - (double)bf2f(hb)));
-  lmk_hi[(long long)u * D + d] = hb;
-  lmk_lo[(long long)u * D + d] = lb;
-  lmv[vpos] = f2bf(mv);
+  const u16 kb16 = f2bf((float)mk);
+  krow[d] = kb16;
+  vblk[d * KBLK + value_pos(r)] = f2bf(mv);
+  // radius about the bf16-rounded mean the attention kernel uses
+  const double kq = (double)bf2f(kb16);
+  double dev = 0.0;
+  for (int s = 0; s < n; ++s) dev = fmax(dev, fabs((double)bf2f(kp[(long long)s * D]) - kq));
+  __shared__ double red[64];
+  red[d] = dev * dev;
+  __syncthreads();
+  for (int o = 32; o > 0; o >>= 1) {
+    if (d < o) red[d] += red[d + o];
+    __syncthreads();
+  }
+  if (d == 0) {
+    log2n_row[r] = log2f((float)n);
+    rad_row[r] = (float)(sqrt(red[0]) * 1.0001 + 1e-6);
+  }
   if (h == 0 && d == 0) logn[u] = logf((float)n);
 }
 
@@ -137,7 +162,7 @@ hipError_t launch_pack(const Geom& g, const u16* K, const u16* V, u16* Kt, u16* 
 hipError_t launch_landmarks(const Geom& g, const u16* Kt, const u16* Vt, double* kbar,
                             float* vbar, float* logn, u16* LM, hipStream_t s) {
   hipLaunchKernelGGL(landmark_kernel, dim3(g.T_pad, g.H), dim3(64), 0, s, g, Kt, Vt, kbar, vbar,
-                     logn, LM);
+                     logn, (char*)LM);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ namespace zebra {
 
 __device__ inline long long tile_token_s(const Geom& g, int f, int tl, int s) {
   const int a = tl / g.tc, b = tl - a * g.tc;
-  const int tw = g.tw[tl];
+  const int tw = tile_w(g, tl);
   const int r = TILE * a + s / tw, c = TILE * b + s % tw;
   return (long long)f * g.tok_pf + g.S + (long long)r * g.C + c;
 }
@@ -28,7 +28,7 @@ __global__ void __launch_bounds__(64) qbar_kernel(Geom g, const u16* __restrict_
                                                   double* __restrict__ qbar) {
   const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
   const int f = t / g.tpf, tl = t - f * g.tpf;
-  const int n = g.th[tl] * g.tw[tl];
+  const int n = tile_n(g, tl);
   double s = 0.0;
   for (int i = 0; i < n; ++i) {
     const long long tok = tile_token_s(g, f, tl, i);

@@ -16,7 +16,8 @@ hipError_t launch_landmarks(const Geom&, const u16*, const u16*, double*, float*
 size_t select_workspace_bytes(const Geom&);
 hipError_t launch_select(const Geom&, int, const u16*, const double*, int*, unsigned*, double*,
                          void*, hipStream_t);
-hipError_t launch_attn(const Geom&, const AttnArgs&, hipStream_t);
+hipError_t launch_attn(const Geom&, const AttnArgs&, int*, hipStream_t);
+size_t attn_flag_bytes(const Geom&);
 size_t linear_workspace_bytes(const Geom&);
 hipError_t launch_linear(const Geom&, float, float, const u16*, const u16*, const u16*,
                          const float*, const float*, const float*, const float*, const float*,
@@ -64,9 +65,7 @@ zebra_status make_geom(const zebra_layout* L, Geom& g) {
       const int tl = a * g.tc + b;
       const int th = (g.R - TILE * a) < TILE ? (g.R - TILE * a) : TILE;
       const int tw = (g.C - TILE * b) < TILE ? (g.C - TILE * b) : TILE;
-      g.th[tl] = (unsigned char)th;
-      g.tw[tl] = (unsigned char)tw;
-      g.slot_off[tl] = off;
+      g.tile[tl] = off | (th << 20) | (tw << 24);
       off += pad32(th * tw);
     }
   g.slots_pf = off;
@@ -97,13 +96,16 @@ size_t buf_bytes(const Geom& g, int64_t k, int which) {
     case ZEBRA_BUF_KBAR: return H * T * D * sizeof(double);
     case ZEBRA_BUF_VBAR: return H * T * D * sizeof(float);
     case ZEBRA_BUF_LOGN: return T * sizeof(float);
-    case ZEBRA_BUF_LM: return H * 3 * (size_t)g.T_pad * D * sizeof(u16);
+    case ZEBRA_BUF_LM: return H * (size_t)g.T_pad * LM_BYTES_PER_TILE;
     case ZEBRA_BUF_SEL: return H * T * (size_t)(k > 0 ? k : 1) * sizeof(int32_t);
     case ZEBRA_BUF_SELMASK: return H * T * ((T + 31) / 32) * sizeof(uint32_t);
     case ZEBRA_BUF_GAP: return H * T * sizeof(double);
     case ZEBRA_BUF_WORKSPACE: {
-      const size_t a = select_workspace_bytes(g), b = linear_workspace_bytes(g);
-      return a > b ? a : b;
+      size_t m = select_workspace_bytes(g);
+      const size_t b = linear_workspace_bytes(g), c = attn_flag_bytes(g);
+      if (b > m) m = b;
+      if (c > m) m = c;
+      return m;
     }
     default: return 0;
   }
@@ -160,6 +162,9 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
       NEED(a->lm, "lm");
       NEED(a->logn, "logn");
       NEED(a->selmask, "selmask");
+      NEED(a->workspace, "workspace");
+      if (a->workspace_bytes < attn_flag_bytes(g))
+        return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_sparse_attn");
       break;
     case ZEBRA_OP_LINEAR:
       NEED(a->q, "q");
@@ -182,6 +187,13 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
       NEED(a->vt, "vt");
       NEED(a->ks, "ks");
       NEED(a->vs, "vs");
+      NEED(a->kbar, "kbar");
+      NEED(a->vbar, "vbar");
+      NEED(a->logn, "logn");
+      NEED(a->lm, "lm");
+      NEED(a->workspace, "workspace");
+      if (a->workspace_bytes < attn_flag_bytes(g))
+        return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_dense_attn");
       break;
     default:
       return fail(ZEBRA_ERR_INVALID_ARG, "unknown operation");
@@ -272,7 +284,7 @@ zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream) {
   AttnArgs A{(const u16*)a->q, (u16*)a->out, (const u16*)a->kt, (const u16*)a->vt,
              (const u16*)a->ks, (const u16*)a->vs, (const u16*)a->lm, a->logn,
              (const unsigned*)a->selmask, (g.T + 31) / 32, 1};
-  return hip_result(launch_attn(g, A, (hipStream_t)stream), "zebra_sparse_attn");
+  return hip_result(launch_attn(g, A, (int*)a->workspace, (hipStream_t)stream), "zebra_sparse_attn");
 }
 
 zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream) {
@@ -284,9 +296,14 @@ zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream) {
                              (u16*)a->ks, (u16*)a->vs, (hipStream_t)stream),
                  "zebra_dense_attn (pack)");
   if (s != ZEBRA_OK) return s;
+  s = hip_result(launch_landmarks(g, (const u16*)a->kt, (const u16*)a->vt, a->kbar, a->vbar, a->logn,
+                                  (u16*)a->lm, (hipStream_t)stream),
+                 "zebra_dense_attn (landmarks)");
+  if (s != ZEBRA_OK) return s;
   AttnArgs A{(const u16*)a->q, (u16*)a->out, (const u16*)a->kt, (const u16*)a->vt,
-             (const u16*)a->ks, (const u16*)a->vs, nullptr, nullptr, nullptr, (g.T + 31) / 32, 0};
-  return hip_result(launch_attn(g, A, (hipStream_t)stream), "zebra_dense_attn");
+             (const u16*)a->ks, (const u16*)a->vs, (const u16*)a->lm, a->logn, (const unsigned*)nullptr,
+             (g.T + 31) / 32, 0};
+  return hip_result(launch_attn(g, A, (int*)a->workspace, (hipStream_t)stream), "zebra_dense_attn");
 }
 
 zebra_status zebra_linear_attn(const zebra_args* a, zebra_stream stream) {

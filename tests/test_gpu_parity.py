@@ -93,7 +93,8 @@ def test_pack_and_landmarks_exact(name, L, y):
         pad = -(-n // 32) * 32
         assert not kt[:, s0 + n:s0 + pad].any()
         for j, tok in enumerate(toks):
-            blk, col = (s0 + j) // 32, (s0 + j) % 32
+            blk, kk = (s0 + j) // 32, (s0 + j) % 32
+            col = ((kk & 15) >> 2) * 8 + (kk >> 4) * 4 + (kk & 3)  # keys permuted per block
             assert np.array_equal(vt[:, blk, :, col], v[tok]), (u, j)
     kbar = st.bufs.kbar().cpu().numpy()
     for h in range(H):

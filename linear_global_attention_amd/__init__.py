@@ -64,6 +64,11 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m linear_global_attention_amd.build`")
+    # One HIP runtime per process: the torch wheel bundles its own
+    # libamdhip64 (same soname as /opt/rocm's). Loading torch first makes
+    # libzebra bind to that copy; loaded the other way round, the process
+    # would hold two runtimes and the second one sees no device.
+    import torch  # noqa: F401
     so = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     for name in ("zebra_pack_tiles", "zebra_landmarks", "zebra_select_tiles",

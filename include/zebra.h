@@ -156,9 +156,13 @@ zebra_status zebra_select_tiles(const zebra_args* a, zebra_stream stream);
  * of every kept tile, the landmark of every omitted tile (logit
  * q.kbar_u/8 + ln n_u, value vbar_u), every special key, and its own key
  * when tile t itself is not kept. Special rows: dense over all N keys.
- * Reads q, kt, vt, ks, vs, lm, logn, selmask; writes out. Uses the workspace
- * (one flag per work item: rows whose cheap logit bound is too loose are
- * recomputed with an exact online softmax). */
+ * Reads q, kt, vt, ks, vs, lm, logn, selmask; writes out. Uses the workspace:
+ * per-row softmax offsets, one flag per query tile (rows whose cheap logit
+ * bound is too loose are recomputed with an exact online softmax) and, when
+ * the key tiles are walked in several ranges, fp32 partial outputs. The
+ * range size (default 96 MiB of one head's packed K/V) can be set with the
+ * environment variable ZEBRA_ATTN_RANGE_MB; the workspace size depends on
+ * it, so set it before calling zebra_buffer_bytes. */
 zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream);
 
 /* Linear attention with the centred affine correction. For each head:

@@ -8,123 +8,220 @@
 // dominates runtime as views grow": dense attention over all tokens is the
 // baseline this stage replaces.
 //
-// Work decomposition. A workgroup of 4 waves owns G query groups of one head
-// (a query group is a patch query tile of <= 64 rows, or 64 special rows).
-// Row block j (16 rows) of group s belongs to wave (s + j) % 4, so every wave
-// holds at most one 16-row slot of every group and all four waves do the
-// same work for every key block. The workgroup streams staged items through
-// a ring of NBUF LDS buffers (async global->LDS loads, exact vmcnt waits,
-// one barrier per item):
-//   1. bound pass: every landmark block and every special-key block, S only;
-//   2. the landmark blocks again (tile-sparse only; a group masks the tiles
-//      it kept), the UNION of the tiles the groups kept in ascending order
-//      (all tiles when dense) and the special blocks, with P.V;
-// then each group's self key.
+// Work decomposition. A workgroup of 4 waves owns FG = 5 query groups of one
+// head (a group is a patch query tile of <= 64 rows, or 64 special rows);
+// two workgroups share a CU. Row block j (16 rows) of group s belongs to wave
+// (s + j) % 4, so every wave holds one 16-row slot of (almost) every group:
+// all four waves have the same active slots for every staged key tile and
+// none waits for another at the tile barrier, while the two workgroups of
+// a CU, each with its own barrier, fill each other's MFMA and VALU gaps.
+// Tiles are streamed through a ring of FNBUF LDS buffers (async
+// global->LDS loads, exact vmcnt waits, one barrier per tile). The tiles a
+// workgroup stages are the union of its groups' kept tiles, and the more
+// groups share a staged tile the fewer bytes each kept (row, key) pair costs.
 //
-// Softmax offsets. Instead of a running max (a per-block max, cross-lane
-// reductions and O rescaling), each row i uses one offset M_i that is >=
-// every logit it can see, found in the bound pass: for a tile u and every
-// key j of u, q.k_j <= q.kbar_u + |q| r_u (r_u: the tile's key radius);
-// a landmark's logit is q.kbar_u/8 + ln n_u; special logits are exact. With
-// p = exp2(x - M_i) <= 1 nothing overflows. The row's own key is always
-// visible, so M_i minus the own logit bounds how far below 1 the largest p
-// can be; rows where that gap exceeds SAFE_GAP (log2 units) are flagged and
-// recomputed by an exact online-softmax kernel (attn_exact.hip).
+// Softmax offsets. Instead of a running max, each row i uses one offset M_i
+// that is >= every logit it can see, found by attn_bound_kernel: for a tile
+// u and every key j of u, q.k_j <= q.kbar_u + |q| r_u (r_u: the tile's key
+// radius); a landmark's logit is q.kbar_u/8 + ln n_u; special logits are
+// exact. With p = exp2(x - M_i) <= 1 nothing overflows, and the partial sums
+// of different key ranges simply add. The row's own key is always visible,
+// so M_i minus the own logit bounds how far below 1 the largest p can be;
+// groups with a row where that gap exceeds SAFE_GAP (log2 units) are flagged
+// and recomputed by an exact online-softmax kernel (attn_exact.hip).
+//
+// Key ranges. The main kernel runs once per range of 32-tile words, sized so
+// that one head's packed keys and values of a range stay resident in the
+// 256 MB memory-side cache while every CU streams it; O and l are carried
+// between launches as fp32 partials in the workspace, and the last launch
+// adds the special keys and the self key and writes bf16 output.
 //
 // Per 32-key block and 16-row slot: S^T = K Q^T (4 v_mfma_f32_16x16x32_bf16,
 // A = keys from LDS, B = Q in registers), p = exp2(S*log2(e)/8 - M),
 // O^T += V^T P^T (4 MFMAs; lane group g holds keys 4g..4g+3 of both 16-key
 // halves of S^T, the k-slot order of the value fragment, whose 32-key
-// blocks are stored [64 channels][32] with keys permuted by value_pos).
+// blocks are stored [64 channels][32] with keys permuted by value_pos). Row
+// sums use the bf16-rounded p that P.V sees.
 // LDS layouts are XOR-swizzled at 16-byte granularity (keys: column ^ key%8,
 // values: column ^ (channel/2)%4) so fragment reads are bank-conflict free;
 // the swizzle is applied through the per-lane source address of the async
 // loads, which write LDS linearly.
+#include <stdlib.h>
 
 #include "attn_common.hpp"
 
 namespace zebra {
 
+// wait until at most n of this wave's vector memory operations are pending
+#define ZEBRA_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+// Wait until at most `later` staged items (LPI loads per wave each) are in flight.
+template <int LPI>
+__device__ __forceinline__ void wait_items(int later) {
+  switch (later) {
+    case 0: ZEBRA_VMCNT(0); break;
+    case 1: ZEBRA_VMCNT(1 * LPI); break;
+    case 2: ZEBRA_VMCNT(2 * LPI); break;
+    case 3: ZEBRA_VMCNT(3 * LPI); break;
+    case 4: ZEBRA_VMCNT(4 * LPI); break;
+    case 5: ZEBRA_VMCNT(5 * LPI); break;
+    default: ZEBRA_VMCNT(6 * LPI); break;
+  }
+}
+static_assert(FNBUF - 2 <= 6, "wait_items covers at most 6 later items");
+
+// Per-lane source offsets of a wave's 1 KB shares (chunks c = wave,
+// wave + FWAVES, ...) of a staged 8 KB key or value half (swizzled as in
+// stage_keys / stage_vals), for an 8 KB source and for a 4 KB source (read
+// twice). Computed once per wave.
+constexpr int FCHUNKS = 8 / FWAVES;  // 1 KB shares per wave per 8 KB half
+struct StageOffsets {
+  unsigned k8[FCHUNKS], k4[FCHUNKS], v8[FCHUNKS], v4[FCHUNKS];
+  __device__ StageOffsets(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < FCHUNKS; ++i) {
+      const int c = wave + i * FWAVES;
+      const int P8 = c * 1024 + lane * 16, P4 = (c * 1024) % 4096 + lane * 16;
+      k8[i] = koff(P8);
+      k4[i] = koff(P4);
+      v8[i] = voff(P8);
+      v4[i] = voff(P4);
+    }
+  }
+  static __device__ unsigned koff(int P) {
+    const int key = P >> 7, col = (P >> 4) & 7;
+    return (unsigned)(key * 128 + ((col ^ (key & 7)) << 4));
+  }
+  static __device__ unsigned voff(int P) {
+    const int d = (P >> 6) & 63, col = (P >> 4) & 3;
+    return (unsigned)((P & ~63) + ((col ^ ((d >> 1) & 3)) << 4));
+  }
+};
+
+// One wave's shares of the async copy of an 8 KB half of a staged item;
+// `off` holds the wave's per-chunk offsets for the source's size.
+__device__ __forceinline__ void stage_share(char* dst, int wave, const char* src, const unsigned (&off)[FCHUNKS]) {
+#pragma unroll
+  for (int i = 0; i < FCHUNKS; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(src + off[i]), (lds_void*)(dst + (wave + i * FWAVES) * 1024),
+                                     16, 0, 0);
+}
+
 template <int G>
-struct WaveState {
-  bf16x8 q[G][2];  // B operand of each slot: query (lane%16), channels ds*32+8g..+7
-  f32x4 o[G][4];   // O^T of each slot: channel db*16+4g+r, query lane%16
-  float l[G];      // lane-partial row sums
-  float negm[G];   // -M (log2 units); during the bound pass: the running bound
-  float qnc[G];    // |q| * log2(e)/8
+struct BoundState {
+  bf16x8 q[G][2];
+  float negm[G];  // running bound (log2 units)
+  float qnc[G];   // |q| * log2(e)/8
 };
 
 template <int G>
-__device__ __forceinline__ void qk(const WaveState<G>& st, int s, const bf16x8 kf[2][2], f32x4& s0, f32x4& s1) {
-  s0 = f32x4{0.f, 0.f, 0.f, 0.f};
-  s1 = s0;
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][0], st.q[s][0], s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][0], st.q[s][0], s1, 0, 0, 0);
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][1], st.q[s][1], s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][1], st.q[s][1], s1, 0, 0, 0);
-}
+struct MainState {
+  bf16x8 q[G][2];  // B operand of each slot: query (lane%16), channels ds*32+8g..+7
+  f32x4 o[G][4];   // O^T of each slot: channel db*16+4g+r, query lane%16
+  float l[G];      // lane-partial row sums
+  float negm[G];   // -M (log2 units)
+};
 
-// p (8 lane values, in S^T order) -> row sums and O^T += V^T P^T.
+// Slot s of this wave: its queries as MFMA B fragments (zero for rows past
+// the group's end).
 template <int G>
-__device__ __forceinline__ void accumulate(WaveState<G>& st, int s, const float p[8], const bf16x8 vf[4]) {
-  st.l[s] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-  uint4 w;
-  w.x = pack_bf16(p[0], p[1]);
-  w.y = pack_bf16(p[2], p[3]);
-  w.z = pack_bf16(p[4], p[5]);
-  w.w = pack_bf16(p[6], p[7]);
-  const bf16x8 P = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-    st.o[s][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], P, st.o[s][db], 0, 0, 0);
-}
-
-// Main pass over one staged 32-key block for every user slot:
-// p = exp2(s*C - M), times n_u for a landmark (its logit carries + ln n_u);
-// keys past nvalid, and landmarks of tiles the slot's group kept, drop out.
-template <int G>
-__device__ __forceinline__ void main_block(WaveState<G>& st, unsigned users, const char* kb, int key0,
-                                           const char* vb, int nvalid, cmask_ptr mrow0, int nwords,
-                                           int lb, int lane) {
-  bf16x8 kf[2][2], vf[4];
-  load_kfrag(kb, key0, lane, kf);
-  load_vfrag(vb, lane, vf);
-  const int lg = lane >> 4;
-  const bool is_lm = lb >= 0;
-  float nmul[8];  // n_u = 2^log2(n_u) of the lane's 8 landmarks
-  if (is_lm) {
-    load_row8(kb + LM_LOG2N_ROW * 128, lane, nmul);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) nmul[i] = __builtin_amdgcn_exp2f(nmul[i]);
-  }
-  const unsigned valid = lane_valid_mask(nvalid, lane);
+__device__ __forceinline__ void load_queries(const Geom& g, const AttnArgs& A, const QueryGroups& qg, int h,
+                                             unsigned slots, int lane, bf16x8 q[G][2]) {
+  const int lg = lane >> 4, tl = lane & 15;
+  const long long rs = (long long)g.H * D;
 #pragma unroll
   for (int s = 0; s < G; ++s) {
-    if (!((users >> s) & 1u)) continue;
-    unsigned keep = valid;
+    const int j = qg.row_block(s) * 16 + tl;
+    const bool ok = ((slots >> s) & 1u) && j < qg.rows(s);
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (ok) w = *(const uint4*)(A.Q + qg.token(s, j) * rs + h * D + ds * 32 + 8 * lg);
+      q[s][ds] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+}
+
+__device__ __forceinline__ void qk(const bf16x8 q[2], const bf16x8 kf[2][2], f32x4& s0, f32x4& s1) {
+  s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+  s1 = s0;
+  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][0], q[0], s0, 0, 0, 0);
+  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][0], q[0], s1, 0, 0, 0);
+  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][1], q[1], s0, 0, 0, 0);
+  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][1], q[1], s1, 0, 0, 0);
+}
+
+// p = exp2(s*C + off_i) for the lane's 8 keys of a 32-key block
+__device__ __forceinline__ void probs(const f32x4& s0, const f32x4& s1, const float off[8], float p[8]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    p[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], QK_LOG2, off[r]));
+    p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s1[r], QK_LOG2, off[4 + r]));
+  }
+}
+
+__device__ __forceinline__ void probs(const f32x4& s0, const f32x4& s1, float off, float p[8]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    p[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], QK_LOG2, off));
+    p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s1[r], QK_LOG2, off));
+  }
+}
+
+__device__ __forceinline__ void drop(float p[8], unsigned keep) {
+  if (keep != 0xFFu) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!((keep >> i) & 1u)) p[i] = 0.f;
+  }
+}
+
+// Row sums and O^T += V^T bf16(P)^T.
+__device__ __forceinline__ void pv(const float p[8], const bf16x8 vf[4], f32x4 o[4], float& l) {
+  l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  const unsigned w0 = pack_bf16(p[0], p[1]), w1 = pack_bf16(p[2], p[3]);
+  const unsigned w2 = pack_bf16(p[4], p[5]), w3 = pack_bf16(p[6], p[7]);
+  const bf16x8 P = __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], P, o[db], 0, 0, 0);
+}
+
+// One staged 32-key block (keys key0.. of the LDS item) for every user
+// slot. Token or special keys: p = exp2(s*C - M), keys past nvalid dropped.
+// Landmark block lb >= 0: logit q.kbar/8 + ln n_u, so p is taken with the
+// offset log2 n_u - M (-inf past the last tile), and a slot drops the tiles
+// its group kept. All three share one P.V update per slot.
+template <int SW>
+__device__ __forceinline__ void attend_block(MainState<SW>& st, unsigned us, const char* kb, int key0, int nvalid,
+                                             int lb, cmask_ptr mrow0, int nwords, int lane) {
+  bf16x8 kf[2][2], vf[4];
+  load_kfrag(kb, key0, lane, kf);
+  load_vfrag(kb + LDS_V + key0 * 128, lane, vf);
+  const int lg = lane >> 4;
+  const bool is_lm = lb >= 0;             // uniform
+  const bool partial = nvalid < KBLK;     // uniform
+  const unsigned valid = partial ? lane_valid_mask(nvalid, lane) : 0xFFu;
+  float l2n[8];
+  if (is_lm) load_row8(kb + LM_LOG2N_ROW * 128, lane, l2n);
+#pragma unroll
+  for (int s = 0; s < SW; ++s) {
+    if (!((us >> s) & 1u)) continue;
+    f32x4 a0, a1;
+    qk(st.q[s], kf, a0, a1);
+    float p[8];
     if (is_lm) {
       const unsigned kept = mrow0[(long long)s * nwords + lb];
-      keep &= ~(((kept >> (4 * lg)) & 0xFu) | (((kept >> (16 + 4 * lg)) & 0xFu) << 4));
-    }
-    f32x4 s0, s1;
-    qk(st, s, kf, s0, s1);
-    const float nm = st.negm[s];
-    float p[8];
+      const unsigned keep = ~(((kept >> (4 * lg)) & 0xFu) | (((kept >> (16 + 4 * lg)) & 0xFu) << 4)) & 0xFFu;
+      float off[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], QK_LOG2, nm));
-      p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s1[r], QK_LOG2, nm));
+      for (int i = 0; i < 8; ++i) off[i] = st.negm[s] + l2n[i];
+      probs(a0, a1, off, p);
+      drop(p, keep);
+    } else {
+      probs(a0, a1, st.negm[s], p);
+      if (partial) drop(p, valid);
     }
-    if (is_lm) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] *= nmul[i];
-    }
-    if (keep != 0xFFu) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (!((keep >> i) & 1u)) p[i] = 0.f;
-    }
-    accumulate(st, s, p, vf);
+    pv(p, vf, st.o[s], st.l[s]);
   }
 }
 
@@ -132,8 +229,8 @@ __device__ __forceinline__ void main_block(WaveState<G>& st, unsigned users, con
 // by max over keys of s*C + max(log2 n_u, |q| r_u C) for a landmark block
 // (an upper bound of the logits of the tile's tokens and of its landmark),
 // or by the exact logits s*C of a special block's valid keys.
-template <int G>
-__device__ __forceinline__ void bound_block(WaveState<G>& st, unsigned slots, const char* kb, bool is_lm,
+template <int SW>
+__device__ __forceinline__ void bound_block(BoundState<SW>& st, unsigned slots, const char* kb, bool is_lm,
                                             int nvalid, int lane) {
   bf16x8 kf[2][2];
   load_kfrag(kb, 0, lane, kf);
@@ -150,10 +247,10 @@ __device__ __forceinline__ void bound_block(WaveState<G>& st, unsigned slots, co
     }
   }
 #pragma unroll
-  for (int s = 0; s < G; ++s) {
+  for (int s = 0; s < SW; ++s) {
     if (!((slots >> s) & 1u)) continue;
     f32x4 s0, s1;
-    qk(st, s, kf, s0, s1);
+    qk(st.q[s], kf, s0, s1);
     float b = st.negm[s];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -164,45 +261,110 @@ __device__ __forceinline__ void bound_block(WaveState<G>& st, unsigned slots, co
   }
 }
 
-template <int G>
-__device__ __forceinline__ void attend_item(const Geom& g, const AttnArgs& A, int work, int items_per_head,
-                                            int patch_items, char* lds, int* qcode, unsigned* qusers,
-                                            int* unsafe) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lg = lane >> 4, tl = lane & 15;
-  const int h = work / items_per_head;
-  const int item = work - h * items_per_head;
-  const QueryGroups qg(g, item, patch_items, G, wave);
-  const bool sparse = A.sparse && qg.patch;
-  const long long rs = (long long)g.H * D;
-  const u16* Kt16 = A.Kt + (long long)h * g.slots * D;
-  const u16* Vt16 = A.Vt + (long long)h * g.slots * D;
-  const u16* Ks16 = A.Ks + (long long)h * g.spec_pad * D;
-  const u16* Vs16 = A.Vs + (long long)h * g.spec_pad * D;
-
-  unsigned slots = 0u, valid_groups = 0u;
-#pragma unroll
-  for (int s = 0; s < G; ++s) {
-    const int n = qg.rows(s);
-    if (qg.row_block(s) * 16 < n) slots |= 1u << s;
-    if (n > 0) valid_groups |= 1u << s;
+// Work item -> (head, query groups): per head the special items first (they
+// walk every key tile), then the patch items.
+struct FastItem {
+  int h, item;  // item in QueryGroups numbering
+  __device__ FastItem(const Geom& g, int block) {
+    const FastItems fi(g);
+    h = block / fi.per_head;
+    const int b = block - h * fi.per_head;
+    item = b < fi.spec_items ? fi.patch_items + b : b - fi.spec_items;
   }
+};
 
-  WaveState<G> st;
-  float own[G];  // own-key logit (log2 units): a visible key of every row
+// Index of this lane's record of slot s in the per-lane workspace arrays;
+// record >> 8 is the group's index (head-major) in the flag array.
+__device__ __forceinline__ long long lane_record(const Geom& g, const QueryGroups& qg, int h, int s, int lane) {
+  const FastItems fi(g);
+  const int gid = (qg.patch ? 0 : g.T) + qg.gid0 + s;
+  return (((long long)h * fi.groups_per_head + gid) * 4 + qg.row_block(s)) * 64 + lane;
+}
+
+// Streams `next()`'s items through the LDS ring: for each item, `issue`
+// starts its async loads, and once they have landed in every wave
+// `consume(code, users, buffer)` runs. LPI: loads per wave per item.
+template <int LPI, typename Next, typename Issue, typename Consume>
+__device__ __forceinline__ void stream_items(char* lds, int* qcode, unsigned* qusers, Next next, Issue issue,
+                                             Consume consume) {
+  int issued = 0;
+  bool done = false;
+  for (int j = 0; j < FNBUF - 1; ++j) {
+    int c;
+    unsigned u;
+    if (!next(c, u)) {
+      done = true;
+      break;
+    }
+    if (threadIdx.x == 0) {
+      qcode[j] = c;
+      qusers[j] = u;
+    }
+    issue(c, lds + j * LDS_BUF);
+    ++issued;
+  }
+  for (int i = 0; i < issued; ++i) {
+    wait_items<LPI>(min(FNBUF - 2, issued - i - 1));
+    ring_barrier();
+    if (!done) {
+      int c;
+      unsigned u;
+      if (next(c, u)) {
+        const int jn = issued % FNBUF;
+        if (threadIdx.x == 0) {
+          qcode[jn] = c;
+          qusers[jn] = u;
+        }
+        issue(c, lds + jn * LDS_BUF);
+        ++issued;
+      } else {
+        done = true;
+      }
+    }
+    const int buf = i % FNBUF;
+    consume(uni(qcode[buf]), (unsigned)uni((int)qusers[buf]), lds + buf * LDS_BUF);
+  }
+  ring_barrier();
+}
+
+// Offsets: M_i = max over the row's visible keys of an upper bound of the
+// logit (landmark blocks with tile radii, exact special logits, the own
+// key's logit). Writes -M per lane record and flags groups whose bound is
+// more than SAFE_GAP above some row's own logit.
+template <int G, int SW>
+__global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, AttnArgs A, float* ws_negm,
+                                                                    int* flags) {
+  __shared__ __attribute__((aligned(1024))) char lds[FNBUF * LDS_BUF];
+  __shared__ int qcode[FNBUF];
+  __shared__ unsigned qusers[FNBUF];
+  const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
+  const int lg = lane >> 4, tl = lane & 15;
+  const int simd = wave & 3, s0 = (wave >> 2) * SW;
+  const FastItem it(g, blockIdx.x);
+  const int h = it.h;
+  const FastItems fi(g);
+  const QueryGroups qgi(g, it.item, fi.patch_items, G, simd);      // the item's G groups
+  const QueryGroups qg(g, it.item, fi.patch_items, G, simd, s0);   // this wave's SW slots
+  const u16* Kt16 = A.Kt + (long long)h * g.slots * D;
+  const u16* Ks16 = A.Ks + (long long)h * g.spec_pad * D;
+
+  unsigned slots = 0u;
 #pragma unroll
-  for (int s = 0; s < G; ++s) {
+  for (int s = 0; s < SW; ++s)
+    if (qg.row_block(s) * 16 < qg.rows(s)) slots |= 1u << s;
+
+  BoundState<SW> st;
+  float own[SW];
+  load_queries<SW>(g, A, qg, h, slots, lane, st.q);
+#pragma unroll
+  for (int s = 0; s < SW; ++s) {
     const int j = qg.row_block(s) * 16 + tl;
     const bool ok = ((slots >> s) & 1u) && j < qg.rows(s);
     float qq = 0.f, qko = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
-      uint4 w = make_uint4(0, 0, 0, 0), kw = make_uint4(0, 0, 0, 0);
-      if (ok) {
-        w = *(const uint4*)(A.Q + qg.token(s, j) * rs + h * D + ds * 32 + 8 * lg);
-        kw = *(const uint4*)((qg.patch ? Kt16 : Ks16) + qg.own_slot(s, j) * D + ds * 32 + 8 * lg);
-      }
-      st.q[s][ds] = __builtin_bit_cast(bf16x8, w);
+      uint4 kw = make_uint4(0, 0, 0, 0);
+      if (ok) kw = *(const uint4*)((qg.patch ? Kt16 : Ks16) + qg.own_slot(s, j) * D + ds * 32 + 8 * lg);
       const bf16x8 kv = __builtin_bit_cast(bf16x8, kw);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -215,241 +377,249 @@ __device__ __forceinline__ void attend_item(const Geom& g, const AttnArgs& A, in
     qko = xsum32(xsum16(qko));
     st.qnc[s] = sqrtf(qq) * QK_LOG2 * 1.0001f;
     own[s] = qko * QK_LOG2;
-    st.negm[s] = own[s];  // running bound during the bound pass
+    st.negm[s] = own[s];
+  }
+  ZEBRA_VMCNT(0);
+
+  const char* lmh = (const char*)A.LM + (long long)h * g.T_pad * LM_BYTES_PER_TILE;
+  const int nlb = g.T_pad / KBLK, nsb = g.spec_pad / KBLK;
+  int cnt = 0;
+  auto next = [&](int& code, unsigned& users) -> bool {
+    if (cnt >= nlb + nsb) return false;
+    code = cnt++;
+    users = slots;
+    return true;
+  };
+  const StageOffsets so(wave, lane);
+  auto issue = [&](int code_in, char* d) {
+    const int code = uni(code_in);
+    if (code < nlb) stage_share(d, wave, lmh + (long long)code * LM_KEY_BLOCK, so.k8);
+    else stage_share(d, wave, (const char*)Ks16 + (long long)(code - nlb) * KBLK * D * 2, so.k4);
+  };
+  auto consume = [&](int code, unsigned, const char* kb) {
+    if (!slots) return;
+    const bool is_lm = code < nlb;
+    bound_block<SW>(st, slots, kb, is_lm, is_lm ? KBLK : min(KBLK, g.nspec - (code - nlb) * KBLK), lane);
+  };
+  stream_items<FCHUNKS>(lds, qcode, qusers, next, issue, consume);
+
+#pragma unroll
+  for (int s = 0; s < SW; ++s) {
+    if (!((slots >> s) & 1u)) continue;
+    const float m = xmax32(xmax16(st.negm[s]));
+    const bool okrow = qg.row_block(s) * 16 + tl < qg.rows(s);
+    const bool bad = __builtin_amdgcn_ballot_w64(okrow && m - own[s] > SAFE_GAP) != 0;
+    const long long rec = lane_record(g, qg, h, s, lane);
+    ws_negm[rec] = -m;
+    if (bad && lane == 0) flags[rec >> 8] = 1;
+  }
+}
+
+// One key range [w0, w1) of 32-tile words for every work item: tile-sparse
+// patch items see the landmark block of each word (minus the tiles each
+// group kept) and the union of the kept tiles of the word; dense items see
+// every tile. The first range starts from zero partials, the last one adds
+// the special keys and the self key and writes the bf16 output.
+template <int G, int SW>
+__global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, AttnArgs A, int w0, int w1,
+                                                                   int first, int last, const float* ws_negm,
+                                                                   float* ws_l, f32x4* ws_o) {
+  __shared__ __attribute__((aligned(1024))) char lds[FNBUF * LDS_BUF];
+  __shared__ int qcode[FNBUF];
+  __shared__ unsigned qusers[FNBUF];
+  const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
+  const int lg = lane >> 4, tl = lane & 15;
+  const int simd = wave & 3, s0 = (wave >> 2) * SW;
+  const FastItem it(g, blockIdx.x);
+  const int h = it.h;
+  const FastItems fi(g);
+  const QueryGroups qgi(g, it.item, fi.patch_items, G, simd);      // the item's G groups
+  const QueryGroups qg(g, it.item, fi.patch_items, G, simd, s0);   // this wave's SW slots
+  const bool sparse = A.sparse && qg.patch;
+  const long long rs = (long long)g.H * D;
+  const u16* Kt16 = A.Kt + (long long)h * g.slots * D;
+  const u16* Vt16 = A.Vt + (long long)h * g.slots * D;
+  const u16* Ks16 = A.Ks + (long long)h * g.spec_pad * D;
+  const u16* Vs16 = A.Vs + (long long)h * g.spec_pad * D;
+
+  unsigned slots = 0u, valid_groups = 0u;  // this wave's slots; the item's non-empty groups
+#pragma unroll
+  for (int s = 0; s < SW; ++s)
+    if (qg.row_block(s) * 16 < qg.rows(s)) slots |= 1u << s;
+#pragma unroll
+  for (int s = 0; s < G; ++s)
+    if (qgi.rows(s) > 0) valid_groups |= 1u << s;
+
+  MainState<SW> st;
+  load_queries<SW>(g, A, qg, h, slots, lane, st.q);
+#pragma unroll
+  for (int s = 0; s < SW; ++s) {
+    st.negm[s] = 0.f;
     st.l[s] = 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db) st.o[s][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if ((slots >> s) & 1u) {
+      const long long rec = lane_record(g, qg, h, s, lane);
+      st.negm[s] = ws_negm[rec];
+      if (!first) {
+        st.l[s] = ws_l[rec];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) st.o[s][db] = ws_o[rec * 4 + db];
+      }
+    }
   }
+  ZEBRA_VMCNT(0);
 
   const char* lmh = (const char*)A.LM + (long long)h * g.T_pad * LM_BYTES_PER_TILE;
-  // kept-tile bitmap row of group s: mrow0 + s * nwords (patch groups are
-  // consecutive query tiles)
-  const cmask_ptr mrow0 =
-      (cmask_ptr)(sparse ? A.selmask + ((long long)h * g.T + qg.gid0) * A.nwords : A.selmask);
-  auto mask_word = [&](int s, int word) -> unsigned { return mrow0[(long long)s * A.nwords + word]; };
+  // kept-tile bitmap rows (patch groups are consecutive query tiles): group
+  // s of the item at mitem + s * nwords, slot s of this wave at mrow0 + s * nwords
+  const cmask_ptr mitem =
+      (cmask_ptr)(sparse ? A.selmask + ((long long)h * g.T + qgi.gid0) * A.nwords : A.selmask);
+  const cmask_ptr mrow0 = mitem + (sparse ? s0 * A.nwords : 0);
+  const int nlb = g.T_pad / KBLK, nsb = g.spec_pad / KBLK;
 
-  // Item codes. Bound pass (flag BOUND): T + lb landmark block lb < nlb_all,
-  // T + nlb_all + b special block b. Main pass: u < T token tile u,
-  // T + lb landmark block (tile-sparse only), T + nlb + b special block b.
-  const int nlb_all = g.T_pad / KBLK;
-  const int nlb = sparse ? nlb_all : 0;
-  const int nsb = g.spec_pad / KBLK;
-  constexpr int BOUND = 1 << 30;
-  int phase = 0, w = -1, cnt = 0;
-  unsigned bits = 0u;
+  // Item codes: u < T token tile u, T + lb landmark block lb, T + nlb + b
+  // special block b.
+  int w = w0 - 1, scnt = 0;
+  unsigned bits = 0u, lm_users = 0u, lane_word = 0u;
+  bool lm_due = false;
   auto next = [&](int& code, unsigned& users) -> bool {
-    if (phase == 0) {  // bound pass
-      if (cnt < nlb_all + nsb) {
-        code = BOUND | (g.T + cnt++);
-        users = valid_groups;
+    for (;;) {
+      if (lm_due) {
+        lm_due = false;
+        code = g.T + w;
+        users = lm_users;
         return true;
       }
-      phase = 1;
-      cnt = 0;
-    }
-    if (phase == 1) {  // landmark blocks not kept entirely by every group
-      while (cnt < nlb) {
-        const int lb = cnt++;
-        unsigned us = 0u;
-#pragma unroll
-        for (int s = 0; s < G; ++s)
-          if (((valid_groups >> s) & 1u) && mask_word(s, lb) != 0xFFFFFFFFu) us |= 1u << s;
-        if (us) {
-          code = g.T + lb;
-          users = us;
-          return true;
-        }
-      }
-      phase = 2;
-    }
-    if (phase == 2) {  // union of the kept tiles (every tile when dense)
-      while (bits == 0u) {
-        if (++w >= A.nwords) {
-          phase = 3;
-          cnt = 0;
-          break;
-        }
-        if (sparse) {
-          unsigned un = 0u;
-#pragma unroll
-          for (int s = 0; s < G; ++s)
-            if ((valid_groups >> s) & 1u) un |= mask_word(s, w);
-          bits = un;
-        } else {
-          const int rem = g.T - w * 32;
-          bits = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
-        }
-      }
-      if (phase == 2) {
+      if (bits) {
         const int b = __builtin_ctz(bits);
         bits &= bits - 1u;
         code = w * 32 + b;
-        if (sparse) {
-          unsigned us = 0u;
-#pragma unroll
-          for (int s = 0; s < G; ++s)
-            if ((valid_groups >> s) & 1u) us |= ((mask_word(s, w) >> b) & 1u) << s;
-          users = us;
-        } else {
-          users = valid_groups;
-        }
+        users = sparse ? (unsigned)__builtin_amdgcn_ballot_w64((lane_word >> b) & 1u) : valid_groups;
         return true;
       }
+      if (w + 1 >= w1) break;
+      ++w;
+      if (sparse) {
+        // lane s < G holds group s's word; landmark users: groups that did
+        // not keep every tile of the word
+        unsigned un = 0u, lu = 0u, lw = 0u;
+#pragma unroll
+        for (int s = 0; s < G; ++s) {
+          const unsigned m = ((valid_groups >> s) & 1u) ? mitem[(long long)s * A.nwords + w] : 0u;
+          un |= m;
+          if (((valid_groups >> s) & 1u) && m != 0xFFFFFFFFu) lu |= 1u << s;
+          lw = lane == s ? m : lw;
+        }
+        bits = un;
+        lane_word = lw;
+        lm_users = lu;
+        lm_due = lu != 0u;
+      } else {
+        const int rem = g.T - w * 32;
+        bits = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
+      }
     }
-    if (cnt < nsb) {  // special blocks
-      code = g.T + nlb + cnt++;
+    if (last && scnt < nsb) {
+      code = g.T + nlb + scnt++;
       users = valid_groups;
       return true;
     }
     return false;
   };
-  auto issue = [&](int code_in, int buf) {
-    const int cin = uni(code_in);
-    const int code = cin & ~BOUND;
-    char* d = lds + buf * LDS_BUF;
-    const char *ksrc, *vsrc;
-    int kbytes, vbytes;
-    int lb = -1, sb = -1;
-    if (cin & BOUND) {
-      if (code < g.T + nlb_all) lb = code - g.T;
-      else sb = code - g.T - nlb_all;
-    } else if (code >= g.T) {
-      if (code < g.T + nlb) lb = code - g.T;
-      else sb = code - g.T - nlb;
-    }
-    if (lb >= 0) {
-      ksrc = lmh + (long long)lb * LM_KEY_BLOCK;
-      vsrc = lmh + (long long)nlb_all * LM_KEY_BLOCK + (long long)lb * (KBLK * D * 2);
-      kbytes = LM_KEY_BLOCK;
-      vbytes = KBLK * D * 2;
-    } else if (sb >= 0) {
-      ksrc = (const char*)Ks16 + (long long)sb * KBLK * D * 2;
-      vsrc = (const char*)Vs16 + (long long)sb * KBLK * D * 2;
-      kbytes = vbytes = KBLK * D * 2;
-    } else {
-      const int fu = code / g.tpf, tu = code - fu * g.tpf;
-      const long long base = (long long)fu * g.slots_pf + tile_off(g, tu);
-      kbytes = vbytes = pad32(tile_n(g, tu)) * D * 2;
-      ksrc = (const char*)Kt16 + base * D * 2;
-      vsrc = (const char*)Vt16 + base * D * 2;
-    }
-    stage_keys(d, ksrc, kbytes, wave, lane);
-    stage_vals(d + LDS_V, vsrc, vbytes, wave, lane);
-  };
-  bool bound_done = false;
-  auto finish_bound = [&]() {
-    // M = max over the row's lanes; flag rows whose bound is too far above
-    // their own logit (underflow risk) for the exact kernel
-    bool bad = false;
-#pragma unroll
-    for (int s = 0; s < G; ++s) {
-      const float m = xmax32(xmax16(st.negm[s]));
-      const bool okrow = ((slots >> s) & 1u) && qg.row_block(s) * 16 + tl < qg.rows(s);
-      if (okrow && m - own[s] > SAFE_GAP) bad = true;
-      st.negm[s] = -m;
-    }
-    if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) atomicOr(unsafe + work, 1);
-  };
-
-  int issued = 0;
-  bool done = false;
-  for (int j = 0; j < NBUF - 1; ++j) {
-    int c;
-    unsigned u;
-    if (!next(c, u)) {
-      done = true;
-      break;
-    }
-    if (threadIdx.x == 0) {
-      qcode[j] = c;
-      qusers[j] = u;
-    }
-    issue(c, j);
-    ++issued;
-  }
-  for (int i = 0; i < issued; ++i) {
-    wait_loads(min(NBUF - 2, issued - i - 1));
-    ring_barrier();
-    if (!done) {
-      int c;
-      unsigned u;
-      if (next(c, u)) {
-        const int jn = issued % NBUF;
-        if (threadIdx.x == 0) {
-          qcode[jn] = c;
-          qusers[jn] = u;
-        }
-        issue(c, jn);
-        ++issued;
-      } else {
-        done = true;
-      }
-    }
-    const int buf = i % NBUF;
-    const int cin = uni(qcode[buf]);
-    const int code = cin & ~BOUND;
-    const unsigned us = (unsigned)uni((int)qusers[buf]) & slots;
-    const char* kb = lds + buf * LDS_BUF;
-    if (cin & BOUND) {
-      if (us) {
-        const bool is_lm = code < g.T + nlb_all;
-        bound_block<G>(st, us, kb, is_lm, is_lm ? 32 : min(32, g.nspec - (code - g.T - nlb_all) * KBLK),
-                       lane);
-      }
-      continue;
-    }
-    if (!bound_done) {
-      finish_bound();
-      bound_done = true;
-    }
-    if (!us) continue;
-    int nkeys, lb = -1;
+  const StageOffsets so(wave, lane);
+  auto issue = [&](int code_in, char* d) {
+    const int code = uni(code_in);
     if (code < g.T) {
-      nkeys = tile_n(g, code % g.tpf);
+      const int fu = frame_of_tile(g, code), tu = code - fu * g.tpf;
+      const long long base = ((long long)fu * g.slots_pf + tile_off(g, tu)) * D * 2;
+      if (tile_n(g, tu) > KBLK) {
+        stage_share(d, wave, (const char*)Kt16 + base, so.k8);
+        stage_share(d + LDS_V, wave, (const char*)Vt16 + base, so.v8);
+      } else {
+        stage_share(d, wave, (const char*)Kt16 + base, so.k4);
+        stage_share(d + LDS_V, wave, (const char*)Vt16 + base, so.v4);
+      }
     } else if (code < g.T + nlb) {
-      nkeys = 32;
-      lb = code - g.T;
+      const long long lb = code - g.T;
+      stage_share(d, wave, lmh + lb * LM_KEY_BLOCK, so.k8);
+      stage_share(d + LDS_V, wave, lmh + (long long)nlb * LM_KEY_BLOCK + lb * (KBLK * D * 2), so.v4);
     } else {
-      nkeys = min(32, g.nspec - (code - g.T - nlb) * KBLK);
+      const long long b = (long long)(code - g.T - nlb) * KBLK * D * 2;
+      stage_share(d, wave, (const char*)Ks16 + b, so.k4);
+      stage_share(d + LDS_V, wave, (const char*)Vs16 + b, so.v4);
     }
-#pragma nounroll
-    for (int k0 = 0; k0 < nkeys; k0 += KBLK)
-      main_block<G>(st, us, kb, k0, kb + LDS_V + k0 * 128, nkeys - k0, mrow0, A.nwords, lb, lane);
+  };
+  auto consume = [&](int code, unsigned users, const char* kb) {
+    const unsigned us = (users >> s0) & slots;
+    if (!us) return;
+    int nkeys = KBLK, lb = -1;
+    if (code < g.T) nkeys = tile_n(g, code - frame_of_tile(g, code) * g.tpf);
+    else if (code < g.T + nlb) lb = code - g.T;
+    else nkeys = min(KBLK, g.nspec - (code - g.T - nlb) * KBLK);
+    attend_block<SW>(st, us, kb, 0, nkeys, lb, mrow0, A.nwords, lane);
+    if (nkeys > KBLK) attend_block<SW>(st, us, kb, KBLK, nkeys - KBLK, -1, mrow0, A.nwords, lane);
+  };
+  stream_items<2 * FCHUNKS>(lds, qcode, qusers, next, issue, consume);
+  // Per-lane indices are recomputed after the walk rather than kept live
+  // across it from the set-up (register pressure).
+  int lane_a = lane;
+  asm volatile("" : "+v"(lane_a));
+  const int lg_a = lane_a >> 4, tl_a = lane_a & 15;
+
+  if (!last) {
+#pragma unroll
+    for (int s = 0; s < SW; ++s) {
+      if (!((slots >> s) & 1u)) continue;
+      const long long rec = lane_record(g, qg, h, s, lane_a);
+      ws_l[rec] = st.l[s];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) ws_o[rec * 4 + db] = st.o[s][db];
+    }
+    return;
   }
-  if (!bound_done) finish_bound();
-  ring_barrier();
 
   // self key of patch rows whose own tile was not kept
   if (sparse) {
 #pragma unroll
-    for (int s = 0; s < G; ++s) {
+    for (int s = 0; s < SW; ++s) {
       if (!((slots >> s) & 1u)) continue;
       const int t = qg.gid0 + s;
-      if ((mask_word(s, t >> 5) >> (t & 31)) & 1u) continue;
-      const int j = qg.row_block(s) * 16 + tl;
+      if ((mrow0[(long long)s * A.nwords + (t >> 5)] >> (t & 31)) & 1u) continue;
+      const int j = qg.row_block(s) * 16 + tl_a;
       const bool okrow = j < qg.rows(s);
-      const float p = okrow ? __builtin_amdgcn_exp2f(own[s] + st.negm[s]) : 0.f;
-      st.l[s] += (lg == 0 ? p : 0.f);
       const long long slot = qg.own_slot(s, j);
+      float dot = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < 2; ++ds) {
+        uint4 kw = make_uint4(0, 0, 0, 0);
+        if (okrow) kw = *(const uint4*)(Kt16 + slot * D + ds * 32 + 8 * lg_a);
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, kw);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) dot = fmaf((float)st.q[s][ds][m], (float)kv[m], dot);
+      }
+      dot = xsum32(xsum16(dot));
+      const float p = okrow ? __builtin_amdgcn_exp2f(fmaf(dot, QK_LOG2, st.negm[s])) : 0.f;
+      st.l[s] += (lg_a == 0 ? p : 0.f);
       const long long vblk = slot / KBLK;
       const int pos = value_pos((int)(slot % KBLK));
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int d = db * 16 + 4 * lg + r;
+          const int d = db * 16 + 4 * lg_a + r;
           const float v = okrow ? bf2f(Vt16[(vblk * D + d) * KBLK + pos]) : 0.f;
           st.o[s][db][r] = fmaf(p, v, st.o[s][db][r]);
         }
     }
   }
 
-  // finalize: O = O^T / l; row = query (rb*16 + lane%16), channels db*16+4g+r
+  // finalize: O = O^T / l; row = query (rb*16 + lane_a%16), channels db*16+4g+r
 #pragma unroll
-  for (int s = 0; s < G; ++s) {
+  for (int s = 0; s < SW; ++s) {
     if (!((slots >> s) & 1u)) continue;
     const float inv = 1.0f / xsum32(xsum16(st.l[s]));
-    const int j = qg.row_block(s) * 16 + tl;
+    const int j = qg.row_block(s) * 16 + tl_a;
     if (j < qg.rows(s)) {
       u16* orow = A.O + qg.token(s, j) * rs + h * D;
 #pragma unroll
@@ -457,37 +627,82 @@ __device__ __forceinline__ void attend_item(const Geom& g, const AttnArgs& A, in
         uint2 wv;
         wv.x = pack_bf16(st.o[s][db][0] * inv, st.o[s][db][1] * inv);
         wv.y = pack_bf16(st.o[s][db][2] * inv, st.o[s][db][3] * inv);
-        *(uint2*)(orow + db * 16 + 4 * lg) = wv;
+        *(uint2*)(orow + db * 16 + 4 * lg_a) = wv;
       }
     }
   }
 }
 
-// One work item (head, G query groups) per workgroup; items first..first+n-1
-// of the head-major numbering (blockIdx.x -> head h, item within head).
-template <int G>
-__global__ void __launch_bounds__(ATT_THREADS, 2) attn_kernel(Geom g, AttnArgs A, int items_per_head,
-                                                              int patch_items, int first, int count,
-                                                              int* unsafe) {
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF * LDS_BUF];
-  __shared__ int qcode[NBUF];
-  __shared__ unsigned qusers[NBUF];
-  const int h = blockIdx.x / count, i = blockIdx.x - h * count;
-  attend_item<G>(g, A, h * items_per_head + first + i, items_per_head, patch_items, lds, qcode, qusers,
-                 unsafe);
+// Zeroes the per-group flags before the bound kernel (a kernel, not a
+// memset, so that the sequence can be captured in a graph).
+__global__ void clear_flags_kernel(int* flags, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) flags[i] = 0;
 }
 
-// Patch items (one workgroup per item, head-major), then the special-row
-// items (dense over every key, one workgroup each).
-hipError_t launch_attn_fast(const Geom& g, const AttnArgs& a, int* unsafe, hipStream_t s) {
-  const ItemCounts ic(g, ATTN_GROUPS);
-  hipLaunchKernelGGL(attn_kernel<ATTN_GROUPS>, dim3(ic.patch_items * g.H), dim3(ATT_THREADS), 0, s, g, a,
-                     ic.per_head, ic.patch_items, 0, ic.patch_items, unsafe);
-  const int spec_items = ic.per_head - ic.patch_items;
-  if (spec_items > 0)
-    hipLaunchKernelGGL(attn_kernel<ATTN_GROUPS>, dim3(spec_items * g.H), dim3(ATT_THREADS), 0, s, g, a,
-                       ic.per_head, ic.patch_items, ic.patch_items, spec_items, unsafe);
-  return hipGetLastError();
+// Bytes of one head's packed keys and values that a key range may span so
+// that it stays resident in the memory-side cache (ZEBRA_ATTN_RANGE_MB
+// overrides the default of 96 MiB; the workspace size depends on it).
+static double range_bytes() {
+  const char* e = getenv("ZEBRA_ATTN_RANGE_MB");
+  const double v = e ? atof(e) : 0.0;
+  return v > 0.0 ? v * 1048576.0 : 96.0 * 1048576.0;
+}
+
+int attn_ranges(const Geom& g) {
+  const int nwords = (g.T + 31) / 32;
+  const double kv = (double)g.slots * D * 2 * 2, rb = range_bytes();
+  const double r = (kv + rb - 1.0) / rb;
+  return r < 1.0 ? 1 : (r > nwords ? nwords : (int)r);
+}
+
+// Workspace of the attention entry points: flags (one int per group), then
+// per lane record -M, l and O partials (l and O only with several ranges).
+struct AttnWorkspace {
+  long long groups, records;
+  size_t flags_off, negm_off, l_off, o_off, bytes;
+  explicit AttnWorkspace(const Geom& g) {
+    const FastItems fi(g);
+    groups = (long long)g.H * fi.groups_per_head;
+    records = groups * 4 * 64;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    flags_off = 0;
+    negm_off = up((size_t)groups * sizeof(int));
+    l_off = up(negm_off + (size_t)records * sizeof(float));
+    o_off = l_off;
+    bytes = l_off;
+    if (attn_ranges(g) > 1) {
+      o_off = up(l_off + (size_t)records * sizeof(float));
+      bytes = o_off + (size_t)records * 4 * sizeof(f32x4);
+    }
+  }
+};
+
+size_t attn_workspace_bytes(const Geom& g) { return AttnWorkspace(g).bytes; }
+
+hipError_t launch_attn_exact(const Geom& g, const AttnArgs& a, const int* flags, hipStream_t s);
+
+// Offsets, the key ranges, then the exact kernel for flagged groups.
+hipError_t launch_attn(const Geom& g, const AttnArgs& a, void* workspace, hipStream_t s) {
+  const AttnWorkspace ws(g);
+  char* base = (char*)workspace;
+  int* flags = (int*)(base + ws.flags_off);
+  float* negm = (float*)(base + ws.negm_off);
+  float* wl = (float*)(base + ws.l_off);
+  f32x4* wo = (f32x4*)(base + ws.o_off);
+  const FastItems fi(g);
+  hipLaunchKernelGGL(clear_flags_kernel, dim3((unsigned)((ws.groups + 255) / 256)), dim3(256), 0, s, flags,
+                     ws.groups);
+  hipLaunchKernelGGL((attn_bound_kernel<FG, FSLOTS>), dim3(fi.total), dim3(FWAVES * 64), 0, s, g, a, negm, flags);
+  const int nwords = (g.T + 31) / 32, R = attn_ranges(g);
+  for (int r = 0; r < R; ++r) {
+    const int w0 = (int)((long long)nwords * r / R), w1 = (int)((long long)nwords * (r + 1) / R);
+    hipLaunchKernelGGL((attn_main_kernel<FG, FSLOTS>), dim3(fi.total), dim3(FWAVES * 64), 0, s, g, a, w0, w1,
+                       r == 0 ? 1 : 0, r == R - 1 ? 1 : 0, (const float*)negm, wl, wo);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attn_exact(g, a, flags, s);
 }
 
 }  // namespace zebra

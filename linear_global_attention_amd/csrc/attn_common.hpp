@@ -14,7 +14,15 @@ constexpr float QK_LOG2 = 1.4426950408889634f * 0.125f;  // log2(e) / sqrt(64)
 constexpr float SAFE_GAP = 100.0f;  // largest allowed bound - own-logit gap (log2 units)
 constexpr int LDS_BUF = 16384;      // one staged item: keys [0, 8K), values [8K, 16K)
 constexpr int LDS_V = 8192;
-constexpr int NBUF = 4;             // staged items in flight (LDS ring)
+constexpr int NBUF = 4;             // LDS ring of the exact kernel
+// Fast kernels: FOCC workgroups of FWAVES waves per CU; each workgroup owns
+// FG query groups, each wave FSLOTS 16-row slots of them.
+constexpr int FG = 5;
+constexpr int FWAVES = 4;
+constexpr int FOCC = 2;
+constexpr int FSLOTS = FG * 4 / FWAVES;
+constexpr int FNBUF = 4;            // LDS ring per workgroup (16 KB items)
+static_assert(FG * 4 % FWAVES == 0 && (FWAVES == 4 || FWAVES == 8), "fast kernel layout");
 constexpr int LOADS_PER_ITEM = 4;   // async 1 KB loads per wave per item
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -53,10 +61,12 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 
 // Async copy of 8 KB of key rows (128 B each) into LDS at `dst`, swizzled:
 // 16-byte column c' of key row k holds column c' ^ (k%8). A source of
-// `bytes` < 8 KB is repeated (only its first `bytes` are read back).
+// `bytes` < 8 KB is repeated (only its first `bytes` are read back). NW
+// waves share the copy (1 KB per wave per load).
+template <int NW = NWAVES>
 __device__ __forceinline__ void stage_keys(char* dst, const char* src, int bytes, int wave, int lane) {
 #pragma unroll
-  for (int c = wave; c < 8; c += NWAVES) {
+  for (int c = wave; c < 8; c += NW) {
     const int P = (c * 1024) % bytes + lane * 16;
     const int key = P >> 7, col = (P >> 4) & 7;
     const char* s = src + key * 128 + ((col ^ (key & 7)) << 4);
@@ -66,9 +76,10 @@ __device__ __forceinline__ void stage_keys(char* dst, const char* src, int bytes
 
 // Async copy of 8 KB of value blocks ([64][32] bf16, 4 KB each) into LDS,
 // swizzled: 16-byte column c' of channel row d holds column c' ^ ((d/2)%4).
+template <int NW = NWAVES>
 __device__ __forceinline__ void stage_vals(char* dst, const char* src, int bytes, int wave, int lane) {
 #pragma unroll
-  for (int c = wave; c < 8; c += NWAVES) {
+  for (int c = wave; c < 8; c += NW) {
     const int P = (c * 1024) % bytes + lane * 16;
     const int d = (P >> 6) & 63, col = (P >> 4) & 3;
     const char* s = src + (P & ~63) + ((col ^ ((d >> 1) & 3)) << 4);
@@ -140,23 +151,26 @@ __device__ __forceinline__ unsigned lane_valid_mask(int nvalid, int lane) {
   return m;
 }
 
-// The G query groups of one work item, seen from one wave. Patch item:
-// query tiles gid0..gid0+G-1; special item: groups of 64 special rows.
-// Row block j (16 rows) of group s belongs to wave (s + j) % 4.
+// The query groups of one work item (G groups), seen from one wave that
+// holds slots i = 0.. for groups s = s0 + i. Patch item: query tiles
+// gid0..gid0+G-1; special item: groups of 64 special rows. Row block j (16
+// rows) of group s belongs to the wave with `wave` == (s + j) % 4 (the SIMD
+// index when two waves share a SIMD).
 struct QueryGroups {
   const Geom& g;
   bool patch;
   int gid0;
   int wave;
-  __device__ QueryGroups(const Geom& g_, int item, int patch_items, int G, int wave_)
+  int s0;
+  __device__ QueryGroups(const Geom& g_, int item, int patch_items, int G, int wave_, int s0_ = 0)
       : g(g_), patch(item < patch_items),
-        gid0(item < patch_items ? item * G : (item - patch_items) * G), wave(wave_) {}
+        gid0((item < patch_items ? item * G : (item - patch_items) * G) + s0_), wave(wave_), s0(s0_) {}
   __device__ int rows(int s) const {
     const int id = gid0 + s;
     if (patch) return id < g.T ? tile_n(g, id % g.tpf) : 0;
     return max(0, min(64, g.nspec - id * 64));
   }
-  __device__ int row_block(int s) const { return (wave - s) & 3; }
+  __device__ int row_block(int s) const { return (wave - s0 - s) & 3; }
   // token index of row j of group s
   __device__ long long token(int s, int j) const {
     const int id = gid0 + s;
@@ -190,6 +204,21 @@ struct ItemCounts {
     const int spec_groups = (g.nspec + 63) / 64;
     per_head = patch_items + (spec_groups + G - 1) / G;
     total = per_head * g.H;
+  }
+};
+
+// Work items of the fast kernels (FG groups each), per head: the special
+// items first, then the patch items. Groups of a head: T patch query tiles,
+// then ceil(nspec/64) special groups.
+struct FastItems {
+  int spec_items, patch_items, per_head, total, groups_per_head;
+  __host__ __device__ explicit FastItems(const Geom& g) {
+    patch_items = (g.T + FG - 1) / FG;
+    const int sg = (g.nspec + 63) / 64;
+    spec_items = (sg + FG - 1) / FG;
+    per_head = spec_items + patch_items;
+    total = per_head * g.H;
+    groups_per_head = g.T + sg;
   }
 };
 

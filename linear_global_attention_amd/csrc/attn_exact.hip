@@ -1,10 +1,11 @@
 // Exact-offset fallback of the attention kernel (gfx950).
 //
-// Same work items, staging and visible key set as attn.hip, but with an
-// online softmax: a running row max (raised only when a block exceeds it by
-// more than TAU, then O and l are rescaled). It recomputes only the work
-// items attn.hip flagged (a row whose logit bound was too loose to use as a
-// fixed offset); every other workgroup exits at once.
+// Same staging and visible key set as attn.hip, but with an online softmax:
+// a running row max (raised only when a block exceeds it by more than TAU,
+// then O and l are rescaled). Its work items hold ATTN_GROUPS query groups;
+// it recomputes only the items with a group that attn_bound_kernel flagged
+// (a row whose logit bound was too loose to use as a fixed offset); every
+// other workgroup exits at once.
 #include "attn_common.hpp"
 
 namespace zebra {
@@ -93,13 +94,22 @@ __device__ __forceinline__ void exact_block(ExactState<G>& st, unsigned users, c
 
 template <int G>
 __global__ void __launch_bounds__(ATT_THREADS, 1) attn_exact_kernel(Geom g, AttnArgs A, int items_per_head,
-                                                                    int patch_items, const int* unsafe) {
+                                                                    int patch_items, const int* flags) {
   const int work = blockIdx.x;
-  if (unsafe[work] == 0) return;  // uniform over the workgroup
+  {  // any flagged group in this item? (uniform over the workgroup)
+    const int h = work / items_per_head, item = work - h * items_per_head;
+    const FastItems fi(g);
+    const bool patch = item < patch_items;
+    const int gid0 = (patch ? 0 : g.T) + (patch ? item : item - patch_items) * G;
+    const int gend = patch ? g.T : fi.groups_per_head;
+    int any = 0;
+    for (int s = 0; s < G && gid0 + s < gend; ++s) any |= flags[(long long)h * fi.groups_per_head + gid0 + s];
+    if (!any) return;
+  }
   __shared__ __attribute__((aligned(1024))) char lds[NBUF * LDS_BUF];
   __shared__ int qcode[NBUF];
   __shared__ unsigned qusers[NBUF];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
   const int lg = lane >> 4, tl = lane & 15;
   const int h = work / items_per_head;
   const int item = work - h * items_per_head;
@@ -336,29 +346,13 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) attn_exact_kernel(Geom g, Attn
   }
 }
 
-// Zeroes the per-item flags before the fast kernel (a kernel, not a memset,
-// so that the sequence can be captured in a graph).
-__global__ void clear_flags_kernel(int* flags, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) flags[i] = 0;
-}
-
-hipError_t launch_attn_fast(const Geom& g, const AttnArgs& a, int* unsafe, hipStream_t s);
-
-// Fast kernel (fixed offsets) then the exact kernel for the flagged items.
-// `unsafe` holds one int per work item (attn_flag_bytes).
-hipError_t launch_attn(const Geom& g, const AttnArgs& a, int* unsafe, hipStream_t s) {
+// Recomputes the work items that hold a flagged group (one int per group,
+// head-major, as written by attn_bound_kernel).
+hipError_t launch_attn_exact(const Geom& g, const AttnArgs& a, const int* flags, hipStream_t s) {
   const ItemCounts ic(g, ATTN_GROUPS);
-  hipLaunchKernelGGL(clear_flags_kernel, dim3((ic.total + 255) / 256), dim3(256), 0, s, unsafe, ic.total);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = launch_attn_fast(g, a, unsafe, s);
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_exact_kernel<ATTN_GROUPS>, dim3(ic.total), dim3(ATT_THREADS), 0, s, g, a,
-                     ic.per_head, ic.patch_items, (const int*)unsafe);
+                     ic.per_head, ic.patch_items, flags);
   return hipGetLastError();
 }
-
-size_t attn_flag_bytes(const Geom& g) { return (size_t)ItemCounts(g, ATTN_GROUPS).total * sizeof(int); }
 
 }  // namespace zebra

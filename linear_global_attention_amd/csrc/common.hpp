@@ -40,11 +40,17 @@ struct Geom {
   int nspec;           // F*S special tokens
   int spec_pad;        // nspec rounded up to KBLK
   int T_pad;           // T rounded up to KBLK
+  unsigned tpf_magic;  // floor(2^32 / tpf) + 1 (tpf >= 2): u / tpf = umulhi(u, magic) for u*tpf < 2^32
   // per tile of a frame: bits 0..19 first packed slot (within the frame),
   // bits 20..23 patch rows th, bits 24..27 patch columns tw. One 32-bit word
   // per tile so that uniform lookups are scalar loads.
   int tile[MAX_TPF];
 };
+
+// Frame of tile u (u / tpf without a division; exact because T * tpf < 2^32).
+__device__ inline int frame_of_tile(const Geom& g, int u) {
+  return g.tpf == 1 ? u : (int)__umulhi((unsigned)u, g.tpf_magic);
+}
 
 __host__ __device__ inline int tile_off(const Geom& g, int tl) { return g.tile[tl] & 0xFFFFF; }
 __host__ __device__ inline int tile_h(const Geom& g, int tl) { return (g.tile[tl] >> 20) & 15; }

@@ -16,8 +16,8 @@ hipError_t launch_landmarks(const Geom&, const u16*, const u16*, double*, float*
 size_t select_workspace_bytes(const Geom&);
 hipError_t launch_select(const Geom&, int, const u16*, const double*, int*, unsigned*, double*,
                          void*, hipStream_t);
-hipError_t launch_attn(const Geom&, const AttnArgs&, int*, hipStream_t);
-size_t attn_flag_bytes(const Geom&);
+hipError_t launch_attn(const Geom&, const AttnArgs&, void*, hipStream_t);
+size_t attn_workspace_bytes(const Geom&);
 size_t linear_workspace_bytes(const Geom&);
 hipError_t launch_linear(const Geom&, float, float, const u16*, const u16*, const u16*,
                          const float*, const float*, const float*, const float*, const float*,
@@ -56,9 +56,10 @@ zebra_status make_geom(const zebra_layout* L, Geom& g) {
   const long long T = (long long)g.F * g.tpf;
   g.tok_pf = g.S + g.R * g.C;
   g.N = (long long)g.F * g.tok_pf;
-  if (T > (1LL << 30) || g.N > (1LL << 40))
+  if (T > (1LL << 30) || g.N > (1LL << 40) || T * g.tpf >= (1LL << 32))
     return fail(ZEBRA_ERR_UNSUPPORTED, "sequence too long");
   g.T = (int)T;
+  g.tpf_magic = g.tpf >= 2 ? (unsigned)((1ULL << 32) / (unsigned)g.tpf + 1) : 0u;
   int off = 0;
   for (int a = 0; a < g.tr; ++a)
     for (int b = 0; b < g.tc; ++b) {
@@ -102,7 +103,7 @@ size_t buf_bytes(const Geom& g, int64_t k, int which) {
     case ZEBRA_BUF_GAP: return H * T * sizeof(double);
     case ZEBRA_BUF_WORKSPACE: {
       size_t m = select_workspace_bytes(g);
-      const size_t b = linear_workspace_bytes(g), c = attn_flag_bytes(g);
+      const size_t b = linear_workspace_bytes(g), c = attn_workspace_bytes(g);
       if (b > m) m = b;
       if (c > m) m = c;
       return m;
@@ -163,7 +164,7 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
       NEED(a->logn, "logn");
       NEED(a->selmask, "selmask");
       NEED(a->workspace, "workspace");
-      if (a->workspace_bytes < attn_flag_bytes(g))
+      if (a->workspace_bytes < attn_workspace_bytes(g))
         return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_sparse_attn");
       break;
     case ZEBRA_OP_LINEAR:
@@ -192,7 +193,7 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
       NEED(a->logn, "logn");
       NEED(a->lm, "lm");
       NEED(a->workspace, "workspace");
-      if (a->workspace_bytes < attn_flag_bytes(g))
+      if (a->workspace_bytes < attn_workspace_bytes(g))
         return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_dense_attn");
       break;
     default:
@@ -284,7 +285,7 @@ zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream) {
   AttnArgs A{(const u16*)a->q, (u16*)a->out, (const u16*)a->kt, (const u16*)a->vt,
              (const u16*)a->ks, (const u16*)a->vs, (const u16*)a->lm, a->logn,
              (const unsigned*)a->selmask, (g.T + 31) / 32, 1};
-  return hip_result(launch_attn(g, A, (int*)a->workspace, (hipStream_t)stream), "zebra_sparse_attn");
+  return hip_result(launch_attn(g, A, a->workspace, (hipStream_t)stream), "zebra_sparse_attn");
 }
 
 zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream) {
@@ -303,7 +304,7 @@ zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream) {
   AttnArgs A{(const u16*)a->q, (u16*)a->out, (const u16*)a->kt, (const u16*)a->vt,
              (const u16*)a->ks, (const u16*)a->vs, (const u16*)a->lm, a->logn, (const unsigned*)nullptr,
              (g.T + 31) / 32, 0};
-  return hip_result(launch_attn(g, A, (int*)a->workspace, (hipStream_t)stream), "zebra_dense_attn");
+  return hip_result(launch_attn(g, A, a->workspace, (hipStream_t)stream), "zebra_dense_attn");
 }
 
 zebra_status zebra_linear_attn(const zebra_args* a, zebra_stream stream) {

@@ -217,3 +217,29 @@ def test_c2_linear_full():
     log("c2: oracle linear stage")
     ref = olin.linear_attention(Q, K, V, tm, W, b, mu)
     close(out, ref, "c2 linear (all 175,872 x 16 rows)")
+
+
+def test_c1_sparse_in_key_ranges(monkeypatch):
+    """The main attention kernel walks the key tiles in several ranges and
+    carries fp32 partial outputs between launches (forced here with a small
+    range size): the result matches the oracle and the one-range result."""
+    L = zs.CONFIGS["c1"]
+    y = 0.8
+    q, k, v = _inputs(L, seed=7)
+    Q, K, V = widen(q), widen(k), widen(v)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    monkeypatch.delenv("ZEBRA_ATTN_RANGE_MB", raising=False)
+    one = bf16_host(Stage(L, q, k, v, y).sparse())
+    monkeypatch.setenv("ZEBRA_ATTN_RANGE_MB", "2")  # 12.8 MB of K/V per head -> 7 ranges
+    log("c1: sparse stage in 7 key ranges")
+    st = Stage(L, q, k, v, y)
+    many = bf16_host(st.sparse())
+    close(many, one, "c1 7 ranges vs 1 range")
+    rows = zs.sample_rows(L, 384, seed=7, special_frames=1)
+    ref, _ = osp.sparse_rows(Q, K, V, tm, y, rows)
+    close(st.rows(rows), ref, "c1 7-range sparse rows")
+    monkeypatch.setenv("ZEBRA_ATTN_RANGE_MB", "5")
+    st = Stage(L, q, k, v, 0.0)
+    st.dense()
+    ref = np.stack([osp.dense_rows(Q[:, h], K[:, h], V[:, h], [t])[0] for h, t in rows])
+    close(st.rows(rows), ref, "c1 3-range dense rows")

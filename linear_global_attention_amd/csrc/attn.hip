@@ -281,48 +281,48 @@ __device__ __forceinline__ long long lane_record(const Geom& g, const QueryGroup
   return (((long long)h * fi.groups_per_head + gid) * 4 + qg.row_block(s)) * 64 + lane;
 }
 
-// Streams `next()`'s items through the LDS ring: for each item, `issue`
-// starts its async loads, and once they have landed in every wave
-// `consume(code, users, buffer)` runs. LPI: loads per wave per item.
+// One staged item: its code (token tile, landmark block or special block),
+// the groups that use it, its key count and (token tiles) its first packed
+// slot within the head.
+struct Item {
+  int code;
+  unsigned users;
+  int nkeys;
+  int slot;
+};
+
+// Streams `next(item)`'s items through the LDS ring: `issue(item, buf)`
+// starts an item's async loads, and once they have landed in every wave
+// `consume(item, buf)` runs. Every wave walks the same sequence itself and
+// keeps the items in flight in a shift register (scalar registers), so no
+// item descriptor goes through LDS. LPI: loads per wave per item.
 template <int LPI, typename Next, typename Issue, typename Consume>
-__device__ __forceinline__ void stream_items(char* lds, int* qcode, unsigned* qusers, Next next, Issue issue,
-                                             Consume consume) {
-  int issued = 0;
-  bool done = false;
-  for (int j = 0; j < FNBUF - 1; ++j) {
-    int c;
-    unsigned u;
-    if (!next(c, u)) {
-      done = true;
-      break;
+__device__ __forceinline__ void stream_items(char* lds, Next next, Issue issue, Consume consume) {
+  constexpr int R = FNBUF - 1;  // items in flight
+  Item ring[R];
+  int n = 0;  // items in flight; ring[0..n) valid
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (n == j && next(ring[j])) {
+      issue(ring[j], lds + j * LDS_BUF);
+      n = j + 1;
     }
-    if (threadIdx.x == 0) {
-      qcode[j] = c;
-      qusers[j] = u;
-    }
-    issue(c, lds + j * LDS_BUF);
-    ++issued;
   }
-  for (int i = 0; i < issued; ++i) {
-    wait_items<LPI>(min(FNBUF - 2, issued - i - 1));
+  bool more = n == R;  // the walk may have further items
+  int head = 0;        // LDS buffer of ring[0]
+  while (n > 0) {
+    wait_items<LPI>(n - 1);
     ring_barrier();
-    if (!done) {
-      int c;
-      unsigned u;
-      if (next(c, u)) {
-        const int jn = issued % FNBUF;
-        if (threadIdx.x == 0) {
-          qcode[jn] = c;
-          qusers[jn] = u;
-        }
-        issue(c, lds + jn * LDS_BUF);
-        ++issued;
-      } else {
-        done = true;
-      }
-    }
-    const int buf = i % FNBUF;
-    consume(uni(qcode[buf]), (unsigned)uni((int)qusers[buf]), lds + buf * LDS_BUF);
+    Item nw;
+    const bool okn = more && next(nw);
+    more = okn;
+    if (okn) issue(nw, lds + ((head + R) % FNBUF) * LDS_BUF);
+    consume(ring[0], lds + head * LDS_BUF);
+#pragma unroll
+    for (int j = 0; j + 1 < R; ++j) ring[j] = ring[j + 1];
+    ring[R - 1] = nw;
+    n = okn ? n : n - 1;
+    head = (head + 1) % FNBUF;
   }
   ring_barrier();
 }
@@ -335,8 +335,6 @@ template <int G, int SW>
 __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, AttnArgs A, float* ws_negm,
                                                                     int* flags) {
   __shared__ __attribute__((aligned(1024))) char lds[FNBUF * LDS_BUF];
-  __shared__ int qcode[FNBUF];
-  __shared__ unsigned qusers[FNBUF];
   const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
   const int lg = lane >> 4, tl = lane & 15;
   const int simd = wave & 3, s0 = (wave >> 2) * SW;
@@ -383,25 +381,26 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, A
 
   const char* lmh = (const char*)A.LM + (long long)h * g.T_pad * LM_BYTES_PER_TILE;
   const int nlb = g.T_pad / KBLK, nsb = g.spec_pad / KBLK;
+  // items: landmark key blocks 0..nlb-1, then special key blocks
   int cnt = 0;
-  auto next = [&](int& code, unsigned& users) -> bool {
+  auto next = [&](Item& it) -> bool {
     if (cnt >= nlb + nsb) return false;
-    code = cnt++;
-    users = slots;
+    it.code = cnt++;
+    it.users = slots;
+    it.nkeys = it.code < nlb ? KBLK : min(KBLK, g.nspec - (it.code - nlb) * KBLK);
+    it.slot = 0;
     return true;
   };
   const StageOffsets so(wave, lane);
-  auto issue = [&](int code_in, char* d) {
-    const int code = uni(code_in);
-    if (code < nlb) stage_share(d, wave, lmh + (long long)code * LM_KEY_BLOCK, so.k8);
-    else stage_share(d, wave, (const char*)Ks16 + (long long)(code - nlb) * KBLK * D * 2, so.k4);
+  auto issue = [&](const Item& it, char* d) {
+    if (it.code < nlb) stage_share(d, wave, lmh + (long long)it.code * LM_KEY_BLOCK, so.k8);
+    else stage_share(d, wave, (const char*)Ks16 + (long long)(it.code - nlb) * KBLK * D * 2, so.k4);
   };
-  auto consume = [&](int code, unsigned, const char* kb) {
+  auto consume = [&](const Item& it, const char* kb) {
     if (!slots) return;
-    const bool is_lm = code < nlb;
-    bound_block<SW>(st, slots, kb, is_lm, is_lm ? KBLK : min(KBLK, g.nspec - (code - nlb) * KBLK), lane);
+    bound_block<SW>(st, slots, kb, it.code < nlb, it.nkeys, lane);
   };
-  stream_items<FCHUNKS>(lds, qcode, qusers, next, issue, consume);
+  stream_items<FCHUNKS>(lds, next, issue, consume);
 
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
@@ -425,8 +424,6 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
                                                                    int first, int last, const float* ws_negm,
                                                                    float* ws_l, f32x4* ws_o) {
   __shared__ __attribute__((aligned(1024))) char lds[FNBUF * LDS_BUF];
-  __shared__ int qcode[FNBUF];
-  __shared__ unsigned qusers[FNBUF];
   const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
   const int lg = lane >> 4, tl = lane & 15;
   const int simd = wave & 3, s0 = (wave >> 2) * SW;
@@ -483,19 +480,25 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   int w = w0 - 1, scnt = 0;
   unsigned bits = 0u, lm_users = 0u, lane_word = 0u;
   bool lm_due = false;
-  auto next = [&](int& code, unsigned& users) -> bool {
+  auto next = [&](Item& it) -> bool {
     for (;;) {
       if (lm_due) {
         lm_due = false;
-        code = g.T + w;
-        users = lm_users;
+        it.code = g.T + w;
+        it.users = lm_users;
+        it.nkeys = KBLK;
+        it.slot = 0;
         return true;
       }
       if (bits) {
         const int b = __builtin_ctz(bits);
         bits &= bits - 1u;
-        code = w * 32 + b;
-        users = sparse ? (unsigned)__builtin_amdgcn_ballot_w64((lane_word >> b) & 1u) : valid_groups;
+        const int u = w * 32 + b;
+        const int fu = frame_of_tile(g, u), te = g.tile[u - fu * g.tpf];
+        it.code = u;
+        it.users = sparse ? (unsigned)__builtin_amdgcn_ballot_w64((lane_word >> b) & 1u) : valid_groups;
+        it.nkeys = ((te >> 20) & 15) * ((te >> 24) & 15);
+        it.slot = fu * g.slots_pf + (te & 0xFFFFF);
         return true;
       }
       if (w + 1 >= w1) break;
@@ -521,19 +524,21 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
       }
     }
     if (last && scnt < nsb) {
-      code = g.T + nlb + scnt++;
-      users = valid_groups;
+      it.code = g.T + nlb + scnt;
+      it.users = valid_groups;
+      it.nkeys = min(KBLK, g.nspec - scnt * KBLK);
+      it.slot = 0;
+      ++scnt;
       return true;
     }
     return false;
   };
   const StageOffsets so(wave, lane);
-  auto issue = [&](int code_in, char* d) {
-    const int code = uni(code_in);
+  auto issue = [&](const Item& it, char* d) {
+    const int code = it.code;
     if (code < g.T) {
-      const int fu = frame_of_tile(g, code), tu = code - fu * g.tpf;
-      const long long base = ((long long)fu * g.slots_pf + tile_off(g, tu)) * D * 2;
-      if (tile_n(g, tu) > KBLK) {
+      const long long base = (long long)it.slot * D * 2;
+      if (it.nkeys > KBLK) {
         stage_share(d, wave, (const char*)Kt16 + base, so.k8);
         stage_share(d + LDS_V, wave, (const char*)Vt16 + base, so.v8);
       } else {
@@ -550,17 +555,14 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
       stage_share(d + LDS_V, wave, (const char*)Vs16 + b, so.v4);
     }
   };
-  auto consume = [&](int code, unsigned users, const char* kb) {
-    const unsigned us = (users >> s0) & slots;
+  auto consume = [&](const Item& it, const char* kb) {
+    const unsigned us = (it.users >> s0) & slots;
     if (!us) return;
-    int nkeys = KBLK, lb = -1;
-    if (code < g.T) nkeys = tile_n(g, code - frame_of_tile(g, code) * g.tpf);
-    else if (code < g.T + nlb) lb = code - g.T;
-    else nkeys = min(KBLK, g.nspec - (code - g.T - nlb) * KBLK);
-    attend_block<SW>(st, us, kb, 0, nkeys, lb, mrow0, A.nwords, lane);
-    if (nkeys > KBLK) attend_block<SW>(st, us, kb, KBLK, nkeys - KBLK, -1, mrow0, A.nwords, lane);
+    const int lb = it.code >= g.T && it.code < g.T + nlb ? it.code - g.T : -1;
+    attend_block<SW>(st, us, kb, 0, it.nkeys, lb, mrow0, A.nwords, lane);
+    if (it.nkeys > KBLK) attend_block<SW>(st, us, kb, KBLK, it.nkeys - KBLK, -1, mrow0, A.nwords, lane);
   };
-  stream_items<2 * FCHUNKS>(lds, qcode, qusers, next, issue, consume);
+  stream_items<2 * FCHUNKS>(lds, next, issue, consume);
   // Per-lane indices are recomputed after the walk rather than kept live
   // across it from the set-up (register pressure).
   int lane_a = lane;

@@ -94,7 +94,7 @@ def cpu_baseline(L, q, k, v, y, seed):
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas = 1
-    R = 192
+    R = 640
     g = np.random.default_rng(seed)
     tm = TileMap(L.frames, L.specials, L.rows, L.cols)
     patch = np.nonzero(tm.tile_of >= 0)[0]

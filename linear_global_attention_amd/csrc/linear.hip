@@ -7,12 +7,13 @@
 // feature map. "A closed-form fit avoids retraining from scratch": a centred
 // affine correction y = mu + W (o - mu) + b is applied to the output.
 //
-// Three kernels:
+// Four kernels:
 //   linear_state  stream K and V once: phi(k) for 16 tokens per wave pass,
 //                 staged with V in LDS, then S += phi(K)^T V (bf16 MFMA,
 //                 fp32 accumulators) and z += phi(k); one partial per wave.
-//   linear_reduce fixed-order sum of the partials (fp64), then
-//                 S' = S W^T split into bf16 high/low parts and
+//   linear_sum    fixed-order fp64 sum of the partials, one element per
+//                 thread over all of a head's partials;
+//   linear_fold   S' = S W^T split into bf16 high/low parts and
 //                 b' = mu - W mu + b, because W o = phi(q)^T S W^T / den.
 //   linear_apply  stream Q once: phi(q), y^T = S'^T phi(q)^T on MFMA,
 //                 divide by phi(q).z, add b', store bf16.
@@ -30,6 +31,7 @@ constexpr int LIN_THREADS = 256;
 constexpr int LIN_WAVES = LIN_THREADS / 64;
 constexpr int LIN_TOKENS_PER_WG = 8192;
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int LIN_STATE = D * D + D;  // floats of one partial state: S [64][64] then z [64]
 
 struct LinParams {
   float eps;
@@ -63,8 +65,11 @@ __device__ inline void token_pos(const Geom& g, long long tok, int& pr, int& pc)
 }
 
 // Feature map of one token's 16 lane channels (x holds them, fp32, in
-// lane order). On return x holds phi(x) for those channels.
-__device__ inline void featurize16(float x[16], const float gain[16], const float2* tab, int pr,
+// lane order). On return x holds phi(x) for those channels, or, with
+// NORMALIZE false, phi(x) times a positive per-token constant (enough where
+// phi only enters a ratio). `gained`: multiply by the RMSNorm gains.
+template <bool NORMALIZE>
+__device__ inline void featurize16(float x[16], bool gained, const float gain[16], const float2* tab, int pr,
                                    int pc, int g, float eps) {
   float ss = 0.f;
 #pragma unroll
@@ -72,8 +77,10 @@ __device__ inline void featurize16(float x[16], const float gain[16], const floa
   ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
   const float r = 1.0f / sqrtf(ss * (1.0f / 64.0f) + eps);
+  if (gained) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] *= gain[i];
+    for (int i = 0; i < 16; ++i) x[i] *= gain[i];
+  }
   // rotary: pairs (i, i+4) for i in 0..3 (row) and 8..11 (column)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -92,39 +99,56 @@ __device__ inline void featurize16(float x[16], const float gain[16], const floa
   for (int i = 1; i < 16; ++i) m = fmaxf(m, x[i]);
   m = fmaxf(m, __shfl_xor(m, 16, 64));
   m = fmaxf(m, __shfl_xor(m, 32, 64));
-  const float sc = r * LOG2E;
-  float s = 0.f;
+  const float sc = r * LOG2E, off = -m * sc;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    x[i] = __builtin_amdgcn_exp2f((x[i] - m) * sc);
-    s += x[i];
+  for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_exp2f(fmaf(x[i], sc, off));
+  if (NORMALIZE) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += x[i];
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] *= inv;
   }
-  s += __shfl_xor(s, 16, 64);
-  s += __shfl_xor(s, 32, 64);
-  const float inv = 1.0f / s;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] *= inv;
 }
 
-__device__ inline void load16(const u16* row, int g, float x[16]) {
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 (hardware round to nearest even), a in the low half
+__device__ inline unsigned pack_bf16x2(float a, float b) {
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2_t));
+}
+
+// The lane's 16 channels of one bf16 row, raw (4 x 8 bytes); zeros past the end.
+__device__ inline void fetch16(const u16* row, int g, bool ok, uint2 w[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w[q] = ok ? *(const uint2*)(row + q * 16 + 4 * g) : make_uint2(0u, 0u);
+}
+
+__device__ inline void unpack16(const uint2 w[4], float x[16]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint2 w = *(const uint2*)(row + q * 16 + 4 * g);
-    x[q * 4 + 0] = __uint_as_float(w.x << 16);
-    x[q * 4 + 1] = __uint_as_float(w.x & 0xFFFF0000u);
-    x[q * 4 + 2] = __uint_as_float(w.y << 16);
-    x[q * 4 + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+    x[q * 4 + 0] = __uint_as_float(w[q].x << 16);
+    x[q * 4 + 1] = __uint_as_float(w[q].x & 0xFFFF0000u);
+    x[q * 4 + 2] = __uint_as_float(w[q].y << 16);
+    x[q * 4 + 3] = __uint_as_float(w[q].y & 0xFFFF0000u);
   }
 }
 
 // grid (nchunks, H), block 256. partial p = chunk*4 + wave holds
 // S [64][64] (row a = phi channel, column c = value channel) then z [64].
-__global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
+__global__ void __launch_bounds__(LIN_THREADS, 2) linear_state_kernel(
     Geom g, LinParams P, const u16* __restrict__ K, const u16* __restrict__ V,
     const float* __restrict__ gk, float* __restrict__ partials, int nchunks) {
   __shared__ float2 tab[MAX_GRID * 16];
-  __shared__ u16 phis[LIN_WAVES][32][D + 8];
-  __shared__ u16 vals[LIN_WAVES][32][D + 8];
+  // phi(k) and v of a wave's 32 tokens, channel-major ([channel][token],
+  // rows of 40 u16 = 80 bytes): an MFMA operand fragment (one channel, 8
+  // consecutive tokens) is one 16-byte read
+  __shared__ __attribute__((aligned(16))) u16 phis[LIN_WAVES][D][40];
+  __shared__ __attribute__((aligned(16))) u16 vals[LIN_WAVES][D][40];
   const int h = blockIdx.y, chunk = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, tl = lane & 15;
@@ -146,32 +170,45 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
   const long long t_begin = (long long)chunk * LIN_TOKENS_PER_WG;
   const long long t_end = min((long long)g.N, t_begin + LIN_TOKENS_PER_WG);
   const long long rs = (long long)g.H * D;
-  for (long long t0 = t_begin + wave * 32; t0 < t_end; t0 += 32 * LIN_WAVES) {
+  constexpr int STRIDE = 32 * LIN_WAVES;
+  // raw K and V of the wave's 32 tokens: this iteration's and the next's
+  // (requested one iteration ahead so the wave always has loads in flight)
+  uint2 kc[2][4], vc[2][4];
+  auto fetch = [&](long long t0, uint2 kr[2][4], uint2 vr[2][4]) {
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const long long tok = t0 + pass * 16 + tl;
+      fetch16(K + tok * rs + h * D, grp, tok < t_end, kr[pass]);
+      fetch16(V + tok * rs + h * D, grp, tok < t_end, vr[pass]);
+    }
+  };
+  fetch(t_begin + wave * 32, kc, vc);
+  for (long long t0 = t_begin + wave * 32; t0 < t_end; t0 += STRIDE) {
+    uint2 kn[2][4], vn[2][4];
+    fetch(t0 + STRIDE, kn, vn);
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
       const int slot = pass * 16 + tl;
       const long long tok = t0 + slot;
-      float x[16], vv[16];
-      if (tok < t_end) {
-        load16(K + tok * rs + h * D, grp, x);
-        load16(V + tok * rs + h * D, grp, vv);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = vv[i] = 0.f;
-      }
+      float x[16];
+      unpack16(kc[pass], x);
       int pr = 0, pc = 0;
       if (tok < t_end) token_pos(g, tok, pr, pc);
-      featurize16(x, gain, tab, pr, pc, grp, P.eps);
+      featurize16<true>(x, gk != nullptr, gain, tab, pr, pc, grp, P.eps);
       if (tok >= t_end) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[i] = 0.f;
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const u16 pb = f2bf(x[i]);
-        zacc[i] += bf2f(pb);
-        phis[wave][slot][lane_channel(grp, i)] = pb;
-        vals[wave][slot][lane_channel(grp, i)] = f2bf(vv[i]);
+      for (int i = 0; i < 16; i += 2) {
+        const unsigned pw = pack_bf16x2(x[i], x[i + 1]);  // round to nearest even
+        zacc[i] += __uint_as_float(pw << 16);
+        zacc[i + 1] += __uint_as_float(pw & 0xFFFF0000u);
+        phis[wave][lane_channel(grp, i)][slot] = (u16)(pw & 0xFFFFu);
+        phis[wave][lane_channel(grp, i + 1)][slot] = (u16)(pw >> 16);
+        const unsigned vw = (i & 2) ? vc[pass][i >> 2].y : vc[pass][i >> 2].x;  // raw bf16 values
+        vals[wave][lane_channel(grp, i)][slot] = (u16)(vw & 0xFFFFu);
+        vals[wave][lane_channel(grp, i + 1)][slot] = (u16)(vw >> 16);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS writes done (single wave)
@@ -180,13 +217,8 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
     bf16x8 A[4], B[4];
 #pragma unroll
     for (int ab = 0; ab < 4; ++ab) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const u16 pa = phis[wave][8 * grp + m][ab * 16 + tl];
-        const u16 vb = vals[wave][8 * grp + m][ab * 16 + tl];
-        A[ab][m] = __builtin_bit_cast(__bf16, pa);
-        B[ab][m] = __builtin_bit_cast(__bf16, vb);
-      }
+      A[ab] = *(const bf16x8*)&phis[wave][ab * 16 + tl][8 * grp];
+      B[ab] = *(const bf16x8*)&vals[wave][ab * 16 + tl][8 * grp];
     }
 #pragma unroll
     for (int ab = 0; ab < 4; ++ab)
@@ -194,6 +226,13 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
       for (int cb = 0; cb < 4; ++cb)
         acc[ab][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ab], B[cb], acc[ab][cb], 0, 0, 0);
     __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        kc[pass][q] = kn[pass][q];
+        vc[pass][q] = vn[pass][q];
+      }
   }
   // z: sum the 16 lanes of each channel group
 #pragma unroll
@@ -205,7 +244,7 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
     v += __shfl_xor(v, 8, 64);
     zacc[i] = v;
   }
-  float* out = partials + ((long long)h * nchunks * LIN_WAVES + chunk * LIN_WAVES + wave) * (D * D + D);
+  float* out = partials + ((long long)h * nchunks * LIN_WAVES + chunk * LIN_WAVES + wave) * LIN_STATE;
   // MFMA 16x16 output: lane holds column tl, rows 4*grp + 0..3
 #pragma unroll
   for (int ab = 0; ab < 4; ++ab)
@@ -219,22 +258,29 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
   }
 }
 
-// grid (H), block 256. Writes per head: Sp_hi, Sp_lo bf16 [64][64] holding
-// (S W^T)^T with columns in lane-channel order, z fp32 [64], bp fp32 [64].
-__global__ void __launch_bounds__(256) linear_reduce_kernel(
-    Geom g, const float* __restrict__ partials, int nparts, const float* __restrict__ W,
-    const float* __restrict__ b, const float* __restrict__ mu, u16* __restrict__ sp,
-    float* __restrict__ zb) {
+// grid (ceil(LIN_STATE / 256), H), block 256: fixed-order fp64 sum of the
+// per-wave partial states of a head, one element per thread.
+__global__ void __launch_bounds__(256) linear_sum_kernel(const float* __restrict__ partials, int nparts,
+                                                         double* __restrict__ state) {
+  const int h = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= LIN_STATE) return;
+  const float* base = partials + (long long)h * nparts * LIN_STATE + e;
+  double s = 0.0;
+  for (int p = 0; p < nparts; ++p) s += (double)base[(long long)p * LIN_STATE];
+  state[(long long)h * LIN_STATE + e] = s;
+}
+
+// grid (H), block 256. Folds the affine correction into the state: writes
+// per head Sp_hi, Sp_lo bf16 [64][64] holding (S W^T)^T with columns in
+// lane-channel order, z fp32 [64] and b' = mu - W mu + b fp32 [64].
+__global__ void __launch_bounds__(256) linear_fold_kernel(const double* __restrict__ state,
+                                                          const float* __restrict__ W, const float* __restrict__ b,
+                                                          const float* __restrict__ mu, u16* __restrict__ sp,
+                                                          float* __restrict__ zb) {
   __shared__ double S[D][D + 1];
-  __shared__ double z[D];
   const int h = blockIdx.x, tid = threadIdx.x;
-  const float* base = partials + (long long)h * nparts * (D * D + D);
-  for (int e = tid; e < D * D + D; e += 256) {
-    double s = 0.0;
-    for (int p = 0; p < nparts; ++p) s += (double)base[(long long)p * (D * D + D) + e];
-    if (e < D * D) S[e / D][e % D] = s;
-    else z[e - D * D] = s;
-  }
+  const double* st = state + (long long)h * LIN_STATE;
+  for (int e = tid; e < D * D; e += 256) S[e / D][e % D] = st[e];
   __syncthreads();
   const float* Wh = W ? W + (long long)h * D * D : nullptr;
   u16* hi = sp + (long long)h * 2 * D * D;
@@ -244,21 +290,20 @@ __global__ void __launch_bounds__(256) linear_reduce_kernel(
     const int e = idx / D, p = idx % D;
     const int ks = p >> 5, gg = (p & 31) >> 3, m = p & 7;
     const int a = lane_channel(gg, ks * 8 + m);
-    double s;
+    double v;
     if (Wh) {
-      s = 0.0;
-      for (int c = 0; c < D; ++c) s += S[a][c] * (double)Wh[e * D + c];
+      v = 0.0;
+      for (int c = 0; c < D; ++c) v += S[a][c] * (double)Wh[e * D + c];
     } else {
-      s = S[a][e];
+      v = S[a][e];
     }
-    const float sf = (float)s;
-    const u16 hb = f2bf(sf);
+    const u16 hb = f2bf((float)v);
     hi[idx] = hb;
-    lo[idx] = f2bf((float)(s - (double)bf2f(hb)));
+    lo[idx] = f2bf((float)(v - (double)bf2f(hb)));
   }
   float* zo = zb + (long long)h * 2 * D;
   if (tid < D) {
-    zo[tid] = (float)z[tid];
+    zo[tid] = (float)st[D * D + tid];
     // b' = mu - W mu + b
     double wm = 0.0, m_e = mu ? (double)mu[h * D + tid] : 0.0;
     if (mu) {
@@ -270,7 +315,7 @@ __global__ void __launch_bounds__(256) linear_reduce_kernel(
 }
 
 // grid (nchunks, H), block 256.
-__global__ void __launch_bounds__(LIN_THREADS) linear_apply_kernel(
+__global__ void __launch_bounds__(LIN_THREADS, 3) linear_apply_kernel(
     Geom g, LinParams P, const u16* __restrict__ Q, const float* __restrict__ gq,
     const u16* __restrict__ sp, const float* __restrict__ zb, u16* __restrict__ out) {
   __shared__ float2 tab[MAX_GRID * 16];
@@ -306,25 +351,37 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_apply_kernel(
   const long long t_begin = (long long)chunk * LIN_TOKENS_PER_WG;
   const long long t_end = min((long long)g.N, t_begin + LIN_TOKENS_PER_WG);
   const long long rs = (long long)g.H * D;
-  for (long long t0 = t_begin + wave * 16; t0 < t_end; t0 += 16 * LIN_WAVES) {
+  constexpr int STRIDE = 16 * LIN_WAVES;
+  // raw Q rows of this iteration and the next two (requested ahead)
+  uint2 q0[4], q1[4];
+  fetch16(Q + (t_begin + wave * 16 + tl) * rs + h * D, grp, t_begin + wave * 16 + tl < t_end, q0);
+  fetch16(Q + (t_begin + wave * 16 + STRIDE + tl) * rs + h * D, grp, t_begin + wave * 16 + STRIDE + tl < t_end, q1);
+  for (long long t0 = t_begin + wave * 16; t0 < t_end; t0 += STRIDE) {
     const long long tok = t0 + tl;
+    uint2 q2[4];
+    fetch16(Q + (tok + 2 * STRIDE) * rs + h * D, grp, tok + 2 * STRIDE < t_end, q2);
     float x[16];
-    if (tok < t_end) load16(Q + tok * rs + h * D, grp, x);
-    else {
+    unpack16(q0, x);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = 0.f;
+    for (int q = 0; q < 4; ++q) {
+      q0[q] = q1[q];
+      q1[q] = q2[q];
     }
     int pr = 0, pc = 0;
     if (tok < t_end) token_pos(g, tok, pr, pc);
-    featurize16(x, gain, tab, pr, pc, grp, P.eps);
-    bf16x8 Bk[2];
+    // phi(q) enters o = phi(q)^T S' / phi(q)^T z only as a ratio
+    featurize16<false>(x, gq != nullptr, gain, tab, pr, pc, grp, P.eps);
+    unsigned pw[8];
     float den = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const u16 pb = f2bf(x[i]);
-      den += bf2f(pb) * zl[i];
-      Bk[i >> 3][i & 7] = __builtin_bit_cast(__bf16, pb);
+    for (int i = 0; i < 16; i += 2) {
+      pw[i >> 1] = pack_bf16x2(x[i], x[i + 1]);
+      den = fmaf(__uint_as_float(pw[i >> 1] << 16), zl[i], den);
+      den = fmaf(__uint_as_float(pw[i >> 1] & 0xFFFF0000u), zl[i + 1], den);
     }
+    bf16x8 Bk[2];
+    Bk[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    Bk[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
     den += __shfl_xor(den, 16, 64);
     den += __shfl_xor(den, 32, 64);
     const float inv = 1.0f / den;
@@ -345,12 +402,8 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_apply_kernel(
 #pragma unroll
       for (int eb = 0; eb < 4; ++eb) {
         uint2 w;
-        const u16 b0 = f2bf(y[eb][0] * inv + bp[eb * 4 + 0]);
-        const u16 b1 = f2bf(y[eb][1] * inv + bp[eb * 4 + 1]);
-        const u16 b2 = f2bf(y[eb][2] * inv + bp[eb * 4 + 2]);
-        const u16 b3 = f2bf(y[eb][3] * inv + bp[eb * 4 + 3]);
-        w.x = (unsigned)b0 | ((unsigned)b1 << 16);
-        w.y = (unsigned)b2 | ((unsigned)b3 << 16);
+        w.x = pack_bf16x2(fmaf(y[eb][0], inv, bp[eb * 4 + 0]), fmaf(y[eb][1], inv, bp[eb * 4 + 1]));
+        w.y = pack_bf16x2(fmaf(y[eb][2], inv, bp[eb * 4 + 2]), fmaf(y[eb][3], inv, bp[eb * 4 + 3]));
         *(uint2*)(orow + eb * 16 + 4 * grp) = w;
       }
     }
@@ -360,24 +413,28 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_apply_kernel(
 int linear_chunks(const Geom& g) { return (int)((g.N + LIN_TOKENS_PER_WG - 1) / LIN_TOKENS_PER_WG); }
 
 size_t linear_workspace_bytes(const Geom& g) {
-  const size_t parts = (size_t)g.H * linear_chunks(g) * LIN_WAVES * (D * D + D) * sizeof(float);
+  const size_t parts = (size_t)g.H * linear_chunks(g) * LIN_WAVES * LIN_STATE * sizeof(float);
+  const size_t state = (size_t)g.H * LIN_STATE * sizeof(double);
   const size_t red = (size_t)g.H * (2 * D * D * sizeof(u16) + 2 * D * sizeof(float));
-  return parts + red;
+  return parts + state + red;
 }
 
-// Workspace: partials, then Sp [H][2][64][64] bf16, then zb [H][2][64] fp32.
+// Workspace: partials, the summed states fp64 [H][LIN_STATE], then Sp
+// [H][2][64][64] bf16, then zb [H][2][64] fp32.
 hipError_t launch_linear(const Geom& g, float eps, float base, const u16* Q, const u16* K,
                          const u16* V, const float* W, const float* b, const float* mu,
                          const float* gq, const float* gk, u16* out, void* ws, hipStream_t s) {
   const int nch = linear_chunks(g);
   float* parts = (float*)ws;
-  u16* sp = (u16*)(parts + (size_t)g.H * nch * LIN_WAVES * (D * D + D));
+  double* state = (double*)(parts + (size_t)g.H * nch * LIN_WAVES * LIN_STATE);
+  u16* sp = (u16*)(state + (size_t)g.H * LIN_STATE);
   float* zb = (float*)(sp + (size_t)g.H * 2 * D * D);
   LinParams P{eps, base};
   hipLaunchKernelGGL(linear_state_kernel, dim3(nch, g.H), dim3(LIN_THREADS), 0, s, g, P, K, V, gk,
                      parts, nch);
-  hipLaunchKernelGGL(linear_reduce_kernel, dim3(g.H), dim3(256), 0, s, g, parts, nch * LIN_WAVES,
-                     W, b, mu, sp, zb);
+  hipLaunchKernelGGL(linear_sum_kernel, dim3((LIN_STATE + 255) / 256, g.H), dim3(256), 0, s,
+                     (const float*)parts, nch * LIN_WAVES, state);
+  hipLaunchKernelGGL(linear_fold_kernel, dim3(g.H), dim3(256), 0, s, (const double*)state, W, b, mu, sp, zb);
   hipLaunchKernelGGL(linear_apply_kernel, dim3(nch, g.H), dim3(LIN_THREADS), 0, s, g, P, Q, gq, sp,
                      zb, out);
   return hipGetLastError();

@@ -51,17 +51,33 @@ __device__ inline void build_rope_table(float2* tab, int npos, float base) {
   }
 }
 
-__device__ inline void token_pos(const Geom& g, long long tok, int& pr, int& pc) {
-  const long long f = tok / g.tok_pf;
-  const int loc = (int)(tok - f * g.tok_pf);
-  if (loc < g.S) {
-    pr = 0;
-    pc = 0;
-  } else {
-    const int p = loc - g.S;
-    pr = p / g.C;
-    pc = p - pr * g.C;
+// Reciprocals for token -> (frame, patch row, patch column) without integer
+// division: quotients from a rounded reciprocal, then one exact correction.
+struct PosDiv {
+  double inv_tpf;  // 1 / tokens per frame
+  float inv_c;     // 1 / patch columns
+  __device__ explicit PosDiv(const Geom& g) : inv_tpf(1.0 / (double)g.tok_pf), inv_c(1.0f / (float)g.C) {}
+};
+
+// Rotary position of token tok: (patch row, patch column), specials (0, 0).
+__device__ inline void token_pos(const Geom& g, const PosDiv& dv, long long tok, int& pr, int& pc) {
+  long long f = (long long)((double)tok * dv.inv_tpf);
+  long long loc = tok - f * g.tok_pf;
+  if (loc < 0) loc += g.tok_pf;
+  else if (loc >= g.tok_pf) loc -= g.tok_pf;
+  const int p = max((int)loc - g.S, 0);  // p < 2^14: exact in fp32
+  int r = (int)((float)p * dv.inv_c);
+  int c = p - r * g.C;
+  if (c < 0) {
+    --r;
+    c += g.C;
+  } else if (c >= g.C) {
+    ++r;
+    c -= g.C;
   }
+  const bool special = loc < g.S;
+  pr = special ? 0 : r;
+  pc = special ? 0 : c;
 }
 
 // Feature map of one token's 16 lane channels (x holds them, fp32, in
@@ -76,7 +92,7 @@ __device__ inline void featurize16(float x[16], bool gained, const float gain[16
   for (int i = 0; i < 16; ++i) ss += x[i] * x[i];
   ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
-  const float r = 1.0f / sqrtf(ss * (1.0f / 64.0f) + eps);
+  const float r = __builtin_amdgcn_rsqf(ss * (1.0f / 64.0f) + eps);
   if (gained) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] *= gain[i];
@@ -108,7 +124,7 @@ __device__ inline void featurize16(float x[16], bool gained, const float gain[16
     for (int i = 0; i < 16; ++i) s += x[i];
     s += __shfl_xor(s, 16, 64);
     s += __shfl_xor(s, 32, 64);
-    const float inv = 1.0f / s;
+    const float inv = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] *= inv;
   }
@@ -121,6 +137,32 @@ __device__ inline unsigned pack_bf16x2(float a, float b) {
   const f32x2_t f = {a, b};
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2_t));
 }
+
+typedef void __attribute__((address_space(3))) lin_lds_void;
+constexpr int AP_NB = 6;  // LDS ring slots per wave in linear_apply
+
+// Wait until at most n (even, <= 24) of this wave's vector memory
+// operations are pending.
+#define LIN_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+__device__ inline void lin_wait_vm(int n) {
+  switch (n) {
+    case 0: LIN_VMCNT(0); break;
+    case 2: LIN_VMCNT(2); break;
+    case 4: LIN_VMCNT(4); break;
+    case 6: LIN_VMCNT(6); break;
+    case 8: LIN_VMCNT(8); break;
+    case 10: LIN_VMCNT(10); break;
+    case 12: LIN_VMCNT(12); break;
+    case 14: LIN_VMCNT(14); break;
+    case 16: LIN_VMCNT(16); break;
+    case 18: LIN_VMCNT(18); break;
+    case 20: LIN_VMCNT(20); break;
+    case 22: LIN_VMCNT(22); break;
+    case 24: LIN_VMCNT(24); break;
+    default: LIN_VMCNT(0); break;
+  }
+}
+static_assert(6 * (AP_NB - 2) <= 24, "lin_wait_vm covers the pending counts of linear_apply");
 
 // The lane's 16 channels of one bf16 row, raw (4 x 8 bytes); zeros past the end.
 __device__ inline void fetch16(const u16* row, int g, bool ok, uint2 w[4]) {
@@ -153,6 +195,7 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_state_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, tl = lane & 15;
   build_rope_table(tab, max(g.R, g.C), P.base);
+  const PosDiv dv(g);
   float gain[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) gain[i] = gk ? gk[h * D + lane_channel(grp, i)] : 1.0f;
@@ -193,7 +236,7 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_state_kernel(
       float x[16];
       unpack16(kc[pass], x);
       int pr = 0, pc = 0;
-      if (tok < t_end) token_pos(g, tok, pr, pc);
+      if (tok < t_end) token_pos(g, dv, tok, pr, pc);
       featurize16<true>(x, gk != nullptr, gain, tab, pr, pc, grp, P.eps);
       if (tok >= t_end) {
 #pragma unroll
@@ -314,15 +357,19 @@ __global__ void __launch_bounds__(256) linear_fold_kernel(const double* __restri
   }
 }
 
-// grid (nchunks, H), block 256.
-__global__ void __launch_bounds__(LIN_THREADS, 3) linear_apply_kernel(
+// grid (nchunks, H), block 256. Each wave streams its 16-token groups of Q
+// through a private LDS ring of AP_NB slots (async global->LDS loads, no
+// workgroup barrier), AP_NB - 1 groups ahead.
+__global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
     Geom g, LinParams P, const u16* __restrict__ Q, const float* __restrict__ gq,
     const u16* __restrict__ sp, const float* __restrict__ zb, u16* __restrict__ out) {
   __shared__ float2 tab[MAX_GRID * 16];
+  __shared__ __attribute__((aligned(1024))) char qring[LIN_WAVES][AP_NB][2048];
   const int h = blockIdx.y, chunk = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, tl = lane & 15;
   build_rope_table(tab, max(g.R, g.C), P.base);
+  const PosDiv dv(g);
   float gain[16], zl[16], bp[16];
   const float* zo = zb + (long long)h * 2 * D;
 #pragma unroll
@@ -351,24 +398,48 @@ __global__ void __launch_bounds__(LIN_THREADS, 3) linear_apply_kernel(
   const long long t_begin = (long long)chunk * LIN_TOKENS_PER_WG;
   const long long t_end = min((long long)g.N, t_begin + LIN_TOKENS_PER_WG);
   const long long rs = (long long)g.H * D;
-  constexpr int STRIDE = 16 * LIN_WAVES;
-  // raw Q rows of this iteration and the next two (requested ahead)
-  uint2 q0[4], q1[4];
-  fetch16(Q + (t_begin + wave * 16 + tl) * rs + h * D, grp, t_begin + wave * 16 + tl < t_end, q0);
-  fetch16(Q + (t_begin + wave * 16 + STRIDE + tl) * rs + h * D, grp, t_begin + wave * 16 + STRIDE + tl < t_end, q1);
-  for (long long t0 = t_begin + wave * 16; t0 < t_end; t0 += STRIDE) {
-    const long long tok = t0 + tl;
-    uint2 q2[4];
-    fetch16(Q + (tok + 2 * STRIDE) * rs + h * D, grp, tok + 2 * STRIDE < t_end, q2);
-    float x[16];
-    unpack16(q0, x);
+  // This wave's 16-token groups: m = 0..n-1, first token t_begin + 16 (wave + 4m).
+  const long long first = t_begin + 16 * wave;
+  const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
+  char* ring = &qring[wave][0][0];
+  // Stage group m's 16 Q rows (2 KB) into ring slot m % AP_NB: two async
+  // 1 KB loads, lane l -> row 8j + l/8, 16-byte column (l%8) ^ (row%8)
+  // (swizzled so the row-per-lane reads below are spread over the banks).
+  // Rows past t_end repeat the last token, whose output they then rewrite
+  // with the same value: every lane issues every load and store, so the
+  // wave's memory counter advances by exactly 2 per group staged and 4 per
+  // group stored.
+  auto stage = [&](int m) {
+    const long long r0 = first + 64LL * m;
+    char* dst = ring + (m % AP_NB) * 2048;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 8 * j + (lane >> 3);
+      const long long tok = min(r0 + r, t_end - 1);
+      const int c = (lane & 7) ^ (r & 7);
+      const char* src = (const char*)(Q + tok * rs + h * D) + c * 16;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
+    }
+  };
+  for (int m = 0; m < AP_NB - 1 && m < n; ++m) stage(m);
+  for (int m = 0; m < n; ++m) {
+    // group m has landed once at most `later` newer memory operations of
+    // this wave are pending: the newer stages (2 each) and stores (4 each)
+    const int later = 2 * min(AP_NB - 2, n - 1 - m) + 4 * min(m, AP_NB - 2);
+    lin_wait_vm(later);
+    asm volatile("" ::: "memory");
+    const char* src = ring + (m % AP_NB) * 2048 + tl * 128;
+    uint2 qr[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      q0[q] = q1[q];
-      q1[q] = q2[q];
+      const int cc = (2 * q + (grp >> 1)) ^ (tl & 7);
+      qr[q] = *(const uint2*)(src + cc * 16 + (grp & 1) * 8);
     }
+    const long long tok = min(first + 64LL * m + tl, t_end - 1);
+    float x[16];
+    unpack16(qr, x);
     int pr = 0, pc = 0;
-    if (tok < t_end) token_pos(g, tok, pr, pc);
+    token_pos(g, dv, tok, pr, pc);
     // phi(q) enters o = phi(q)^T S' / phi(q)^T z only as a ratio
     featurize16<false>(x, gq != nullptr, gain, tab, pr, pc, grp, P.eps);
     unsigned pw[8];
@@ -384,7 +455,7 @@ __global__ void __launch_bounds__(LIN_THREADS, 3) linear_apply_kernel(
     Bk[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
     den += __shfl_xor(den, 16, 64);
     den += __shfl_xor(den, 32, 64);
-    const float inv = 1.0f / den;
+    const float inv = __builtin_amdgcn_rcpf(den);
     f32x4 y[4];
 #pragma unroll
     for (int eb = 0; eb < 4; ++eb) {
@@ -396,17 +467,16 @@ __global__ void __launch_bounds__(LIN_THREADS, 3) linear_apply_kernel(
       }
       y[eb] = a;
     }
-    // output token = t0 + tl (MFMA column), channels eb*16 + 4*grp + r
-    if (tok < t_end) {
-      u16* orow = out + tok * rs + h * D;
+    // output token = tok (MFMA column), channels eb*16 + 4*grp + r
+    u16* orow = out + tok * rs + h * D;
 #pragma unroll
-      for (int eb = 0; eb < 4; ++eb) {
-        uint2 w;
-        w.x = pack_bf16x2(fmaf(y[eb][0], inv, bp[eb * 4 + 0]), fmaf(y[eb][1], inv, bp[eb * 4 + 1]));
-        w.y = pack_bf16x2(fmaf(y[eb][2], inv, bp[eb * 4 + 2]), fmaf(y[eb][3], inv, bp[eb * 4 + 3]));
-        *(uint2*)(orow + eb * 16 + 4 * grp) = w;
-      }
+    for (int eb = 0; eb < 4; ++eb) {
+      uint2 w;
+      w.x = pack_bf16x2(fmaf(y[eb][0], inv, bp[eb * 4 + 0]), fmaf(y[eb][1], inv, bp[eb * 4 + 1]));
+      w.y = pack_bf16x2(fmaf(y[eb][2], inv, bp[eb * 4 + 2]), fmaf(y[eb][3], inv, bp[eb * 4 + 3]));
+      *(uint2*)(orow + eb * 16 + 4 * grp) = w;
     }
+    if (m + AP_NB - 1 < n) stage(m + AP_NB - 1);
   }
 }
 

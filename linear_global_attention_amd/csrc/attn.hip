@@ -15,8 +15,9 @@
 // all four waves have the same active slots for every staged key tile and
 // none waits for another at the tile barrier, while the two workgroups of
 // a CU, each with its own barrier, fill each other's MFMA and VALU gaps.
-// Tiles are streamed through a ring of FNBUF LDS buffers (async
-// global->LDS loads, exact vmcnt waits, one barrier per tile). The tiles a
+// Tiles are streamed through a ring of FNBUF = 4 LDS buffers in batches of
+// two (async global->LDS loads; one wait and one barrier per batch, while
+// the next batch loads). The tiles a
 // workgroup stages are the union of its groups' kept tiles, and the more
 // groups share a staged tile the fewer bytes each kept (row, key) pair costs.
 //
@@ -55,20 +56,6 @@ namespace zebra {
 // wait until at most n of this wave's vector memory operations are pending
 #define ZEBRA_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
-// Wait until at most `later` staged items (LPI loads per wave each) are in flight.
-template <int LPI>
-__device__ __forceinline__ void wait_items(int later) {
-  switch (later) {
-    case 0: ZEBRA_VMCNT(0); break;
-    case 1: ZEBRA_VMCNT(1 * LPI); break;
-    case 2: ZEBRA_VMCNT(2 * LPI); break;
-    case 3: ZEBRA_VMCNT(3 * LPI); break;
-    case 4: ZEBRA_VMCNT(4 * LPI); break;
-    case 5: ZEBRA_VMCNT(5 * LPI); break;
-    default: ZEBRA_VMCNT(6 * LPI); break;
-  }
-}
-static_assert(FNBUF - 2 <= 6, "wait_items covers at most 6 later items");
 
 // Per-lane source offsets of a wave's 1 KB shares (chunks c = wave,
 // wave + FWAVES, ...) of a staged 8 KB key or value half (swizzled as in
@@ -291,38 +278,46 @@ struct Item {
   int slot;
 };
 
-// Streams `next(item)`'s items through the LDS ring: `issue(item, buf)`
-// starts an item's async loads, and once they have landed in every wave
-// `consume(item, buf)` runs. Every wave walks the same sequence itself and
-// keeps the items in flight in a shift register (scalar registers), so no
-// item descriptor goes through LDS. LPI: loads per wave per item.
-template <int LPI, typename Next, typename Issue, typename Consume>
+// Streams `next(item)`'s items through the LDS ring in batches of two:
+// `issue(item, buf)` starts an item's async loads, and once a batch has
+// landed in every wave `consume(item, buf)` runs for each of its items while
+// the next batch loads into the other half of the ring. One wait and one
+// barrier per two items. Every wave walks the same sequence itself and
+// keeps the batches in scalar registers, so no item descriptor goes through
+// LDS.
+template <typename Next, typename Issue, typename Consume>
 __device__ __forceinline__ void stream_items(char* lds, Next next, Issue issue, Consume consume) {
-  constexpr int R = FNBUF - 1;  // items in flight
-  Item ring[R];
-  int n = 0;  // items in flight; ring[0..n) valid
+  static_assert(FNBUF == 4, "two batches of two items");
+  Item a[2];
+  int na = 0;
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    if (n == j && next(ring[j])) {
-      issue(ring[j], lds + j * LDS_BUF);
-      n = j + 1;
+  for (int j = 0; j < 2; ++j)
+    if (na == j && next(a[j])) {
+      issue(a[j], lds + j * LDS_BUF);
+      na = j + 1;
     }
-  }
-  bool more = n == R;  // the walk may have further items
-  int head = 0;        // LDS buffer of ring[0]
-  while (n > 0) {
-    wait_items<LPI>(n - 1);
-    ring_barrier();
-    Item nw;
-    const bool okn = more && next(nw);
-    more = okn;
-    if (okn) issue(nw, lds + ((head + R) % FNBUF) * LDS_BUF);
-    consume(ring[0], lds + head * LDS_BUF);
+  bool more = na == 2;
+  int hb = 0;  // first LDS buffer of batch a (0 or 2)
+  while (na > 0) {
+    ZEBRA_VMCNT(0);  // batch a has landed (nothing newer is in flight)
+    ring_barrier();  // ... in every wave; the previous batch's buffers are free
+    Item b[2];
+    int nb = 0;
+    if (more) {
 #pragma unroll
-    for (int j = 0; j + 1 < R; ++j) ring[j] = ring[j + 1];
-    ring[R - 1] = nw;
-    n = okn ? n : n - 1;
-    head = (head + 1) % FNBUF;
+      for (int j = 0; j < 2; ++j)
+        if (nb == j && next(b[j])) {
+          issue(b[j], lds + ((hb ^ 2) + j) * LDS_BUF);
+          nb = j + 1;
+        }
+    }
+    more = more && nb == 2;
+#pragma nounroll
+    for (int j = 0; j < na; ++j) consume(j == 0 ? a[0] : a[1], lds + (hb + j) * LDS_BUF);
+    a[0] = b[0];
+    a[1] = b[1];
+    na = nb;
+    hb ^= 2;
   }
   ring_barrier();
 }
@@ -400,7 +395,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, A
     if (!slots) return;
     bound_block<SW>(st, slots, kb, it.code < nlb, it.nkeys, lane);
   };
-  stream_items<FCHUNKS>(lds, next, issue, consume);
+  stream_items(lds, next, issue, consume);
 
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
@@ -562,7 +557,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
     attend_block<SW>(st, us, kb, 0, it.nkeys, lb, mrow0, A.nwords, lane);
     if (it.nkeys > KBLK) attend_block<SW>(st, us, kb, KBLK, it.nkeys - KBLK, -1, mrow0, A.nwords, lane);
   };
-  stream_items<2 * FCHUNKS>(lds, next, issue, consume);
+  stream_items(lds, next, issue, consume);
   // Per-lane indices are recomputed after the walk rather than kept live
   // across it from the set-up (register pressure).
   int lane_a = lane;

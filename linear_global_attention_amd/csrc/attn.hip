@@ -268,15 +268,19 @@ __device__ __forceinline__ long long lane_record(const Geom& g, const QueryGroup
   return (((long long)h * fi.groups_per_head + gid) * 4 + qg.row_block(s)) * 64 + lane;
 }
 
-// One staged item: its code (token tile, landmark block or special block),
-// the groups that use it, its key count and (token tiles) its first packed
-// slot within the head.
+// One staged item, as a plan entry: x = kind << 28 | index (kind 0: token
+// tile, index = its first 32-slot block within the head; kind 1: landmark
+// block; kind 2: special-key block), y = users | key count << 8 (users: the
+// item's groups that see it).
 struct Item {
-  int code;
-  unsigned users;
-  int nkeys;
-  int slot;
+  unsigned x, y;
+  __device__ int kind() const { return (int)(x >> 28); }
+  __device__ int index() const { return (int)(x & 0x0FFFFFFFu); }
+  __device__ unsigned users() const { return y & 0xFFu; }
+  __device__ int nkeys() const { return (int)(y >> 8); }
 };
+constexpr int KIND_TILE = 0, KIND_LANDMARK = 1, KIND_SPECIAL = 2;
+static_assert(FG <= 8, "plan entries hold 8 user bits");
 
 // Streams `next(item)`'s items through the LDS ring in batches of two:
 // `issue(item, buf)` starts an item's async loads, and once a batch has
@@ -380,20 +384,21 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, A
   int cnt = 0;
   auto next = [&](Item& it) -> bool {
     if (cnt >= nlb + nsb) return false;
-    it.code = cnt++;
-    it.users = slots;
-    it.nkeys = it.code < nlb ? KBLK : min(KBLK, g.nspec - (it.code - nlb) * KBLK);
-    it.slot = 0;
+    const bool lm = cnt < nlb;
+    const int b = lm ? cnt : cnt - nlb;
+    it.x = (unsigned)((lm ? KIND_LANDMARK : KIND_SPECIAL) << 28) | (unsigned)b;
+    it.y = (unsigned)((lm ? KBLK : min(KBLK, g.nspec - b * KBLK)) << 8);
+    ++cnt;
     return true;
   };
   const StageOffsets so(wave, lane);
   auto issue = [&](const Item& it, char* d) {
-    if (it.code < nlb) stage_share(d, wave, lmh + (long long)it.code * LM_KEY_BLOCK, so.k8);
-    else stage_share(d, wave, (const char*)Ks16 + (long long)(it.code - nlb) * KBLK * D * 2, so.k4);
+    if (it.kind() == KIND_LANDMARK) stage_share(d, wave, lmh + (long long)it.index() * LM_KEY_BLOCK, so.k8);
+    else stage_share(d, wave, (const char*)Ks16 + (long long)it.index() * KBLK * D * 2, so.k4);
   };
   auto consume = [&](const Item& it, const char* kb) {
     if (!slots) return;
-    bound_block<SW>(st, slots, kb, it.code < nlb, it.nkeys, lane);
+    bound_block<SW>(st, slots, kb, it.kind() == KIND_LANDMARK, it.nkeys(), lane);
   };
   stream_items(lds, next, issue, consume);
 
@@ -409,13 +414,91 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, A
   }
 }
 
+// The plan of every work item for the key range [w0, w1) of 32-tile words
+// (one wave per item, one word per lane): for each word in order, the
+// landmark block of the word if some group omitted one of its tiles
+// (tile-sparse patch items), then the word's tiles that some group kept in
+// ascending order (every tile for dense items), each with the bit set of
+// groups that see it; after the last range's words, the special-key
+// blocks. Writes `count[item]` entries of at most `stride` to plan + item * stride.
+template <int G>
+__global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int w0, int w1, int last,
+                                                        uint2* plan, int* count, int stride) {
+  __shared__ int tiles[MAX_TPF];
+  for (int i = threadIdx.x; i < g.tpf; i += blockDim.x) tiles[i] = g.tile[i];
+  __syncthreads();
+  const FastItems fi(g);
+  const int lane = threadIdx.x & 63;
+  const int item_id = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item_id >= fi.total) return;  // uniform per wave
+  const FastItem it(g, item_id);
+  const QueryGroups qgi(g, it.item, fi.patch_items, G, 0);
+  const bool sparse = A.sparse && qgi.patch;
+  unsigned valid = 0u;
+#pragma unroll
+  for (int s = 0; s < G; ++s)
+    if (qgi.rows(s) > 0) valid |= 1u << s;
+  const unsigned* mrow = sparse ? A.selmask + ((long long)it.h * g.T + qgi.gid0) * A.nwords : A.selmask;
+  uint2* out = plan + (long long)item_id * stride;
+  int base = 0;
+  for (int wb = w0; wb < w1; wb += 64) {
+    const int w = wb + lane;
+    const bool on = w < w1;
+    unsigned m[G], un = 0u, lm = 0u;
+#pragma unroll
+    for (int s = 0; s < G; ++s) {
+      unsigned v = 0u;
+      if (on && ((valid >> s) & 1u)) {
+        if (sparse) {
+          v = mrow[(long long)s * A.nwords + w];
+        } else {
+          const int rem = g.T - w * 32;
+          v = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
+        }
+        if (sparse && v != 0xFFFFFFFFu) lm |= 1u << s;
+      }
+      m[s] = v;
+      un |= v;
+    }
+    const int cnt = __builtin_popcount(un) + (lm ? 1 : 0);
+    int incl = cnt;  // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += t;
+    }
+    int o = base + incl - cnt;
+    if (lm) out[o++] = make_uint2((unsigned)(KIND_LANDMARK << 28) | (unsigned)w, lm | (unsigned)(KBLK << 8));
+    for (unsigned bits = un; bits; bits &= bits - 1u) {
+      const int b = __builtin_ctz(bits), u = w * 32 + b;
+      unsigned users = 0u;
+#pragma unroll
+      for (int s = 0; s < G; ++s) users |= ((m[s] >> b) & 1u) << s;
+      const int fu = frame_of_tile(g, u), te = tiles[u - fu * g.tpf];
+      const int slot = fu * g.slots_pf + (te & 0xFFFFF);
+      const int nk = ((te >> 20) & 15) * ((te >> 24) & 15);
+      out[o++] = make_uint2((unsigned)(KIND_TILE << 28) | (unsigned)(slot / KBLK), users | (unsigned)(nk << 8));
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  if (last) {
+    const int nsb = g.spec_pad / KBLK;
+    for (int b = lane; b < nsb; b += 64)
+      out[base + b] = make_uint2((unsigned)(KIND_SPECIAL << 28) | (unsigned)b,
+                                 valid | (unsigned)(min(KBLK, g.nspec - b * KBLK) << 8));
+    base += nsb;
+  }
+  if (lane == 0) count[item_id] = base;
+}
+
 // One key range [w0, w1) of 32-tile words for every work item: tile-sparse
 // patch items see the landmark block of each word (minus the tiles each
 // group kept) and the union of the kept tiles of the word; dense items see
 // every tile. The first range starts from zero partials, the last one adds
 // the special keys and the self key and writes the bf16 output.
 template <int G, int SW>
-__global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, AttnArgs A, int w0, int w1,
+__global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, AttnArgs A, const uint2* plan,
+                                                                   const int* plan_count, int plan_stride,
                                                                    int first, int last, const float* ws_negm,
                                                                    float* ws_l, f32x4* ws_o) {
   __shared__ __attribute__((aligned(1024))) char lds[FNBUF * LDS_BUF];
@@ -425,7 +508,6 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   const FastItem it(g, blockIdx.x);
   const int h = it.h;
   const FastItems fi(g);
-  const QueryGroups qgi(g, it.item, fi.patch_items, G, simd);      // the item's G groups
   const QueryGroups qg(g, it.item, fi.patch_items, G, simd, s0);   // this wave's SW slots
   const bool sparse = A.sparse && qg.patch;
   const long long rs = (long long)g.H * D;
@@ -434,13 +516,10 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   const u16* Ks16 = A.Ks + (long long)h * g.spec_pad * D;
   const u16* Vs16 = A.Vs + (long long)h * g.spec_pad * D;
 
-  unsigned slots = 0u, valid_groups = 0u;  // this wave's slots; the item's non-empty groups
+  unsigned slots = 0u;  // this wave's non-empty slots
 #pragma unroll
   for (int s = 0; s < SW; ++s)
     if (qg.row_block(s) * 16 < qg.rows(s)) slots |= 1u << s;
-#pragma unroll
-  for (int s = 0; s < G; ++s)
-    if (qgi.rows(s) > 0) valid_groups |= 1u << s;
 
   MainState<SW> st;
   load_queries<SW>(g, A, qg, h, slots, lane, st.q);
@@ -463,99 +542,62 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   ZEBRA_VMCNT(0);
 
   const char* lmh = (const char*)A.LM + (long long)h * g.T_pad * LM_BYTES_PER_TILE;
-  // kept-tile bitmap rows (patch groups are consecutive query tiles): group
-  // s of the item at mitem + s * nwords, slot s of this wave at mrow0 + s * nwords
-  const cmask_ptr mitem =
-      (cmask_ptr)(sparse ? A.selmask + ((long long)h * g.T + qgi.gid0) * A.nwords : A.selmask);
-  const cmask_ptr mrow0 = mitem + (sparse ? s0 * A.nwords : 0);
-  const int nlb = g.T_pad / KBLK, nsb = g.spec_pad / KBLK;
+  // kept-tile bitmap row of this wave's slot s: mrow0 + s * nwords (patch
+  // groups are consecutive query tiles)
+  const cmask_ptr mrow0 =
+      (cmask_ptr)(sparse ? A.selmask + ((long long)h * g.T + qg.gid0) * A.nwords : A.selmask);
+  const int nlb = g.T_pad / KBLK;
 
-  // Item codes: u < T token tile u, T + lb landmark block lb, T + nlb + b
-  // special block b.
-  int w = w0 - 1, scnt = 0;
-  unsigned bits = 0u, lm_users = 0u, lane_word = 0u;
-  bool lm_due = false;
+  // This item's plan for the key range: `count` entries, read 64 at a time
+  // by one vector load per lane (the next 64 prefetched a chunk ahead; every
+  // batch of the ring starts with a full vmcnt wait) and taken out with
+  // readlane.
+  const uint2* pl = plan + (long long)blockIdx.x * plan_stride;
+  const int count = uni(plan_count[blockIdx.x]);
+  const uint2 zero2 = make_uint2(0u, 0u);
+  uint2 ev_cur = lane < count ? pl[lane] : zero2;
+  uint2 ev_nxt = 64 + lane < count ? pl[64 + lane] : zero2;
+  int e = 0;
   auto next = [&](Item& it) -> bool {
-    for (;;) {
-      if (lm_due) {
-        lm_due = false;
-        it.code = g.T + w;
-        it.users = lm_users;
-        it.nkeys = KBLK;
-        it.slot = 0;
-        return true;
-      }
-      if (bits) {
-        const int b = __builtin_ctz(bits);
-        bits &= bits - 1u;
-        const int u = w * 32 + b;
-        const int fu = frame_of_tile(g, u), te = g.tile[u - fu * g.tpf];
-        it.code = u;
-        it.users = sparse ? (unsigned)__builtin_amdgcn_ballot_w64((lane_word >> b) & 1u) : valid_groups;
-        it.nkeys = ((te >> 20) & 15) * ((te >> 24) & 15);
-        it.slot = fu * g.slots_pf + (te & 0xFFFFF);
-        return true;
-      }
-      if (w + 1 >= w1) break;
-      ++w;
-      if (sparse) {
-        // lane s < G holds group s's word; landmark users: groups that did
-        // not keep every tile of the word
-        unsigned un = 0u, lu = 0u, lw = 0u;
-#pragma unroll
-        for (int s = 0; s < G; ++s) {
-          const unsigned m = ((valid_groups >> s) & 1u) ? mitem[(long long)s * A.nwords + w] : 0u;
-          un |= m;
-          if (((valid_groups >> s) & 1u) && m != 0xFFFFFFFFu) lu |= 1u << s;
-          lw = lane == s ? m : lw;
-        }
-        bits = un;
-        lane_word = lw;
-        lm_users = lu;
-        lm_due = lu != 0u;
-      } else {
-        const int rem = g.T - w * 32;
-        bits = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
-      }
+    if (e >= count) return false;
+    const int j = e & 63;
+    it.x = (unsigned)__builtin_amdgcn_readlane((int)ev_cur.x, j);
+    it.y = (unsigned)__builtin_amdgcn_readlane((int)ev_cur.y, j);
+    if (++e % 64 == 0) {
+      ev_cur = ev_nxt;
+      ev_nxt = e + 64 + lane < count ? pl[e + 64 + lane] : zero2;
     }
-    if (last && scnt < nsb) {
-      it.code = g.T + nlb + scnt;
-      it.users = valid_groups;
-      it.nkeys = min(KBLK, g.nspec - scnt * KBLK);
-      it.slot = 0;
-      ++scnt;
-      return true;
-    }
-    return false;
+    return true;
   };
   const StageOffsets so(wave, lane);
   auto issue = [&](const Item& it, char* d) {
-    const int code = it.code;
-    if (code < g.T) {
-      const long long base = (long long)it.slot * D * 2;
-      if (it.nkeys > KBLK) {
+    const int kind = it.kind();
+    if (kind == KIND_TILE) {
+      const long long base = (long long)it.index() * KBLK * D * 2;
+      if (it.nkeys() > KBLK) {
         stage_share(d, wave, (const char*)Kt16 + base, so.k8);
         stage_share(d + LDS_V, wave, (const char*)Vt16 + base, so.v8);
       } else {
         stage_share(d, wave, (const char*)Kt16 + base, so.k4);
         stage_share(d + LDS_V, wave, (const char*)Vt16 + base, so.v4);
       }
-    } else if (code < g.T + nlb) {
-      const long long lb = code - g.T;
+    } else if (kind == KIND_LANDMARK) {
+      const long long lb = it.index();
       stage_share(d, wave, lmh + lb * LM_KEY_BLOCK, so.k8);
       stage_share(d + LDS_V, wave, lmh + (long long)nlb * LM_KEY_BLOCK + lb * (KBLK * D * 2), so.v4);
     } else {
-      const long long b = (long long)(code - g.T - nlb) * KBLK * D * 2;
+      const long long b = (long long)it.index() * KBLK * D * 2;
       stage_share(d, wave, (const char*)Ks16 + b, so.k4);
       stage_share(d + LDS_V, wave, (const char*)Vs16 + b, so.v4);
     }
   };
   auto consume = [&](const Item& it, const char* kb) {
-    const unsigned us = (it.users >> s0) & slots;
+    const unsigned us = (it.users() >> s0) & slots;
     if (!us) return;
-    const int lb = it.code >= g.T && it.code < g.T + nlb ? it.code - g.T : -1;
-    attend_block<SW>(st, us, kb, 0, it.nkeys, lb, mrow0, A.nwords, lane);
-    if (it.nkeys > KBLK) attend_block<SW>(st, us, kb, KBLK, it.nkeys - KBLK, -1, mrow0, A.nwords, lane);
+    const int nk = it.nkeys();
+    const int lb = it.kind() == KIND_LANDMARK ? it.index() : -1;
+    attend_block<SW>(st, us, kb, 0, nk, lb, mrow0, A.nwords, lane);
+    if (nk > KBLK) attend_block<SW>(st, us, kb, KBLK, nk - KBLK, -1, mrow0, A.nwords, lane);
   };
   stream_items(lds, next, issue, consume);
   // Per-lane indices are recomputed after the walk rather than kept live
@@ -657,18 +699,23 @@ int attn_ranges(const Geom& g) {
 // per lane record -M, l and O partials (l and O only with several ranges).
 struct AttnWorkspace {
   long long groups, records;
-  size_t flags_off, negm_off, l_off, o_off, bytes;
+  int plan_stride;  // plan entries per work item: words of the longest range x 33 + special blocks
+  size_t flags_off, negm_off, count_off, plan_off, l_off, o_off, bytes;
   explicit AttnWorkspace(const Geom& g) {
     const FastItems fi(g);
     groups = (long long)g.H * fi.groups_per_head;
     records = groups * 4 * 64;
+    const int nwords = (g.T + 31) / 32, R = attn_ranges(g);
+    plan_stride = (nwords + R - 1) / R * 33 + g.spec_pad / KBLK;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     flags_off = 0;
     negm_off = up((size_t)groups * sizeof(int));
-    l_off = up(negm_off + (size_t)records * sizeof(float));
+    count_off = up(negm_off + (size_t)records * sizeof(float));
+    plan_off = up(count_off + (size_t)fi.total * sizeof(int));
+    l_off = up(plan_off + (size_t)fi.total * plan_stride * sizeof(uint2));
     o_off = l_off;
     bytes = l_off;
-    if (attn_ranges(g) > 1) {
+    if (R > 1) {
       o_off = up(l_off + (size_t)records * sizeof(float));
       bytes = o_off + (size_t)records * 4 * sizeof(f32x4);
     }
@@ -691,11 +738,17 @@ hipError_t launch_attn(const Geom& g, const AttnArgs& a, void* workspace, hipStr
   hipLaunchKernelGGL(clear_flags_kernel, dim3((unsigned)((ws.groups + 255) / 256)), dim3(256), 0, s, flags,
                      ws.groups);
   hipLaunchKernelGGL((attn_bound_kernel<FG, FSLOTS>), dim3(fi.total), dim3(FWAVES * 64), 0, s, g, a, negm, flags);
+  int* count = (int*)(base + ws.count_off);
+  uint2* plan = (uint2*)(base + ws.plan_off);
   const int nwords = (g.T + 31) / 32, R = attn_ranges(g);
   for (int r = 0; r < R; ++r) {
     const int w0 = (int)((long long)nwords * r / R), w1 = (int)((long long)nwords * (r + 1) / R);
-    hipLaunchKernelGGL((attn_main_kernel<FG, FSLOTS>), dim3(fi.total), dim3(FWAVES * 64), 0, s, g, a, w0, w1,
-                       r == 0 ? 1 : 0, r == R - 1 ? 1 : 0, (const float*)negm, wl, wo);
+    const int last = r == R - 1 ? 1 : 0;
+    hipLaunchKernelGGL(attn_plan_kernel<FG>, dim3((fi.total + 3) / 4), dim3(256), 0, s, g, a, w0, w1, last, plan,
+                       count, ws.plan_stride);
+    hipLaunchKernelGGL((attn_main_kernel<FG, FSLOTS>), dim3(fi.total), dim3(FWAVES * 64), 0, s, g, a,
+                       (const uint2*)plan, (const int*)count, ws.plan_stride, r == 0 ? 1 : 0, last,
+                       (const float*)negm, wl, wo);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

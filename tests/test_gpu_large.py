@@ -1,0 +1,58 @@
+"""GPU parity at the 512- and 1,024-view shapes, in the launch configuration
+the benchmark times (default key ranges), on seeded sampled query rows.
+
+The expected values were written by tests/golden/make_large.py, which calls
+only the fp64 oracle on the same seeded inputs: tile-sparse outputs (with
+every special row of the sampled frames), the kept-tile list of every
+sampled query tile (as a 64-bit digest, compared bit-exactly except on
+near-tie tiles), and linear-stage outputs with the centred affine
+correction. Tolerances: max-abs 2e-2, mean-abs 2e-3."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import zebra_synth as zs
+from gpu_helpers import Stage, close, log
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+sys.path.insert(0, GOLDEN)
+from make_large import CASES, digest  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("case", ["c3", "c4"])
+def test_large_shape_sampled_rows(case):
+    path = os.path.join(GOLDEN, f"{case}_rows.npz")
+    d = np.load(path)
+    c = CASES[case]
+    L = zs.CONFIGS[c["layout"]]
+
+    log(f"{case}: sparse stage {c['sparse_stage']} y={c['y']} ({L.tokens} tokens)")
+    q, k, v = zs.stage_inputs(L, seed=c["seed"], stage=c["sparse_stage"])
+    st = Stage(L, q, k, v, c["y"])
+    st.sparse()
+    close(st.rows(d["sparse_rows"]), d["sparse_ref"].astype(np.float64),
+          f"{case} sparse ({len(d['sparse_rows'])} sampled rows)")
+    sel_tiles = d["sel_tiles"]
+    sel = st.bufs.sel()[torch.from_numpy(sel_tiles[:, 0]).cuda(), torch.from_numpy(sel_tiles[:, 1]).cuda()]
+    sel = sel.cpu().numpy()
+    got = np.array([digest(s) for s in sel], dtype=np.uint64)
+    differ = got != d["sel_digest"]
+    bad = differ & ~d["sel_tie"]
+    log(f"{case} selection: {differ.sum()} of {len(sel_tiles)} sampled tiles differ, "
+        f"{d['sel_tie'].sum()} near-tie, {bad.sum()} differing non-tie")
+    assert not bad.any(), f"{case}: kept-tile lists differ on {bad.sum()} non-tie tiles"
+    del st
+    torch.cuda.empty_cache()
+
+    log(f"{case}: linear stage {c['linear_stage']}")
+    q, k, v = zs.stage_inputs(L, seed=c["seed"], stage=c["linear_stage"])
+    W, b = zs.affine_params(L, seed=c["seed"], stage=c["linear_stage"])
+    st = Stage(L, q, k, v, 0.0, sparse=False)
+    st.linear(W, b, d["mu"])
+    close(st.rows(d["linear_rows"]), d["linear_ref"].astype(np.float64),
+          f"{case} linear ({len(d['linear_rows'])} sampled rows)")

@@ -158,11 +158,10 @@ zebra_status zebra_select_tiles(const zebra_args* a, zebra_stream stream);
  * when tile t itself is not kept. Special rows: dense over all N keys.
  * Reads q, kt, vt, ks, vs, lm, logn, selmask; writes out. Uses the workspace:
  * per-row softmax offsets, one flag per query tile (rows whose cheap logit
- * bound is too loose are recomputed with an exact online softmax) and, when
- * the key tiles are walked in several ranges, fp32 partial outputs. The
- * range size (default 96 MiB of one head's packed K/V) can be set with the
- * environment variable ZEBRA_ATTN_RANGE_MB; the workspace size depends on
- * it, so set it before calling zebra_buffer_bytes. */
+ * bound is too loose are recomputed with an exact online softmax), the
+ * staging plans of one round of work units, and fp32 partial outputs of the
+ * special rows, whose keys are split into segments. Launches one kernel
+ * pair per round of as many workgroups as the device holds at once. */
 zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream);
 
 /* Linear attention with the centred affine correction. For each head:

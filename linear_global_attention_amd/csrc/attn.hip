@@ -26,16 +26,18 @@
 // u and every key j of u, q.k_j <= q.kbar_u + |q| r_u (r_u: the tile's key
 // radius); a landmark's logit is q.kbar_u/8 + ln n_u; special logits are
 // exact. With p = exp2(x - M_i) <= 1 nothing overflows, and the partial sums
-// of different key ranges simply add. The row's own key is always visible,
+// of different key segments simply add. The row's own key is always visible,
 // so M_i minus the own logit bounds how far below 1 the largest p can be;
 // groups with a row where that gap exceeds SAFE_GAP (log2 units) are flagged
 // and recomputed by an exact online-softmax kernel (attn_exact.hip).
 //
-// Key ranges. The main kernel runs once per range of 32-tile words, sized so
-// that one head's packed keys and values of a range stay resident in the
-// 256 MB memory-side cache while every CU streams it; O and l are carried
-// between launches as fp32 partials in the workspace, and the last launch
-// adds the special keys and the self key and writes bf16 output.
+// Rounds. The main kernel runs once per round of work units, a round being
+// the workgroups that are resident at once: they all start together on the
+// same head and walk its key tiles in ascending order, so each XCD's L2
+// fetches a tile once for all of its workgroups that use it (reads past the
+// L2 run at about the HBM rate, reads that hit it at about four times that).
+// A special item sees every key; it is split into key segments whose
+// partial O and l are summed by attn_special_combine_kernel.
 //
 // Per 32-key block and 16-row slot: S^T = K Q^T (4 v_mfma_f32_16x16x32_bf16,
 // A = keys from LDS, B = Q in registers), p = exp2(S*log2(e)/8 - M),
@@ -47,8 +49,6 @@
 // values: column ^ (channel/2)%4) so fragment reads are bank-conflict free;
 // the swizzle is applied through the per-lane source address of the async
 // loads, which write LDS linearly.
-#include <stdlib.h>
-
 #include "attn_common.hpp"
 
 namespace zebra {
@@ -138,28 +138,12 @@ __device__ __forceinline__ void qk(const bf16x8 q[2], const bf16x8 kf[2][2], f32
   s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][1], q[1], s1, 0, 0, 0);
 }
 
-// p = exp2(s*C + off_i) for the lane's 8 keys of a 32-key block
-__device__ __forceinline__ void probs(const f32x4& s0, const f32x4& s1, const float off[8], float p[8]) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    p[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], QK_LOG2, off[r]));
-    p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s1[r], QK_LOG2, off[4 + r]));
-  }
-}
-
+// p = exp2(s*C + off) for the lane's 8 keys of a 32-key block
 __device__ __forceinline__ void probs(const f32x4& s0, const f32x4& s1, float off, float p[8]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     p[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], QK_LOG2, off));
     p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s1[r], QK_LOG2, off));
-  }
-}
-
-__device__ __forceinline__ void drop(float p[8], unsigned keep) {
-  if (keep != 0xFFu) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (!((keep >> i) & 1u)) p[i] = 0.f;
   }
 }
 
@@ -173,41 +157,57 @@ __device__ __forceinline__ void pv(const float p[8], const bf16x8 vf[4], f32x4 o
   for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], P, o[db], 0, 0, 0);
 }
 
-// One staged 32-key block (keys key0.. of the LDS item) for every user
-// slot. Token or special keys: p = exp2(s*C - M), keys past nvalid dropped.
-// Landmark block lb >= 0: logit q.kbar/8 + ln n_u, so p is taken with the
-// offset log2 n_u - M (-inf past the last tile), and a slot drops the tiles
-// its group kept. All three share one P.V update per slot.
+// One staged 32-key block for every user slot: token or special keys
+// (rows key0.. of the LDS item, the first n valid) or, with lb >= 0, the
+// landmark block lb (the landmarks of tiles 32lb..32lb+31). Masking and the
+// landmark term go into the initial value of the S^T accumulators, so that
+// p = exp2(S*C - M) needs no per-key fix-up:
+//   keys past n           -inf
+//   landmark of tile u    log2(n_u)/C (-inf past the last tile), and -inf
+//                         in a slot whose group kept tile u
+//   other keys            0
 template <int SW>
-__device__ __forceinline__ void attend_block(MainState<SW>& st, unsigned us, const char* kb, int key0, int nvalid,
+__device__ __forceinline__ void attend_block(MainState<SW>& st, unsigned us, const char* kb, int key0, int n,
                                              int lb, cmask_ptr mrow0, int nwords, int lane) {
   bf16x8 kf[2][2], vf[4];
   load_kfrag(kb, key0, lane, kf);
   load_vfrag(kb + LDS_V + key0 * 128, lane, vf);
   const int lg = lane >> 4;
-  const bool is_lm = lb >= 0;             // uniform
-  const bool partial = nvalid < KBLK;     // uniform
-  const unsigned valid = partial ? lane_valid_mask(nvalid, lane) : 0xFFu;
-  float l2n[8];
-  if (is_lm) load_row8(kb + LM_LOG2N_ROW * 128, lane, l2n);
+  const bool is_lm = lb >= 0;  // uniform
+  f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
+  if (is_lm) {
+    float l2n[8];
+    load_row8(kb + LM_LOG2N_ROW * 128, lane, l2n);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      b0[r] = l2n[r] * (1.0f / QK_LOG2);
+      b1[r] = l2n[4 + r] * (1.0f / QK_LOG2);
+    }
+  } else if (n < KBLK) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      b0[r] = 4 * lg + r < n ? 0.f : -INFINITY;
+      b1[r] = 16 + 4 * lg + r < n ? 0.f : -INFINITY;
+    }
+  }
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
     if (!((us >> s) & 1u)) continue;
-    f32x4 a0, a1;
-    qk(st.q[s], kf, a0, a1);
-    float p[8];
+    f32x4 c0 = b0, c1 = b1;
     if (is_lm) {
       const unsigned kept = mrow0[(long long)s * nwords + lb];
-      const unsigned keep = ~(((kept >> (4 * lg)) & 0xFu) | (((kept >> (16 + 4 * lg)) & 0xFu) << 4)) & 0xFFu;
-      float off[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) off[i] = st.negm[s] + l2n[i];
-      probs(a0, a1, off, p);
-      drop(p, keep);
-    } else {
-      probs(a0, a1, st.negm[s], p);
-      if (partial) drop(p, valid);
+      for (int r = 0; r < 4; ++r) {
+        if ((kept >> (4 * lg + r)) & 1u) c0[r] = -INFINITY;
+        if ((kept >> (16 + 4 * lg + r)) & 1u) c1[r] = -INFINITY;
+      }
     }
+    f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][0], st.q[s][0], c0, 0, 0, 0);
+    f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][0], st.q[s][0], c1, 0, 0, 0);
+    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][1], st.q[s][1], a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][1], st.q[s][1], a1, 0, 0, 0);
+    float p[8];
+    probs(a0, a1, st.negm[s], p);
     pv(p, vf, st.o[s], st.l[s]);
   }
 }
@@ -279,7 +279,15 @@ struct Item {
   __device__ unsigned users() const { return y & 0xFFu; }
   __device__ int nkeys() const { return (int)(y >> 8); }
 };
-constexpr int KIND_TILE = 0, KIND_LANDMARK = 1, KIND_SPECIAL = 2;
+constexpr int KIND_TILE = 0, KIND_LANDMARK = 1, KIND_SPECIAL = 2, KIND_CHECKPOINT = 3;
+// Patch units meet every CK_WORDS words of key tiles (a checkpoint entry in
+// their plans), so that the workgroups of a round, which drift apart as
+// they walk the keys at slightly different speeds, stay within a few
+// hundred tiles of each other and an XCD's L2 still holds a tile when the
+// last of them reads it. The wait is bounded: after CK_SPIN_MAX polls a
+// wave goes on regardless.
+constexpr int CK_WORDS = 32;
+constexpr int CK_SPIN_MAX = 1000;
 static_assert(FG <= 8, "plan entries hold 8 user bits");
 
 // Streams `next(item)`'s items through the LDS ring in batches of two:
@@ -414,37 +422,45 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, A
   }
 }
 
-// The plan of every work item for the key range [w0, w1) of 32-tile words
-// (one wave per item, one word per lane): for each word in order, the
+// The plan of the units [unit0, unit0 + nunits) (one wave per unit, one
+// word of 32 tiles per lane): for each key word of the unit in order, the
 // landmark block of the word if some group omitted one of its tiles
 // (tile-sparse patch items), then the word's tiles that some group kept in
-// ascending order (every tile for dense items), each with the bit set of
-// groups that see it; after the last range's words, the special-key
-// blocks. Writes `count[item]` entries of at most `stride` to plan + item * stride.
+// ascending order (every tile for dense items and special segments), each
+// with the bit set of groups that see it; then, for patch items and the last
+// segment of a special item, the special-key blocks. Patch units also get a
+// checkpoint entry after every CK_WORDS-th word but the last. Writes
+// `count[i]` entries of at most `stride` to plan + i * stride for unit
+// unit0 + i, and zeroes the round's checkpoint counters.
 template <int G>
-__global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int w0, int w1, int last,
-                                                        uint2* plan, int* count, int stride) {
+__global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int segs, int unit0, int nunits,
+                                                        uint2* plan, int* count, int stride, int* ckpt,
+                                                        int nckpt) {
   __shared__ int tiles[MAX_TPF];
   for (int i = threadIdx.x; i < g.tpf; i += blockDim.x) tiles[i] = g.tile[i];
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nckpt; i += blockDim.x) ckpt[i] = 0;  // this round's checkpoint counters
   __syncthreads();
   const FastItems fi(g);
   const int lane = threadIdx.x & 63;
-  const int item_id = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item_id >= fi.total) return;  // uniform per wave
-  const FastItem it(g, item_id);
-  const QueryGroups qgi(g, it.item, fi.patch_items, G, 0);
+  const int local = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (local >= nunits) return;  // uniform per wave
+  const Unit un(g, segs, unit0 + local);
+  const QueryGroups qgi(g, un.item, fi.patch_items, G, 0);
   const bool sparse = A.sparse && qgi.patch;
+  int w0, w1;
+  seg_words(A.nwords, segs, un.seg, w0, w1);
   unsigned valid = 0u;
 #pragma unroll
   for (int s = 0; s < G; ++s)
     if (qgi.rows(s) > 0) valid |= 1u << s;
-  const unsigned* mrow = sparse ? A.selmask + ((long long)it.h * g.T + qgi.gid0) * A.nwords : A.selmask;
-  uint2* out = plan + (long long)item_id * stride;
+  const unsigned* mrow = sparse ? A.selmask + ((long long)un.h * g.T + qgi.gid0) * A.nwords : A.selmask;
+  uint2* out = plan + (long long)local * stride;
   int base = 0;
   for (int wb = w0; wb < w1; wb += 64) {
     const int w = wb + lane;
     const bool on = w < w1;
-    unsigned m[G], un = 0u, lm = 0u;
+    unsigned m[G], un_bits = 0u, lm = 0u;
 #pragma unroll
     for (int s = 0; s < G; ++s) {
       unsigned v = 0u;
@@ -458,9 +474,10 @@ __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int 
         if (sparse && v != 0xFFFFFFFFu) lm |= 1u << s;
       }
       m[s] = v;
-      un |= v;
+      un_bits |= v;
     }
-    const int cnt = __builtin_popcount(un) + (lm ? 1 : 0);
+    const bool ck = qgi.patch && on && (w + 1) % CK_WORDS == 0 && w + 1 < w1;
+    const int cnt = __builtin_popcount(un_bits) + (lm ? 1 : 0) + (ck ? 1 : 0);
     int incl = cnt;  // inclusive prefix sum over the lanes
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -469,7 +486,7 @@ __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int 
     }
     int o = base + incl - cnt;
     if (lm) out[o++] = make_uint2((unsigned)(KIND_LANDMARK << 28) | (unsigned)w, lm | (unsigned)(KBLK << 8));
-    for (unsigned bits = un; bits; bits &= bits - 1u) {
+    for (unsigned bits = un_bits; bits; bits &= bits - 1u) {
       const int b = __builtin_ctz(bits), u = w * 32 + b;
       unsigned users = 0u;
 #pragma unroll
@@ -479,38 +496,80 @@ __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int 
       const int nk = ((te >> 20) & 15) * ((te >> 24) & 15);
       out[o++] = make_uint2((unsigned)(KIND_TILE << 28) | (unsigned)(slot / KBLK), users | (unsigned)(nk << 8));
     }
+    if (ck) out[o++] = make_uint2((unsigned)(KIND_CHECKPOINT << 28) | (unsigned)((w + 1) / CK_WORDS - 1), 0u);
     base += __shfl(incl, 63, 64);
   }
-  if (last) {
+  if (un.seg < 0 || un.seg == segs - 1) {
     const int nsb = g.spec_pad / KBLK;
     for (int b = lane; b < nsb; b += 64)
       out[base + b] = make_uint2((unsigned)(KIND_SPECIAL << 28) | (unsigned)b,
                                  valid | (unsigned)(min(KBLK, g.nspec - b * KBLK) << 8));
     base += nsb;
   }
-  if (lane == 0) count[item_id] = base;
+  if (lane == 0) count[local] = base;
 }
 
-// One key range [w0, w1) of 32-tile words for every work item: tile-sparse
-// patch items see the landmark block of each word (minus the tiles each
-// group kept) and the union of the kept tiles of the word; dense items see
-// every tile. The first range starts from zero partials, the last one adds
-// the special keys and the self key and writes the bf16 output.
+// Index of this lane's partial record of slot s of a special segment unit:
+// (head, special item, segment, group of the item, row block, lane).
+__device__ __forceinline__ long long spec_record(const Geom& g, int h, int item, int seg, const QueryGroups& qg,
+                                                 int s, int lane) {
+  const FastItems fi(g);
+  const int si = item - fi.patch_items;
+  return ((((long long)(h * fi.spec_items + si) * SPEC_SEGS_MAX + seg) * FG + (qg.s0 + s)) * 4 +
+          qg.row_block(s)) * 64 + lane;
+}
+
+// O = O^T / l for slot s and bf16 store of its rows (row = query
+// row_block*16 + lane%16, channels db*16 + 4g + r). Every lane takes part in
+// the row-sum reduction.
+__device__ __forceinline__ void store_slot(const Geom& g, const AttnArgs& A, const QueryGroups& qg, int h, int s,
+                                           const f32x4 o[4], float l, int lane) {
+  const int lg = lane >> 4, tl = lane & 15;
+  const float inv = 1.0f / xsum32(xsum16(l));
+  const int j = qg.row_block(s) * 16 + tl;
+  if (j < qg.rows(s)) {
+    u16* orow = A.O + qg.token(s, j) * ((long long)g.H * D) + h * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      uint2 wv;
+      wv.x = pack_bf16(o[db][0] * inv, o[db][1] * inv);
+      wv.y = pack_bf16(o[db][2] * inv, o[db][3] * inv);
+      *(uint2*)(orow + db * 16 + 4 * lg) = wv;
+    }
+  }
+}
+
+// One work unit: a patch item over every key word (tile-sparse: landmark
+// block of each word minus the tiles each group kept, and the union of the
+// kept tiles; dense: every tile), then the special keys, the self key and
+// the bf16 output; or one key segment of a special item, whose partial O
+// and l go to the workspace for attn_special_combine_kernel.
+// Checkpoint c of a round: this wave arrives, then polls (vector atomic
+// loads, bounded) until every wave of the round's patch units has arrived.
+__device__ __forceinline__ void checkpoint_wait(int* ctr, int target) {
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma nounroll
+  for (int i = 0; i < CK_SPIN_MAX; ++i) {
+    const int v = uni(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (v >= target) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 template <int G, int SW>
-__global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, AttnArgs A, const uint2* plan,
-                                                                   const int* plan_count, int plan_stride,
-                                                                   int first, int last, const float* ws_negm,
-                                                                   float* ws_l, f32x4* ws_o) {
+__global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, AttnArgs A, int segs, int unit0,
+                                                                   const uint2* plan, const int* plan_count,
+                                                                   int plan_stride, const float* ws_negm,
+                                                                   float* sp_l, f32x4* sp_o, int* ckpt,
+                                                                   int ck_target) {
   __shared__ __attribute__((aligned(1024))) char lds[FNBUF * LDS_BUF];
   const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
-  const int lg = lane >> 4, tl = lane & 15;
   const int simd = wave & 3, s0 = (wave >> 2) * SW;
-  const FastItem it(g, blockIdx.x);
-  const int h = it.h;
+  const Unit un(g, segs, unit0 + blockIdx.x);
+  const int h = un.h;
   const FastItems fi(g);
-  const QueryGroups qg(g, it.item, fi.patch_items, G, simd, s0);   // this wave's SW slots
+  const QueryGroups qg(g, un.item, fi.patch_items, G, simd, s0);   // this wave's SW slots
   const bool sparse = A.sparse && qg.patch;
-  const long long rs = (long long)g.H * D;
   const u16* Kt16 = A.Kt + (long long)h * g.slots * D;
   const u16* Vt16 = A.Vt + (long long)h * g.slots * D;
   const u16* Ks16 = A.Ks + (long long)h * g.spec_pad * D;
@@ -529,15 +588,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
     st.l[s] = 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db) st.o[s][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if ((slots >> s) & 1u) {
-      const long long rec = lane_record(g, qg, h, s, lane);
-      st.negm[s] = ws_negm[rec];
-      if (!first) {
-        st.l[s] = ws_l[rec];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) st.o[s][db] = ws_o[rec * 4 + db];
-      }
-    }
+    if ((slots >> s) & 1u) st.negm[s] = ws_negm[lane_record(g, qg, h, s, lane)];
   }
   ZEBRA_VMCNT(0);
 
@@ -548,10 +599,9 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
       (cmask_ptr)(sparse ? A.selmask + ((long long)h * g.T + qg.gid0) * A.nwords : A.selmask);
   const int nlb = g.T_pad / KBLK;
 
-  // This item's plan for the key range: `count` entries, read 64 at a time
-  // by one vector load per lane (the next 64 prefetched a chunk ahead; every
-  // batch of the ring starts with a full vmcnt wait) and taken out with
-  // readlane.
+  // This unit's plan: `count` entries, read 64 at a time by one vector load
+  // per lane (the next 64 prefetched a chunk ahead; every batch of the ring
+  // starts with a full vmcnt wait) and taken out with readlane.
   const uint2* pl = plan + (long long)blockIdx.x * plan_stride;
   const int count = uni(plan_count[blockIdx.x]);
   const uint2 zero2 = make_uint2(0u, 0u);
@@ -559,15 +609,18 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   uint2 ev_nxt = 64 + lane < count ? pl[64 + lane] : zero2;
   int e = 0;
   auto next = [&](Item& it) -> bool {
-    if (e >= count) return false;
-    const int j = e & 63;
-    it.x = (unsigned)__builtin_amdgcn_readlane((int)ev_cur.x, j);
-    it.y = (unsigned)__builtin_amdgcn_readlane((int)ev_cur.y, j);
-    if (++e % 64 == 0) {
-      ev_cur = ev_nxt;
-      ev_nxt = e + 64 + lane < count ? pl[e + 64 + lane] : zero2;
+    for (;;) {
+      if (e >= count) return false;
+      const int j = e & 63;
+      it.x = (unsigned)__builtin_amdgcn_readlane((int)ev_cur.x, j);
+      it.y = (unsigned)__builtin_amdgcn_readlane((int)ev_cur.y, j);
+      if (++e % 64 == 0) {
+        ev_cur = ev_nxt;
+        ev_nxt = e + 64 + lane < count ? pl[e + 64 + lane] : zero2;
+      }
+      if (it.kind() != KIND_CHECKPOINT) return true;
+      checkpoint_wait(ckpt + it.index(), ck_target);
     }
-    return true;
   };
   const StageOffsets so(wave, lane);
   auto issue = [&](const Item& it, char* d) {
@@ -585,7 +638,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
       const long long lb = it.index();
       stage_share(d, wave, lmh + lb * LM_KEY_BLOCK, so.k8);
       stage_share(d + LDS_V, wave, lmh + (long long)nlb * LM_KEY_BLOCK + lb * (KBLK * D * 2), so.v4);
-    } else {
+    } else if (kind == KIND_SPECIAL) {
       const long long b = (long long)it.index() * KBLK * D * 2;
       stage_share(d, wave, (const char*)Ks16 + b, so.k4);
       stage_share(d + LDS_V, wave, (const char*)Vs16 + b, so.v4);
@@ -606,14 +659,14 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   asm volatile("" : "+v"(lane_a));
   const int lg_a = lane_a >> 4, tl_a = lane_a & 15;
 
-  if (!last) {
+  if (un.seg >= 0) {
 #pragma unroll
     for (int s = 0; s < SW; ++s) {
       if (!((slots >> s) & 1u)) continue;
-      const long long rec = lane_record(g, qg, h, s, lane_a);
-      ws_l[rec] = st.l[s];
+      const long long rec = spec_record(g, h, un.item, un.seg, qg, s, lane_a);
+      sp_l[rec] = st.l[s];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) ws_o[rec * 4 + db] = st.o[s][db];
+      for (int db = 0; db < 4; ++db) sp_o[rec * 4 + db] = st.o[s][db];
     }
     return;
   }
@@ -653,22 +706,34 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
     }
   }
 
-  // finalize: O = O^T / l; row = query (rb*16 + lane_a%16), channels db*16+4g+r
+#pragma unroll
+  for (int s = 0; s < SW; ++s)
+    if ((slots >> s) & 1u) store_slot(g, A, qg, h, s, st.o[s], st.l[s], lane_a);
+}
+
+// Sums the key-segment partials of every special item (one workgroup per
+// head and special item, the slot layout of the main kernel) and writes
+// the special rows.
+template <int G, int SW>
+__global__ void __launch_bounds__(FWAVES * 64) attn_special_combine_kernel(Geom g, AttnArgs A, int segs,
+                                                                          const float* sp_l, const f32x4* sp_o) {
+  const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
+  const int simd = wave & 3, s0 = (wave >> 2) * SW;
+  const FastItems fi(g);
+  const int h = blockIdx.x / fi.spec_items, si = blockIdx.x - h * fi.spec_items;
+  const QueryGroups qg(g, fi.patch_items + si, fi.patch_items, G, simd, s0);
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
-    if (!((slots >> s) & 1u)) continue;
-    const float inv = 1.0f / xsum32(xsum16(st.l[s]));
-    const int j = qg.row_block(s) * 16 + tl_a;
-    if (j < qg.rows(s)) {
-      u16* orow = A.O + qg.token(s, j) * rs + h * D;
+    if (qg.row_block(s) * 16 >= qg.rows(s)) continue;  // uniform
+    f32x4 o[4] = {};
+    float l = 0.f;
+    for (int seg = 0; seg < segs; ++seg) {
+      const long long rec = spec_record(g, h, fi.patch_items + si, seg, qg, s, lane);
+      l += sp_l[rec];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        uint2 wv;
-        wv.x = pack_bf16(st.o[s][db][0] * inv, st.o[s][db][1] * inv);
-        wv.y = pack_bf16(st.o[s][db][2] * inv, st.o[s][db][3] * inv);
-        *(uint2*)(orow + db * 16 + 4 * lg_a) = wv;
-      }
+      for (int db = 0; db < 4; ++db) o[db] += sp_o[rec * 4 + db];
     }
+    store_slot(g, A, qg, h, s, o, l, lane);
   }
 }
 
@@ -679,46 +744,51 @@ __global__ void clear_flags_kernel(int* flags, long long n) {
   if (i < n) flags[i] = 0;
 }
 
-// Bytes of one head's packed keys and values that a key range may span so
-// that it stays resident in the memory-side cache (ZEBRA_ATTN_RANGE_MB
-// overrides the default of 96 MiB; the workspace size depends on it).
-static double range_bytes() {
-  const char* e = getenv("ZEBRA_ATTN_RANGE_MB");
-  const double v = e ? atof(e) : 0.0;
-  return v > 0.0 ? v * 1048576.0 : 96.0 * 1048576.0;
-}
-
-int attn_ranges(const Geom& g) {
+// Key segments per special item: about T / k, so that a special segment
+// (every tile of 1/segs of the keys for all of its groups) costs about as
+// much as a tile-sparse patch item (k of the T tiles).
+static int spec_segs(const Geom& g, const AttnArgs& a) {
+  if (!a.sparse) return 1;
   const int nwords = (g.T + 31) / 32;
-  const double kv = (double)g.slots * D * 2 * 2, rb = range_bytes();
-  const double r = (kv + rb - 1.0) / rb;
-  return r < 1.0 ? 1 : (r > nwords ? nwords : (int)r);
+  const int k = a.keep > 0 ? a.keep : 1;
+  int s = (int)((2LL * g.T + k) / (2LL * k));  // round(T / k)
+  if (s > SPEC_SEGS_MAX) s = SPEC_SEGS_MAX;
+  if (s > nwords) s = nwords;
+  return s < 1 ? 1 : s;
 }
 
-// Workspace of the attention entry points: flags (one int per group), then
-// per lane record -M, l and O partials (l and O only with several ranges).
+// Units per round: one launch of the main kernel holds exactly the
+// workgroups that are resident at once (FOCC per CU), so they all start
+// together on the same head and walk its key tiles in the same order, and
+// each XCD's L2 serves one fetch of a tile to all of its workgroups that
+// use it. The kernel boundary keeps the rounds in step.
+constexpr int ROUND_MAX = 512;
+
+// Workspace of the attention entry points: flags (one int per group), -M
+// per lane record, the plans of one round, and the special-segment
+// partials.
 struct AttnWorkspace {
-  long long groups, records;
-  int plan_stride;  // plan entries per work item: words of the longest range x 33 + special blocks
-  size_t flags_off, negm_off, count_off, plan_off, l_off, o_off, bytes;
+  long long groups, records, sp_records;
+  int plan_stride;  // plan entries per unit: words x 33 + checkpoints + special blocks
+  int nckpt;        // checkpoint counters of a round
+  size_t flags_off, negm_off, count_off, ckpt_off, plan_off, spl_off, spo_off, bytes;
   explicit AttnWorkspace(const Geom& g) {
     const FastItems fi(g);
     groups = (long long)g.H * fi.groups_per_head;
     records = groups * 4 * 64;
-    const int nwords = (g.T + 31) / 32, R = attn_ranges(g);
-    plan_stride = (nwords + R - 1) / R * 33 + g.spec_pad / KBLK;
+    sp_records = (long long)g.H * fi.spec_items * SPEC_SEGS_MAX * FG * 4 * 64;
+    const int nwords = (g.T + 31) / 32;
+    nckpt = nwords / CK_WORDS + 1;
+    plan_stride = nwords * 33 + nckpt + g.spec_pad / KBLK;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     flags_off = 0;
     negm_off = up((size_t)groups * sizeof(int));
     count_off = up(negm_off + (size_t)records * sizeof(float));
-    plan_off = up(count_off + (size_t)fi.total * sizeof(int));
-    l_off = up(plan_off + (size_t)fi.total * plan_stride * sizeof(uint2));
-    o_off = l_off;
-    bytes = l_off;
-    if (R > 1) {
-      o_off = up(l_off + (size_t)records * sizeof(float));
-      bytes = o_off + (size_t)records * 4 * sizeof(f32x4);
-    }
+    ckpt_off = up(count_off + (size_t)ROUND_MAX * sizeof(int));
+    plan_off = up(ckpt_off + (size_t)nckpt * sizeof(int));
+    spl_off = up(plan_off + (size_t)ROUND_MAX * plan_stride * sizeof(uint2));
+    spo_off = up(spl_off + (size_t)sp_records * sizeof(float));
+    bytes = spo_off + (size_t)sp_records * 4 * sizeof(f32x4);
   }
 };
 
@@ -726,31 +796,51 @@ size_t attn_workspace_bytes(const Geom& g) { return AttnWorkspace(g).bytes; }
 
 hipError_t launch_attn_exact(const Geom& g, const AttnArgs& a, const int* flags, hipStream_t s);
 
-// Offsets, the key ranges, then the exact kernel for flagged groups.
+// Offsets, the rounds of units (plan, then main kernel), the special
+// combine, then the exact kernel for flagged groups.
 hipError_t launch_attn(const Geom& g, const AttnArgs& a, void* workspace, hipStream_t s) {
   const AttnWorkspace ws(g);
   char* base = (char*)workspace;
   int* flags = (int*)(base + ws.flags_off);
   float* negm = (float*)(base + ws.negm_off);
-  float* wl = (float*)(base + ws.l_off);
-  f32x4* wo = (f32x4*)(base + ws.o_off);
+  int* count = (int*)(base + ws.count_off);
+  int* ckpt = (int*)(base + ws.ckpt_off);
+  uint2* plan = (uint2*)(base + ws.plan_off);
+  float* spl = (float*)(base + ws.spl_off);
+  f32x4* spo = (f32x4*)(base + ws.spo_off);
   const FastItems fi(g);
+  const int segs = spec_segs(g, a);
+  const Units units(g, segs);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  int round = FOCC * cus;
+  if (round > ROUND_MAX) round = ROUND_MAX;
+  if (round < 1) round = 1;
   hipLaunchKernelGGL(clear_flags_kernel, dim3((unsigned)((ws.groups + 255) / 256)), dim3(256), 0, s, flags,
                      ws.groups);
   hipLaunchKernelGGL((attn_bound_kernel<FG, FSLOTS>), dim3(fi.total), dim3(FWAVES * 64), 0, s, g, a, negm, flags);
-  int* count = (int*)(base + ws.count_off);
-  uint2* plan = (uint2*)(base + ws.plan_off);
-  const int nwords = (g.T + 31) / 32, R = attn_ranges(g);
-  for (int r = 0; r < R; ++r) {
-    const int w0 = (int)((long long)nwords * r / R), w1 = (int)((long long)nwords * (r + 1) / R);
-    const int last = r == R - 1 ? 1 : 0;
-    hipLaunchKernelGGL(attn_plan_kernel<FG>, dim3((fi.total + 3) / 4), dim3(256), 0, s, g, a, w0, w1, last, plan,
-                       count, ws.plan_stride);
-    hipLaunchKernelGGL((attn_main_kernel<FG, FSLOTS>), dim3(fi.total), dim3(FWAVES * 64), 0, s, g, a,
-                       (const uint2*)plan, (const int*)count, ws.plan_stride, r == 0 ? 1 : 0, last,
-                       (const float*)negm, wl, wo);
+  for (int u0 = 0; u0 < units.total; u0 += round) {
+    const int n = units.total - u0 < round ? units.total - u0 : round;
+    int patch_units = 0;  // units of the round that are patch items (they meet at the checkpoints)
+    for (int u = u0; u < u0 + n;) {
+      const int b = u % units.per_head, sp = fi.spec_items * segs;
+      const int end = u - b + units.per_head < u0 + n ? u - b + units.per_head : u0 + n;
+      const int first_patch = u - b + sp;
+      if (end > first_patch) patch_units += end - (u > first_patch ? u : first_patch);
+      u = end;
+    }
+    hipLaunchKernelGGL(attn_plan_kernel<FG>, dim3((n + 3) / 4), dim3(256), 0, s, g, a, segs, u0, n, plan, count,
+                       ws.plan_stride, ckpt, ws.nckpt);
+    hipLaunchKernelGGL((attn_main_kernel<FG, FSLOTS>), dim3(n), dim3(FWAVES * 64), 0, s, g, a, segs, u0,
+                       (const uint2*)plan, (const int*)count, ws.plan_stride, (const float*)negm, spl, spo, ckpt,
+                       patch_units * FWAVES);
   }
-  const hipError_t e = hipGetLastError();
+  if (fi.spec_items > 0)
+    hipLaunchKernelGGL((attn_special_combine_kernel<FG, FSLOTS>), dim3(g.H * fi.spec_items), dim3(FWAVES * 64), 0,
+                       s, g, a, segs, (const float*)spl, (const f32x4*)spo);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_attn_exact(g, a, flags, s);
 }

@@ -222,4 +222,48 @@ struct FastItems {
   }
 };
 
+// Work units of the main attention kernel, per head: every special item
+// split into `segs` key segments (units item * segs + seg, so the segments
+// of one item run side by side), then the patch items. A special group sees
+// every key, so splitting its keys keeps a special unit about as long as a
+// patch unit; the segments' partial sums are added afterwards.
+constexpr int SPEC_SEGS_MAX = 8;
+struct Units {
+  int segs, per_head, total;
+  __host__ __device__ Units(const Geom& g, int segs_) : segs(segs_) {
+    const FastItems fi(g);
+    per_head = fi.spec_items * segs + fi.patch_items;
+    total = per_head * g.H;
+  }
+};
+
+struct Unit {
+  int h, item, seg;  // item in QueryGroups numbering; seg = -1 for a patch item
+  __device__ Unit(const Geom& g, int segs, int u) {
+    const FastItems fi(g);
+    const int per_head = fi.spec_items * segs + fi.patch_items;
+    h = u / per_head;
+    const int b = u - h * per_head;
+    if (b < fi.spec_items * segs) {
+      const int si = b / segs;
+      seg = b - si * segs;
+      item = fi.patch_items + si;
+    } else {
+      seg = -1;
+      item = b - fi.spec_items * segs;
+    }
+  }
+};
+
+// Key words [w0, w1) of segment `seg` (seg < 0: every word).
+__host__ __device__ inline void seg_words(int nwords, int segs, int seg, int& w0, int& w1) {
+  if (seg < 0) {
+    w0 = 0;
+    w1 = nwords;
+  } else {
+    w0 = (int)((long long)nwords * seg / segs);
+    w1 = (int)((long long)nwords * (seg + 1) / segs);
+  }
+}
+
 }  // namespace zebra

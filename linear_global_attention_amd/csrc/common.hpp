@@ -84,6 +84,7 @@ struct AttnArgs {
   const unsigned* selmask;  // nullptr: every tile kept (dense)
   int nwords;               // ceil(T/32)
   int sparse;               // 1: landmarks + self key for patch groups
+  int keep;                 // kept tiles per query tile (T when dense)
 };
 
 // Position of key k (0..31) inside a 32-key value block: the 8 keys

@@ -284,7 +284,7 @@ zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream) {
   if (s != ZEBRA_OK) return s;
   AttnArgs A{(const u16*)a->q, (u16*)a->out, (const u16*)a->kt, (const u16*)a->vt,
              (const u16*)a->ks, (const u16*)a->vs, (const u16*)a->lm, a->logn,
-             (const unsigned*)a->selmask, (g.T + 31) / 32, 1};
+             (const unsigned*)a->selmask, (g.T + 31) / 32, 1, (int)k};
   return hip_result(launch_attn(g, A, a->workspace, (hipStream_t)stream), "zebra_sparse_attn");
 }
 
@@ -303,7 +303,7 @@ zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream) {
   if (s != ZEBRA_OK) return s;
   AttnArgs A{(const u16*)a->q, (u16*)a->out, (const u16*)a->kt, (const u16*)a->vt,
              (const u16*)a->ks, (const u16*)a->vs, (const u16*)a->lm, a->logn, (const unsigned*)nullptr,
-             (g.T + 31) / 32, 0};
+             (g.T + 31) / 32, 0, g.T};
   return hip_result(launch_attn(g, A, a->workspace, (hipStream_t)stream), "zebra_dense_attn");
 }
 

@@ -287,49 +287,62 @@ constexpr int KIND_TILE = 0, KIND_LANDMARK = 1, KIND_SPECIAL = 2, KIND_CHECKPOIN
 // last of them reads it. The wait is bounded: after CK_SPIN_MAX polls a
 // wave goes on regardless.
 constexpr int CK_WORDS = 32;
+// Plan entries a wave copies to LDS at a time (one 16-byte async load per lane).
+constexpr int PLAN_CHUNK = 128;
 constexpr int CK_SPIN_MAX = 1000;
 static_assert(FG <= 8, "plan entries hold 8 user bits");
 
-// Streams `next(item)`'s items through the LDS ring in batches of two:
+// Streams `next(item)`'s items through an LDS ring of two halves, ringA
+// and ringB (two items each, separate arrays), in batches of two:
 // `issue(item, buf)` starts an item's async loads, and once a batch has
 // landed in every wave `consume(item, buf)` runs for each of its items while
-// the next batch loads into the other half of the ring. One wait and one
-// barrier per two items. Every wave walks the same sequence itself and
-// keeps the batches in scalar registers, so no item descriptor goes through
-// LDS.
-template <typename Next, typename Issue, typename Consume>
-__device__ __forceinline__ void stream_items(char* lds, Next next, Issue issue, Consume consume) {
-  static_assert(FNBUF == 4, "two batches of two items");
-  Item a[2];
-  int na = 0;
+// the next batch loads into the other half. One wait and one barrier per two
+// items. The loop is unrolled over the two halves so that every LDS read
+// names the half it reads: the compiler then knows that it cannot alias the
+// copies in flight into the other half and adds no wait for them. A batch's
+// plan entries are all taken (next) before its copies are issued, and
+// `refill()` then starts any plan copy that next() asked for. Every wave
+// walks the same sequence itself and keeps the batches in scalar registers.
+template <typename Next, typename Issue, typename Consume, typename Refill>
+__device__ __forceinline__ void stream_items(char* ringA, char* ringB, Next next, Issue issue, Consume consume,
+                                             Refill refill) {
+  static_assert(FNBUF == 4, "two halves of two items");
+  bool more = true;
+  auto fetch = [&](Item (&it)[2]) -> int {
+    int n = 0;
+    if (more && next(it[0])) {
+      n = 1;
+      if (next(it[1])) n = 2;
+    }
+    more = n == 2;
+    return n;
+  };
+  Item a[2], b[2];
+  int na = fetch(a), nb = 0;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (na == j && next(a[j])) {
-      issue(a[j], lds + j * LDS_BUF);
-      na = j + 1;
-    }
-  bool more = na == 2;
-  int hb = 0;  // first LDS buffer of batch a (0 or 2)
+    if (j < na) issue(a[j], ringA + j * LDS_BUF);
+  refill();
   while (na > 0) {
-    ZEBRA_VMCNT(0);  // batch a has landed (nothing newer is in flight)
-    ring_barrier();  // ... in every wave; the previous batch's buffers are free
-    Item b[2];
-    int nb = 0;
-    if (more) {
+    ZEBRA_VMCNT(0);  // batch a (ringA) has landed
+    ring_barrier();  // ... in every wave; ringB is free
+    nb = fetch(b);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        if (nb == j && next(b[j])) {
-          issue(b[j], lds + ((hb ^ 2) + j) * LDS_BUF);
-          nb = j + 1;
-        }
-    }
-    more = more && nb == 2;
-#pragma nounroll
-    for (int j = 0; j < na; ++j) consume(j == 0 ? a[0] : a[1], lds + (hb + j) * LDS_BUF);
-    a[0] = b[0];
-    a[1] = b[1];
-    na = nb;
-    hb ^= 2;
+    for (int j = 0; j < 2; ++j)
+      if (j < nb) issue(b[j], ringB + j * LDS_BUF);
+    refill();
+    consume(a[0], ringA);
+    if (na > 1) consume(a[1], ringA + LDS_BUF);
+    if (nb == 0) break;
+    ZEBRA_VMCNT(0);  // batch b (ringB) has landed
+    ring_barrier();  // ... in every wave; ringA is free
+    na = fetch(a);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (j < na) issue(a[j], ringA + j * LDS_BUF);
+    refill();
+    consume(b[0], ringB);
+    if (nb > 1) consume(b[1], ringB + LDS_BUF);
   }
   ring_barrier();
 }
@@ -341,7 +354,8 @@ __device__ __forceinline__ void stream_items(char* lds, Next next, Issue issue, 
 template <int G, int SW>
 __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, AttnArgs A, float* ws_negm,
                                                                     int* flags) {
-  __shared__ __attribute__((aligned(1024))) char lds[FNBUF * LDS_BUF];
+  __shared__ __attribute__((aligned(1024))) char ringA[2 * LDS_BUF];
+  __shared__ __attribute__((aligned(1024))) char ringB[2 * LDS_BUF];
   const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
   const int lg = lane >> 4, tl = lane & 15;
   const int simd = wave & 3, s0 = (wave >> 2) * SW;
@@ -408,7 +422,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, A
     if (!slots) return;
     bound_block<SW>(st, slots, kb, it.kind() == KIND_LANDMARK, it.nkeys(), lane);
   };
-  stream_items(lds, next, issue, consume);
+  stream_items(ringA, ringB, next, issue, consume, [] {});
 
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
@@ -562,7 +576,9 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
                                                                    int plan_stride, const float* ws_negm,
                                                                    float* sp_l, f32x4* sp_o, int* ckpt,
                                                                    int ck_target) {
-  __shared__ __attribute__((aligned(1024))) char lds[FNBUF * LDS_BUF];
+  __shared__ __attribute__((aligned(1024))) char ringA[2 * LDS_BUF];
+  __shared__ __attribute__((aligned(1024))) char ringB[2 * LDS_BUF];
+  __shared__ __attribute__((aligned(16))) uint2 plan_lds[FWAVES * 2 * PLAN_CHUNK];
   const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
   const int simd = wave & 3, s0 = (wave >> 2) * SW;
   const Unit un(g, segs, unit0 + blockIdx.x);
@@ -599,50 +615,65 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
       (cmask_ptr)(sparse ? A.selmask + ((long long)h * g.T + qg.gid0) * A.nwords : A.selmask);
   const int nlb = g.T_pad / KBLK;
 
-  // This unit's plan: `count` entries, read 64 at a time by one vector load
-  // per lane (the next 64 prefetched a chunk ahead; every batch of the ring
-  // starts with a full vmcnt wait) and taken out with readlane.
+  // This unit's plan: `count` entries, in chunks of PLAN_CHUNK that each
+  // wave copies into its own LDS buffer with one async load, a chunk ahead
+  // (every batch of the ring starts with a full vmcnt wait, so a chunk has
+  // landed long before it is read); entries are read back as uniform LDS
+  // loads at the start of a batch, before its copies are issued.
   const uint2* pl = plan + (long long)blockIdx.x * plan_stride;
   const int count = uni(plan_count[blockIdx.x]);
-  const uint2 zero2 = make_uint2(0u, 0u);
-  uint2 ev_cur = lane < count ? pl[lane] : zero2;
-  uint2 ev_nxt = 64 + lane < count ? pl[64 + lane] : zero2;
-  int e = 0;
+  uint2* pbuf = plan_lds + wave * 2 * PLAN_CHUNK;
+  auto load_chunk = [&](int c) {
+    if (c * PLAN_CHUNK < count)
+      __builtin_amdgcn_global_load_lds((const void*)(pl + c * PLAN_CHUNK + 2 * lane),
+                                       (lds_void*)(pbuf + (c & 1) * PLAN_CHUNK), 16, 0, 0);
+  };
+  load_chunk(0);
+  load_chunk(1);
+  ZEBRA_VMCNT(0);
+  int e = 0, want = -1;
   auto next = [&](Item& it) -> bool {
     for (;;) {
       if (e >= count) return false;
-      const int j = e & 63;
-      it.x = (unsigned)__builtin_amdgcn_readlane((int)ev_cur.x, j);
-      it.y = (unsigned)__builtin_amdgcn_readlane((int)ev_cur.y, j);
-      if (++e % 64 == 0) {
-        ev_cur = ev_nxt;
-        ev_nxt = e + 64 + lane < count ? pl[e + 64 + lane] : zero2;
-      }
+      const int j = e & (PLAN_CHUNK - 1);
+      if (j == 0 && e > 0) want = e / PLAN_CHUNK + 1;  // into the buffer of the chunk just finished
+      const uint2 v = pbuf[((e / PLAN_CHUNK) & 1) * PLAN_CHUNK + j];
+      it.x = (unsigned)uni((int)v.x);
+      it.y = (unsigned)uni((int)v.y);
+      ++e;
       if (it.kind() != KIND_CHECKPOINT) return true;
       checkpoint_wait(ckpt + it.index(), ck_target);
     }
   };
+  // Per-lane source offsets of this wave's async-load shares: the 8 KB and
+  // 4 KB forms are picked with selects (not by indexing an array, which the
+  // compiler would place in scratch memory and wait for with vmcnt).
   const StageOffsets so(wave, lane);
   auto issue = [&](const Item& it, char* d) {
     const int kind = it.kind();
+    const bool vbig = kind == KIND_TILE && it.nkeys() > KBLK;
+    const bool kbig = vbig || kind == KIND_LANDMARK;
+    const long long idx = it.index();
+    const char* ks;
+    const char* vs;
     if (kind == KIND_TILE) {
-      const long long base = (long long)it.index() * KBLK * D * 2;
-      if (it.nkeys() > KBLK) {
-        stage_share(d, wave, (const char*)Kt16 + base, so.k8);
-        stage_share(d + LDS_V, wave, (const char*)Vt16 + base, so.v8);
-      } else {
-        stage_share(d, wave, (const char*)Kt16 + base, so.k4);
-        stage_share(d + LDS_V, wave, (const char*)Vt16 + base, so.v4);
-      }
+      ks = (const char*)Kt16 + idx * (KBLK * D * 2);
+      vs = (const char*)Vt16 + idx * (KBLK * D * 2);
     } else if (kind == KIND_LANDMARK) {
-      const long long lb = it.index();
-      stage_share(d, wave, lmh + lb * LM_KEY_BLOCK, so.k8);
-      stage_share(d + LDS_V, wave, lmh + (long long)nlb * LM_KEY_BLOCK + lb * (KBLK * D * 2), so.v4);
-    } else if (kind == KIND_SPECIAL) {
-      const long long b = (long long)it.index() * KBLK * D * 2;
-      stage_share(d, wave, (const char*)Ks16 + b, so.k4);
-      stage_share(d + LDS_V, wave, (const char*)Vs16 + b, so.v4);
+      ks = lmh + idx * LM_KEY_BLOCK;
+      vs = lmh + (long long)nlb * LM_KEY_BLOCK + idx * (KBLK * D * 2);
+    } else {
+      ks = (const char*)Ks16 + idx * (KBLK * D * 2);
+      vs = (const char*)Vs16 + idx * (KBLK * D * 2);
     }
+    unsigned ko[FCHUNKS], vo[FCHUNKS];
+#pragma unroll
+    for (int i = 0; i < FCHUNKS; ++i) {
+      ko[i] = kbig ? so.k8[i] : so.k4[i];
+      vo[i] = vbig ? so.v8[i] : so.v4[i];
+    }
+    stage_share(d, wave, ks, ko);
+    stage_share(d + LDS_V, wave, vs, vo);
   };
   auto consume = [&](const Item& it, const char* kb) {
     const unsigned us = (it.users() >> s0) & slots;
@@ -652,7 +683,13 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
     attend_block<SW>(st, us, kb, 0, nk, lb, mrow0, A.nwords, lane);
     if (nk > KBLK) attend_block<SW>(st, us, kb, KBLK, nk - KBLK, -1, mrow0, A.nwords, lane);
   };
-  stream_items(lds, next, issue, consume);
+  auto refill = [&] {
+    if (want >= 0) {
+      load_chunk(want);
+      want = -1;
+    }
+  };
+  stream_items(ringA, ringB, next, issue, consume, refill);
   // Per-lane indices are recomputed after the walk rather than kept live
   // across it from the set-up (register pressure).
   int lane_a = lane;
@@ -786,7 +823,8 @@ struct AttnWorkspace {
     count_off = up(negm_off + (size_t)records * sizeof(float));
     ckpt_off = up(count_off + (size_t)ROUND_MAX * sizeof(int));
     plan_off = up(ckpt_off + (size_t)nckpt * sizeof(int));
-    spl_off = up(plan_off + (size_t)ROUND_MAX * plan_stride * sizeof(uint2));
+    // the last unit's final plan chunk may be read past its stride
+    spl_off = up(plan_off + ((size_t)ROUND_MAX * plan_stride + PLAN_CHUNK) * sizeof(uint2));
     spo_off = up(spl_off + (size_t)sp_records * sizeof(float));
     bytes = spo_off + (size_t)sp_records * 4 * sizeof(f32x4);
   }

@@ -282,14 +282,17 @@ struct Item {
 constexpr int KIND_TILE = 0, KIND_LANDMARK = 1, KIND_SPECIAL = 2, KIND_CHECKPOINT = 3;
 // Patch units meet every CK_WORDS words of key tiles (a checkpoint entry in
 // their plans), so that the workgroups of a round, which drift apart as
-// they walk the keys at slightly different speeds, stay within a few
-// hundred tiles of each other and an XCD's L2 still holds a tile when the
-// last of them reads it. The wait is bounded: after CK_SPIN_MAX polls a
-// wave goes on regardless.
-constexpr int CK_WORDS = 32;
+// they walk the keys at slightly different speeds, stay close enough for an
+// XCD's L2 to still hold a tile when most of them read it. A wave goes on
+// once half of the round's waves have arrived (CK_RELEASE_PCT): the fast
+// half waits for the median and none runs more than a segment ahead of it,
+// while the slow tail never waits. The wait is bounded: after CK_SPIN_MAX
+// polls a wave goes on regardless.
+constexpr int CK_WORDS = 128;
 // Plan entries a wave copies to LDS at a time (one 16-byte async load per lane).
 constexpr int PLAN_CHUNK = 128;
 constexpr int CK_SPIN_MAX = 1000;
+constexpr int CK_RELEASE_PCT = 50;
 static_assert(FG <= 8, "plan entries hold 8 user bits");
 
 // Streams `next(item)`'s items through an LDS ring of two halves, ringA
@@ -553,13 +556,9 @@ __device__ __forceinline__ void store_slot(const Geom& g, const AttnArgs& A, con
   }
 }
 
-// One work unit: a patch item over every key word (tile-sparse: landmark
-// block of each word minus the tiles each group kept, and the union of the
-// kept tiles; dense: every tile), then the special keys, the self key and
-// the bf16 output; or one key segment of a special item, whose partial O
-// and l go to the workspace for attn_special_combine_kernel.
 // Checkpoint c of a round: this wave arrives, then polls (vector atomic
-// loads, bounded) until every wave of the round's patch units has arrived.
+// loads, bounded) until `target` waves of the round's patch units have
+// arrived.
 __device__ __forceinline__ void checkpoint_wait(int* ctr, int target) {
   if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma nounroll
@@ -570,6 +569,11 @@ __device__ __forceinline__ void checkpoint_wait(int* ctr, int target) {
   }
 }
 
+// One work unit: a patch item over every key word (tile-sparse: landmark
+// block of each word minus the tiles each group kept, and the union of the
+// kept tiles; dense: every tile), then the special keys, the self key and
+// the bf16 output; or one key segment of a special item, whose partial O
+// and l go to the workspace for attn_special_combine_kernel.
 template <int G, int SW>
 __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, AttnArgs A, int segs, int unit0,
                                                                    const uint2* plan, const int* plan_count,
@@ -873,7 +877,7 @@ hipError_t launch_attn(const Geom& g, const AttnArgs& a, void* workspace, hipStr
                        ws.plan_stride, ckpt, ws.nckpt);
     hipLaunchKernelGGL((attn_main_kernel<FG, FSLOTS>), dim3(n), dim3(FWAVES * 64), 0, s, g, a, segs, u0,
                        (const uint2*)plan, (const int*)count, ws.plan_stride, (const float*)negm, spl, spo, ckpt,
-                       patch_units * FWAVES);
+                       (patch_units * FWAVES * CK_RELEASE_PCT + 99) / 100);
   }
   if (fi.spec_items > 0)
     hipLaunchKernelGGL((attn_special_combine_kernel<FG, FSLOTS>), dim3(g.H * fi.spec_items), dim3(FWAVES * 64), 0,

@@ -239,3 +239,34 @@ def test_c1_special_rows_in_key_segments(y):
     rows = zs.sample_rows(L, 256, seed=7, special_frames=0)
     ref, _ = osp.sparse_rows(Q, K, V, tm, y, rows)
     close(st.rows(rows), ref, f"c1 y={y} sparse rows")
+
+
+def test_exact_fallback_rows():
+    """Rows whose cheap logit bound lies far above their own logit are
+    recomputed by the exact online-softmax kernel. Scaling the queries of a
+    few query tiles and of one frame's special rows by 40 makes their
+    |q| r_u term dominate the bound, so those groups are flagged; every
+    output, flagged or not, matches the oracle."""
+    L = zs.Layout(3, 2, 16, 24, heads=2)
+    y = 0.5
+    q, k, v = _inputs(L, seed=9)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    Qf = zs.bf16_to_f32(q).copy()
+    for t in (0, 7, 13):
+        Qf[tm.tokens[t], 1] *= 40.0
+    Qf[tm.specials[L.specials:2 * L.specials], 0] *= 40.0
+    q = zs.f32_to_bf16(Qf)
+    Q, K, V = widen(q), widen(k), widen(v)
+    st = Stage(L, q, k, v, y)
+    out = bf16_host(st.sparse()).reshape(L.tokens, L.heads, 64)
+    # white-box check that the fallback ran: the attention workspace starts
+    # with one int flag per (head, query group), groups being the T query
+    # tiles then the special groups of 64 rows
+    gph = tm.T + (L.frames * L.specials + 63) // 64
+    flags = st.bufs.t["WORKSPACE"][: 4 * L.heads * gph].view(torch.int32).view(L.heads, gph).cpu().numpy()
+    assert all(flags[1, t] for t in (0, 7, 13)) and flags[0, tm.T], flags
+    O_ref, _, _ = osp.sparse_attention(Q, K, V, tm, y)
+    close(out, O_ref, "exact-fallback sparse (all rows)")
+    st2 = Stage(L, q, k, v, 0.0)
+    out = bf16_host(st2.dense()).reshape(L.tokens, L.heads, 64)
+    close(out, osp.dense_attention(Q, K, V), "exact-fallback dense (all rows)")

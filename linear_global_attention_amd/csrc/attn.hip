@@ -157,33 +157,19 @@ __device__ __forceinline__ void pv(const float p[8], const bf16x8 vf[4], f32x4 o
   for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], P, o[db], 0, 0, 0);
 }
 
-// One staged 32-key block for every user slot: token or special keys
-// (rows key0.. of the LDS item, the first n valid) or, with lb >= 0, the
-// landmark block lb (the landmarks of tiles 32lb..32lb+31). Masking and the
-// landmark term go into the initial value of the S^T accumulators, so that
-// p = exp2(S*C - M) needs no per-key fix-up:
-//   keys past n           -inf
-//   landmark of tile u    log2(n_u)/C (-inf past the last tile), and -inf
-//                         in a slot whose group kept tile u
-//   other keys            0
+// One staged 32-key block of token or special keys (rows key0.. of the
+// LDS item, the first n valid) for every user slot. Keys past n get -inf as
+// the initial value of their S^T accumulator, so that p = exp2(S*C - M)
+// needs no per-key fix-up.
 template <int SW>
 __device__ __forceinline__ void attend_block(MainState<SW>& st, unsigned us, const char* kb, int key0, int n,
-                                             int lb, cmask_ptr mrow0, int nwords, int lane) {
+                                             int lane) {
   bf16x8 kf[2][2], vf[4];
   load_kfrag(kb, key0, lane, kf);
   load_vfrag(kb + LDS_V + key0 * 128, lane, vf);
   const int lg = lane >> 4;
-  const bool is_lm = lb >= 0;  // uniform
   f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
-  if (is_lm) {
-    float l2n[8];
-    load_row8(kb + LM_LOG2N_ROW * 128, lane, l2n);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      b0[r] = l2n[r] * (1.0f / QK_LOG2);
-      b1[r] = l2n[4 + r] * (1.0f / QK_LOG2);
-    }
-  } else if (n < KBLK) {
+  if (n < KBLK) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       b0[r] = 4 * lg + r < n ? 0.f : -INFINITY;
@@ -193,14 +179,38 @@ __device__ __forceinline__ void attend_block(MainState<SW>& st, unsigned us, con
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
     if (!((us >> s) & 1u)) continue;
-    f32x4 c0 = b0, c1 = b1;
-    if (is_lm) {
-      const unsigned kept = mrow0[(long long)s * nwords + lb];
+    f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][0], st.q[s][0], b0, 0, 0, 0);
+    f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][0], st.q[s][0], b1, 0, 0, 0);
+    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][1], st.q[s][1], a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][1], st.q[s][1], a1, 0, 0, 0);
+    float p[8];
+    probs(a0, a1, st.negm[s], p);
+    pv(p, vf, st.o[s], st.l[s]);
+  }
+}
+
+// The landmark block lb (landmarks of tiles 32lb..32lb+31) for every user
+// slot: logit q.kbar/8 + ln n_u, value vbar_u. The landmark term log2(n_u)/C
+// (-inf past the last tile, and -inf for the tiles the slot's group kept)
+// is the initial value of the S^T accumulators.
+template <int SW>
+__device__ __forceinline__ void attend_landmarks(MainState<SW>& st, unsigned us, const char* kb, int lb,
+                                                 cmask_ptr mrow0, int nwords, int lane) {
+  bf16x8 kf[2][2], vf[4];
+  load_kfrag(kb, 0, lane, kf);
+  load_vfrag(kb + LDS_V, lane, vf);
+  const int lg = lane >> 4;
+  float l2n[8];
+  load_row8(kb + LM_LOG2N_ROW * 128, lane, l2n);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if ((kept >> (4 * lg + r)) & 1u) c0[r] = -INFINITY;
-        if ((kept >> (16 + 4 * lg + r)) & 1u) c1[r] = -INFINITY;
-      }
+  for (int s = 0; s < SW; ++s) {
+    if (!((us >> s) & 1u)) continue;
+    const unsigned kept = mrow0[(long long)s * nwords + lb];
+    f32x4 c0, c1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      c0[r] = (kept >> (4 * lg + r)) & 1u ? -INFINITY : l2n[r] * (1.0f / QK_LOG2);
+      c1[r] = (kept >> (16 + 4 * lg + r)) & 1u ? -INFINITY : l2n[4 + r] * (1.0f / QK_LOG2);
     }
     f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][0], st.q[s][0], c0, 0, 0, 0);
     f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][0], st.q[s][0], c1, 0, 0, 0);
@@ -440,12 +450,12 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, A
 }
 
 // The plan of the units [unit0, unit0 + nunits) (one wave per unit, one
-// word of 32 tiles per lane): for each key word of the unit in order, the
-// landmark block of the word if some group omitted one of its tiles
-// (tile-sparse patch items), then the word's tiles that some group kept in
-// ascending order (every tile for dense items and special segments), each
-// with the bit set of groups that see it; then, for patch items and the last
-// segment of a special item, the special-key blocks. Patch units also get a
+// word of 32 tiles per lane): first, for tile-sparse patch items, the
+// landmark block of every word of which some group omitted a tile; then for
+// each key word in order the word's tiles that some group kept, ascending
+// (every tile for dense items and special segments), each with the bit set
+// of groups that see it; then, for patch items and the last segment of a
+// special item, the special-key blocks. Patch units also get a
 // checkpoint entry after every CK_WORDS-th word but the last. Writes
 // `count[i]` entries of at most `stride` to plan + i * stride for unit
 // unit0 + i, and zeroes the round's checkpoint counters.
@@ -474,10 +484,24 @@ __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int 
   const unsigned* mrow = sparse ? A.selmask + ((long long)un.h * g.T + qgi.gid0) * A.nwords : A.selmask;
   uint2* out = plan + (long long)local * stride;
   int base = 0;
+  if (sparse) {  // the landmark blocks first
+    for (int wb = w0; wb < w1; wb += 64) {
+      const int w = wb + lane;
+      unsigned lm = 0u;
+#pragma unroll
+      for (int s = 0; s < G; ++s)
+        if (w < w1 && ((valid >> s) & 1u) && mrow[(long long)s * A.nwords + w] != 0xFFFFFFFFu) lm |= 1u << s;
+      const unsigned long long bal = __ballot(lm != 0u);
+      if (lm)
+        out[base + __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u))] =
+            make_uint2((unsigned)(KIND_LANDMARK << 28) | (unsigned)w, lm | (unsigned)(KBLK << 8));
+      base += __builtin_popcountll(bal);
+    }
+  }
   for (int wb = w0; wb < w1; wb += 64) {
     const int w = wb + lane;
     const bool on = w < w1;
-    unsigned m[G], un_bits = 0u, lm = 0u;
+    unsigned m[G], un_bits = 0u;
 #pragma unroll
     for (int s = 0; s < G; ++s) {
       unsigned v = 0u;
@@ -488,13 +512,12 @@ __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int 
           const int rem = g.T - w * 32;
           v = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
         }
-        if (sparse && v != 0xFFFFFFFFu) lm |= 1u << s;
       }
       m[s] = v;
       un_bits |= v;
     }
     const bool ck = qgi.patch && on && (w + 1) % CK_WORDS == 0 && w + 1 < w1;
-    const int cnt = __builtin_popcount(un_bits) + (lm ? 1 : 0) + (ck ? 1 : 0);
+    const int cnt = __builtin_popcount(un_bits) + (ck ? 1 : 0);
     int incl = cnt;  // inclusive prefix sum over the lanes
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -502,7 +525,6 @@ __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int 
       if (lane >= d) incl += t;
     }
     int o = base + incl - cnt;
-    if (lm) out[o++] = make_uint2((unsigned)(KIND_LANDMARK << 28) | (unsigned)w, lm | (unsigned)(KBLK << 8));
     for (unsigned bits = un_bits; bits; bits &= bits - 1u) {
       const int b = __builtin_ctz(bits), u = w * 32 + b;
       unsigned users = 0u;
@@ -636,15 +658,29 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   load_chunk(1);
   ZEBRA_VMCNT(0);
   int e = 0, want = -1;
+  auto peek = [&](Item& it) {
+    const uint2 v = pbuf[((e / PLAN_CHUNK) & 1) * PLAN_CHUNK + (e & (PLAN_CHUNK - 1))];
+    it.x = (unsigned)uni((int)v.x);
+    it.y = (unsigned)uni((int)v.y);
+  };
+  auto take = [&] {
+    if ((e & (PLAN_CHUNK - 1)) == 0 && e > 0) want = e / PLAN_CHUNK + 1;  // into the buffer of the chunk just finished
+    ++e;
+  };
+  // the landmark blocks (they lead the plan)
+  auto next_lm = [&](Item& it) -> bool {
+    if (e >= count) return false;
+    peek(it);
+    if (it.kind() != KIND_LANDMARK) return false;
+    take();
+    return true;
+  };
+  // the rest: token tiles, checkpoints, special blocks
   auto next = [&](Item& it) -> bool {
     for (;;) {
       if (e >= count) return false;
-      const int j = e & (PLAN_CHUNK - 1);
-      if (j == 0 && e > 0) want = e / PLAN_CHUNK + 1;  // into the buffer of the chunk just finished
-      const uint2 v = pbuf[((e / PLAN_CHUNK) & 1) * PLAN_CHUNK + j];
-      it.x = (unsigned)uni((int)v.x);
-      it.y = (unsigned)uni((int)v.y);
-      ++e;
+      peek(it);
+      take();
       if (it.kind() != KIND_CHECKPOINT) return true;
       checkpoint_wait(ckpt + it.index(), ck_target);
     }
@@ -679,13 +715,16 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
     stage_share(d, wave, ks, ko);
     stage_share(d + LDS_V, wave, vs, vo);
   };
+  auto consume_lm = [&](const Item& it, const char* kb) {
+    const unsigned us = (it.users() >> s0) & slots;
+    if (us) attend_landmarks<SW>(st, us, kb, it.index(), mrow0, A.nwords, lane);
+  };
   auto consume = [&](const Item& it, const char* kb) {
     const unsigned us = (it.users() >> s0) & slots;
     if (!us) return;
     const int nk = it.nkeys();
-    const int lb = it.kind() == KIND_LANDMARK ? it.index() : -1;
-    attend_block<SW>(st, us, kb, 0, nk, lb, mrow0, A.nwords, lane);
-    if (nk > KBLK) attend_block<SW>(st, us, kb, KBLK, nk - KBLK, -1, mrow0, A.nwords, lane);
+    attend_block<SW>(st, us, kb, 0, nk, lane);
+    if (nk > KBLK) attend_block<SW>(st, us, kb, KBLK, nk - KBLK, lane);
   };
   auto refill = [&] {
     if (want >= 0) {
@@ -693,6 +732,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
       want = -1;
     }
   };
+  stream_items(ringA, ringB, next_lm, issue, consume_lm, refill);
   stream_items(ringA, ringB, next, issue, consume, refill);
   // Per-lane indices are recomputed after the walk rather than kept live
   // across it from the set-up (register pressure).

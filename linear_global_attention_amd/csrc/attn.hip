@@ -147,6 +147,15 @@ __device__ __forceinline__ void probs(const f32x4& s0, const f32x4& s1, float of
   }
 }
 
+// Whether slot s is set in the wave-uniform mask m, as a scalar test: the
+// value passes through readfirstlane so that the compiler branches on it
+// directly (s_bitcmp + s_cbranch) instead of building exec-mask flow blocks
+// around each slot (measured faster in the token-block loop; not in the
+// landmark and bound loops).
+__device__ __forceinline__ bool slot_on(unsigned m, int s) {
+  return __builtin_amdgcn_readfirstlane((int)((m >> s) & 1u)) != 0;
+}
+
 // Row sums and O^T += V^T bf16(P)^T.
 __device__ __forceinline__ void pv(const float p[8], const bf16x8 vf[4], f32x4 o[4], float& l) {
   l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
@@ -178,7 +187,7 @@ __device__ __forceinline__ void attend_block(MainState<SW>& st, unsigned us, con
   }
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
-    if (!((us >> s) & 1u)) continue;
+    if (!slot_on(us, s)) continue;
     f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][0], st.q[s][0], b0, 0, 0, 0);
     f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][0], st.q[s][0], b1, 0, 0, 0);
     a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][1], st.q[s][1], a0, 0, 0, 0);

@@ -298,7 +298,7 @@ struct Item {
   __device__ unsigned users() const { return y & 0xFFu; }
   __device__ int nkeys() const { return (int)(y >> 8); }
 };
-constexpr int KIND_TILE = 0, KIND_LANDMARK = 1, KIND_SPECIAL = 2, KIND_CHECKPOINT = 3;
+constexpr int KIND_TILE = 0, KIND_LANDMARK = 1, KIND_SPECIAL = 2, KIND_CHECKPOINT = 3, KIND_NOP = 4;
 // Patch units meet every CK_WORDS words of key tiles (a checkpoint entry in
 // their plans), so that the workgroups of a round, which drift apart as
 // they walk the keys at slightly different speeds, stay close enough for an
@@ -314,28 +314,25 @@ constexpr int CK_SPIN_MAX = 1000;
 constexpr int CK_RELEASE_PCT = 50;
 static_assert(FG <= 8, "plan entries hold 8 user bits");
 
-// Streams `next(item)`'s items through an LDS ring of two halves, ringA
-// and ringB (two items each, separate arrays), in batches of two:
-// `issue(item, buf)` starts an item's async loads, and once a batch has
-// landed in every wave `consume(item, buf)` runs for each of its items while
-// the next batch loads into the other half. One wait and one barrier per two
-// items. The loop is unrolled over the two halves so that every LDS read
-// names the half it reads: the compiler then knows that it cannot alias the
-// copies in flight into the other half and adds no wait for them. A batch's
-// plan entries are all taken (next) before its copies are issued, and
-// `refill()` then starts any plan copy that next() asked for. Every wave
-// walks the same sequence itself and keeps the batches in scalar registers.
+// Streams items through an LDS ring of two halves, ringA and ringB (two
+// items each, separate arrays), in batches of two: `next(items)` yields the
+// next batch (up to two items), `issue(item, buf)` starts an item's async
+// loads, and once a batch has landed in every wave `consume(item, buf)` runs
+// for each of its items while the next batch loads into the other half. One
+// wait and one barrier per batch. The loop is unrolled over the two halves
+// so that every LDS read names the half it reads: the compiler then knows
+// that it cannot alias the copies in flight into the other half and adds no
+// wait for them. A batch's plan entries are taken before its copies are
+// issued, and `refill()` then starts any plan copy that next() asked for.
+// Every wave walks the same sequence itself and keeps the batches in scalar
+// registers.
 template <typename Next, typename Issue, typename Consume, typename Refill>
 __device__ __forceinline__ void stream_items(char* ringA, char* ringB, Next next, Issue issue, Consume consume,
                                              Refill refill) {
   static_assert(FNBUF == 4, "two halves of two items");
   bool more = true;
   auto fetch = [&](Item (&it)[2]) -> int {
-    int n = 0;
-    if (more && next(it[0])) {
-      n = 1;
-      if (next(it[1])) n = 2;
-    }
+    const int n = more ? next(it) : 0;
     more = n == 2;
     return n;
   };
@@ -426,14 +423,19 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, A
   const int nlb = g.T_pad / KBLK, nsb = g.spec_pad / KBLK;
   // items: landmark key blocks 0..nlb-1, then special key blocks
   int cnt = 0;
-  auto next = [&](Item& it) -> bool {
-    if (cnt >= nlb + nsb) return false;
-    const bool lm = cnt < nlb;
-    const int b = lm ? cnt : cnt - nlb;
-    it.x = (unsigned)((lm ? KIND_LANDMARK : KIND_SPECIAL) << 28) | (unsigned)b;
-    it.y = (unsigned)((lm ? KBLK : min(KBLK, g.nspec - b * KBLK)) << 8);
-    ++cnt;
-    return true;
+  auto next = [&](Item (&it)[2]) -> int {
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (cnt >= nlb + nsb) break;
+      const bool lm = cnt < nlb;
+      const int b = lm ? cnt : cnt - nlb;
+      it[j].x = (unsigned)((lm ? KIND_LANDMARK : KIND_SPECIAL) << 28) | (unsigned)b;
+      it[j].y = (unsigned)((lm ? KBLK : min(KBLK, g.nspec - b * KBLK)) << 8);
+      ++cnt;
+      ++n;
+    }
+    return n;
   };
   const StageOffsets so(wave, lane);
   auto issue = [&](const Item& it, char* d) {
@@ -465,9 +467,12 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, A
 // (every tile for dense items and special segments), each with the bit set
 // of groups that see it; then, for patch items and the last segment of a
 // special item, the special-key blocks. Patch units also get a
-// checkpoint entry after every CK_WORDS-th word but the last. Writes
-// `count[i]` entries of at most `stride` to plan + i * stride for unit
-// unit0 + i, and zeroes the round's checkpoint counters.
+// checkpoint entry after every CK_WORDS-th word but the last. The landmark
+// section is padded to an even length with a no-op entry, so that the main
+// kernel takes both entries of a batch with one LDS read. Writes count[2i]
+// entries of at most `stride` to plan + i * stride for unit unit0 + i and
+// the landmark section's length to count[2i + 1], and zeroes the round's
+// checkpoint counters.
 template <int G>
 __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int segs, int unit0, int nunits,
                                                         uint2* plan, int* count, int stride, int* ckpt,
@@ -506,7 +511,12 @@ __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int 
             make_uint2((unsigned)(KIND_LANDMARK << 28) | (unsigned)w, lm | (unsigned)(KBLK << 8));
       base += __builtin_popcountll(bal);
     }
+    if (base & 1) {  // pad the landmark section to whole batches of two
+      if (lane == 0) out[base] = make_uint2((unsigned)(KIND_NOP << 28), 0u);
+      ++base;
+    }
   }
+  const int nlm = base;
   for (int wb = w0; wb < w1; wb += 64) {
     const int w = wb + lane;
     const bool on = w < w1;
@@ -554,7 +564,10 @@ __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int 
                                  valid | (unsigned)(min(KBLK, g.nspec - b * KBLK) << 8));
     base += nsb;
   }
-  if (lane == 0) count[local] = base;
+  if (lane == 0) {
+    count[2 * local] = base;
+    count[2 * local + 1] = nlm;
+  }
 }
 
 // Index of this lane's partial record of slot s of a special segment unit:
@@ -656,7 +669,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   // landed long before it is read); entries are read back as uniform LDS
   // loads at the start of a batch, before its copies are issued.
   const uint2* pl = plan + (long long)blockIdx.x * plan_stride;
-  const int count = uni(plan_count[blockIdx.x]);
+  const int count = uni(plan_count[2 * blockIdx.x]), nlm = uni(plan_count[2 * blockIdx.x + 1]);
   uint2* pbuf = plan_lds + wave * 2 * PLAN_CHUNK;
   auto load_chunk = [&](int c) {
     if (c * PLAN_CHUNK < count)
@@ -666,40 +679,31 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   load_chunk(0);
   load_chunk(1);
   ZEBRA_VMCNT(0);
-  int e = 0, want = -1;
-  auto peek = [&](Item& it) {
-    const uint2 v = pbuf[((e / PLAN_CHUNK) & 1) * PLAN_CHUNK + (e & (PLAN_CHUNK - 1))];
-    it.x = (unsigned)uni((int)v.x);
-    it.y = (unsigned)uni((int)v.y);
+  // The plan is taken two entries at a time (one 16-byte LDS read; e stays
+  // even, so a pair never straddles two chunks): first the landmark section
+  // [0, nlm), then the rest up to `count`. Checkpoint entries are waited for
+  // here; they and no-op entries stage and compute nothing.
+  unsigned e = 0u, end = (unsigned)nlm;
+  int want = -1;
+  auto next2 = [&](Item (&it)[2]) -> int {
+    if (e >= end) return 0;
+    const uint4 v = *(const uint4*)(pbuf + (e & (2 * PLAN_CHUNK - 1)));
+    it[0].x = (unsigned)uni((int)v.x);
+    it[0].y = (unsigned)uni((int)v.y);
+    it[1].x = (unsigned)uni((int)v.z);
+    it[1].y = (unsigned)uni((int)v.w);
+    if ((e & (PLAN_CHUNK - 1)) == 0 && e > 0) want = (int)(e / PLAN_CHUNK) + 1;  // into the chunk just finished
+    const int n = end - e >= 2u ? 2 : 1;
+    e += 2u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (j < n && it[j].kind() == KIND_CHECKPOINT) checkpoint_wait(ckpt + it[j].index(), ck_target);
+    return n;
   };
-  auto take = [&] {
-    if ((e & (PLAN_CHUNK - 1)) == 0 && e > 0) want = e / PLAN_CHUNK + 1;  // into the buffer of the chunk just finished
-    ++e;
-  };
-  // the landmark blocks (they lead the plan)
-  auto next_lm = [&](Item& it) -> bool {
-    if (e >= count) return false;
-    peek(it);
-    if (it.kind() != KIND_LANDMARK) return false;
-    take();
-    return true;
-  };
-  // the rest: token tiles, checkpoints, special blocks
-  auto next = [&](Item& it) -> bool {
-    for (;;) {
-      if (e >= count) return false;
-      peek(it);
-      take();
-      if (it.kind() != KIND_CHECKPOINT) return true;
-      checkpoint_wait(ckpt + it.index(), ck_target);
-    }
-  };
-  // Per-lane source offsets of this wave's async-load shares: the 8 KB and
-  // 4 KB forms are picked with selects (not by indexing an array, which the
-  // compiler would place in scratch memory and wait for with vmcnt).
   const StageOffsets so(wave, lane);
   auto issue = [&](const Item& it, char* d) {
     const int kind = it.kind();
+    if (kind >= KIND_CHECKPOINT) return;
     const bool vbig = kind == KIND_TILE && it.nkeys() > KBLK;
     const bool kbig = vbig || kind == KIND_LANDMARK;
     const long long idx = it.index();
@@ -725,6 +729,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
     stage_share(d + LDS_V, wave, vs, vo);
   };
   auto consume_lm = [&](const Item& it, const char* kb) {
+    if (it.kind() != KIND_LANDMARK) return;
     const unsigned us = (it.users() >> s0) & slots;
     if (us) attend_landmarks<SW>(st, us, kb, it.index(), mrow0, A.nwords, lane);
   };
@@ -741,8 +746,9 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
       want = -1;
     }
   };
-  stream_items(ringA, ringB, next_lm, issue, consume_lm, refill);
-  stream_items(ringA, ringB, next, issue, consume, refill);
+  stream_items(ringA, ringB, next2, issue, consume_lm, refill);
+  end = (unsigned)count;
+  stream_items(ringA, ringB, next2, issue, consume, refill);
   // Per-lane indices are recomputed after the walk rather than kept live
   // across it from the set-up (register pressure).
   int lane_a = lane;
@@ -874,7 +880,7 @@ struct AttnWorkspace {
     flags_off = 0;
     negm_off = up((size_t)groups * sizeof(int));
     count_off = up(negm_off + (size_t)records * sizeof(float));
-    ckpt_off = up(count_off + (size_t)ROUND_MAX * sizeof(int));
+    ckpt_off = up(count_off + (size_t)ROUND_MAX * 2 * sizeof(int));
     plan_off = up(ckpt_off + (size_t)nckpt * sizeof(int));
     // the last unit's final plan chunk may be read past its stride
     spl_off = up(plan_off + ((size_t)ROUND_MAX * plan_stride + PLAN_CHUNK) * sizeof(uint2));

@@ -9,9 +9,10 @@
 //
 // Three kernels: qbar (mean patch query per tile, exact fp64 sums),
 // scores (a 64x64-blocked fp64 product qbar . kbar^T into a workspace
-// chunk) and topk (one 1024-thread workgroup per query tile: MSB-first
-// radix select over order-preserving 64-bit keys, then an ascending
-// compaction by workgroup prefix sums that also writes the bitmap).
+// chunk) and topk (one 1024-thread workgroup per query tile: the k-th key
+// found by histogram range narrowing over order-preserving 64-bit keys, then
+// an ascending compaction from one scan of per-wave counts that also writes
+// the bitmap).
 #include "common.hpp"
 
 namespace zebra {
@@ -96,52 +97,87 @@ __device__ inline double key_score(unsigned long long k) {
   return __longlong_as_double((long long)b);
 }
 
-// Exclusive prefix over the workgroup (tid order) of two flags at once.
-// Returns prefix in .x/.y and writes the totals.
-__device__ inline int2 wg_prefix2(bool a, bool b, int* lds /*[2*16]*/, int& tot_a, int& tot_b) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long ba = __ballot(a), bb = __ballot(b);
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int pa = __popcll(ba & below), pb = __popcll(bb & below);
-  __syncthreads();
-  if (lane == 0) {
-    lds[wave] = __popcll(ba);
-    lds[16 + wave] = __popcll(bb);
-  }
-  __syncthreads();
-  int ta = 0, tb = 0;
-  for (int w = 0; w < TOPK_THREADS / 64; ++w) {
-    const int ca = lds[w], cb = lds[16 + w];
-    if (w < wave) {
-      pa += ca;
-      pb += cb;
+constexpr int TOPK_BINS = 4096;  // histogram bins per refinement level
+constexpr int TOPK_CAND = 256;   // candidates ranked pairwise in LDS
+
+// Exclusive prefix, in place, of the per-(round, wave) counts tab[0, nvalid)
+// (round-major, so in tile order), by the first wave; entries past nvalid
+// (rounds past the last tile) count as zero.
+__device__ inline void table_scan(unsigned* tab, int nvalid) {
+  constexpr int N = TOPK_PER_THREAD * (TOPK_THREADS / 64), PER = N / 64;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    unsigned v[PER], sum = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      v[j] = lane * PER + j < nvalid ? tab[lane * PER + j] : 0u;
+      sum += v[j];
     }
-    ta += ca;
-    tb += cb;
+    unsigned incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    unsigned run = incl - sum;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      tab[lane * PER + j] = run;
+      run += v[j];
+    }
   }
-  tot_a = ta;
-  tot_b = tb;
-  return make_int2(pa, pb);
+}
+
+// Workgroup min and max of 64-bit keys into r[0], r[1]; r must hold (~0, 0)
+// on entry (visible to all waves). Ends with a barrier.
+__device__ inline void block_range(unsigned long long lo, unsigned long long hi, unsigned long long* r) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long ol = __shfl_xor(lo, off, 64), oh = __shfl_xor(hi, off, 64);
+    lo = ol < lo ? ol : lo;
+    hi = oh > hi ? oh : hi;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicMin(&r[0], lo);
+    atomicMax(&r[1], hi);
+  }
+  __syncthreads();
 }
 
 // grid (nq), block 1024: top-k of query tile t0+blockIdx.x of head h.
+// Thread tid holds the keys of tiles u = i * 1024 + tid (round i).
+//
+// The kept set is every (key, u) ranked at or above the k-th in the order
+// (key descending, tile index ascending). That k-th pair is found by
+// narrowing a key range: a 4096-bin histogram of the range (bins uniform in
+// score on the first level, in key bits after that), the bin holding the
+// k-th key becomes the next range, until the bin holds few enough keys to
+// rank them pairwise, or holds one key value (then the tie is cut by tile
+// index). Every bin map is monotone in the key, so bins are key intervals.
 __global__ void __launch_bounds__(TOPK_THREADS) topk_kernel(Geom g, int h, int t0, int k,
                                                             const double* __restrict__ scores,
                                                             int* __restrict__ sel,
                                                             unsigned* __restrict__ selmask,
                                                             double* __restrict__ gap) {
-  __shared__ unsigned hist[256];
-  __shared__ unsigned long long sh_prefix;
-  __shared__ unsigned sh_want;
-  __shared__ int lds[32];
-  __shared__ unsigned long long sh_below;
-  const int tid = threadIdx.x;
+  constexpr int NW = TOPK_THREADS / 64, BPT = TOPK_BINS / TOPK_THREADS;
+  __shared__ unsigned hist[TOPK_BINS];
+  __shared__ unsigned wsum[NW];
+  __shared__ unsigned cnt_take[TOPK_PER_THREAD * NW];
+  __shared__ unsigned long long cand_key[TOPK_CAND];
+  __shared__ int cand_u[TOPK_CAND];
+  __shared__ unsigned long long rng[8];  // range reductions, two per use
+  __shared__ unsigned sh_bin, sh_want, sh_cnt, sh_nc;
+  __shared__ unsigned long long sh_kt;
+  __shared__ int sh_ut;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = t0 + blockIdx.x;
   const int T = g.T;
   const int nwords = (T + 31) / 32;
+  const int rounds = (T + TOPK_THREADS - 1) / TOPK_THREADS;
   const double* row = scores + (long long)blockIdx.x * T;
   int* selrow = sel + ((long long)h * T + t) * k;
   unsigned* maskrow = selmask + ((long long)h * T + t) * nwords;
+  const unsigned long long below_lanes = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 
   unsigned long long key[TOPK_PER_THREAD];
 #pragma unroll
@@ -165,84 +201,195 @@ __global__ void __launch_bounds__(TOPK_THREADS) topk_kernel(Geom g, int h, int t
     return;
   }
 
-  // MSB-first radix select of the k-th largest key.
-  unsigned long long prefix = 0ull, pmask = 0ull;
-  unsigned want = (unsigned)k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += TOPK_THREADS) hist[i] = 0u;
+  if (tid < 4) {
+    rng[2 * tid] = ~0ull;
+    rng[2 * tid + 1] = 0ull;
+  }
+  __syncthreads();
+  unsigned long long lo = ~0ull, hi = 0ull;
+#pragma unroll
+  for (int i = 0; i < TOPK_PER_THREAD; ++i) {
+    if (i >= rounds) continue;  // uniform
+    if (i * TOPK_THREADS + tid < T) {
+      lo = key[i] < lo ? key[i] : lo;
+      hi = key[i] > hi ? key[i] : hi;
+    }
+  }
+  block_range(lo, hi, &rng[0]);
+  lo = rng[0];
+  hi = rng[1];
+  unsigned want = (unsigned)k, cnt = (unsigned)T;
+  // One narrowing step: histogram of the keys in [lo, hi] under the
+  // monotone bin map `digit`, the bin holding the want-th key, and that
+  // bin's key interval as the new [lo, hi].
+  auto narrow = [&](auto digit) {
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) hist[j * TOPK_THREADS + tid] = 0u;
+    if (tid < 2) rng[2 + tid] = tid == 0 ? ~0ull : 0ull;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-      const int u = i * TOPK_THREADS + tid;
-      if (u < T && (key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
+      if (i >= rounds) continue;  // uniform
+      if (i * TOPK_THREADS + tid < T && key[i] >= lo && key[i] <= hi) atomicAdd(&hist[digit(key[i])], 1u);
     }
     __syncthreads();
-    if (tid < 64) {
-      // lane l owns bins 255-4l .. 252-4l (descending order)
-      unsigned c[4], s = 0u;
+    // thread tid owns bins 4095-4tid .. 4092-4tid (descending key order)
+    unsigned c[BPT], sum = 0u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = hist[255 - 4 * tid - j];
-        s += c[j];
-      }
-      // exclusive prefix of s over lanes (lane order = descending bins)
-      unsigned incl = s;
+    for (int j = 0; j < BPT; ++j) {
+      c[j] = hist[TOPK_BINS - 1 - BPT * tid - j];
+      sum += c[j];
+    }
+    unsigned incl = sum;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned o = __shfl_up(incl, off, 64);
-        if (tid >= off) incl += o;
-      }
-      unsigned above = incl - s;
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    unsigned above = incl - sum;
+    for (int w = 0; w < wave; ++w) above += wsum[w];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (above < want && want <= above + c[j]) {
-          sh_prefix = prefix | ((unsigned long long)(255 - 4 * tid - j) << shift);
-          sh_want = want - above;
-        }
-        above += c[j];
+    for (int j = 0; j < BPT; ++j) {
+      if (above < want && want <= above + c[j]) {
+        sh_bin = TOPK_BINS - 1 - BPT * tid - j;
+        sh_want = want - above;
+        sh_cnt = c[j];
       }
+      above += c[j];
     }
     __syncthreads();
-    prefix = sh_prefix;
+    const unsigned bin = sh_bin;
     want = sh_want;
-    pmask |= 255ull << shift;
-    __syncthreads();
+    cnt = sh_cnt;
+    unsigned long long blo = ~0ull, bhi = 0ull;
+#pragma unroll
+    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
+      if (i >= rounds) continue;
+      if (i * TOPK_THREADS + tid < T && key[i] >= lo && key[i] <= hi && digit(key[i]) == bin) {
+        blo = key[i] < blo ? key[i] : blo;
+        bhi = key[i] > bhi ? key[i] : bhi;
+      }
+    }
+    block_range(blo, bhi, &rng[2]);
+    lo = rng[2];
+    hi = rng[3];
+  };
+  if (lo != hi) {
+    // first step: bins uniform in score, when the span is a normal number
+    const double flo = key_score(lo), fspan = key_score(hi) - flo;
+    const double inv = (double)TOPK_BINS / fspan;
+    if (fspan > 1e-300 && fspan < 1e300 && inv < 1e300)
+      narrow([&](unsigned long long kk) -> unsigned {
+        const double x = (key_score(kk) - flo) * inv;
+        return x < (double)(TOPK_BINS - 1) ? (unsigned)x : (unsigned)(TOPK_BINS - 1);
+      });
   }
-  const unsigned long long kth = prefix;  // key of the k-th ranked tile
+  // then bins uniform in key bits, 12 bits per step
+  while (lo != hi && cnt > (unsigned)TOPK_CAND) {
+    const unsigned long long span = hi - lo;
+    const int top = 64 - __clzll((long long)span);
+    const int sh = top > 12 ? top - 12 : 0;
+    const unsigned long long base = lo;
+    narrow([&](unsigned long long kk) -> unsigned { return (unsigned)((kk - base) >> sh); });
+  }
 
-  // Ascending compaction: keys above kth, then the first `want` ties.
-  if (tid == 0) sh_below = 0ull;
-  int sel_base = 0, tie_base = 0;
+  // the k-th pair (kt, ut): the want-th of the cnt keys in [lo, hi]
+  if (lo == hi) {
+    // one key value: the want-th smallest tile index holding it
+#pragma unroll
+    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
+      if (i >= rounds) continue;
+      const unsigned long long be = __ballot(i * TOPK_THREADS + tid < T && key[i] == lo);
+      if (lane == 0) cnt_take[i * NW + wave] = (unsigned)__popcll(be);
+    }
+    __syncthreads();
+    table_scan(cnt_take, rounds * NW);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
+      if (i >= rounds) continue;
+      const int u = i * TOPK_THREADS + tid;
+      const bool eq = u < T && key[i] == lo;
+      const unsigned long long be = __ballot(eq);
+      if (eq && cnt_take[i * NW + wave] + (unsigned)__popcll(be & below_lanes) == want - 1u) {
+        sh_kt = lo;
+        sh_ut = u;
+      }
+    }
+  } else {
+    if (tid == 0) sh_nc = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
+      if (i >= rounds) continue;
+      const int u = i * TOPK_THREADS + tid;
+      const bool in = u < T && key[i] >= lo && key[i] <= hi;
+      const unsigned long long bi = __ballot(in);
+      if (bi) {
+        unsigned base = 0u;
+        if (lane == 0) base = atomicAdd(&sh_nc, (unsigned)__popcll(bi));
+        base = (unsigned)__shfl(base, 0, 64);
+        if (in) {
+          const unsigned slot = base + (unsigned)__popcll(bi & below_lanes);
+          cand_key[slot] = key[i];
+          cand_u[slot] = u;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < (int)cnt) {
+      const unsigned long long kc = cand_key[tid];
+      const int uc = cand_u[tid];
+      unsigned rank = 0u;
+      for (int j = 0; j < (int)cnt; ++j) {
+        const unsigned long long kj = cand_key[j];
+        rank += (kj > kc || (kj == kc && cand_u[j] < uc)) ? 1u : 0u;
+      }
+      if (rank == want - 1u) {
+        sh_kt = kc;
+        sh_ut = uc;
+      }
+    }
+  }
+  __syncthreads();
+  const unsigned long long kt = sh_kt;
+  const int ut = sh_ut;
+
+  // kept tiles in ascending order: per-(round, wave) counts scanned once
   unsigned long long below_max = 0ull;
+#pragma unroll
   for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-    if (i * TOPK_THREADS >= T) break;  // uniform across the workgroup
+    if (i >= rounds) continue;
     const int u = i * TOPK_THREADS + tid;
-    const bool valid = u < T;
-    const bool gt = valid && key[i] > kth;
-    const bool eq = valid && key[i] == kth;
-    if (valid && key[i] < kth && key[i] > below_max) below_max = key[i];
-    int teq, dummy;
-    const int2 pe = wg_prefix2(eq, false, lds, teq, dummy);
-    const bool take = gt || (eq && (tie_base + pe.x) < (int)want);
-    int ttake;
-    const int2 pt = wg_prefix2(take, false, lds, ttake, dummy);
-    if (take && sel_base + pt.x < k) selrow[sel_base + pt.x] = u;
-    const unsigned long long bal = __ballot(take);
-    const int lane = tid & 63;
-    const int word = (i * TOPK_THREADS + (tid - lane)) / 32;
-    if (lane == 0 && word < nwords) maskrow[word] = (unsigned)bal;
-    if (lane == 0 && word + 1 < nwords) maskrow[word + 1] = (unsigned)(bal >> 32);
-    sel_base += ttake;
-    tie_base += teq;
+    const bool take = u < T && (key[i] > kt || (key[i] == kt && u <= ut));
+    const unsigned long long bt = __ballot(take);
+    if (lane == 0) cnt_take[i * NW + wave] = (unsigned)__popcll(bt);
+    const int word = (i * TOPK_THREADS + wave * 64) / 32;
+    if (lane == 0 && word < nwords) maskrow[word] = (unsigned)bt;
+    if (lane == 0 && word + 1 < nwords) maskrow[word + 1] = (unsigned)(bt >> 32);
+    if (u < T && !take) below_max = key[i] > below_max ? key[i] : below_max;
+  }
+  __syncthreads();
+  table_scan(cnt_take, rounds * NW);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TOPK_PER_THREAD; ++i) {
+    if (i >= rounds) continue;
+    const int u = i * TOPK_THREADS + tid;
+    const bool take = u < T && (key[i] > kt || (key[i] == kt && u <= ut));
+    const unsigned long long bt = __ballot(take);
+    const unsigned pos = cnt_take[i * NW + wave] + (unsigned)__popcll(bt & below_lanes);
+    if (take && pos < (unsigned)k) selrow[pos] = u;
   }
   if (gap) {
-    atomicMax(&sh_below, below_max);
-    __syncthreads();
+    block_range(~0ull, below_max, &rng[4]);
     if (tid == 0) {
-      const double sk = key_score(kth);
-      double sk1;
-      if (tie_base > (int)want) sk1 = sk;  // another tile ties the k-th
-      else sk1 = key_score(sh_below);
+      // k-th ranked score and (k+1)-th (greatest not kept; equal to the
+      // k-th when a tie straddles the cut)
+      const double sk = key_score(kt);
+      const double sk1 = key_score(rng[5]);
       const double den = fmax(fmax(fabs(sk), fabs(sk1)), 1e-300);
       gap[(long long)h * T + t] = fabs(sk - sk1) / den;
     }

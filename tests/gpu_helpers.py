@@ -68,6 +68,15 @@ class Stage:
         torch.cuda.synchronize()
         return self.out
 
+    def select(self):
+        """Pack, landmarks and tile selection only."""
+        a = self.args()
+        zb.pack_tiles(a)
+        zb.landmarks(a)
+        zb.select_tiles(a)
+        torch.cuda.synchronize()
+        return self.bufs.sel().cpu().numpy()
+
     def dense(self):
         zb.dense_attn(self.args())
         torch.cuda.synchronize()

@@ -270,3 +270,73 @@ def test_exact_fallback_rows():
     st2 = Stage(L, q, k, v, 0.0)
     out = bf16_host(st2.dense()).reshape(L.tokens, L.heads, 64)
     close(out, osp.dense_attention(Q, K, V), "exact-fallback dense (all rows)")
+
+
+# ------------------------------------------------------------- selector
+def test_selection_exact_ties():
+    """Equal scores are ranked by lower tile index. Every frame holds the same
+    keys, so each of a frame's 9 tile means repeats in all 6 frames and every
+    score occurs 6 times; k = 27 splits one such class. Query tiles 5 and 20
+    are all-zero, so all 54 of their scores tie and tiles 0..26 are kept.
+    Expected lists are built here from the 9 class scores; rows whose class
+    scores lie within 1e-9 of each other are skipped."""
+    L = zs.Layout(6, 2, 24, 24, heads=2)
+    y = 0.5
+    q, k, v = _inputs(L, seed=11)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    tok_pf = L.specials + L.rows * L.cols
+    Kf = zs.bf16_to_f32(k).copy()
+    for f in range(1, L.frames):
+        Kf[f * tok_pf:(f + 1) * tok_pf] = Kf[:tok_pf]
+    k = zs.f32_to_bf16(Kf)
+    zero_tiles = (5, 20)
+    Qf = zs.bf16_to_f32(q).copy()
+    for t in zero_tiles:
+        Qf[tm.tokens[t]] = 0.0
+    q = zs.f32_to_bf16(Qf)
+    Q, K = widen(q), widen(k)
+    kk = keep_count(y, tm.T)
+    tpf = tm.T // L.frames
+    assert kk % L.frames != 0
+    sel = Stage(L, q, k, v, y).select()
+    sel_ref, _ = _sel_ref(Q, K, tm, y)
+    checked = 0
+    for h in range(L.heads):
+        kbar, _, _ = osp.landmarks(K[:, h], K[:, h], tm)
+        assert all(np.array_equal(kbar[u], kbar[u % tpf]) for u in range(tm.T))
+        for t in range(tm.T):
+            if t in zero_tiles:
+                expect = np.arange(kk)
+            else:
+                qbar = Q[tm.tokens[t], h].sum(axis=0) / tm.n[t]
+                cls = kbar[:tpf] @ qbar
+                cs = np.sort(cls)
+                if np.min(np.diff(cs)) <= 1e-9 * np.max(np.abs(cs)):
+                    continue
+                order = sorted(range(tm.T), key=lambda u: (-cls[u % tpf], u))
+                expect = np.sort(np.array(order[:kk]))
+            assert np.array_equal(sel[h, t], expect), (h, t, sel[h, t], expect)
+            assert np.array_equal(sel_ref[h, t], expect), (h, t)
+            checked += 1
+    log(f"exact ties: {checked} of {L.heads * tm.T} rows checked")
+    assert checked >= L.heads * tm.T // 2
+
+
+def test_selection_with_outlier_tiles():
+    """A few key tiles scaled by 1e4 put their scores far outside the rest,
+    so nearly all scores fall into one bin of the first score-uniform
+    histogram and the selector must narrow by key bits over several levels.
+    Lists match the oracle except on near-tie rows."""
+    L = zs.Layout(16, 1, 64, 64, heads=1)
+    y = 0.7
+    q, k, v = _inputs(L, seed=12)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    Kf = zs.bf16_to_f32(k).copy()
+    for u, f in ((100, 1e4), (517, -1e4), (1000, 3e3)):
+        Kf[tm.tokens[u]] *= f
+    k = zs.f32_to_bf16(Kf)
+    Q, K = widen(q), widen(k)
+    sel = Stage(L, q, k, v, y).select()
+    sel_ref, tie_ref = _sel_ref(Q, K, tm, y)
+    r = compare_selection(sel, sel_ref, tie_ref, "outlier tiles selection")
+    assert r["near_tie"] < r["rows"] // 10

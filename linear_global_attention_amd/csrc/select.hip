@@ -128,32 +128,53 @@ __device__ inline void table_scan(unsigned* tab, int nvalid) {
   }
 }
 
-// Workgroup min and max of 64-bit keys into r[0], r[1]; r must hold (~0, 0)
-// on entry (visible to all waves). Ends with a barrier.
-__device__ inline void block_range(unsigned long long lo, unsigned long long hi, unsigned long long* r) {
+// A copy of x the compiler cannot see through: bin maps are recomputed in
+// each pass instead of being kept live across passes in registers.
+__device__ inline double opaque(double x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
+}
+
+// Workgroup min and max (by comparisons: the scores hold no NaN, and fmin
+// would make canonicalised copies of them) of the scores (lo, hi) through per-wave slots w[0..31];
+// every thread gets the result. Barrier on entry and exit.
+__device__ inline void block_minmax(double& lo, double& hi, double* w) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    const unsigned long long ol = __shfl_xor(lo, off, 64), oh = __shfl_xor(hi, off, 64);
+    const double ol = __shfl_xor(lo, off, 64), oh = __shfl_xor(hi, off, 64);
     lo = ol < lo ? ol : lo;
     hi = oh > hi ? oh : hi;
   }
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
   if ((threadIdx.x & 63) == 0) {
-    atomicMin(&r[0], lo);
-    atomicMax(&r[1], hi);
+    w[wave] = lo;
+    w[16 + wave] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < TOPK_THREADS / 64; ++j) {
+    lo = w[j] < lo ? w[j] : lo;
+    hi = w[16 + j] > hi ? w[16 + j] : hi;
   }
   __syncthreads();
 }
 
 // grid (nq), block 1024: top-k of query tile t0+blockIdx.x of head h.
-// Thread tid holds the keys of tiles u = i * 1024 + tid (round i).
+// Thread tid holds the scores of tiles u = i * 1024 + tid (round i).
 //
-// The kept set is every (key, u) ranked at or above the k-th in the order
-// (key descending, tile index ascending). That k-th pair is found by
-// narrowing a key range: a 4096-bin histogram of the range (bins uniform in
-// score on the first level, in key bits after that), the bin holding the
-// k-th key becomes the next range, until the bin holds few enough keys to
-// rank them pairwise, or holds one key value (then the tie is cut by tile
-// index). Every bin map is monotone in the key, so bins are key intervals.
+// The kept set is every (score, u) ranked at or above the k-th in the order
+// (score descending, tile index ascending). That k-th pair is found by
+// narrowing a score interval: a 4096-bin histogram of the interval (bins
+// uniform in score on the first level, in the order-preserving key bits
+// after that), and the bin holding the k-th score becomes the next
+// interval, until the bin holds at most 256 scores, which are ranked
+// pairwise in LDS, or one score value, whose tie is cut by tile index. Every
+// bin map is monotone, so bins are score intervals and a key in a higher bin
+// is strictly greater. Keys above the chosen bin are counted per (round,
+// wave) as each level is scanned; with the ranked candidates this gives
+// every kept key's output position, and one last pass writes the list and
+// the bitmap.
 __global__ void __launch_bounds__(TOPK_THREADS) topk_kernel(Geom g, int h, int t0, int k,
                                                             const double* __restrict__ scores,
                                                             int* __restrict__ sel,
@@ -162,28 +183,32 @@ __global__ void __launch_bounds__(TOPK_THREADS) topk_kernel(Geom g, int h, int t
   constexpr int NW = TOPK_THREADS / 64, BPT = TOPK_BINS / TOPK_THREADS;
   __shared__ unsigned hist[TOPK_BINS];
   __shared__ unsigned wsum[NW];
-  __shared__ unsigned cnt_take[TOPK_PER_THREAD * NW];
-  __shared__ unsigned long long cand_key[TOPK_CAND];
+  __shared__ unsigned take_tab[TOPK_PER_THREAD * NW];  // kept keys per (round, wave)
+  __shared__ unsigned eq_tab[TOPK_PER_THREAD * NW];
+  __shared__ double cand_s[TOPK_CAND];
   __shared__ int cand_u[TOPK_CAND];
-  __shared__ unsigned long long rng[8];  // range reductions, two per use
+  __shared__ double wred[2 * NW];
   __shared__ unsigned sh_bin, sh_want, sh_cnt, sh_nc;
-  __shared__ unsigned long long sh_kt;
+  __shared__ double sh_st;
   __shared__ int sh_ut;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = t0 + blockIdx.x;
   const int T = g.T;
   const int nwords = (T + 31) / 32;
   const int rounds = (T + TOPK_THREADS - 1) / TOPK_THREADS;
+  const int last = rounds - 1;
+  const bool tail_ok = tid < T - last * TOPK_THREADS;  // valid in the last round
   const double* row = scores + (long long)blockIdx.x * T;
   int* selrow = sel + ((long long)h * T + t) * k;
   unsigned* maskrow = selmask + ((long long)h * T + t) * nwords;
   const unsigned long long below_lanes = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+#define TOPK_VALID(i) ((i) < last || tail_ok)
 
-  unsigned long long key[TOPK_PER_THREAD];
+  double sc[TOPK_PER_THREAD];
 #pragma unroll
   for (int i = 0; i < TOPK_PER_THREAD; ++i) {
     const int u = i * TOPK_THREADS + tid;
-    key[i] = (u < T) ? score_key(row[u]) : 0ull;
+    sc[i] = (u < T) ? row[u] : 0.0;
   }
 
   if (k == 0 || k == T) {  // nothing to rank
@@ -201,39 +226,37 @@ __global__ void __launch_bounds__(TOPK_THREADS) topk_kernel(Geom g, int h, int t
     return;
   }
 
-  if (tid < 4) {
-    rng[2 * tid] = ~0ull;
-    rng[2 * tid + 1] = 0ull;
-  }
-  __syncthreads();
-  unsigned long long lo = ~0ull, hi = 0ull;
+  if (tid < TOPK_PER_THREAD * NW) take_tab[tid] = 0u;
+  double lo = __longlong_as_double(0x7FF0000000000000ll), hi = -lo;
 #pragma unroll
   for (int i = 0; i < TOPK_PER_THREAD; ++i) {
     if (i >= rounds) continue;  // uniform
-    if (i * TOPK_THREADS + tid < T) {
-      lo = key[i] < lo ? key[i] : lo;
-      hi = key[i] > hi ? key[i] : hi;
+    if (TOPK_VALID(i)) {
+      lo = sc[i] < lo ? sc[i] : lo;
+      hi = sc[i] > hi ? sc[i] : hi;
     }
   }
-  block_range(lo, hi, &rng[0]);
-  lo = rng[0];
-  hi = rng[1];
+  block_minmax(lo, hi, wred);
+
   unsigned want = (unsigned)k, cnt = (unsigned)T;
-  // One narrowing step: histogram of the keys in [lo, hi] under the
-  // monotone bin map `digit`, the bin holding the want-th key, and that
-  // bin's key interval as the new [lo, hi].
-  auto narrow = [&](auto digit) {
+  bool gathered = false;
+  // One narrowing step over the scores in [lo, hi] (all scores when `all`)
+  // under the monotone bin map `digit`: histogram, the bin holding the
+  // want-th score, per-(round, wave) counts of the scores above that bin,
+  // and then either the bin's scores gathered as candidates (at most
+  // TOPK_CAND) or the bin's interval as the new [lo, hi].
+  auto narrow = [&](auto digit, bool all) {
 #pragma unroll
     for (int j = 0; j < BPT; ++j) hist[j * TOPK_THREADS + tid] = 0u;
-    if (tid < 2) rng[2 + tid] = tid == 0 ? ~0ull : 0ull;
+    if (tid == 0) sh_nc = 0u;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-      if (i >= rounds) continue;  // uniform
-      if (i * TOPK_THREADS + tid < T && key[i] >= lo && key[i] <= hi) atomicAdd(&hist[digit(key[i])], 1u);
+      if (i >= rounds) continue;
+      if (TOPK_VALID(i) && (all || (sc[i] >= lo && sc[i] <= hi))) atomicAdd(&hist[digit(opaque(sc[i]))], 1u);
     }
     __syncthreads();
-    // thread tid owns bins 4095-4tid .. 4092-4tid (descending key order)
+    // thread tid owns bins 4095-4tid .. 4092-4tid (descending order)
     unsigned c[BPT], sum = 0u;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
@@ -263,135 +286,159 @@ __global__ void __launch_bounds__(TOPK_THREADS) topk_kernel(Geom g, int h, int t
     const unsigned bin = sh_bin;
     want = sh_want;
     cnt = sh_cnt;
-    unsigned long long blo = ~0ull, bhi = 0ull;
+    const bool gather = cnt <= (unsigned)TOPK_CAND;
+    double blo = __longlong_as_double(0x7FF0000000000000ll), bhi = -blo;
 #pragma unroll
     for (int i = 0; i < TOPK_PER_THREAD; ++i) {
       if (i >= rounds) continue;
-      if (i * TOPK_THREADS + tid < T && key[i] >= lo && key[i] <= hi && digit(key[i]) == bin) {
-        blo = key[i] < blo ? key[i] : blo;
-        bhi = key[i] > bhi ? key[i] : bhi;
+      const int u = i * TOPK_THREADS + tid;
+      const bool inr = TOPK_VALID(i) && (all || (sc[i] >= lo && sc[i] <= hi));
+      const unsigned d = inr ? digit(opaque(sc[i])) : 0u;
+      const unsigned long long ba = __ballot(inr && d > bin);
+      if (lane == 0) take_tab[i * NW + wave] += (unsigned)__popcll(ba);
+      const bool inb = inr && d == bin;
+      if (gather) {
+        const unsigned long long bi = __ballot(inb);
+        if (bi) {
+          unsigned base = 0u;
+          if (lane == 0) base = atomicAdd(&sh_nc, (unsigned)__popcll(bi));
+          base = (unsigned)__shfl(base, 0, 64);
+          if (inb) {
+            const unsigned slot = base + (unsigned)__popcll(bi & below_lanes);
+            cand_s[slot] = sc[i];
+            cand_u[slot] = u;
+          }
+        }
+      } else if (inb) {
+        blo = sc[i] < blo ? sc[i] : blo;
+        bhi = sc[i] > bhi ? sc[i] : bhi;
       }
     }
-    block_range(blo, bhi, &rng[2]);
-    lo = rng[2];
-    hi = rng[3];
+    if (gather) {
+      gathered = true;
+      __syncthreads();
+    } else {
+      block_minmax(blo, bhi, wred);
+      lo = blo;
+      hi = bhi;
+    }
   };
-  if (lo != hi) {
+  if (lo != hi && cnt > (unsigned)TOPK_CAND) {
     // first step: bins uniform in score, when the span is a normal number
-    const double flo = key_score(lo), fspan = key_score(hi) - flo;
+    const double fspan = hi - lo;
     const double inv = (double)TOPK_BINS / fspan;
-    if (fspan > 1e-300 && fspan < 1e300 && inv < 1e300)
-      narrow([&](unsigned long long kk) -> unsigned {
-        const double x = (key_score(kk) - flo) * inv;
-        return x < (double)(TOPK_BINS - 1) ? (unsigned)x : (unsigned)(TOPK_BINS - 1);
-      });
+    if (fspan > 1e-300 && fspan < 1e300 && inv < 1e300) {
+      const double flo = lo;
+      narrow(
+          [&](double x) -> unsigned {
+            const double y = (x - flo) * inv;
+            return y < (double)(TOPK_BINS - 1) ? (unsigned)y : (unsigned)(TOPK_BINS - 1);
+          },
+          true);
+    }
   }
   // then bins uniform in key bits, 12 bits per step
-  while (lo != hi && cnt > (unsigned)TOPK_CAND) {
-    const unsigned long long span = hi - lo;
+  while (!gathered && lo != hi && cnt > (unsigned)TOPK_CAND) {
+    const unsigned long long klo = score_key(lo), span = score_key(hi) - klo;
     const int top = 64 - __clzll((long long)span);
     const int sh = top > 12 ? top - 12 : 0;
-    const unsigned long long base = lo;
-    narrow([&](unsigned long long kk) -> unsigned { return (unsigned)((kk - base) >> sh); });
+    narrow([&](double x) -> unsigned { return (unsigned)((score_key(x) - klo) >> sh); }, false);
   }
 
-  // the k-th pair (kt, ut): the want-th of the cnt keys in [lo, hi]
-  if (lo == hi) {
-    // one key value: the want-th smallest tile index holding it
+  // the k-th pair (st, ut) and the kept keys of the final bin
+  if (gathered || (lo != hi && cnt <= (unsigned)TOPK_CAND)) {
+    if (!gathered) {  // few scores from the start: all are candidates
+      if (tid == 0) sh_nc = 0u;
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-      if (i >= rounds) continue;
-      const unsigned long long be = __ballot(i * TOPK_THREADS + tid < T && key[i] == lo);
-      if (lane == 0) cnt_take[i * NW + wave] = (unsigned)__popcll(be);
-    }
-    __syncthreads();
-    table_scan(cnt_take, rounds * NW);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-      if (i >= rounds) continue;
-      const int u = i * TOPK_THREADS + tid;
-      const bool eq = u < T && key[i] == lo;
-      const unsigned long long be = __ballot(eq);
-      if (eq && cnt_take[i * NW + wave] + (unsigned)__popcll(be & below_lanes) == want - 1u) {
-        sh_kt = lo;
-        sh_ut = u;
-      }
-    }
-  } else {
-    if (tid == 0) sh_nc = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-      if (i >= rounds) continue;
-      const int u = i * TOPK_THREADS + tid;
-      const bool in = u < T && key[i] >= lo && key[i] <= hi;
-      const unsigned long long bi = __ballot(in);
-      if (bi) {
-        unsigned base = 0u;
-        if (lane == 0) base = atomicAdd(&sh_nc, (unsigned)__popcll(bi));
-        base = (unsigned)__shfl(base, 0, 64);
-        if (in) {
-          const unsigned slot = base + (unsigned)__popcll(bi & below_lanes);
-          cand_key[slot] = key[i];
-          cand_u[slot] = u;
+      for (int i = 0; i < TOPK_PER_THREAD; ++i) {
+        if (i >= rounds) continue;
+        const bool inb = TOPK_VALID(i);
+        const unsigned long long bi = __ballot(inb);
+        if (bi) {
+          unsigned base = 0u;
+          if (lane == 0) base = atomicAdd(&sh_nc, (unsigned)__popcll(bi));
+          base = (unsigned)__shfl(base, 0, 64);
+          if (inb) {
+            const unsigned slot = base + (unsigned)__popcll(bi & below_lanes);
+            cand_s[slot] = sc[i];
+            cand_u[slot] = i * TOPK_THREADS + tid;
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
     if (tid < (int)cnt) {
-      const unsigned long long kc = cand_key[tid];
+      const double sc_c = cand_s[tid];
       const int uc = cand_u[tid];
       unsigned rank = 0u;
       for (int j = 0; j < (int)cnt; ++j) {
-        const unsigned long long kj = cand_key[j];
-        rank += (kj > kc || (kj == kc && cand_u[j] < uc)) ? 1u : 0u;
+        const double sj = cand_s[j];
+        rank += (sj > sc_c || (sj == sc_c && cand_u[j] < uc)) ? 1u : 0u;
       }
       if (rank == want - 1u) {
-        sh_kt = kc;
+        sh_st = sc_c;
         sh_ut = uc;
+      }
+      if (rank < want) atomicAdd(&take_tab[(uc / TOPK_THREADS) * NW + (uc % TOPK_THREADS) / 64], 1u);
+    }
+  } else {
+    // one score value (lo == hi) in the final interval: keep the want
+    // smallest tile indices holding it
+#pragma unroll
+    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
+      if (i >= rounds) continue;
+      const unsigned long long be = __ballot(TOPK_VALID(i) && sc[i] == lo);
+      if (lane == 0) eq_tab[i * NW + wave] = (unsigned)__popcll(be);
+    }
+    __syncthreads();
+    table_scan(eq_tab, rounds * NW);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
+      if (i >= rounds) continue;
+      const bool eq = TOPK_VALID(i) && sc[i] == lo;
+      const unsigned long long be = __ballot(eq);
+      const unsigned r = eq_tab[i * NW + wave] + (unsigned)__popcll(be & below_lanes);
+      const unsigned long long bk = __ballot(eq && r < want);
+      if (lane == 0) take_tab[i * NW + wave] += (unsigned)__popcll(bk);
+      if (eq && r == want - 1u) {
+        sh_st = lo;
+        sh_ut = i * TOPK_THREADS + tid;
       }
     }
   }
   __syncthreads();
-  const unsigned long long kt = sh_kt;
+  table_scan(take_tab, rounds * NW);
+  __syncthreads();
+  const double st = sh_st;
   const int ut = sh_ut;
 
-  // kept tiles in ascending order: per-(round, wave) counts scanned once
-  unsigned long long below_max = 0ull;
+  // kept tiles in ascending order, and the bitmap
+  double below_max = -__longlong_as_double(0x7FF0000000000000ll);
 #pragma unroll
   for (int i = 0; i < TOPK_PER_THREAD; ++i) {
     if (i >= rounds) continue;
     const int u = i * TOPK_THREADS + tid;
-    const bool take = u < T && (key[i] > kt || (key[i] == kt && u <= ut));
+    const bool v = TOPK_VALID(i);
+    const bool take = v && (sc[i] > st || (sc[i] == st && u <= ut));
     const unsigned long long bt = __ballot(take);
-    if (lane == 0) cnt_take[i * NW + wave] = (unsigned)__popcll(bt);
     const int word = (i * TOPK_THREADS + wave * 64) / 32;
     if (lane == 0 && word < nwords) maskrow[word] = (unsigned)bt;
     if (lane == 0 && word + 1 < nwords) maskrow[word + 1] = (unsigned)(bt >> 32);
-    if (u < T && !take) below_max = key[i] > below_max ? key[i] : below_max;
-  }
-  __syncthreads();
-  table_scan(cnt_take, rounds * NW);
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-    if (i >= rounds) continue;
-    const int u = i * TOPK_THREADS + tid;
-    const bool take = u < T && (key[i] > kt || (key[i] == kt && u <= ut));
-    const unsigned long long bt = __ballot(take);
-    const unsigned pos = cnt_take[i * NW + wave] + (unsigned)__popcll(bt & below_lanes);
+    const unsigned pos = take_tab[i * NW + wave] + (unsigned)__popcll(bt & below_lanes);
     if (take && pos < (unsigned)k) selrow[pos] = u;
+    if (v && !take && sc[i] > below_max) below_max = sc[i];
   }
+#undef TOPK_VALID
   if (gap) {
-    block_range(~0ull, below_max, &rng[4]);
+    double dummy = 0.0;
+    block_minmax(dummy, below_max, wred);
     if (tid == 0) {
       // k-th ranked score and (k+1)-th (greatest not kept; equal to the
       // k-th when a tie straddles the cut)
-      const double sk = key_score(kt);
-      const double sk1 = key_score(rng[5]);
-      const double den = fmax(fmax(fabs(sk), fabs(sk1)), 1e-300);
-      gap[(long long)h * T + t] = fabs(sk - sk1) / den;
+      const double den = fmax(fmax(fabs(st), fabs(below_max)), 1e-300);
+      gap[(long long)h * T + t] = fabs(st - below_max) / den;
     }
   }
 }

@@ -340,3 +340,42 @@ def test_selection_with_outlier_tiles():
     sel_ref, tie_ref = _sel_ref(Q, K, tm, y)
     r = compare_selection(sel, sel_ref, tie_ref, "outlier tiles selection")
     assert r["near_tie"] < r["rows"] // 10
+
+
+def test_selection_tie_group_after_narrowing():
+    """600 of 1,024 key tiles are all-zero, so every query scores them 0
+    exactly, and the cut at k = 307 falls inside that group on most rows. The
+    first histogram level puts the whole group into one bin of more than 256
+    keys, which narrows to a single score value; the tie is then cut by tile
+    index. Expected lists: every tile scoring above 0, then the lowest-index
+    zero tiles up to k (rows whose cut is elsewhere, or with a score within
+    1e-9 of 0, are skipped)."""
+    L = zs.Layout(16, 1, 64, 64, heads=1)
+    y = 0.7
+    q, k, v = _inputs(L, seed=13)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    zero = np.arange(200, 800)
+    Kf = zs.bf16_to_f32(k).copy()
+    for u in zero:
+        Kf[tm.tokens[u]] = 0.0
+    k = zs.f32_to_bf16(Kf)
+    Q, K = widen(q), widen(k)
+    kk = keep_count(y, tm.T)
+    sel = Stage(L, q, k, v, y).select()
+    kbar, _, _ = osp.landmarks(K[:, 0], K[:, 0], tm)
+    assert not kbar[zero].any()
+    checked = 0
+    for t in range(tm.T):
+        qbar = Q[tm.tokens[t], 0].sum(axis=0) / tm.n[t]
+        s = kbar @ qbar
+        nz = np.abs(s[s != 0])
+        if nz.size and nz.min() <= 1e-9 * nz.max():
+            continue
+        pos = np.flatnonzero(s > 0)
+        if not (len(pos) < kk <= len(pos) + len(zero)):
+            continue
+        expect = np.sort(np.concatenate([pos, zero[:kk - len(pos)]]))
+        assert np.array_equal(sel[0, t], expect), (t, len(pos))
+        checked += 1
+    log(f"tie group: {checked} of {tm.T} rows checked")
+    assert checked >= tm.T // 2

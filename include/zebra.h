@@ -133,7 +133,10 @@ enum {
  * input views": the sparse-stage kernels pack the key/value sequence into
  * tile-major order). Reads k, v; writes kt, vt (each tile's tokens
  * row-major, zero-padded to a multiple of 32 slots) and ks, vs (all special
- * tokens in frame order, zero-padded to a multiple of 32). */
+ * tokens in frame order, zero-padded to a multiple of 32). When kbar is
+ * non-NULL (then vbar, logn and lm must be too) the same pass also writes
+ * every landmark exactly as zebra_landmarks would from kt and vt, so K and V
+ * are read once; zebra_landmarks need not be called after it. */
 zebra_status zebra_pack_tiles(const zebra_args* a, zebra_stream stream);
 
 /* Mean key/value landmark of every tile ("Linear-centered stages plus

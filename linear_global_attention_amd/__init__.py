@@ -245,8 +245,8 @@ def dense_attn(args: Args, stream=None):
 
 
 def sparse_stage(args: Args, stream=None):
-    """One tile-sparse global stage: pack, landmarks, select, attention."""
+    """One tile-sparse global stage: pack (with the landmarks in the same
+    pass), select, attention."""
     pack_tiles(args, stream)
-    landmarks(args, stream)
     select_tiles(args, stream)
     sparse_attn(args, stream)

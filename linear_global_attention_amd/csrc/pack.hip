@@ -21,17 +21,67 @@ __device__ inline long long tile_token(const Geom& g, int f, int tl, int s) {
   return (long long)f * g.tok_pf + g.S + (long long)r * g.C + c;
 }
 
-// grid (T + spec_pad/32, H), block 256.
+// Landmark outputs of tile u (< T) of head h from its per-channel fp64 sums
+// and max deviations, written by the thread of channel d. The radius is the
+// Euclidean norm of the 64 per-channel deviations, summed in a fixed pairwise
+// tree (lane d adds lane d + o for o = 32, 16, ..., 1), inflated to cover the
+// bf16 rounding of kbar.
+struct LandmarkOut {
+  double* kbar;
+  float* vbar;
+  float* logn;
+  char* LM;
+};
+
+__device__ inline char* lm_key_block(const Geom& g, char* LM, int h, int u) {
+  return LM + (long long)h * g.T_pad * LM_BYTES_PER_TILE + (long long)(u / KBLK) * LM_KEY_BLOCK;
+}
+
+__device__ inline u16* lm_value_block(const Geom& g, char* LM, int h, int u) {
+  char* lmh = LM + (long long)h * g.T_pad * LM_BYTES_PER_TILE;
+  return (u16*)(lmh + (long long)(g.T_pad / KBLK) * LM_KEY_BLOCK + (long long)(u / KBLK) * KBLK * D * 2);
+}
+
+// Rows 32..63 of a key block other than the two table rows are zero; the
+// tile at position r of the block writes row 32 + r.
+__device__ inline void lm_zero_row(char* kblk, int r, int d) {
+  if (KBLK + r != LM_LOG2N_ROW && KBLK + r != LM_RADIUS_ROW) ((u16*)(kblk + (KBLK + r) * D * 2))[d] = 0;
+}
+
+// grid (T + spec_pad/32 [+ T_pad - T when LMK], H), block 256. With LMK the
+// same pass also writes every tile's landmark (as landmark_kernel does from
+// the packed buffers) and the padding landmarks past T.
+template <bool LMK>
 __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict__ K,
                                                    const u16* __restrict__ V, u16* __restrict__ Kt,
                                                    u16* __restrict__ Vt, u16* __restrict__ Ks,
-                                                   u16* __restrict__ Vs) {
+                                                   u16* __restrict__ Vs, LandmarkOut lo) {
   __shared__ u16 vstage[KBLK][D + 8];
+  __shared__ u16 kstage[LMK ? 2 * KBLK : 1][D + 8];  // the tile's keys (landmark radius)
+  __shared__ double red[LMK ? 2 : 1][4][D];
+  __shared__ double kq_s[LMK ? D : 1];
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
   const int slot_in = tid >> 3;  // 0..31
   const int chunk = tid & 7;     // 8 channels each
+  const int lane = tid & 63, wave = tid >> 6;
   const long long rowstride = (long long)g.H * D;
+  const int spec_blocks = g.spec_pad / KBLK;
+
+  if (LMK && blockIdx.x >= (unsigned)(g.T + spec_blocks)) {  // padding landmark
+    const int u = g.T + (blockIdx.x - g.T - spec_blocks), r = u % KBLK;
+    if (tid < D) {
+      char* kblk = lm_key_block(g, lo.LM, h, u);
+      lm_zero_row(kblk, r, tid);
+      ((u16*)(kblk + r * D * 2))[tid] = 0;
+      lm_value_block(g, lo.LM, h, u)[tid * KBLK + value_pos(r)] = 0;
+      if (tid == 0) {
+        ((float*)(kblk + LM_LOG2N_ROW * D * 2))[r] = -INFINITY;
+        ((float*)(kblk + LM_RADIUS_ROW * D * 2))[r] = 0.f;
+      }
+    }
+    return;
+  }
 
   long long base_slot;  // first packed slot of this group
   int nslots, nreal, f = 0, tl = 0;
@@ -54,6 +104,9 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
     Kdst = Ks + (long long)h * g.spec_pad * D;
     Vdst = Vs + (long long)h * g.spec_pad * D;
   }
+  // landmark sums: lane = channel, wave w adds slots 8w..8w+7 of each block.
+  // Sums of at most 64 bf16 values are exact in fp64, in any order.
+  double sk = 0.0, sv = 0.0;
   for (int blk = 0; blk < nslots / KBLK; ++blk) {
     const int s = blk * KBLK + slot_in;
     uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
@@ -72,6 +125,11 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
     const u16* pv = (const u16*)&vv;
 #pragma unroll
     for (int i = 0; i < 8; ++i) vstage[slot_in][chunk * 8 + i] = pv[i];
+    if (LMK && !special) {
+      const u16* pk = (const u16*)&kv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kstage[s][chunk * 8 + i] = pk[i];
+    }
     __syncthreads();
     // transpose: thread -> (d = tid>>2, 8 keys starting at (tid&3)*8)
     {
@@ -82,7 +140,57 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
       const long long vblk = (base_slot / KBLK) + blk;
       *(uint4*)(Vdst + (vblk * D + d) * KBLK + k0) = *(const uint4*)w;
     }
+    if (LMK && !special) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        sk += (double)bf2f(kstage[blk * KBLK + 8 * wave + j][lane]);
+        sv += (double)bf2f(vstage[8 * wave + j][lane]);
+      }
+    }
     __syncthreads();
+  }
+  if (!LMK || special) return;  // uniform
+
+  const int u = blockIdx.x, r = u % KBLK;
+  red[0][wave][lane] = sk;
+  red[1][wave][lane] = sv;
+  __syncthreads();
+  char* kblk = lm_key_block(g, lo.LM, h, u);
+  if (tid < D) {
+    const int d = tid;
+    const double tk = (red[0][0][d] + red[0][1][d]) + (red[0][2][d] + red[0][3][d]);
+    const double tv = (red[1][0][d] + red[1][1][d]) + (red[1][2][d] + red[1][3][d]);
+    const double mk = tk / nreal;
+    const float mv = (float)(tv / nreal);
+    lo.kbar[((long long)h * g.T + u) * D + d] = mk;
+    lo.vbar[((long long)h * g.T + u) * D + d] = mv;
+    const u16 kb16 = f2bf((float)mk);
+    ((u16*)(kblk + r * D * 2))[d] = kb16;
+    lm_value_block(g, lo.LM, h, u)[d * KBLK + value_pos(r)] = f2bf(mv);
+    lm_zero_row(kblk, r, d);
+    kq_s[d] = (double)bf2f(kb16);
+  }
+  __syncthreads();
+  // per-channel max |k - kbar (bf16)| over the tile's real keys: wave w
+  // takes slots w, w+4, ...
+  {
+    const double kq = kq_s[lane];
+    double dev = 0.0;
+    for (int s = wave; s < nreal; s += 4) dev = fmax(dev, fabs((double)bf2f(kstage[s][lane]) - kq));
+    red[0][wave][lane] = dev;
+  }
+  __syncthreads();
+  if (tid < D) {
+    const int d = tid;
+    const double m = fmax(fmax(red[0][0][d], red[0][1][d]), fmax(red[0][2][d], red[0][3][d]));
+    double e = m * m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) e += __shfl_down(e, o, 64);
+    if (d == 0) {
+      ((float*)(kblk + LM_LOG2N_ROW * D * 2))[r] = log2f((float)nreal);
+      ((float*)(kblk + LM_RADIUS_ROW * D * 2))[r] = (float)(sqrt(e) * 1.0001 + 1e-6);
+      if (h == 0) lo.logn[u] = logf((float)nreal);
+    }
   }
 }
 
@@ -153,9 +261,15 @@ __global__ void __launch_bounds__(64) landmark_kernel(Geom g, const u16* __restr
 }
 
 hipError_t launch_pack(const Geom& g, const u16* K, const u16* V, u16* Kt, u16* Vt, u16* Ks,
-                       u16* Vs, hipStream_t s) {
-  hipLaunchKernelGGL(pack_kernel, dim3(g.T + g.spec_pad / KBLK, g.H), dim3(256), 0, s, g, K, V,
-                     Kt, Vt, Ks, Vs);
+                       u16* Vs, double* kbar, float* vbar, float* logn, u16* LM, hipStream_t s) {
+  const LandmarkOut lo{kbar, vbar, logn, (char*)LM};
+  const int blocks = g.T + g.spec_pad / KBLK;
+  if (kbar)
+    hipLaunchKernelGGL(pack_kernel<true>, dim3(blocks + (g.T_pad - g.T), g.H), dim3(256), 0, s, g, K,
+                       V, Kt, Vt, Ks, Vs, lo);
+  else
+    hipLaunchKernelGGL(pack_kernel<false>, dim3(blocks, g.H), dim3(256), 0, s, g, K, V, Kt, Vt, Ks,
+                       Vs, lo);
   return hipGetLastError();
 }
 

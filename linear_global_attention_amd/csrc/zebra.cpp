@@ -10,7 +10,8 @@
 #include "common.hpp"
 
 namespace zebra {
-hipError_t launch_pack(const Geom&, const u16*, const u16*, u16*, u16*, u16*, u16*, hipStream_t);
+hipError_t launch_pack(const Geom&, const u16*, const u16*, u16*, u16*, u16*, u16*, double*, float*, float*,
+                       u16*, hipStream_t);
 hipError_t launch_landmarks(const Geom&, const u16*, const u16*, double*, float*, float*, u16*,
                             hipStream_t);
 size_t select_workspace_bytes(const Geom&);
@@ -132,6 +133,12 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
       NEED(a->vt, "vt");
       NEED(a->ks, "ks");
       NEED(a->vs, "vs");
+      if (a->kbar || a->vbar || a->logn || a->lm) {  // landmarks in the same pass
+        NEED(a->kbar, "kbar");
+        NEED(a->vbar, "vbar");
+        NEED(a->logn, "logn");
+        NEED(a->lm, "lm");
+      }
       break;
     case ZEBRA_OP_LANDMARKS:
       NEED(a->kt, "kt");
@@ -252,7 +259,8 @@ zebra_status zebra_pack_tiles(const zebra_args* a, zebra_stream stream) {
   zebra_status s = validate(a, ZEBRA_OP_PACK, g, k);
   if (s != ZEBRA_OK) return s;
   return hip_result(launch_pack(g, (const u16*)a->k, (const u16*)a->v, (u16*)a->kt, (u16*)a->vt,
-                                (u16*)a->ks, (u16*)a->vs, (hipStream_t)stream),
+                                (u16*)a->ks, (u16*)a->vs, a->kbar, a->vbar, a->logn, (u16*)a->lm,
+                                (hipStream_t)stream),
                     "zebra_pack_tiles");
 }
 
@@ -294,12 +302,9 @@ zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream) {
   zebra_status s = validate(a, ZEBRA_OP_DENSE, g, k);
   if (s != ZEBRA_OK) return s;
   s = hip_result(launch_pack(g, (const u16*)a->k, (const u16*)a->v, (u16*)a->kt, (u16*)a->vt,
-                             (u16*)a->ks, (u16*)a->vs, (hipStream_t)stream),
-                 "zebra_dense_attn (pack)");
-  if (s != ZEBRA_OK) return s;
-  s = hip_result(launch_landmarks(g, (const u16*)a->kt, (const u16*)a->vt, a->kbar, a->vbar, a->logn,
-                                  (u16*)a->lm, (hipStream_t)stream),
-                 "zebra_dense_attn (landmarks)");
+                             (u16*)a->ks, (u16*)a->vs, a->kbar, a->vbar, a->logn, (u16*)a->lm,
+                             (hipStream_t)stream),
+                 "zebra_dense_attn (pack and landmarks)");
   if (s != ZEBRA_OK) return s;
   AttnArgs A{(const u16*)a->q, (u16*)a->out, (const u16*)a->kt, (const u16*)a->vt,
              (const u16*)a->ks, (const u16*)a->vs, (const u16*)a->lm, a->logn, (const unsigned*)nullptr,

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import linear_global_attention_amd as zb
 import zebra_synth as zs
 from oracle import linear as olin
 from oracle import sparse as osp
@@ -100,6 +101,17 @@ def test_pack_and_landmarks_exact(name, L, y):
     for h in range(H):
         kb, _, _ = osp.landmarks(widen(k)[:, h], widen(v)[:, h], tm)
         assert np.array_equal(kbar[h], kb), h  # exact fp64 sums, one rounding
+    # the landmarks written by the pack pass equal zebra_landmarks' from the
+    # packed buffers, byte for byte (landmark table and its padding included)
+    names = ("KBAR", "VBAR", "LOGN", "LM")
+    fused = {n: st.bufs.t[n].clone() for n in names}
+    for n in names:
+        st.bufs.t[n].fill_(0x7F)
+    zb.landmarks(st.args())
+    torch.cuda.synchronize()
+    for n in names:
+        nb = zb.buffer_bytes(st.zL, y, n)
+        assert torch.equal(st.bufs.t[n][:nb], fused[n][:nb]), n
 
 
 def test_landmark_of_identical_tile_equals_tile():

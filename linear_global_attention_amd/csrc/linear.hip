@@ -10,7 +10,8 @@
 // Four kernels:
 //   linear_state  stream K and V once: phi(k) for 16 tokens per wave pass,
 //                 staged with V in LDS, then S += phi(K)^T V (bf16 MFMA,
-//                 fp32 accumulators) and z += phi(k); one partial per wave.
+//                 fp32 accumulators) and z += phi(k); one partial per
+//                 workgroup (its waves added in a fixed order).
 //   linear_sum    fixed-order fp64 sum of the partials, one element per
 //                 thread over all of a head's partials;
 //   linear_fold   S' = S W^T split into bf16 high/low parts and
@@ -29,7 +30,7 @@ namespace zebra {
 
 constexpr int LIN_THREADS = 256;
 constexpr int LIN_WAVES = LIN_THREADS / 64;
-constexpr int LIN_TOKENS_PER_WG = 8192;
+constexpr int LIN_RESIDENT = 512;  // workgroups resident at once: 256 CUs x 2
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int LIN_STATE = D * D + D;  // floats of one partial state: S [64][64] then z [64]
 
@@ -39,6 +40,10 @@ struct LinParams {
 };
 
 __device__ inline int lane_channel(int g, int i) { return (i >> 2) * 16 + 4 * g + (i & 3); }
+
+// Rotary table in dynamic LDS, max(R, C) * 16 entries (rope_table_bytes).
+extern __shared__ float2 rope_tab[];
+inline size_t rope_table_bytes(const Geom& g) { return (size_t)(g.R > g.C ? g.R : g.C) * 16 * sizeof(float2); }
 
 // cos/sin of p * base^(-j/16) for p < npos, j < 16, in LDS: tab[p][j] = {c, s}
 __device__ inline void build_rope_table(float2* tab, int npos, float base) {
@@ -180,12 +185,12 @@ __device__ inline void unpack16(const uint2 w[4], float x[16]) {
   }
 }
 
-// grid (nchunks, H), block 256. partial p = chunk*4 + wave holds
+// grid (nchunks, H), block 256. Partial p = chunk holds
 // S [64][64] (row a = phi channel, column c = value channel) then z [64].
 __global__ void __launch_bounds__(LIN_THREADS, 2) linear_state_kernel(
     Geom g, LinParams P, const u16* __restrict__ K, const u16* __restrict__ V,
-    const float* __restrict__ gk, float* __restrict__ partials, int nchunks) {
-  __shared__ float2 tab[MAX_GRID * 16];
+    const float* __restrict__ gk, float* __restrict__ partials, int nchunks, int tpw) {
+  float2* tab = rope_tab;
   // phi(k) and v of a wave's 32 tokens, channel-major ([channel][token],
   // rows of 40 u16 = 80 bytes): an MFMA operand fragment (one channel, 8
   // consecutive tokens) is one 16-byte read
@@ -210,8 +215,8 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_state_kernel(
 #pragma unroll
   for (int i = 0; i < 16; ++i) zacc[i] = 0.f;
 
-  const long long t_begin = (long long)chunk * LIN_TOKENS_PER_WG;
-  const long long t_end = min((long long)g.N, t_begin + LIN_TOKENS_PER_WG);
+  const long long t_begin = (long long)chunk * tpw;
+  const long long t_end = min((long long)g.N, t_begin + tpw);
   const long long rs = (long long)g.H * D;
   constexpr int STRIDE = 32 * LIN_WAVES;
   // raw K and V of the wave's 32 tokens: this iteration's and the next's
@@ -287,18 +292,35 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_state_kernel(
     v += __shfl_xor(v, 8, 64);
     zacc[i] = v;
   }
-  float* out = partials + ((long long)h * nchunks * LIN_WAVES + chunk * LIN_WAVES + wave) * LIN_STATE;
-  // MFMA 16x16 output: lane holds column tl, rows 4*grp + 0..3
+  // the workgroup's partial: the 4 waves' states added in wave order in LDS
+  // (over the feature staging area), then written once
+  float* red = (float*)&phis[0][0][0];
+  static_assert(sizeof(phis) >= LIN_STATE * sizeof(float), "partial fits the staging area");
+  __syncthreads();
+  for (int w = 0; w < LIN_WAVES; ++w) {
+    if (wave == w) {
+      // MFMA 16x16 output: lane holds column tl, rows 4*grp + 0..3
 #pragma unroll
-  for (int ab = 0; ab < 4; ++ab)
+      for (int ab = 0; ab < 4; ++ab)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) out[(ab * 16 + 4 * grp + r) * D + cb * 16 + tl] = acc[ab][cb][r];
-  if (tl == 0) {
+          for (int r = 0; r < 4; ++r) {
+            float* e = &red[(ab * 16 + 4 * grp + r) * D + cb * 16 + tl];
+            *e = w == 0 ? acc[ab][cb][r] : *e + acc[ab][cb][r];
+          }
+      if (tl == 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) out[D * D + lane_channel(grp, i)] = zacc[i];
+        for (int i = 0; i < 16; ++i) {
+          float* e = &red[D * D + lane_channel(grp, i)];
+          *e = w == 0 ? zacc[i] : *e + zacc[i];
+        }
+      }
+    }
+    __syncthreads();
   }
+  float* out = partials + ((long long)h * nchunks + chunk) * LIN_STATE;
+  for (int e = threadIdx.x; e < LIN_STATE; e += LIN_THREADS) out[e] = red[e];
 }
 
 // grid (ceil(LIN_STATE / 256), H), block 256: fixed-order fp64 sum of the
@@ -362,7 +384,7 @@ __global__ void __launch_bounds__(256) linear_fold_kernel(const double* __restri
 // workgroup barrier), AP_NB - 1 groups ahead.
 __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
     Geom g, LinParams P, const u16* __restrict__ Q, const float* __restrict__ gq,
-    const u16* __restrict__ sp, const float* __restrict__ zb, u16* __restrict__ out) {
+    const u16* __restrict__ sp, const float* __restrict__ zb, u16* __restrict__ out, int tpw) {
   __shared__ float2 tab[MAX_GRID * 16];
   __shared__ __attribute__((aligned(1024))) char qring[LIN_WAVES][AP_NB][2048];
   const int h = blockIdx.y, chunk = blockIdx.x;
@@ -395,8 +417,8 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
       Alo[eb][ks] = *(const bf16x8*)(lo + off);
     }
   __syncthreads();
-  const long long t_begin = (long long)chunk * LIN_TOKENS_PER_WG;
-  const long long t_end = min((long long)g.N, t_begin + LIN_TOKENS_PER_WG);
+  const long long t_begin = (long long)chunk * tpw;
+  const long long t_end = min((long long)g.N, t_begin + tpw);
   const long long rs = (long long)g.H * D;
   // This wave's 16-token groups: m = 0..n-1, first token t_begin + 16 (wave + 4m).
   const long long first = t_begin + 16 * wave;
@@ -480,10 +502,25 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
   }
 }
 
-int linear_chunks(const Geom& g) { return (int)((g.N + LIN_TOKENS_PER_WG - 1) / LIN_TOKENS_PER_WG); }
+// Tokens per workgroup (a multiple of 128), chosen so that the H x chunks
+// workgroups fill whole waves of LIN_RESIDENT: about 8,192 tokens, rounded
+// so that no last, part-filled wave of workgroups runs alone.
+int linear_tokens_per_wg(const Geom& g) {
+  const long long base = 8192;
+  const long long wgs = (long long)g.H * ((g.N + base - 1) / base);
+  const long long waves = (wgs + LIN_RESIDENT - 1) / LIN_RESIDENT;
+  const long long nch = (waves * LIN_RESIDENT + g.H - 1) / g.H;
+  const long long tpw = ((g.N + nch - 1) / nch + 127) / 128 * 128;
+  return (int)tpw;
+}
+
+int linear_chunks(const Geom& g) {
+  const long long tpw = linear_tokens_per_wg(g);
+  return (int)((g.N + tpw - 1) / tpw);
+}
 
 size_t linear_workspace_bytes(const Geom& g) {
-  const size_t parts = (size_t)g.H * linear_chunks(g) * LIN_WAVES * LIN_STATE * sizeof(float);
+  const size_t parts = (size_t)g.H * linear_chunks(g) * LIN_STATE * sizeof(float);
   const size_t state = (size_t)g.H * LIN_STATE * sizeof(double);
   const size_t red = (size_t)g.H * (2 * D * D * sizeof(u16) + 2 * D * sizeof(float));
   return parts + state + red;
@@ -494,19 +531,20 @@ size_t linear_workspace_bytes(const Geom& g) {
 hipError_t launch_linear(const Geom& g, float eps, float base, const u16* Q, const u16* K,
                          const u16* V, const float* W, const float* b, const float* mu,
                          const float* gq, const float* gk, u16* out, void* ws, hipStream_t s) {
-  const int nch = linear_chunks(g);
+  const int nch = linear_chunks(g), tpw = linear_tokens_per_wg(g);
   float* parts = (float*)ws;
-  double* state = (double*)(parts + (size_t)g.H * nch * LIN_WAVES * LIN_STATE);
+  double* state = (double*)(parts + (size_t)g.H * nch * LIN_STATE);
   u16* sp = (u16*)(state + (size_t)g.H * LIN_STATE);
   float* zb = (float*)(sp + (size_t)g.H * 2 * D * D);
   LinParams P{eps, base};
-  hipLaunchKernelGGL(linear_state_kernel, dim3(nch, g.H), dim3(LIN_THREADS), 0, s, g, P, K, V, gk,
-                     parts, nch);
+  const size_t tb = rope_table_bytes(g);
+  hipLaunchKernelGGL(linear_state_kernel, dim3(nch, g.H), dim3(LIN_THREADS), tb, s, g, P, K, V, gk,
+                     parts, nch, tpw);
   hipLaunchKernelGGL(linear_sum_kernel, dim3((LIN_STATE + 255) / 256, g.H), dim3(256), 0, s,
-                     (const float*)parts, nch * LIN_WAVES, state);
+                     (const float*)parts, nch, state);
   hipLaunchKernelGGL(linear_fold_kernel, dim3(g.H), dim3(256), 0, s, (const double*)state, W, b, mu, sp, zb);
   hipLaunchKernelGGL(linear_apply_kernel, dim3(nch, g.H), dim3(LIN_THREADS), 0, s, g, P, Q, gq, sp,
-                     zb, out);
+                     zb, out, tpw);
   return hipGetLastError();
 }
 

@@ -105,7 +105,7 @@ template <int G>
 struct MainState {
   bf16x8 q[G][2];  // B operand of each slot: query (lane%16), channels ds*32+8g..+7
   f32x4 o[G][4];   // O^T of each slot: channel db*16+4g+r, query lane%16
-  float l[G];      // lane-partial row sums
+  f32x4 l[G];      // row sums of bf16(P) by MFMA: every element = sum of query lane%16
   float negm[G];   // -M (log2 units)
 };
 
@@ -156,14 +156,16 @@ __device__ __forceinline__ bool slot_on(unsigned m, int s) {
   return __builtin_amdgcn_readfirstlane((int)((m >> s) & 1u)) != 0;
 }
 
-// Row sums and O^T += V^T bf16(P)^T.
-__device__ __forceinline__ void pv(const float p[8], const bf16x8 vf[4], f32x4 o[4], float& l) {
-  l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+// O^T += V^T bf16(P)^T, and the row sums of bf16(P) as one more MFMA with
+// an all-ones A operand (cheaper than eight adds per lane).
+__device__ __forceinline__ void pv(const float p[8], const bf16x8 vf[4], f32x4 o[4], f32x4& l) {
   const unsigned w0 = pack_bf16(p[0], p[1]), w1 = pack_bf16(p[2], p[3]);
   const unsigned w2 = pack_bf16(p[4], p[5]), w3 = pack_bf16(p[6], p[7]);
   const bf16x8 P = __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], P, o[db], 0, 0, 0);
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, P, l, 0, 0, 0);
 }
 
 // One staged 32-key block of token or special keys (rows key0.. of the
@@ -649,7 +651,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
     st.negm[s] = 0.f;
-    st.l[s] = 0.f;
+    st.l[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < 4; ++db) st.o[s][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     if ((slots >> s) & 1u) st.negm[s] = ws_negm[lane_record(g, qg, h, s, lane)];
@@ -754,13 +756,17 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   int lane_a = lane;
   asm volatile("" : "+v"(lane_a));
   const int lg_a = lane_a >> 4, tl_a = lane_a & 15;
+  // lane-partial row sums: the MFMA row sum counted once, in lanes 0..15
+  float lpart[SW];
+#pragma unroll
+  for (int s = 0; s < SW; ++s) lpart[s] = lg_a == 0 ? st.l[s][0] : 0.f;
 
   if (un.seg >= 0) {
 #pragma unroll
     for (int s = 0; s < SW; ++s) {
       if (!((slots >> s) & 1u)) continue;
       const long long rec = spec_record(g, h, un.item, un.seg, qg, s, lane_a);
-      sp_l[rec] = st.l[s];
+      sp_l[rec] = lpart[s];
 #pragma unroll
       for (int db = 0; db < 4; ++db) sp_o[rec * 4 + db] = st.o[s][db];
     }
@@ -788,7 +794,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
       }
       dot = xsum32(xsum16(dot));
       const float p = okrow ? __builtin_amdgcn_exp2f(fmaf(dot, QK_LOG2, st.negm[s])) : 0.f;
-      st.l[s] += (lg_a == 0 ? p : 0.f);
+      lpart[s] += (lg_a == 0 ? p : 0.f);
       const long long vblk = slot / KBLK;
       const int pos = value_pos((int)(slot % KBLK));
 #pragma unroll
@@ -804,7 +810,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
 
 #pragma unroll
   for (int s = 0; s < SW; ++s)
-    if ((slots >> s) & 1u) store_slot(g, A, qg, h, s, st.o[s], st.l[s], lane_a);
+    if ((slots >> s) & 1u) store_slot(g, A, qg, h, s, st.o[s], lpart[s], lane_a);
 }
 
 // Sums the key-segment partials of every special item (one workgroup per

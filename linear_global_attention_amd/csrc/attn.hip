@@ -94,12 +94,6 @@ __device__ __forceinline__ void stage_share(char* dst, int wave, const char* src
                                      16, 0, 0);
 }
 
-template <int G>
-struct BoundState {
-  bf16x8 q[G][2];
-  float negm[G];  // running bound (log2 units)
-  float qnc[G];   // |q| * log2(e)/8
-};
 
 template <int G>
 struct MainState {
@@ -233,42 +227,6 @@ __device__ __forceinline__ void attend_landmarks(MainState<SW>& st, unsigned us,
   }
 }
 
-// Bound pass over one staged 32-key block: raises each row's running bound
-// by max over keys of s*C + max(log2 n_u, |q| r_u C) for a landmark block
-// (an upper bound of the logits of the tile's tokens and of its landmark),
-// or by the exact logits s*C of a special block's valid keys.
-template <int SW>
-__device__ __forceinline__ void bound_block(BoundState<SW>& st, unsigned slots, const char* kb, bool is_lm,
-                                            int nvalid, int lane) {
-  bf16x8 kf[2][2];
-  load_kfrag(kb, 0, lane, kf);
-  float l2n[8], rad[8];
-  if (is_lm) {
-    load_row8(kb + LM_LOG2N_ROW * 128, lane, l2n);
-    load_row8(kb + LM_RADIUS_ROW * 128, lane, rad);
-  } else {
-    const unsigned valid = lane_valid_mask(nvalid, lane);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      l2n[i] = ((valid >> i) & 1u) ? 0.f : -INFINITY;
-      rad[i] = 0.f;
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < SW; ++s) {
-    if (!((slots >> s) & 1u)) continue;
-    f32x4 s0, s1;
-    qk(st.q[s], kf, s0, s1);
-    float b = st.negm[s];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      b = __builtin_fmaxf(b, fmaf(s0[r], QK_LOG2, __builtin_fmaxf(l2n[r], st.qnc[s] * rad[r])));
-      b = __builtin_fmaxf(b, fmaf(s1[r], QK_LOG2, __builtin_fmaxf(l2n[4 + r], st.qnc[s] * rad[4 + r])));
-    }
-    st.negm[s] = b;
-  }
-}
-
 // Work item -> (head, query groups): per head the special items first (they
 // walk every key tile), then the patch items.
 struct FastItem {
@@ -368,38 +326,65 @@ __device__ __forceinline__ void stream_items(char* ringA, char* ringB, Next next
   ring_barrier();
 }
 
-// Offsets: M_i = max over the row's visible keys of an upper bound of the
-// logit (landmark blocks with tile radii, exact special logits, the own
-// key's logit). Writes -M per lane record and flags groups whose bound is
-// more than SAFE_GAP above some row's own logit.
+// Per head, the largest squared key norm over every packed patch key and
+// special key (zero padding included), as the bits of a non-negative float
+// in kmax2[h] (cleared beforehand). grid (ceil((slots + spec_pad) / 64), H),
+// block 256: four lanes per key row, 16 channels each.
+__global__ void __launch_bounds__(256) key_norm_max_kernel(Geom g, AttnArgs A, unsigned* kmax2) {
+  const int h = blockIdx.y;
+  const long long r = (long long)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int part = threadIdx.x & 3;
+  float ss = 0.f;
+  if (r < g.slots + g.spec_pad) {
+    const u16* row = r < g.slots ? A.Kt + ((long long)h * g.slots + r) * D
+                                 : A.Ks + ((long long)h * g.spec_pad + (r - g.slots)) * D;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint4 w = *(const uint4*)(row + part * 16 + c * 8);
+      const bf16x8 v = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) ss = fmaf((float)v[m], (float)v[m], ss);
+    }
+  }
+  ss += __shfl_xor(ss, 1, 64);  // the row's four lanes
+  ss += __shfl_xor(ss, 2, 64);
+#pragma unroll
+  for (int o = 4; o < 64; o <<= 1) ss = fmaxf(ss, __shfl_xor(ss, o, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(&kmax2[h], __float_as_uint(ss));
+}
+
+// Offsets. Every logit a row sees is at most |q| K_max / 8 (Cauchy-Schwarz,
+// K_max the head's largest key norm, which also bounds a landmark's mean key
+// up to its bf16 rounding), and a landmark adds at most log2(64) = 6 (log2
+// units) for ln n_u. So M_i = C |q_i| K_max * 1.01 + 6 bounds every logit of
+// row i (C = log2(e) / 8); -M goes to the row's lane records. A group with a
+// row whose own logit lies more than SAFE_GAP below M is flagged, and the
+// exact kernel recomputes it afterwards.
 template <int G, int SW>
-__global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, AttnArgs A, float* ws_negm,
-                                                                    int* flags) {
-  __shared__ __attribute__((aligned(1024))) char ringA[2 * LDS_BUF];
-  __shared__ __attribute__((aligned(1024))) char ringB[2 * LDS_BUF];
+__global__ void __launch_bounds__(FWAVES * 64) attn_bound_kernel(Geom g, AttnArgs A, float* ws_negm, int* flags,
+                                                                 const unsigned* kmax2) {
   const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
   const int lg = lane >> 4, tl = lane & 15;
   const int simd = wave & 3, s0 = (wave >> 2) * SW;
   const FastItem it(g, blockIdx.x);
   const int h = it.h;
   const FastItems fi(g);
-  const QueryGroups qgi(g, it.item, fi.patch_items, G, simd);      // the item's G groups
-  const QueryGroups qg(g, it.item, fi.patch_items, G, simd, s0);   // this wave's SW slots
+  const QueryGroups qg(g, it.item, fi.patch_items, G, simd, s0);  // this wave's SW slots
   const u16* Kt16 = A.Kt + (long long)h * g.slots * D;
   const u16* Ks16 = A.Ks + (long long)h * g.spec_pad * D;
+  const float kmax = sqrtf(__uint_as_float(kmax2[h])) * 1.01f;
 
   unsigned slots = 0u;
 #pragma unroll
   for (int s = 0; s < SW; ++s)
     if (qg.row_block(s) * 16 < qg.rows(s)) slots |= 1u << s;
-
-  BoundState<SW> st;
-  float own[SW];
-  load_queries<SW>(g, A, qg, h, slots, lane, st.q);
+  bf16x8 q[SW][2];
+  load_queries<SW>(g, A, qg, h, slots, lane, q);
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
+    if (!((slots >> s) & 1u)) continue;
     const int j = qg.row_block(s) * 16 + tl;
-    const bool ok = ((slots >> s) & 1u) && j < qg.rows(s);
+    const bool ok = j < qg.rows(s);
     float qq = 0.f, qko = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
@@ -408,54 +393,15 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_bound_kernel(Geom g, A
       const bf16x8 kv = __builtin_bit_cast(bf16x8, kw);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const float a = (float)st.q[s][ds][m];
+        const float a = (float)q[s][ds][m];
         qq = fmaf(a, a, qq);
         qko = fmaf(a, (float)kv[m], qko);
       }
     }
     qq = xsum32(xsum16(qq));
     qko = xsum32(xsum16(qko));
-    st.qnc[s] = sqrtf(qq) * QK_LOG2 * 1.0001f;
-    own[s] = qko * QK_LOG2;
-    st.negm[s] = own[s];
-  }
-  ZEBRA_VMCNT(0);
-
-  const char* lmh = (const char*)A.LM + (long long)h * g.T_pad * LM_BYTES_PER_TILE;
-  const int nlb = g.T_pad / KBLK, nsb = g.spec_pad / KBLK;
-  // items: landmark key blocks 0..nlb-1, then special key blocks
-  int cnt = 0;
-  auto next = [&](Item (&it)[2]) -> int {
-    int n = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (cnt >= nlb + nsb) break;
-      const bool lm = cnt < nlb;
-      const int b = lm ? cnt : cnt - nlb;
-      it[j].x = (unsigned)((lm ? KIND_LANDMARK : KIND_SPECIAL) << 28) | (unsigned)b;
-      it[j].y = (unsigned)((lm ? KBLK : min(KBLK, g.nspec - b * KBLK)) << 8);
-      ++cnt;
-      ++n;
-    }
-    return n;
-  };
-  const StageOffsets so(wave, lane);
-  auto issue = [&](const Item& it, char* d) {
-    if (it.kind() == KIND_LANDMARK) stage_share(d, wave, lmh + (long long)it.index() * LM_KEY_BLOCK, so.k8);
-    else stage_share(d, wave, (const char*)Ks16 + (long long)it.index() * KBLK * D * 2, so.k4);
-  };
-  auto consume = [&](const Item& it, const char* kb) {
-    if (!slots) return;
-    bound_block<SW>(st, slots, kb, it.kind() == KIND_LANDMARK, it.nkeys(), lane);
-  };
-  stream_items(ringA, ringB, next, issue, consume, [] {});
-
-#pragma unroll
-  for (int s = 0; s < SW; ++s) {
-    if (!((slots >> s) & 1u)) continue;
-    const float m = xmax32(xmax16(st.negm[s]));
-    const bool okrow = qg.row_block(s) * 16 + tl < qg.rows(s);
-    const bool bad = __builtin_amdgcn_ballot_w64(okrow && m - own[s] > SAFE_GAP) != 0;
+    const float m = sqrtf(qq) * QK_LOG2 * 1.0001f * kmax + 6.0f;
+    const bool bad = __builtin_amdgcn_ballot_w64(ok && m - qko * QK_LOG2 > SAFE_GAP) != 0;
     const long long rec = lane_record(g, qg, h, s, lane);
     ws_negm[rec] = -m;
     if (bad && lane == 0) flags[rec >> 8] = 1;
@@ -873,7 +819,7 @@ struct AttnWorkspace {
   long long groups, records, sp_records;
   int plan_stride;  // plan entries per unit: words x 33 + checkpoints + special blocks
   int nckpt;        // checkpoint counters of a round
-  size_t flags_off, negm_off, count_off, ckpt_off, plan_off, spl_off, spo_off, bytes;
+  size_t flags_off, kmax_off, negm_off, count_off, ckpt_off, plan_off, spl_off, spo_off, bytes;
   explicit AttnWorkspace(const Geom& g) {
     const FastItems fi(g);
     groups = (long long)g.H * fi.groups_per_head;
@@ -884,7 +830,8 @@ struct AttnWorkspace {
     plan_stride = nwords * 33 + nckpt + g.spec_pad / KBLK;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     flags_off = 0;
-    negm_off = up((size_t)groups * sizeof(int));
+    kmax_off = (size_t)groups * sizeof(int);  // H words right after the flags (cleared with them)
+    negm_off = up(kmax_off + (size_t)g.H * sizeof(unsigned));
     count_off = up(negm_off + (size_t)records * sizeof(float));
     ckpt_off = up(count_off + (size_t)ROUND_MAX * 2 * sizeof(int));
     plan_off = up(ckpt_off + (size_t)nckpt * sizeof(int));
@@ -905,6 +852,7 @@ hipError_t launch_attn(const Geom& g, const AttnArgs& a, void* workspace, hipStr
   const AttnWorkspace ws(g);
   char* base = (char*)workspace;
   int* flags = (int*)(base + ws.flags_off);
+  unsigned* kmax2 = (unsigned*)(base + ws.kmax_off);
   float* negm = (float*)(base + ws.negm_off);
   int* count = (int*)(base + ws.count_off);
   int* ckpt = (int*)(base + ws.ckpt_off);
@@ -921,9 +869,12 @@ hipError_t launch_attn(const Geom& g, const AttnArgs& a, void* workspace, hipStr
   int round = FOCC * cus;
   if (round > ROUND_MAX) round = ROUND_MAX;
   if (round < 1) round = 1;
-  hipLaunchKernelGGL(clear_flags_kernel, dim3((unsigned)((ws.groups + 255) / 256)), dim3(256), 0, s, flags,
-                     ws.groups);
-  hipLaunchKernelGGL((attn_bound_kernel<FG, FSLOTS>), dim3(fi.total), dim3(FWAVES * 64), 0, s, g, a, negm, flags);
+  hipLaunchKernelGGL(clear_flags_kernel, dim3((unsigned)((ws.groups + g.H + 255) / 256)), dim3(256), 0, s, flags,
+                     ws.groups + g.H);
+  hipLaunchKernelGGL(key_norm_max_kernel, dim3((unsigned)((g.slots + g.spec_pad + 63) / 64), g.H), dim3(256), 0, s, g,
+                     a, kmax2);
+  hipLaunchKernelGGL((attn_bound_kernel<FG, FSLOTS>), dim3(fi.total), dim3(FWAVES * 64), 0, s, g, a, negm, flags,
+                     (const unsigned*)kmax2);
   for (int u0 = 0; u0 < units.total; u0 += round) {
     const int n = units.total - u0 < round ? units.total - u0 : round;
     int patch_units = 0;  // units of the round that are patch items (they meet at the checkpoints)

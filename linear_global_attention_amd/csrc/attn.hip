@@ -22,10 +22,9 @@
 // groups share a staged tile the fewer bytes each kept (row, key) pair costs.
 //
 // Softmax offsets. Instead of a running max, each row i uses one offset M_i
-// that is >= every logit it can see, found by attn_bound_kernel: for a tile
-// u and every key j of u, q.k_j <= q.kbar_u + |q| r_u (r_u: the tile's key
-// radius); a landmark's logit is q.kbar_u/8 + ln n_u; special logits are
-// exact. With p = exp2(x - M_i) <= 1 nothing overflows, and the partial sums
+// that is >= every logit it can see, found by attn_bound_kernel from |q_i|
+// and the head's largest key norm (Cauchy-Schwarz, plus ln n_u <= ln 64 for
+// a landmark). With p = exp2(x - M_i) <= 1 nothing overflows, and the partial sums
 // of different key segments simply add. The row's own key is always visible,
 // so M_i minus the own logit bounds how far below 1 the largest p can be;
 // groups with a row where that gap exceeds SAFE_GAP (log2 units) are flagged

@@ -15,7 +15,6 @@ constexpr int MAX_TPF = (MAX_GRID / TILE) * (MAX_GRID / TILE);  // tiles per fra
 constexpr int KBLK = 32;       // key-slot granularity of the packed layouts
 constexpr int LM_KEY_BLOCK = 8192;                      // bytes per landmark key block
 constexpr int LM_LOG2N_ROW = 32;                        // row of log2(n_u) in a key block
-constexpr int LM_RADIUS_ROW = 40;                       // row of the key radii r_u
 constexpr int LM_BYTES_PER_TILE = (LM_KEY_BLOCK + KBLK * D * 2) / KBLK;  // 384
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -66,9 +65,7 @@ __host__ __device__ inline int tile_n(const Geom& g, int tl) { return tile_h(g, 
 //   Vs  bf16 [H][spec_pad/32][64][32]
 //   LM  per head: T_pad/32 landmark key blocks of LM_KEY_BLOCK bytes (rows
 //       0..31: kbar of the block's tiles, bf16 [32][64]; row 32: 32 fp32
-//       log2(n_u), -inf past the last tile; row 40: 32 fp32 key radii r_u,
-//       an upper bound of |k_j - kbar_u| over the tile's keys that also
-//       covers the bf16 rounding of kbar; other rows zero), then T_pad/32
+//       log2(n_u), -inf past the last tile; other rows zero), then T_pad/32
 //       value blocks [64][32] bf16 of vbar (keys permuted by value_pos)
 
 // Arguments of the attention kernel (tile-sparse or dense).

@@ -21,11 +21,7 @@ __device__ inline long long tile_token(const Geom& g, int f, int tl, int s) {
   return (long long)f * g.tok_pf + g.S + (long long)r * g.C + c;
 }
 
-// Landmark outputs of tile u (< T) of head h from its per-channel fp64 sums
-// and max deviations, written by the thread of channel d. The radius is the
-// Euclidean norm of the 64 per-channel deviations, summed in a fixed pairwise
-// tree (lane d adds lane d + o for o = 32, 16, ..., 1), inflated to cover the
-// bf16 rounding of kbar.
+// Landmark buffers written by the packing pass.
 struct LandmarkOut {
   double* kbar;
   float* vbar;
@@ -42,10 +38,10 @@ __device__ inline u16* lm_value_block(const Geom& g, char* LM, int h, int u) {
   return (u16*)(lmh + (long long)(g.T_pad / KBLK) * LM_KEY_BLOCK + (long long)(u / KBLK) * KBLK * D * 2);
 }
 
-// Rows 32..63 of a key block other than the two table rows are zero; the
-// tile at position r of the block writes row 32 + r.
+// Rows 32..63 of a key block other than the log2 n row are zero; the tile
+// at position r of the block writes row 32 + r.
 __device__ inline void lm_zero_row(char* kblk, int r, int d) {
-  if (KBLK + r != LM_LOG2N_ROW && KBLK + r != LM_RADIUS_ROW) ((u16*)(kblk + (KBLK + r) * D * 2))[d] = 0;
+  if (KBLK + r != LM_LOG2N_ROW) ((u16*)(kblk + (KBLK + r) * D * 2))[d] = 0;
 }
 
 // grid (T + spec_pad/32 [+ T_pad - T when LMK], H), block 256. With LMK the
@@ -57,9 +53,8 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
                                                    u16* __restrict__ Vt, u16* __restrict__ Ks,
                                                    u16* __restrict__ Vs, LandmarkOut lo) {
   __shared__ u16 vstage[KBLK][D + 8];
-  __shared__ u16 kstage[LMK ? 2 * KBLK : 1][D + 8];  // the tile's keys (landmark radius)
+  __shared__ u16 kstage[LMK ? KBLK : 1][D + 8];  // the block's keys, for the landmark sums
   __shared__ double red[LMK ? 2 : 1][4][D];
-  __shared__ double kq_s[LMK ? D : 1];
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
   const int slot_in = tid >> 3;  // 0..31
@@ -75,10 +70,7 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
       lm_zero_row(kblk, r, tid);
       ((u16*)(kblk + r * D * 2))[tid] = 0;
       lm_value_block(g, lo.LM, h, u)[tid * KBLK + value_pos(r)] = 0;
-      if (tid == 0) {
-        ((float*)(kblk + LM_LOG2N_ROW * D * 2))[r] = -INFINITY;
-        ((float*)(kblk + LM_RADIUS_ROW * D * 2))[r] = 0.f;
-      }
+      if (tid == 0) ((float*)(kblk + LM_LOG2N_ROW * D * 2))[r] = -INFINITY;
     }
     return;
   }
@@ -128,7 +120,7 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
     if (LMK && !special) {
       const u16* pk = (const u16*)&kv;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kstage[s][chunk * 8 + i] = pk[i];
+      for (int i = 0; i < 8; ++i) kstage[slot_in][chunk * 8 + i] = pk[i];
     }
     __syncthreads();
     // transpose: thread -> (d = tid>>2, 8 keys starting at (tid&3)*8)
@@ -143,7 +135,7 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
     if (LMK && !special) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        sk += (double)bf2f(kstage[blk * KBLK + 8 * wave + j][lane]);
+        sk += (double)bf2f(kstage[8 * wave + j][lane]);
         sv += (double)bf2f(vstage[8 * wave + j][lane]);
       }
     }
@@ -168,36 +160,14 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
     ((u16*)(kblk + r * D * 2))[d] = kb16;
     lm_value_block(g, lo.LM, h, u)[d * KBLK + value_pos(r)] = f2bf(mv);
     lm_zero_row(kblk, r, d);
-    kq_s[d] = (double)bf2f(kb16);
-  }
-  __syncthreads();
-  // per-channel max |k - kbar (bf16)| over the tile's real keys: wave w
-  // takes slots w, w+4, ...
-  {
-    const double kq = kq_s[lane];
-    double dev = 0.0;
-    for (int s = wave; s < nreal; s += 4) dev = fmax(dev, fabs((double)bf2f(kstage[s][lane]) - kq));
-    red[0][wave][lane] = dev;
-  }
-  __syncthreads();
-  if (tid < D) {
-    const int d = tid;
-    const double m = fmax(fmax(red[0][0][d], red[0][1][d]), fmax(red[0][2][d], red[0][3][d]));
-    double e = m * m;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) e += __shfl_down(e, o, 64);
     if (d == 0) {
       ((float*)(kblk + LM_LOG2N_ROW * D * 2))[r] = log2f((float)nreal);
-      ((float*)(kblk + LM_RADIUS_ROW * D * 2))[r] = (float)(sqrt(e) * 1.0001 + 1e-6);
       if (h == 0) lo.logn[u] = logf((float)nreal);
     }
   }
 }
 
-// grid (T_pad, H), block 64 (thread = channel). Also writes, per tile, a
-// key radius r_u >= max_j |k_j - kbar_u| (per-channel max deviations, their
-// Euclidean norm, inflated to also cover the bf16 rounding of kbar), which
-// the attention kernel uses to bound the logits of the tile's keys.
+// grid (T_pad, H), block 64 (thread = channel).
 __global__ void __launch_bounds__(64) landmark_kernel(Geom g, const u16* __restrict__ Kt,
                                                       const u16* __restrict__ Vt,
                                                       double* __restrict__ kbar,
@@ -210,18 +180,12 @@ __global__ void __launch_bounds__(64) landmark_kernel(Geom g, const u16* __restr
   char* kblk = lmh + (long long)lb * LM_KEY_BLOCK;
   u16* krow = (u16*)(kblk + r * D * 2);
   float* log2n_row = (float*)(kblk + LM_LOG2N_ROW * D * 2);
-  float* rad_row = (float*)(kblk + LM_RADIUS_ROW * D * 2);
   u16* vblk = (u16*)(lmh + (long long)(g.T_pad / KBLK) * LM_KEY_BLOCK + (long long)lb * KBLK * D * 2);
-  // rows 32..63 beyond the two table rows are zero
-  if (r < KBLK && KBLK + r != LM_LOG2N_ROW && KBLK + r != LM_RADIUS_ROW)
-    ((u16*)(kblk + (KBLK + r) * D * 2))[d] = 0;
+  lm_zero_row(kblk, r, d);
   if (u >= g.T) {  // padding landmarks: zero key and value, log2 n = -inf
     krow[d] = 0;
     vblk[d * KBLK + value_pos(r)] = 0;
-    if (d == 0) {
-      log2n_row[r] = -INFINITY;
-      rad_row[r] = 0.f;
-    }
+    if (d == 0) log2n_row[r] = -INFINITY;
     return;
   }
   const int f = u / g.tpf, tl = u - f * g.tpf;
@@ -242,21 +206,7 @@ __global__ void __launch_bounds__(64) landmark_kernel(Geom g, const u16* __restr
   const u16 kb16 = f2bf((float)mk);
   krow[d] = kb16;
   vblk[d * KBLK + value_pos(r)] = f2bf(mv);
-  // radius about the bf16-rounded mean the attention kernel uses
-  const double kq = (double)bf2f(kb16);
-  double dev = 0.0;
-  for (int s = 0; s < n; ++s) dev = fmax(dev, fabs((double)bf2f(kp[(long long)s * D]) - kq));
-  __shared__ double red[64];
-  red[d] = dev * dev;
-  __syncthreads();
-  for (int o = 32; o > 0; o >>= 1) {
-    if (d < o) red[d] += red[d + o];
-    __syncthreads();
-  }
-  if (d == 0) {
-    log2n_row[r] = log2f((float)n);
-    rad_row[r] = (float)(sqrt(red[0]) * 1.0001 + 1e-6);
-  }
+  if (d == 0) log2n_row[r] = log2f((float)n);
   if (h == 0 && d == 0) logn[u] = logf((float)n);
 }
 

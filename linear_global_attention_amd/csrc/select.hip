@@ -38,48 +38,67 @@ __global__ void __launch_bounds__(64) qbar_kernel(Geom g, const u16* __restrict_
   qbar[((long long)h * g.T + t) * D + d] = s / n;
 }
 
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 // Scores of query tiles [t0, t0+nq) of head h against every key tile:
-// out[tq][u] = (sum_d qbar[t0+tq][d] * kbar[u][d]) * 0.125.
-// grid (ceil(T/64), ceil(nq/64)), block 256 (16x16 threads, 4x4 each).
+// out[tq][u] = (sum_d qbar[t0+tq][d] * kbar[u][d]) * 0.125, on the fp64
+// matrix cores. grid (ceil(T/64), ceil(nq/64)), block 256: a 64 x 64 tile,
+// wave w its 32 x 32 quarter (rows 32 (w >> 1), columns 32 (w & 1)) as 2 x 2
+// 16x16x4 MFMA tiles over the 16 steps of 4 channels. Both operands sit in
+// LDS row-major with a row stride of 68 doubles, so that a step's 64 lane
+// reads (16 rows x 4 channels) cover the 64 banks twice.
+constexpr int SC_LD = D + 4;
 __global__ void __launch_bounds__(256) scores_kernel(Geom g, int h, int t0, int nq,
                                                      const double* __restrict__ qbar,
                                                      const double* __restrict__ kbar,
                                                      double* __restrict__ out) {
-  __shared__ double qs[D][64 + 1];
-  __shared__ double ks[D][64 + 1];
-  const int tid = threadIdx.x;
+  __shared__ double qs[64 * SC_LD];
+  __shared__ double ks[64 * SC_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int u0 = blockIdx.x * 64, q0 = blockIdx.y * 64;
   const double* qb = qbar + ((long long)h * g.T + t0) * D;
   const double* kb = kbar + (long long)h * g.T * D;
   for (int i = tid; i < 64 * D; i += 256) {
     const int r = i / D, d = i % D;
-    qs[d][r] = (q0 + r < nq) ? qb[(long long)(q0 + r) * D + d] : 0.0;
-    ks[d][r] = (u0 + r < g.T) ? kb[(long long)(u0 + r) * D + d] : 0.0;
+    qs[r * SC_LD + d] = (q0 + r < nq) ? qb[(long long)(q0 + r) * D + d] : 0.0;
+    ks[r * SC_LD + d] = (u0 + r < g.T) ? kb[(long long)(u0 + r) * D + d] : 0.0;
   }
   __syncthreads();
-  const int ty = tid >> 4, tx = tid & 15;
-  double acc[4][4] = {};
-  for (int d = 0; d < D; ++d) {
-    double a[4], b[4];
+  const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
+  const int m = lane & 15, kq = lane >> 4;
+  f64x4 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = qs[d][ty * 4 + i];
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = ks[d][tx * 4 + j];
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int s4 = 0; s4 < D / 4; ++s4) {
+    const int k = 4 * s4 + kq;
+    double a[2], b[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = q0 + ty * 4 + i;
-    if (q >= nq) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int u = u0 + tx * 4 + j;
-      if (u < g.T) out[(long long)q * g.T + u] = acc[i][j] * 0.125;
+    for (int i = 0; i < 2; ++i) {
+      a[i] = qs[(wr + 16 * i + m) * SC_LD + k];
+      b[i] = ks[(wc + 16 * i + m) * SC_LD + k];
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
   }
+  // acc[i][j][r]: query row wr + 16 i + 4 r + kq, key column wc + 16 j + m
+  // (the f64 MFMA's output element r of lane l is row 4 r + l / 16)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = q0 + wr + 16 * i + 4 * r + kq;
+      if (q >= nq) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int u = u0 + wc + 16 * j + m;
+        if (u < g.T) out[(long long)q * g.T + u] = acc[i][j][r] * 0.125;
+      }
+    }
 }
 
 constexpr int TOPK_THREADS = 1024;

@@ -327,16 +327,20 @@ __device__ __forceinline__ void stream_items(char* ringA, char* ringB, Next next
 
 // Per head, the largest squared key norm over every packed patch key and
 // special key (zero padding included), as the bits of a non-negative float
-// in kmax2[h] (cleared beforehand). grid (ceil((slots + spec_pad) / 64), H),
-// block 256: four lanes per key row, 16 channels each.
+// in kmax2[h] (cleared beforehand). grid (KN_BLOCKS, H), block 256: four
+// lanes per key row (16 channels each), rows strided over the grid, one
+// atomic per workgroup.
+constexpr int KN_BLOCKS = 256;
 __global__ void __launch_bounds__(256) key_norm_max_kernel(Geom g, AttnArgs A, unsigned* kmax2) {
+  __shared__ float wmax[4];
   const int h = blockIdx.y;
-  const long long r = (long long)blockIdx.x * 64 + (threadIdx.x >> 2);
   const int part = threadIdx.x & 3;
-  float ss = 0.f;
-  if (r < g.slots + g.spec_pad) {
+  const long long nrows = g.slots + g.spec_pad;
+  float best = 0.f;
+  for (long long r = (long long)blockIdx.x * 64 + (threadIdx.x >> 2); r < nrows; r += (long long)KN_BLOCKS * 64) {
     const u16* row = r < g.slots ? A.Kt + ((long long)h * g.slots + r) * D
                                  : A.Ks + ((long long)h * g.spec_pad + (r - g.slots)) * D;
+    float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const uint4 w = *(const uint4*)(row + part * 16 + c * 8);
@@ -344,12 +348,16 @@ __global__ void __launch_bounds__(256) key_norm_max_kernel(Geom g, AttnArgs A, u
 #pragma unroll
       for (int m = 0; m < 8; ++m) ss = fmaf((float)v[m], (float)v[m], ss);
     }
+    ss += __shfl_xor(ss, 1, 64);  // the row's four lanes (all active together)
+    ss += __shfl_xor(ss, 2, 64);
+    best = fmaxf(best, ss);
   }
-  ss += __shfl_xor(ss, 1, 64);  // the row's four lanes
-  ss += __shfl_xor(ss, 2, 64);
 #pragma unroll
-  for (int o = 4; o < 64; o <<= 1) ss = fmaxf(ss, __shfl_xor(ss, o, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(&kmax2[h], __float_as_uint(ss));
+  for (int o = 4; o < 64; o <<= 1) best = fmaxf(best, __shfl_xor(best, o, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(&kmax2[h], __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
 }
 
 // Offsets. Every logit a row sees is at most |q| K_max / 8 (Cauchy-Schwarz,
@@ -870,8 +878,7 @@ hipError_t launch_attn(const Geom& g, const AttnArgs& a, void* workspace, hipStr
   if (round < 1) round = 1;
   hipLaunchKernelGGL(clear_flags_kernel, dim3((unsigned)((ws.groups + g.H + 255) / 256)), dim3(256), 0, s, flags,
                      ws.groups + g.H);
-  hipLaunchKernelGGL(key_norm_max_kernel, dim3((unsigned)((g.slots + g.spec_pad + 63) / 64), g.H), dim3(256), 0, s, g,
-                     a, kmax2);
+  hipLaunchKernelGGL(key_norm_max_kernel, dim3(KN_BLOCKS, g.H), dim3(256), 0, s, g, a, kmax2);
   hipLaunchKernelGGL((attn_bound_kernel<FG, FSLOTS>), dim3(fi.total), dim3(FWAVES * 64), 0, s, g, a, negm, flags,
                      (const unsigned*)kmax2);
   for (int u0 = 0; u0 < units.total; u0 += round) {

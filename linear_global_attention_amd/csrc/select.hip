@@ -52,16 +52,30 @@ __global__ void __launch_bounds__(256) scores_kernel(Geom g, int h, int t0, int 
                                                      const double* __restrict__ qbar,
                                                      const double* __restrict__ kbar,
                                                      double* __restrict__ out) {
-  __shared__ double qs[64 * SC_LD];
-  __shared__ double ks[64 * SC_LD];
+  __shared__ __attribute__((aligned(16))) double qs[64 * SC_LD];
+  __shared__ __attribute__((aligned(16))) double ks[64 * SC_LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int u0 = blockIdx.x * 64, q0 = blockIdx.y * 64;
   const double* qb = qbar + ((long long)h * g.T + t0) * D;
   const double* kb = kbar + (long long)h * g.T * D;
-  for (int i = tid; i < 64 * D; i += 256) {
-    const int r = i / D, d = i % D;
-    qs[r * SC_LD + d] = (q0 + r < nq) ? qb[(long long)(q0 + r) * D + d] : 0.0;
-    ks[r * SC_LD + d] = (u0 + r < g.T) ? kb[(long long)(u0 + r) * D + d] : 0.0;
+  {
+    // thread: row tid / 4, doubles 16 (tid % 4) .. +15 of both tiles; all
+    // sixteen 16-byte loads are issued before the first LDS write. Rows past
+    // the end repeat the last row (their outputs are not stored).
+    const int r = tid >> 2, c0 = (tid & 3) * 16;
+    const uint4* qsrc = (const uint4*)(qb + (long long)min(q0 + r, nq - 1) * D + c0);
+    const uint4* ksrc = (const uint4*)(kb + (long long)min(u0 + r, g.T - 1) * D + c0);
+    uint4 qv[8], kv[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      qv[c] = qsrc[c];
+      kv[c] = ksrc[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      *(uint4*)(qs + r * SC_LD + c0 + 2 * c) = qv[c];
+      *(uint4*)(ks + r * SC_LD + c0 + 2 * c) = kv[c];
+    }
   }
   __syncthreads();
   const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;

@@ -429,7 +429,7 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
   // (swizzled so the row-per-lane reads below are spread over the banks).
   // Rows past t_end repeat the last token, whose output they then rewrite
   // with the same value: every lane issues every load and store, so the
-  // wave's memory counter advances by exactly 2 per group staged and 4 per
+  // wave's memory counter advances by exactly 2 per group staged and 2 per
   // group stored.
   auto stage = [&](int m) {
     const long long r0 = first + 64LL * m;
@@ -446,16 +446,30 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
   for (int m = 0; m < AP_NB - 1 && m < n; ++m) stage(m);
   for (int m = 0; m < n; ++m) {
     // group m has landed once at most `later` newer memory operations of
-    // this wave are pending: the newer stages (2 each) and stores (4 each)
-    const int later = 2 * min(AP_NB - 2, n - 1 - m) + 4 * min(m, AP_NB - 2);
+    // this wave are pending: the newer stages (2 each) and stores (2 each)
+    const int later = 2 * min(AP_NB - 2, n - 1 - m) + 2 * min(m, AP_NB - 2);
     lin_wait_vm(later);
     asm volatile("" ::: "memory");
     const char* src = ring + (m % AP_NB) * 2048 + tl * 128;
     uint2 qr[4];
+    {
+      // one asm block that also waits for its reads: as plain loads the
+      // compiler would first wait for every copy in flight into the ring
+      unsigned qa[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cc = (2 * q + (grp >> 1)) ^ (tl & 7);
-      qr[q] = *(const uint2*)(src + cc * 16 + (grp & 1) * 8);
+      for (int q = 0; q < 4; ++q) {
+        const int cc = (2 * q + (grp >> 1)) ^ (tl & 7);
+        qa[q] = (unsigned)(size_t)(src + cc * 16 + (grp & 1) * 8);
+      }
+      asm volatile(
+          "ds_read_b64 %0, %4\n\t"
+          "ds_read_b64 %1, %5\n\t"
+          "ds_read_b64 %2, %6\n\t"
+          "ds_read_b64 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(qr[0]), "=&v"(qr[1]), "=&v"(qr[2]), "=&v"(qr[3])
+          : "v"(qa[0]), "v"(qa[1]), "v"(qa[2]), "v"(qa[3])
+          : "memory");
     }
     const long long tok = min(first + 64LL * m + tl, t_end - 1);
     float x[16];
@@ -489,14 +503,32 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
       }
       y[eb] = a;
     }
-    // output token = tok (MFMA column), channels eb*16 + 4*grp + r
-    u16* orow = out + tok * rs + h * D;
+    // Output token tl of the group (MFMA column), channels eb*16 + 4*grp + r.
+    // The 16 x 128-byte output tile goes through this group's ring slot
+    // (its queries are already in registers), swizzled as the input, so
+    // that each row is stored whole: 8 lanes x 16 bytes per row.
+    char* slot = ring + (m % AP_NB) * 2048;
 #pragma unroll
     for (int eb = 0; eb < 4; ++eb) {
       uint2 w;
       w.x = pack_bf16x2(fmaf(y[eb][0], inv, bp[eb * 4 + 0]), fmaf(y[eb][1], inv, bp[eb * 4 + 1]));
       w.y = pack_bf16x2(fmaf(y[eb][2], inv, bp[eb * 4 + 2]), fmaf(y[eb][3], inv, bp[eb * 4 + 3]));
-      *(uint2*)(orow + eb * 16 + 4 * grp) = w;
+      const int c = 2 * eb + (grp >> 1);
+      *(uint2*)(slot + tl * 128 + ((c ^ (tl & 7)) << 4) + (grp & 1) * 8) = w;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 8 * j + (lane >> 3), c = lane & 7;
+      uint4 v;
+      {
+        const unsigned va = (unsigned)(size_t)(slot + r * 128 + ((c ^ (r & 7)) << 4));
+        typedef unsigned u4 __attribute__((ext_vector_type(4)));
+        u4 t;
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(t) : "v"(va) : "memory");
+        v = make_uint4(t[0], t[1], t[2], t[3]);
+      }
+      const long long otok = min(first + 64LL * m + r, t_end - 1);
+      *(uint4*)(out + otok * rs + h * D + c * 8) = v;
     }
     if (m + AP_NB - 1 < n) stage(m + AP_NB - 1);
   }

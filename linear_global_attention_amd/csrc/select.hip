@@ -1,18 +1,21 @@
-// Tile selector for gfx950: fp64 tile scores and exact top-k.
+// Tile selector for gfx950: fp64 tile scores and an exact fp64 top-k.
 //
 // Zebra3D pages, "Linear-centered stages plus tile-sparse stages": for each
 // query tile the selector keeps a key-tile fraction 1 - y. A tile's score is
 // the mean query of the query tile dotted with the key tile's mean key,
 // divided by sqrt(64), over all key tiles of all frames. Ties go to the lower
-// tile index. Scores are float64 on both sides of the parity check so that
-// the integer decision (kept or not) is taken in the same precision.
+// tile index. The kept/not-kept decision is taken on float64 scores on both
+// sides of the parity check.
 //
 // Three kernels: qbar (mean patch query per tile, exact fp64 sums),
-// scores (a 64x64-blocked fp64 product qbar . kbar^T into a workspace
-// chunk) and topk (one 1024-thread workgroup per query tile: the k-th key
-// found by histogram range narrowing over order-preserving 64-bit keys, then
-// an ascending compaction from one scan of per-wave counts that also writes
-// the bitmap).
+// scores (a 64x64-blocked fp64 product qbar . kbar^T on the fp64 matrix
+// cores, each score stored rounded to fp32 as an order-preserving 32-bit
+// key) and topk (one 1024-thread workgroup per query tile: the key of the
+// k-th tile found by histogram range narrowing; rounding never reverses an
+// order, so only tiles whose key equals that key can rank differently in
+// fp64, and when they straddle the cut their fp64 scores are recomputed and
+// ranked; then an ascending compaction from one scan of per-wave counts
+// that also writes the bitmap).
 #include "common.hpp"
 
 namespace zebra {
@@ -40,6 +43,18 @@ __global__ void __launch_bounds__(64) qbar_kernel(Geom g, const u16* __restrict_
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
+// Order key of a score rounded to fp32 (round to nearest even, which never
+// reverses an order), -0 taken as +0: unsigned order is score order.
+__device__ inline unsigned f32_key(float x) {
+  if (x == 0.0f) x = 0.0f;
+  const unsigned b = __float_as_uint(x);
+  return (b >> 31) ? ~b : (b | 0x80000000u);
+}
+
+__device__ inline float key_f32(unsigned k) {
+  return __uint_as_float((k >> 31) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // Scores of query tiles [t0, t0+nq) of head h against every key tile:
 // out[tq][u] = (sum_d qbar[t0+tq][d] * kbar[u][d]) * 0.125, on the fp64
 // matrix cores. grid (ceil(T/64), ceil(nq/64)), block 256: a 64 x 64 tile,
@@ -51,7 +66,7 @@ constexpr int SC_LD = D + 4;
 __global__ void __launch_bounds__(256) scores_kernel(Geom g, int h, int t0, int nq,
                                                      const double* __restrict__ qbar,
                                                      const double* __restrict__ kbar,
-                                                     double* __restrict__ out) {
+                                                     unsigned* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) double qs[64 * SC_LD];
   __shared__ __attribute__((aligned(16))) double ks[64 * SC_LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -110,40 +125,32 @@ __global__ void __launch_bounds__(256) scores_kernel(Geom g, int h, int t0, int 
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int u = u0 + wc + 16 * j + m;
-        if (u < g.T) out[(long long)q * g.T + u] = acc[i][j][r] * 0.125;
+        if (u < g.T) out[(long long)q * g.T + u] = f32_key((float)(acc[i][j][r] * 0.125));
       }
     }
 }
 
 constexpr int TOPK_THREADS = 1024;
-constexpr int SELECT_CHUNK = 4096;  // query tiles scored per launch
-constexpr int TOPK_PER_THREAD = 32;  // T <= 32768
-
-__device__ inline unsigned long long score_key(double s) {
-  if (s == 0.0) s = 0.0;  // -0 and +0 compare equal
-  const unsigned long long b = (unsigned long long)__double_as_longlong(s);
-  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
-}
-
-__device__ inline double key_score(unsigned long long k) {
-  const unsigned long long b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
-  return __longlong_as_double((long long)b);
-}
-
-constexpr int TOPK_BINS = 4096;  // histogram bins per refinement level
-constexpr int TOPK_CAND = 256;   // candidates ranked pairwise in LDS
+constexpr int TOPK_NW = TOPK_THREADS / 64;
+constexpr int SELECT_CHUNK = 4096;     // query tiles scored per launch
+constexpr int TOPK_MAX_ROUNDS = 32;    // T <= 32768
+constexpr int TOPK_BINS = 4096;        // histogram bins per refinement level
+constexpr int TOPK_CAND = 256;         // most keys in a bin that ends the narrowing
+constexpr int TOPK_RANK_CHUNK = 2048;  // tie-group scores ranked per LDS pass (in the histogram)
 
 // Exclusive prefix, in place, of the per-(round, wave) counts tab[0, nvalid)
 // (round-major, so in tile order), by the first wave; entries past nvalid
-// (rounds past the last tile) count as zero.
+// count as zero.
+template <int N>
 __device__ inline void table_scan(unsigned* tab, int nvalid) {
-  constexpr int N = TOPK_PER_THREAD * (TOPK_THREADS / 64), PER = N / 64;
+  constexpr int PER = (N + 63) / 64;
   const int lane = threadIdx.x & 63;
   if (threadIdx.x < 64) {
     unsigned v[PER], sum = 0u;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      v[j] = lane * PER + j < nvalid ? tab[lane * PER + j] : 0u;
+      const int e = lane * PER + j;
+      v[j] = e < nvalid ? tab[e] : 0u;
       sum += v[j];
     }
     unsigned incl = sum;
@@ -155,26 +162,27 @@ __device__ inline void table_scan(unsigned* tab, int nvalid) {
     unsigned run = incl - sum;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      tab[lane * PER + j] = run;
+      const int e = lane * PER + j;
+      if (e < N) tab[e] = run;
       run += v[j];
     }
   }
 }
 
-// A copy of x the compiler cannot see through: bin maps are recomputed in
-// each pass instead of being kept live across passes in registers.
-__device__ inline double opaque(double x) {
+// A copy of x the compiler cannot see through: values derived from the keys
+// are recomputed in each pass instead of being kept live in registers.
+__device__ inline unsigned opaque(unsigned x) {
   __asm__ volatile("" : "+v"(x));
   return x;
 }
 
-// Workgroup min and max (by comparisons: the scores hold no NaN, and fmin
-// would make canonicalised copies of them) of the scores (lo, hi) through per-wave slots w[0..31];
-// every thread gets the result. Barrier on entry and exit.
-__device__ inline void block_minmax(double& lo, double& hi, double* w) {
+// Workgroup min and max of (lo, hi) through per-wave slots w[0..2*NW); every
+// thread gets the result. Barrier on entry and exit.
+template <typename V>
+__device__ inline void block_minmax(V& lo, V& hi, V* w) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    const double ol = __shfl_xor(lo, off, 64), oh = __shfl_xor(hi, off, 64);
+    const V ol = __shfl_xor(lo, off, 64), oh = __shfl_xor(hi, off, 64);
     lo = ol < lo ? ol : lo;
     hi = oh > hi ? oh : hi;
   }
@@ -182,71 +190,94 @@ __device__ inline void block_minmax(double& lo, double& hi, double* w) {
   __syncthreads();
   if ((threadIdx.x & 63) == 0) {
     w[wave] = lo;
-    w[16 + wave] = hi;
+    w[TOPK_NW + wave] = hi;
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < TOPK_THREADS / 64; ++j) {
+  for (int j = 0; j < TOPK_NW; ++j) {
     lo = w[j] < lo ? w[j] : lo;
-    hi = w[16 + j] > hi ? w[16 + j] : hi;
+    hi = w[TOPK_NW + j] > hi ? w[TOPK_NW + j] : hi;
   }
   __syncthreads();
 }
 
-// grid (nq), block 1024: top-k of query tile t0+blockIdx.x of head h.
-// Thread tid holds the scores of tiles u = i * 1024 + tid (round i).
+// The fp64 score of one key tile, recomputed as a single fixed-order chain
+// of fused multiply-adds over channels 0..63: equal rows give equal scores.
+__device__ inline double exact_score(const double* __restrict__ qrow, const double* __restrict__ krow) {
+  double s = 0.0;
+#pragma unroll 8
+  for (int c = 0; c < D; c += 2) {
+    const double2 a = *(const double2*)(qrow + c), b = *(const double2*)(krow + c);
+    s = fma(a.x, b.x, s);
+    s = fma(a.y, b.y, s);
+  }
+  return s * 0.125;
+}
+
+// grid (nq), block 1024: top-k of query tile t0+blockIdx.x of head h, from
+// its row of fp32 order keys. Thread tid holds the keys of tiles
+// u = i * 1024 + tid (round i); the rounds number PMIN..P, so rounds below
+// PMIN - 1 are whole.
 //
-// The kept set is every (score, u) ranked at or above the k-th in the order
-// (score descending, tile index ascending). That k-th pair is found by
-// narrowing a score interval: a 4096-bin histogram of the interval (bins
-// uniform in score on the first level, in the order-preserving key bits
-// after that), and the bin holding the k-th score becomes the next
-// interval, until the bin holds at most 256 scores, which are ranked
-// pairwise in LDS, or one score value, whose tie is cut by tile index. Every
-// bin map is monotone, so bins are score intervals and a key in a higher bin
-// is strictly greater. Keys above the chosen bin are counted per (round,
-// wave) as each level is scanned; with the ranked candidates this gives
-// every kept key's output position, and one last pass writes the list and
-// the bitmap.
+// The kept set is the k tiles ranked first by (fp64 score descending, tile
+// index ascending). Rounding to fp32 preserves order, so every tile whose
+// key exceeds the key K* of the k-th ranked tile is kept and every tile
+// below it is not; only the tiles whose key equals K* can rank differently
+// in fp64. K* is found by narrowing a key interval with 4096-bin
+// histograms (bins uniform in score on the first level, in key bits after
+// that) until the bin holding the k-th key has at most 256 keys, which are
+// compared pairwise in LDS, or a single key value. When the tiles with key
+// K* straddle the cut, their fp64 scores are recomputed and ranked (by tile
+// index alone when all are equal). Counts per (round, wave) of the kept
+// tiles then give each one its output position in ascending order.
+template <int PMIN, int P>
 __global__ void __launch_bounds__(TOPK_THREADS) topk_kernel(Geom g, int h, int t0, int k,
-                                                            const double* __restrict__ scores,
+                                                            const unsigned* __restrict__ keys,
+                                                            unsigned* __restrict__ ranks,
+                                                            const double* __restrict__ qbar,
+                                                            const double* __restrict__ kbar,
                                                             int* __restrict__ sel,
                                                             unsigned* __restrict__ selmask,
                                                             double* __restrict__ gap) {
-  constexpr int NW = TOPK_THREADS / 64, BPT = TOPK_BINS / TOPK_THREADS;
-  __shared__ unsigned hist[TOPK_BINS];
+  static_assert(P <= 32 && 2 * P <= 64, "a lane per round and a mask bit per round");
+  constexpr int NW = TOPK_NW, BPT = TOPK_BINS / TOPK_THREADS;
+  __shared__ __attribute__((aligned(16))) unsigned hist[TOPK_BINS];
+  __shared__ unsigned tab[P * NW];
+  __shared__ unsigned gbits[P * TOPK_THREADS / 32];  // kept tiles of a straddling tie group
+  __shared__ unsigned cand[TOPK_CAND];
   __shared__ unsigned wsum[NW];
-  __shared__ unsigned take_tab[TOPK_PER_THREAD * NW];  // kept keys per (round, wave)
-  __shared__ unsigned eq_tab[TOPK_PER_THREAD * NW];
-  __shared__ double cand_s[TOPK_CAND];
-  __shared__ int cand_u[TOPK_CAND];
-  __shared__ double wred[2 * NW];
-  __shared__ unsigned sh_bin, sh_want, sh_cnt, sh_nc;
-  __shared__ double sh_st;
-  __shared__ int sh_ut;
+  __shared__ unsigned wred_u[2 * NW];
+  __shared__ double wred_d[2 * NW];
+  __shared__ unsigned sh_bin, sh_want, sh_cnt, sh_nc, sh_kstar, sh_gt, sh_ge;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = t0 + blockIdx.x;
   const int T = g.T;
   const int nwords = (T + 31) / 32;
   const int rounds = (T + TOPK_THREADS - 1) / TOPK_THREADS;
-  const int last = rounds - 1;
-  const bool tail_ok = tid < T - last * TOPK_THREADS;  // valid in the last round
-  const double* row = scores + (long long)blockIdx.x * T;
+  const unsigned* row = keys + (long long)blockIdx.x * T;
+  unsigned* rank_row = ranks + (long long)blockIdx.x * T;
   int* selrow = sel + ((long long)h * T + t) * k;
   unsigned* maskrow = selmask + ((long long)h * T + t) * nwords;
+  const double* qrow = qbar + ((long long)h * T + t) * D;
+  const double* kb = kbar + (long long)h * T * D;
   const unsigned long long below_lanes = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-#define TOPK_VALID(i) ((i) < last || tail_ok)
 
-  double sc[TOPK_PER_THREAD];
+  // bit i: tile i * 1024 + tid exists (read through opaque() so that the
+  // per-round tests are not kept live across the kernel)
+  unsigned vmask = 0u;
+  unsigned kv[P];
 #pragma unroll
-  for (int i = 0; i < TOPK_PER_THREAD; ++i) {
+  for (int i = 0; i < P; ++i) {
     const int u = i * TOPK_THREADS + tid;
-    sc[i] = (u < T) ? row[u] : 0.0;
+    kv[i] = u < T ? row[u] : 0u;
+    vmask |= (u < T ? 1u : 0u) << i;
   }
+#define TOPK_VALID(i) ((i) < PMIN - 1 || ((opaque(vmask) >> (i)) & 1u))
+#define TOPK_SKIP(i) ((i) >= PMIN && (i) >= rounds)
 
   if (k == 0 || k == T) {  // nothing to rank
 #pragma unroll
-    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
+    for (int i = 0; i < P; ++i) {
       const int u = i * TOPK_THREADS + tid;
       if (u < T && k == T) selrow[u] = u;
     }
@@ -259,34 +290,32 @@ __global__ void __launch_bounds__(TOPK_THREADS) topk_kernel(Geom g, int h, int t
     return;
   }
 
-  if (tid < TOPK_PER_THREAD * NW) take_tab[tid] = 0u;
-  double lo = __longlong_as_double(0x7FF0000000000000ll), hi = -lo;
+  unsigned lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-  for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-    if (i >= rounds) continue;  // uniform
-    if (TOPK_VALID(i)) {
-      lo = sc[i] < lo ? sc[i] : lo;
-      hi = sc[i] > hi ? sc[i] : hi;
-    }
+  for (int i = 0; i < P; ++i) {
+    if (TOPK_SKIP(i)) continue;  // uniform
+    const bool v = TOPK_VALID(i);
+    lo = v && kv[i] < lo ? kv[i] : lo;
+    hi = v && kv[i] > hi ? kv[i] : hi;
   }
-  block_minmax(lo, hi, wred);
+  block_minmax(lo, hi, wred_u);
 
   unsigned want = (unsigned)k, cnt = (unsigned)T;
   bool gathered = false;
-  // One narrowing step over the scores in [lo, hi] (all scores when `all`)
-  // under the monotone bin map `digit`: histogram, the bin holding the
-  // want-th score, per-(round, wave) counts of the scores above that bin,
-  // and then either the bin's scores gathered as candidates (at most
-  // TOPK_CAND) or the bin's interval as the new [lo, hi].
-  auto narrow = [&](auto digit, bool all) {
+  // One narrowing step over the keys in [lo, hi] under the monotone bin map
+  // `digit`: the histogram, the bin holding the want-th key from the top,
+  // and then either that bin's keys gathered (at most TOPK_CAND) or its key
+  // range as the new [lo, hi].
+  auto narrow = [&](auto digit) {
 #pragma unroll
     for (int j = 0; j < BPT; ++j) hist[j * TOPK_THREADS + tid] = 0u;
     if (tid == 0) sh_nc = 0u;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-      if (i >= rounds) continue;
-      if (TOPK_VALID(i) && (all || (sc[i] >= lo && sc[i] <= hi))) atomicAdd(&hist[digit(opaque(sc[i]))], 1u);
+    for (int i = 0; i < P; ++i) {
+      if (TOPK_SKIP(i)) continue;
+      const unsigned x = opaque(kv[i]);
+      if (TOPK_VALID(i) & (x >= lo) & (x <= hi)) atomicAdd(&hist[digit(x)], 1u);
     }
     __syncthreads();
     // thread tid owns bins 4095-4tid .. 4092-4tid (descending order)
@@ -319,184 +348,276 @@ __global__ void __launch_bounds__(TOPK_THREADS) topk_kernel(Geom g, int h, int t
     const unsigned bin = sh_bin;
     want = sh_want;
     cnt = sh_cnt;
-    const bool gather = cnt <= (unsigned)TOPK_CAND;
-    double blo = __longlong_as_double(0x7FF0000000000000ll), bhi = -blo;
+    if (cnt <= (unsigned)TOPK_CAND) {
 #pragma unroll
-    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-      if (i >= rounds) continue;
-      const int u = i * TOPK_THREADS + tid;
-      const bool inr = TOPK_VALID(i) && (all || (sc[i] >= lo && sc[i] <= hi));
-      const unsigned d = inr ? digit(opaque(sc[i])) : 0u;
-      const unsigned long long ba = __ballot(inr && d > bin);
-      if (lane == 0) take_tab[i * NW + wave] += (unsigned)__popcll(ba);
-      const bool inb = inr && d == bin;
-      if (gather) {
+      for (int i = 0; i < P; ++i) {
+        if (TOPK_SKIP(i)) continue;
+        const unsigned x = opaque(kv[i]);
+        const bool inb = TOPK_VALID(i) & (x >= lo) & (x <= hi) & (digit(x) == bin);
         const unsigned long long bi = __ballot(inb);
         if (bi) {
           unsigned base = 0u;
           if (lane == 0) base = atomicAdd(&sh_nc, (unsigned)__popcll(bi));
           base = (unsigned)__shfl(base, 0, 64);
-          if (inb) {
-            const unsigned slot = base + (unsigned)__popcll(bi & below_lanes);
-            cand_s[slot] = sc[i];
-            cand_u[slot] = u;
-          }
+          if (inb) cand[base + (unsigned)__popcll(bi & below_lanes)] = x;
         }
-      } else if (inb) {
-        blo = sc[i] < blo ? sc[i] : blo;
-        bhi = sc[i] > bhi ? sc[i] : bhi;
       }
-    }
-    if (gather) {
       gathered = true;
       __syncthreads();
     } else {
-      block_minmax(blo, bhi, wred);
+      unsigned blo = 0xFFFFFFFFu, bhi = 0u;
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        if (TOPK_SKIP(i)) continue;
+        const unsigned x = opaque(kv[i]);
+        const bool inb = TOPK_VALID(i) & (x >= lo) & (x <= hi) & (digit(x) == bin);
+        blo = inb && x < blo ? x : blo;
+        bhi = inb && x > bhi ? x : bhi;
+      }
+      block_minmax(blo, bhi, wred_u);
       lo = blo;
       hi = bhi;
     }
   };
   if (lo != hi && cnt > (unsigned)TOPK_CAND) {
-    // first step: bins uniform in score, when the span is a normal number
-    const double fspan = hi - lo;
-    const double inv = (double)TOPK_BINS / fspan;
-    if (fspan > 1e-300 && fspan < 1e300 && inv < 1e300) {
-      const double flo = lo;
-      narrow(
-          [&](double x) -> unsigned {
-            const double y = (x - flo) * inv;
-            return y < (double)(TOPK_BINS - 1) ? (unsigned)y : (unsigned)(TOPK_BINS - 1);
-          },
-          true);
-    }
+    // first step: bins uniform in score over [lo, hi], when that span and
+    // its inverse are finite fp32 numbers
+    const float flo = key_f32(lo), fspan = key_f32(hi) - flo, inv = (float)TOPK_BINS / fspan;
+    if (fspan > 0.0f && fspan <= 3.0e38f && inv <= 3.0e38f)
+      narrow([&](unsigned x) -> unsigned {
+        const float y = (key_f32(x) - flo) * inv;
+        return y < (float)(TOPK_BINS - 1) ? (unsigned)y : (unsigned)(TOPK_BINS - 1);
+      });
   }
   // then bins uniform in key bits, 12 bits per step
   while (!gathered && lo != hi && cnt > (unsigned)TOPK_CAND) {
-    const unsigned long long klo = score_key(lo), span = score_key(hi) - klo;
-    const int top = 64 - __clzll((long long)span);
+    const unsigned klo = lo;
+    const int top = 32 - __clz((int)(hi - lo));
     const int sh = top > 12 ? top - 12 : 0;
-    narrow([&](double x) -> unsigned { return (unsigned)((score_key(x) - klo) >> sh); }, false);
+    narrow([&](unsigned x) -> unsigned { return (x - klo) >> sh; });
+  }
+  if (!gathered && lo != hi) {  // few keys from the start: all are candidates
+    if (tid == 0) sh_nc = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      if (TOPK_SKIP(i)) continue;
+      const bool inb = TOPK_VALID(i);
+      const unsigned long long bi = __ballot(inb);
+      if (bi) {
+        unsigned base = 0u;
+        if (lane == 0) base = atomicAdd(&sh_nc, (unsigned)__popcll(bi));
+        base = (unsigned)__shfl(base, 0, 64);
+        if (inb) cand[base + (unsigned)__popcll(bi & below_lanes)] = kv[i];
+      }
+    }
+    gathered = true;
+    __syncthreads();
   }
 
-  // the k-th pair (st, ut) and the kept keys of the final bin
-  if (gathered || (lo != hi && cnt <= (unsigned)TOPK_CAND)) {
-    if (!gathered) {  // few scores from the start: all are candidates
-      if (tid == 0) sh_nc = 0u;
-      __syncthreads();
+  // K*, and how many keys of the final interval lie above it (gt) and at or
+  // above it (ge): gt < want <= ge
+  unsigned kstar, gt, ge;
+  if (gathered) {
+    if (tid < (int)cnt) {
+      const unsigned kc = cand[tid];
+      unsigned a = 0u, b = 0u;
+      for (int j = 0; j < (int)cnt; ++j) {
+        const unsigned kj = cand[j];
+        a += kj > kc ? 1u : 0u;
+        b += kj >= kc ? 1u : 0u;
+      }
+      if (a < want && want <= b) {  // every thread holding K* writes the same
+        sh_kstar = kc;
+        sh_gt = a;
+        sh_ge = b;
+      }
+    }
+    __syncthreads();
+    kstar = sh_kstar;
+    gt = sh_gt;
+    ge = sh_ge;
+  } else {  // one key value left
+    kstar = lo;
+    gt = 0u;
+    ge = cnt;
+  }
+  const bool straddle = ge > want;
+
+  if (straddle) {
+    // The ng tiles with key K* straddle the cut: keep the gwant first by
+    // (fp64 score descending, tile index ascending). gm marks this thread's
+    // slots holding K*; pos is a member's rank by tile index.
+    const unsigned ng = ge - gt, gwant = want - gt;
+    unsigned gm = 0u;
 #pragma unroll
-      for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-        if (i >= rounds) continue;
-        const bool inb = TOPK_VALID(i);
-        const unsigned long long bi = __ballot(inb);
-        if (bi) {
-          unsigned base = 0u;
-          if (lane == 0) base = atomicAdd(&sh_nc, (unsigned)__popcll(bi));
-          base = (unsigned)__shfl(base, 0, 64);
-          if (inb) {
-            const unsigned slot = base + (unsigned)__popcll(bi & below_lanes);
-            cand_s[slot] = sc[i];
-            cand_u[slot] = i * TOPK_THREADS + tid;
+    for (int i = 0; i < P; ++i)
+      if (!TOPK_SKIP(i) && TOPK_VALID(i) && kv[i] == kstar) gm |= 1u << i;
+    for (int w = tid; w < P * TOPK_THREADS / 32; w += TOPK_THREADS) gbits[w] = 0u;
+    for (int i = 0; i < rounds; ++i) {
+      const unsigned long long be = __ballot((gm >> i) & 1u);
+      if (lane == 0) tab[i * NW + wave] = (unsigned)__popcll(be);
+    }
+    __syncthreads();
+    table_scan<P * NW>(tab, rounds * NW);
+    __syncthreads();
+    double smin = __longlong_as_double(0x7FF0000000000000ll), smax = -smin;
+    for (unsigned b = gm; b; b &= b - 1u) {
+      const int u = (__ffs((int)b) - 1) * TOPK_THREADS + tid;
+      const double s = exact_score(qrow, kb + (long long)u * D);
+      smin = s < smin ? s : smin;
+      smax = s > smax ? s : smax;
+    }
+    block_minmax(smin, smax, wred_d);
+    const bool all_equal = smin == smax;  // then the rank is the index rank
+    double* chunk = (double*)hist;
+    static_assert(sizeof(hist) >= TOPK_RANK_CHUNK * sizeof(double), "rank chunk fits the histogram");
+    for (unsigned c0 = 0; c0 < (all_equal ? 0u : ng); c0 += TOPK_RANK_CHUNK) {
+      // the scores of group positions [c0, c0 + cn) into LDS; then every
+      // member adds the chunk's members ranked before it to its running
+      // count, kept in its own slot of this row's rank area
+      const unsigned cn = min((unsigned)TOPK_RANK_CHUNK, ng - c0);
+      __syncthreads();
+      for (int i = 0; i < rounds; ++i) {
+        const bool eq = (gm >> i) & 1u;
+        const unsigned long long be = __ballot(eq);
+        const unsigned pos = tab[i * NW + wave] + (unsigned)__popcll(be & below_lanes);
+        if (eq && pos >= c0 && pos < c0 + cn)
+          chunk[pos - c0] = exact_score(qrow, kb + (long long)(i * TOPK_THREADS + tid) * D);
+      }
+      __syncthreads();
+      for (int i = 0; i < rounds; ++i) {
+        const bool eq = (gm >> i) & 1u;
+        const unsigned long long be = __ballot(eq);
+        const unsigned pos = tab[i * NW + wave] + (unsigned)__popcll(be & below_lanes);
+        if (eq) {
+          const int u = i * TOPK_THREADS + tid;
+          const double s = exact_score(qrow, kb + (long long)u * D);
+          unsigned r = 0u;
+          for (unsigned j = 0; j < cn; ++j) {
+            const double sj = chunk[j];
+            r += (sj > s || (sj == s && c0 + j < pos)) ? 1u : 0u;
           }
+          rank_row[u] = c0 == 0 ? r : rank_row[u] + r;
         }
       }
-      __syncthreads();
     }
-    if (tid < (int)cnt) {
-      const double sc_c = cand_s[tid];
-      const int uc = cand_u[tid];
-      unsigned rank = 0u;
-      for (int j = 0; j < (int)cnt; ++j) {
-        const double sj = cand_s[j];
-        rank += (sj > sc_c || (sj == sc_c && cand_u[j] < uc)) ? 1u : 0u;
-      }
-      if (rank == want - 1u) {
-        sh_st = sc_c;
-        sh_ut = uc;
-      }
-      if (rank < want) atomicAdd(&take_tab[(uc / TOPK_THREADS) * NW + (uc % TOPK_THREADS) / 64], 1u);
-    }
-  } else {
-    // one score value (lo == hi) in the final interval: keep the want
-    // smallest tile indices holding it
-#pragma unroll
-    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-      if (i >= rounds) continue;
-      const unsigned long long be = __ballot(TOPK_VALID(i) && sc[i] == lo);
-      if (lane == 0) eq_tab[i * NW + wave] = (unsigned)__popcll(be);
-    }
-    __syncthreads();
-    table_scan(eq_tab, rounds * NW);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-      if (i >= rounds) continue;
-      const bool eq = TOPK_VALID(i) && sc[i] == lo;
+    for (int i = 0; i < rounds; ++i) {
+      const bool eq = (gm >> i) & 1u;
       const unsigned long long be = __ballot(eq);
-      const unsigned r = eq_tab[i * NW + wave] + (unsigned)__popcll(be & below_lanes);
-      const unsigned long long bk = __ballot(eq && r < want);
-      if (lane == 0) take_tab[i * NW + wave] += (unsigned)__popcll(bk);
-      if (eq && r == want - 1u) {
-        sh_st = lo;
-        sh_ut = i * TOPK_THREADS + tid;
+      const unsigned pos = tab[i * NW + wave] + (unsigned)__popcll(be & below_lanes);
+      const int u = i * TOPK_THREADS + tid;
+      if (eq && (all_equal ? pos : rank_row[u]) < gwant) atomicOr(&gbits[u >> 5], 1u << (u & 31));
+    }
+    __syncthreads();
+  }
+
+  // The kept tiles: keys above K*, and those with key K* (all of them, or
+  // the ranked ones marked in gbits when the group straddles the cut).
+  // Lane i of each wave holds round i's count, then its output offset.
+  unsigned need_t = 0u, need_b = 0u;  // slots whose fp64 score the gap needs
+  auto emit = [&](auto take) {
+    unsigned cntv = 0u;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      if (TOPK_SKIP(i)) continue;
+      const unsigned c = (unsigned)__popcll(__ballot(take(i, opaque(kv[i]))));
+      cntv = lane == i ? c : cntv;
+    }
+    if (lane < rounds) tab[lane * NW + wave] = cntv;
+    __syncthreads();
+    table_scan<P * NW>(tab, rounds * NW);
+    __syncthreads();
+    const unsigned basev = lane < rounds ? tab[lane * NW + wave] : 0u;
+    unsigned maskv = 0u, below_key = 0u;  // below_key: greatest key not kept
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      if (TOPK_SKIP(i)) continue;
+      const int u = i * TOPK_THREADS + tid;
+      const unsigned x = opaque(kv[i]);
+      const bool tk = take(i, x);
+      const unsigned long long bt = __ballot(tk);
+      // lanes 2i and 2i+1 hold this round's two bitmap words
+      maskv = lane == 2 * i ? (unsigned)bt : lane == 2 * i + 1 ? (unsigned)(bt >> 32) : maskv;
+      const unsigned pos = (unsigned)__builtin_amdgcn_readlane((int)basev, i) + (unsigned)__popcll(bt & below_lanes);
+      if (tk && pos < (unsigned)k) selrow[pos] = u;
+      below_key = TOPK_VALID(i) && !tk && x > below_key ? x : below_key;
+    }
+    {
+      const int word = (lane >> 1) * (TOPK_THREADS / 32) + wave * 2 + (lane & 1);
+      if (lane < 2 * rounds && word < nwords) maskrow[word] = maskv;
+    }
+    if (gap) {
+      unsigned dummy = 0u;
+      block_minmax(dummy, below_key, wred_u);
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        if (TOPK_SKIP(i)) continue;
+        const unsigned x = opaque(kv[i]);
+        const bool tk = take(i, x);
+        need_t |= (tk && x == kstar ? 1u : 0u) << i;
+        need_b |= (TOPK_VALID(i) && !tk && x == below_key ? 1u : 0u) << i;
       }
     }
-  }
-  __syncthreads();
-  table_scan(take_tab, rounds * NW);
-  __syncthreads();
-  const double st = sh_st;
-  const int ut = sh_ut;
+  };
+  if (!straddle)
+    emit([&](int i, unsigned x) -> bool { return TOPK_VALID(i) & (x >= kstar); });
+  else
+    emit([&](int i, unsigned x) -> bool {
+      const int u = i * TOPK_THREADS + tid;
+      return TOPK_VALID(i) & ((x > kstar) | ((x == kstar) & (((gbits[u >> 5] >> (u & 31)) & 1u) != 0u)));
+    });
 
-  // kept tiles in ascending order, and the bitmap
-  double below_max = -__longlong_as_double(0x7FF0000000000000ll);
-#pragma unroll
-  for (int i = 0; i < TOPK_PER_THREAD; ++i) {
-    if (i >= rounds) continue;
-    const int u = i * TOPK_THREADS + tid;
-    const bool v = TOPK_VALID(i);
-    const bool take = v && (sc[i] > st || (sc[i] == st && u <= ut));
-    const unsigned long long bt = __ballot(take);
-    const int word = (i * TOPK_THREADS + wave * 64) / 32;
-    if (lane == 0 && word < nwords) maskrow[word] = (unsigned)bt;
-    if (lane == 0 && word + 1 < nwords) maskrow[word + 1] = (unsigned)(bt >> 32);
-    const unsigned pos = take_tab[i * NW + wave] + (unsigned)__popcll(bt & below_lanes);
-    if (take && pos < (unsigned)k) selrow[pos] = u;
-    if (v && !take && sc[i] > below_max) below_max = sc[i];
+  if (gap) {
+    // the k-th ranked fp64 score (least kept score with key K*) and the
+    // (k+1)-th (greatest score among the unkept tiles holding the greatest
+    // unkept key), both recomputed
+    double st = __longlong_as_double(0x7FF0000000000000ll), sb = -st;
+    for (unsigned b = need_t | need_b; b; b &= b - 1u) {
+      const int i = __ffs((int)b) - 1;
+      const double s = exact_score(qrow, kb + (long long)(i * TOPK_THREADS + tid) * D);
+      if ((need_t >> i) & 1u) st = s < st ? s : st;
+      else sb = s > sb ? s : sb;
+    }
+    block_minmax(st, sb, wred_d);
+    if (tid == 0) {
+      const double den = fmax(fmax(fabs(st), fabs(sb)), 1e-300);
+      gap[(long long)h * T + t] = fabs(st - sb) / den;
+    }
   }
 #undef TOPK_VALID
-  if (gap) {
-    double dummy = 0.0;
-    block_minmax(dummy, below_max, wred);
-    if (tid == 0) {
-      // k-th ranked score and (k+1)-th (greatest not kept; equal to the
-      // k-th when a tie straddles the cut)
-      const double den = fmax(fmax(fabs(st), fabs(below_max)), 1e-300);
-      gap[(long long)h * T + t] = fabs(st - below_max) / den;
-    }
-  }
+#undef TOPK_SKIP
 }
 
 size_t select_chunk(const Geom& g) { return (size_t)(g.T < SELECT_CHUNK ? g.T : SELECT_CHUNK); }
 
 size_t select_workspace_bytes(const Geom& g) {
-  return (size_t)g.H * g.T * D * sizeof(double) + select_chunk(g) * (size_t)g.T * sizeof(double);
+  return (size_t)g.H * g.T * D * sizeof(double) + 2 * select_chunk(g) * (size_t)g.T * sizeof(unsigned);
 }
 
-// Workspace: qbar [H][T][64] fp64, then scores [chunk][T] fp64.
+// Workspace: qbar [H][T][64] fp64, then the score keys [chunk][T] u32, then
+// the rank area [chunk][T] u32 (touched only for tie groups that straddle
+// the cut).
 hipError_t launch_select(const Geom& g, int k, const u16* Q, const double* kbar, int* sel,
                          unsigned* selmask, double* gap, void* ws, hipStream_t s) {
   double* qbar = (double*)ws;
-  double* scores = qbar + (size_t)g.H * g.T * D;
-  hipLaunchKernelGGL(qbar_kernel, dim3(g.T, g.H), dim3(64), 0, s, g, Q, qbar);
   const int chunk = (int)select_chunk(g);
+  unsigned* keys = (unsigned*)(qbar + (size_t)g.H * g.T * D);
+  unsigned* ranks = keys + (size_t)chunk * g.T;
+  const int rounds = (g.T + TOPK_THREADS - 1) / TOPK_THREADS;
+  auto topk = rounds <= 4    ? topk_kernel<1, 4>
+              : rounds <= 16 ? topk_kernel<5, 16>
+              : rounds <= 25 ? topk_kernel<17, 25>
+                             : topk_kernel<26, TOPK_MAX_ROUNDS>;
+  hipLaunchKernelGGL(qbar_kernel, dim3(g.T, g.H), dim3(64), 0, s, g, Q, qbar);
   for (int h = 0; h < g.H; ++h) {
     for (int t0 = 0; t0 < g.T; t0 += chunk) {
       const int nq = g.T - t0 < chunk ? g.T - t0 : chunk;
       if (k > 0 && k < g.T)
         hipLaunchKernelGGL(scores_kernel, dim3((g.T + 63) / 64, (nq + 63) / 64), dim3(256), 0, s,
-                           g, h, t0, nq, qbar, kbar, scores);
-      hipLaunchKernelGGL(topk_kernel, dim3(nq), dim3(TOPK_THREADS), 0, s, g, h, t0, k, scores,
-                         sel, selmask, gap);
+                           g, h, t0, nq, qbar, kbar, keys);
+      hipLaunchKernelGGL(topk, dim3(nq), dim3(TOPK_THREADS), 0, s, g, h, t0, k, keys, ranks, qbar,
+                         kbar, sel, selmask, gap);
     }
   }
   return hipGetLastError();

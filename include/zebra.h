@@ -96,8 +96,10 @@ typedef struct {
                           int32 [H][T][k] */
   uint32_t* selmask;   /* the same as a bitmap, [H][T][ceil(T/32)] */
   double* gap;         /* optional (NULL ok): relative gap between the k-th
-                          and (k+1)-th ranked tile score, fp64 [H][T];
-                          +inf when k = 0 or k = T */
+                          and (k+1)-th ranked tile score, fp64 [H][T]; from
+                          the fp64 scores when the two round to the same
+                          fp32 value, else from the fp32-rounded scores
+                          (within 1.2e-7); +inf when k = 0 or k = T */
 
   void* workspace;     /* scratch (ZEBRA_BUF_WORKSPACE bytes) */
   size_t workspace_bytes;

@@ -186,32 +186,105 @@ __device__ inline void block_minmax(V& lo, V& hi, V* w) {
     lo = ol < lo ? ol : lo;
     hi = oh > hi ? oh : hi;
   }
-  const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6, j = threadIdx.x & (TOPK_NW - 1);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) {
     w[wave] = lo;
     w[TOPK_NW + wave] = hi;
   }
   __syncthreads();
+  // lane j of each group of 16 takes wave j's pair; the group reduces it
+  lo = w[j];
+  hi = w[TOPK_NW + j];
 #pragma unroll
-  for (int j = 0; j < TOPK_NW; ++j) {
-    lo = w[j] < lo ? w[j] : lo;
-    hi = w[TOPK_NW + j] > hi ? w[TOPK_NW + j] : hi;
+  for (int off = TOPK_NW / 2; off >= 1; off >>= 1) {
+    const V ol = __shfl_xor(lo, off, 64), oh = __shfl_xor(hi, off, 64);
+    lo = ol < lo ? ol : lo;
+    hi = oh > hi ? oh : hi;
   }
   __syncthreads();
 }
 
 // The fp64 score of one key tile, recomputed as a single fixed-order chain
-// of fused multiply-adds over channels 0..63: equal rows give equal scores.
-__device__ inline double exact_score(const double* __restrict__ qrow, const double* __restrict__ krow) {
+// of fused multiply-adds over channels 0..63 (the query row in LDS): equal
+// rows give equal scores.
+__device__ inline double exact_score(const double* qs, const double* __restrict__ krow) {
   double s = 0.0;
-#pragma unroll 8
+#pragma unroll 4
   for (int c = 0; c < D; c += 2) {
-    const double2 a = *(const double2*)(qrow + c), b = *(const double2*)(krow + c);
-    s = fma(a.x, b.x, s);
-    s = fma(a.y, b.y, s);
+    const double2 b = *(const double2*)(krow + c);
+    s = fma(qs[c], b.x, s);
+    s = fma(qs[c + 1], b.y, s);
   }
   return s * 0.125;
+}
+
+// Per-row record of the top-k kernel for the resolve kernel: flag (1 when
+// the tiles holding K* straddle the cut), K*, how many of them to keep, and
+// how many there are.
+constexpr int TOPK_INFO = 4;
+
+// Keys of tiles u = i * 1024 + tid into kv[i]; bit i of vmask says u < T.
+// The loads are unconditional (the tail repeats the last key).
+template <int P>
+__device__ inline unsigned topk_load(const unsigned* __restrict__ row, int T, unsigned (&kv)[P]) {
+  unsigned vmask = 0u;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int u = i * TOPK_THREADS + (int)threadIdx.x;
+    const bool ok = u < T;
+    kv[i] = row[ok ? u : T - 1];
+    vmask |= (ok ? 1u : 0u) << i;
+  }
+  return vmask;
+}
+
+// Tile u = i * 1024 + tid exists: whole rounds below PMIN - 1; else bit i of
+// vmask, read through opaque() so that per-round tests are not kept live.
+#define TOPK_VALID(i) ((i) < PMIN - 1 || ((opaque(vmask) >> (i)) & 1u))
+// Round i is past the last one (uniform).
+#define TOPK_SKIP(i) ((i) >= PMIN && (i) >= rounds)
+
+// The kept tiles of one row, in ascending order, and its bitmap: lane i of
+// each wave holds round i's kept count, then, after a scan, its output
+// offset. Returns this thread's greatest unkept key (0 if none).
+template <int PMIN, int P, typename Take>
+__device__ inline unsigned topk_emit(const unsigned (&kv)[P], unsigned vmask, int rounds, int k, int nwords,
+                                     unsigned* tab, int* __restrict__ selrow, unsigned* __restrict__ maskrow,
+                                     Take take) {
+  constexpr int NW = TOPK_NW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned long long below_lanes = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  unsigned cntv = 0u;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    if (TOPK_SKIP(i)) continue;
+    const unsigned c = (unsigned)__popcll(__ballot(take(i, opaque(kv[i]))));
+    cntv = lane == i ? c : cntv;
+  }
+  if (lane < rounds) tab[lane * NW + wave] = cntv;
+  __syncthreads();
+  table_scan<P * NW>(tab, rounds * NW);
+  __syncthreads();
+  const unsigned basev = lane < rounds ? tab[lane * NW + wave] : 0u;
+  unsigned maskv = 0u, below_key = 0u;
+  const int utid = (int)opaque((unsigned)tid);  // tile indices recomputed, not held
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    if (TOPK_SKIP(i)) continue;
+    const int u = i * TOPK_THREADS + utid;
+    const unsigned x = opaque(kv[i]);
+    const bool tk = take(i, x);
+    const unsigned long long bt = __ballot(tk);
+    // lanes 2i and 2i+1 hold this round's two bitmap words
+    maskv = lane == 2 * i ? (unsigned)bt : lane == 2 * i + 1 ? (unsigned)(bt >> 32) : maskv;
+    const unsigned pos = (unsigned)__builtin_amdgcn_readlane((int)basev, i) + (unsigned)__popcll(bt & below_lanes);
+    if (tk && pos < (unsigned)k) selrow[pos] = u;
+    below_key = TOPK_VALID(i) && !tk && x > below_key ? x : below_key;
+  }
+  const int word = (lane >> 1) * (TOPK_THREADS / 32) + wave * 2 + (lane & 1);
+  if (lane < 2 * rounds && word < nwords) maskrow[word] = maskv;
+  return below_key;
 }
 
 // grid (nq), block 1024: top-k of query tile t0+blockIdx.x of head h, from
@@ -227,59 +300,39 @@ __device__ inline double exact_score(const double* __restrict__ qrow, const doub
 // histograms (bins uniform in score on the first level, in key bits after
 // that) until the bin holding the k-th key has at most 256 keys, which are
 // compared pairwise in LDS, or a single key value. When the tiles with key
-// K* straddle the cut, their fp64 scores are recomputed and ranked (by tile
-// index alone when all are equal). Counts per (round, wave) of the kept
-// tiles then give each one its output position in ascending order.
+// K* are all kept (the usual case) this kernel writes the row; when they
+// straddle the cut it records K* for topk_resolve_kernel instead.
 template <int PMIN, int P>
-__global__ void __launch_bounds__(TOPK_THREADS) topk_kernel(Geom g, int h, int t0, int k,
-                                                            const unsigned* __restrict__ keys,
-                                                            unsigned* __restrict__ ranks,
-                                                            const double* __restrict__ qbar,
-                                                            const double* __restrict__ kbar,
-                                                            int* __restrict__ sel,
-                                                            unsigned* __restrict__ selmask,
-                                                            double* __restrict__ gap) {
+__global__ void __launch_bounds__(TOPK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+topk_kernel(Geom g, int h, int t0, int k, const unsigned* __restrict__ keys, unsigned* __restrict__ info,
+            int* __restrict__ sel, unsigned* __restrict__ selmask, double* __restrict__ gap) {
   static_assert(P <= 32 && 2 * P <= 64, "a lane per round and a mask bit per round");
   constexpr int NW = TOPK_NW, BPT = TOPK_BINS / TOPK_THREADS;
   __shared__ __attribute__((aligned(16))) unsigned hist[TOPK_BINS];
   __shared__ unsigned tab[P * NW];
-  __shared__ unsigned gbits[P * TOPK_THREADS / 32];  // kept tiles of a straddling tie group
   __shared__ unsigned cand[TOPK_CAND];
   __shared__ unsigned wsum[NW];
   __shared__ unsigned wred_u[2 * NW];
-  __shared__ double wred_d[2 * NW];
-  __shared__ unsigned sh_bin, sh_want, sh_cnt, sh_nc, sh_kstar, sh_gt, sh_ge;
+  __shared__ unsigned sh_bin, sh_want, sh_cnt, sh_nc, sh_kstar, sh_gt, sh_ge, sh_below;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = t0 + blockIdx.x;
   const int T = g.T;
   const int nwords = (T + 31) / 32;
   const int rounds = (T + TOPK_THREADS - 1) / TOPK_THREADS;
   const unsigned* row = keys + (long long)blockIdx.x * T;
-  unsigned* rank_row = ranks + (long long)blockIdx.x * T;
   int* selrow = sel + ((long long)h * T + t) * k;
   unsigned* maskrow = selmask + ((long long)h * T + t) * nwords;
-  const double* qrow = qbar + ((long long)h * T + t) * D;
-  const double* kb = kbar + (long long)h * T * D;
   const unsigned long long below_lanes = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 
-  // bit i: tile i * 1024 + tid exists (read through opaque() so that the
-  // per-round tests are not kept live across the kernel)
-  unsigned vmask = 0u;
   unsigned kv[P];
-#pragma unroll
-  for (int i = 0; i < P; ++i) {
-    const int u = i * TOPK_THREADS + tid;
-    kv[i] = u < T ? row[u] : 0u;
-    vmask |= (u < T ? 1u : 0u) << i;
-  }
-#define TOPK_VALID(i) ((i) < PMIN - 1 || ((opaque(vmask) >> (i)) & 1u))
-#define TOPK_SKIP(i) ((i) >= PMIN && (i) >= rounds)
+  const unsigned vmask = topk_load(row, T, kv);
 
   if (k == 0 || k == T) {  // nothing to rank
+    if (tid == 0) info[blockIdx.x * TOPK_INFO] = 0u;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
       const int u = i * TOPK_THREADS + tid;
-      if (u < T && k == T) selrow[u] = u;
+      if (TOPK_VALID(i) && k == T) selrow[u] = u;
     }
     for (int w = tid; w < nwords; w += TOPK_THREADS) {
       unsigned m = 0u;
@@ -433,182 +486,192 @@ __global__ void __launch_bounds__(TOPK_THREADS) topk_kernel(Geom g, int h, int t
         sh_ge = b;
       }
     }
+    if (tid == 0) sh_below = 0u;
     __syncthreads();
     kstar = sh_kstar;
     gt = sh_gt;
     ge = sh_ge;
+    // the greatest candidate key below K*, if any (read after a barrier)
+    if (tid < (int)cnt && cand[tid] < kstar) atomicMax(&sh_below, cand[tid]);
   } else {  // one key value left
     kstar = lo;
     gt = 0u;
     ge = cnt;
   }
-  const bool straddle = ge > want;
-
-  if (straddle) {
-    // The ng tiles with key K* straddle the cut: keep the gwant first by
-    // (fp64 score descending, tile index ascending). gm marks this thread's
-    // slots holding K*; pos is a member's rank by tile index.
-    const unsigned ng = ge - gt, gwant = want - gt;
-    unsigned gm = 0u;
-#pragma unroll
-    for (int i = 0; i < P; ++i)
-      if (!TOPK_SKIP(i) && TOPK_VALID(i) && kv[i] == kstar) gm |= 1u << i;
-    for (int w = tid; w < P * TOPK_THREADS / 32; w += TOPK_THREADS) gbits[w] = 0u;
-    for (int i = 0; i < rounds; ++i) {
-      const unsigned long long be = __ballot((gm >> i) & 1u);
-      if (lane == 0) tab[i * NW + wave] = (unsigned)__popcll(be);
-    }
-    __syncthreads();
-    table_scan<P * NW>(tab, rounds * NW);
-    __syncthreads();
-    double smin = __longlong_as_double(0x7FF0000000000000ll), smax = -smin;
-    for (unsigned b = gm; b; b &= b - 1u) {
-      const int u = (__ffs((int)b) - 1) * TOPK_THREADS + tid;
-      const double s = exact_score(qrow, kb + (long long)u * D);
-      smin = s < smin ? s : smin;
-      smax = s > smax ? s : smax;
-    }
-    block_minmax(smin, smax, wred_d);
-    const bool all_equal = smin == smax;  // then the rank is the index rank
-    double* chunk = (double*)hist;
-    static_assert(sizeof(hist) >= TOPK_RANK_CHUNK * sizeof(double), "rank chunk fits the histogram");
-    for (unsigned c0 = 0; c0 < (all_equal ? 0u : ng); c0 += TOPK_RANK_CHUNK) {
-      // the scores of group positions [c0, c0 + cn) into LDS; then every
-      // member adds the chunk's members ranked before it to its running
-      // count, kept in its own slot of this row's rank area
-      const unsigned cn = min((unsigned)TOPK_RANK_CHUNK, ng - c0);
-      __syncthreads();
-      for (int i = 0; i < rounds; ++i) {
-        const bool eq = (gm >> i) & 1u;
-        const unsigned long long be = __ballot(eq);
-        const unsigned pos = tab[i * NW + wave] + (unsigned)__popcll(be & below_lanes);
-        if (eq && pos >= c0 && pos < c0 + cn)
-          chunk[pos - c0] = exact_score(qrow, kb + (long long)(i * TOPK_THREADS + tid) * D);
-      }
-      __syncthreads();
-      for (int i = 0; i < rounds; ++i) {
-        const bool eq = (gm >> i) & 1u;
-        const unsigned long long be = __ballot(eq);
-        const unsigned pos = tab[i * NW + wave] + (unsigned)__popcll(be & below_lanes);
-        if (eq) {
-          const int u = i * TOPK_THREADS + tid;
-          const double s = exact_score(qrow, kb + (long long)u * D);
-          unsigned r = 0u;
-          for (unsigned j = 0; j < cn; ++j) {
-            const double sj = chunk[j];
-            r += (sj > s || (sj == s && c0 + j < pos)) ? 1u : 0u;
-          }
-          rank_row[u] = c0 == 0 ? r : rank_row[u] + r;
-        }
-      }
-    }
-    for (int i = 0; i < rounds; ++i) {
-      const bool eq = (gm >> i) & 1u;
-      const unsigned long long be = __ballot(eq);
-      const unsigned pos = tab[i * NW + wave] + (unsigned)__popcll(be & below_lanes);
-      const int u = i * TOPK_THREADS + tid;
-      if (eq && (all_equal ? pos : rank_row[u]) < gwant) atomicOr(&gbits[u >> 5], 1u << (u & 31));
-    }
-    __syncthreads();
-  }
-
-  // The kept tiles: keys above K*, and those with key K* (all of them, or
-  // the ranked ones marked in gbits when the group straddles the cut).
-  // Lane i of each wave holds round i's count, then its output offset.
-  unsigned need_t = 0u, need_b = 0u;  // slots whose fp64 score the gap needs
-  auto emit = [&](auto take) {
-    unsigned cntv = 0u;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      if (TOPK_SKIP(i)) continue;
-      const unsigned c = (unsigned)__popcll(__ballot(take(i, opaque(kv[i]))));
-      cntv = lane == i ? c : cntv;
-    }
-    if (lane < rounds) tab[lane * NW + wave] = cntv;
-    __syncthreads();
-    table_scan<P * NW>(tab, rounds * NW);
-    __syncthreads();
-    const unsigned basev = lane < rounds ? tab[lane * NW + wave] : 0u;
-    unsigned maskv = 0u, below_key = 0u;  // below_key: greatest key not kept
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      if (TOPK_SKIP(i)) continue;
-      const int u = i * TOPK_THREADS + tid;
-      const unsigned x = opaque(kv[i]);
-      const bool tk = take(i, x);
-      const unsigned long long bt = __ballot(tk);
-      // lanes 2i and 2i+1 hold this round's two bitmap words
-      maskv = lane == 2 * i ? (unsigned)bt : lane == 2 * i + 1 ? (unsigned)(bt >> 32) : maskv;
-      const unsigned pos = (unsigned)__builtin_amdgcn_readlane((int)basev, i) + (unsigned)__popcll(bt & below_lanes);
-      if (tk && pos < (unsigned)k) selrow[pos] = u;
-      below_key = TOPK_VALID(i) && !tk && x > below_key ? x : below_key;
-    }
-    {
-      const int word = (lane >> 1) * (TOPK_THREADS / 32) + wave * 2 + (lane & 1);
-      if (lane < 2 * rounds && word < nwords) maskrow[word] = maskv;
-    }
-    if (gap) {
-      unsigned dummy = 0u;
-      block_minmax(dummy, below_key, wred_u);
-#pragma unroll
-      for (int i = 0; i < P; ++i) {
-        if (TOPK_SKIP(i)) continue;
-        const unsigned x = opaque(kv[i]);
-        const bool tk = take(i, x);
-        need_t |= (tk && x == kstar ? 1u : 0u) << i;
-        need_b |= (TOPK_VALID(i) && !tk && x == below_key ? 1u : 0u) << i;
-      }
-    }
-  };
-  if (!straddle)
-    emit([&](int i, unsigned x) -> bool { return TOPK_VALID(i) & (x >= kstar); });
-  else
-    emit([&](int i, unsigned x) -> bool {
-      const int u = i * TOPK_THREADS + tid;
-      return TOPK_VALID(i) & ((x > kstar) | ((x == kstar) & (((gbits[u >> 5] >> (u & 31)) & 1u) != 0u)));
-    });
-
-  if (gap) {
-    // the k-th ranked fp64 score (least kept score with key K*) and the
-    // (k+1)-th (greatest score among the unkept tiles holding the greatest
-    // unkept key), both recomputed
-    double st = __longlong_as_double(0x7FF0000000000000ll), sb = -st;
-    for (unsigned b = need_t | need_b; b; b &= b - 1u) {
-      const int i = __ffs((int)b) - 1;
-      const double s = exact_score(qrow, kb + (long long)(i * TOPK_THREADS + tid) * D);
-      if ((need_t >> i) & 1u) st = s < st ? s : st;
-      else sb = s > sb ? s : sb;
-    }
-    block_minmax(st, sb, wred_d);
+  if (ge > want) {  // the tiles with key K* straddle the cut
     if (tid == 0) {
+      info[blockIdx.x * TOPK_INFO] = 1u;
+      info[blockIdx.x * TOPK_INFO + 1] = kstar;
+      info[blockIdx.x * TOPK_INFO + 2] = want - gt;
+      info[blockIdx.x * TOPK_INFO + 3] = ge - gt;
+    }
+    return;
+  }
+  if (tid == 0) info[blockIdx.x * TOPK_INFO] = 0u;
+
+  // every key at or above K* is kept
+  unsigned below = topk_emit<PMIN, P>(kv, vmask, rounds, k, nwords, tab, selrow, maskrow,
+                                      [&](int i, unsigned x) -> bool { return TOPK_VALID(i) & (x >= kstar); });
+  if (gap) {
+    // Relative gap between the k-th and (k+1)-th ranked scores from their
+    // fp32-rounded values, K* and the greatest unkept key (different keys:
+    // within 1.2e-7 of the fp64 gap)
+    if (gathered && ge < cnt) {
+      below = sh_below;
+    } else {  // no candidate below K*: over all keys
+      unsigned dummy = 0u;
+      block_minmax(dummy, below, wred_u);
+    }
+    if (tid == 0) {
+      const double st = (double)key_f32(kstar), sb = (double)key_f32(below);
       const double den = fmax(fmax(fabs(st), fabs(sb)), 1e-300);
       gap[(long long)h * T + t] = fabs(st - sb) / den;
     }
   }
+}
+
+// grid (nq), block 1024: the rows that topk_kernel left, those where the
+// ng tiles with key K* straddle the cut. Of those tiles the gwant first by
+// (fp64 score descending, tile index ascending) are kept: their fp64 scores
+// are recomputed, and ranked by tile index alone when all are equal, else
+// pairwise in LDS chunks (a running count per tile in this row's rank
+// area). Other rows return at once.
+template <int PMIN, int P>
+__global__ void __launch_bounds__(TOPK_THREADS) topk_resolve_kernel(
+    Geom g, int h, int t0, int k, const unsigned* __restrict__ keys, const unsigned* __restrict__ info,
+    unsigned* __restrict__ ranks, const double* __restrict__ qbar, const double* __restrict__ kbar,
+    int* __restrict__ sel, unsigned* __restrict__ selmask, double* __restrict__ gap) {
+  constexpr int NW = TOPK_NW;
+  if (info[blockIdx.x * TOPK_INFO] == 0u) return;
+  const unsigned kstar = info[blockIdx.x * TOPK_INFO + 1], gwant = info[blockIdx.x * TOPK_INFO + 2];
+  const unsigned ng = info[blockIdx.x * TOPK_INFO + 3];
+  __shared__ __attribute__((aligned(16))) double chunk[TOPK_RANK_CHUNK];
+  __shared__ unsigned tab[P * NW];
+  __shared__ unsigned gbits[P * TOPK_THREADS / 32];
+  __shared__ double wred_d[2 * NW];
+  __shared__ double sh_st, sh_sb;
+  __shared__ double qs[D];  // the query tile's mean query
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = t0 + blockIdx.x;
+  const int T = g.T;
+  const int nwords = (T + 31) / 32;
+  const int rounds = (T + TOPK_THREADS - 1) / TOPK_THREADS;
+  const unsigned* row = keys + (long long)blockIdx.x * T;
+  unsigned* rank_row = ranks + (long long)blockIdx.x * T;
+  int* selrow = sel + ((long long)h * T + t) * k;
+  unsigned* maskrow = selmask + ((long long)h * T + t) * nwords;
+  const double* kb = kbar + (long long)h * T * D;
+  const unsigned long long below_lanes = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  if (tid < D) qs[tid] = qbar[((long long)h * T + t) * D + tid];
+
+  unsigned kv[P];
+  const unsigned vmask = topk_load(row, T, kv);
+  // gm: this thread's rounds holding K*; pos: a member's rank by tile index
+  unsigned gm = 0u;
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+    if (!TOPK_SKIP(i) && TOPK_VALID(i) && kv[i] == kstar) gm |= 1u << i;
+  for (int w = tid; w < P * TOPK_THREADS / 32; w += TOPK_THREADS) gbits[w] = 0u;
+  for (int i = 0; i < rounds; ++i) {
+    const unsigned long long be = __ballot((gm >> i) & 1u);
+    if (lane == 0) tab[i * NW + wave] = (unsigned)__popcll(be);
+  }
+  __syncthreads();
+  table_scan<P * NW>(tab, rounds * NW);
+  __syncthreads();
+  double smin = __longlong_as_double(0x7FF0000000000000ll), smax = -smin;
+  for (unsigned b = gm; b; b &= b - 1u) {
+    const int u = (__ffs((int)b) - 1) * TOPK_THREADS + tid;
+    const double s = exact_score(qs, kb + (long long)u * D);
+    smin = s < smin ? s : smin;
+    smax = s > smax ? s : smax;
+  }
+  block_minmax(smin, smax, wred_d);
+  const bool all_equal = smin == smax;  // then the rank is the index rank
+  for (unsigned c0 = 0; c0 < (all_equal ? 0u : ng); c0 += TOPK_RANK_CHUNK) {
+    // the scores of group positions [c0, c0 + cn) into LDS; then every
+    // member adds the chunk's members ranked before it to its running count
+    const unsigned cn = min((unsigned)TOPK_RANK_CHUNK, ng - c0);
+    __syncthreads();
+    for (int i = 0; i < rounds; ++i) {
+      const bool eq = (gm >> i) & 1u;
+      const unsigned long long be = __ballot(eq);
+      const unsigned pos = tab[i * NW + wave] + (unsigned)__popcll(be & below_lanes);
+      if (eq && pos >= c0 && pos < c0 + cn)
+        chunk[pos - c0] = exact_score(qs, kb + (long long)(i * TOPK_THREADS + tid) * D);
+    }
+    __syncthreads();
+    for (int i = 0; i < rounds; ++i) {
+      const bool eq = (gm >> i) & 1u;
+      const unsigned long long be = __ballot(eq);
+      const unsigned pos = tab[i * NW + wave] + (unsigned)__popcll(be & below_lanes);
+      if (eq) {
+        const int u = i * TOPK_THREADS + tid;
+        const double s = exact_score(qs, kb + (long long)u * D);
+        unsigned r = 0u;
+        for (unsigned j = 0; j < cn; ++j) {
+          const double sj = chunk[j];
+          r += (sj > s || (sj == s && c0 + j < pos)) ? 1u : 0u;
+        }
+        rank_row[u] = c0 == 0 ? r : rank_row[u] + r;
+      }
+    }
+  }
+  for (int i = 0; i < rounds; ++i) {
+    const bool eq = (gm >> i) & 1u;
+    const unsigned long long be = __ballot(eq);
+    const unsigned pos = tab[i * NW + wave] + (unsigned)__popcll(be & below_lanes);
+    const int u = i * TOPK_THREADS + tid;
+    const unsigned r = all_equal ? pos : (eq ? rank_row[u] : 0u);
+    if (eq && r < gwant) atomicOr(&gbits[u >> 5], 1u << (u & 31));
+    // the k-th and (k+1)-th ranked scores are the group's gwant-th and
+    // (gwant+1)-th (ng > gwant)
+    if (gap && eq && (r == gwant - 1u || r == gwant)) {
+      const double sc = all_equal ? smin : exact_score(qs, kb + (long long)u * D);
+      if (r == gwant - 1u) sh_st = sc;
+      else sh_sb = sc;
+    }
+  }
+  __syncthreads();
+  topk_emit<PMIN, P>(kv, vmask, rounds, k, nwords, tab, selrow, maskrow, [&](int i, unsigned x) -> bool {
+    const int u = i * TOPK_THREADS + tid;
+    return TOPK_VALID(i) & ((x > kstar) | ((x == kstar) & (((gbits[u >> 5] >> (u & 31)) & 1u) != 0u)));
+  });
+  if (gap && tid == 0) {
+    const double st = sh_st, sb = sh_sb;
+    const double den = fmax(fmax(fabs(st), fabs(sb)), 1e-300);
+    gap[(long long)h * T + t] = fabs(st - sb) / den;
+  }
+}
 #undef TOPK_VALID
 #undef TOPK_SKIP
-}
 
 size_t select_chunk(const Geom& g) { return (size_t)(g.T < SELECT_CHUNK ? g.T : SELECT_CHUNK); }
 
 size_t select_workspace_bytes(const Geom& g) {
-  return (size_t)g.H * g.T * D * sizeof(double) + 2 * select_chunk(g) * (size_t)g.T * sizeof(unsigned);
+  return (size_t)g.H * g.T * D * sizeof(double) + 2 * select_chunk(g) * (size_t)g.T * sizeof(unsigned) +
+         select_chunk(g) * TOPK_INFO * sizeof(unsigned);
 }
 
-// Workspace: qbar [H][T][64] fp64, then the score keys [chunk][T] u32, then
-// the rank area [chunk][T] u32 (touched only for tie groups that straddle
-// the cut).
+// Workspace: qbar [H][T][64] fp64, the score keys [chunk][T] u32, the rank
+// area [chunk][T] u32 (touched only for tie groups that straddle the cut),
+// then the per-row records [chunk][4] u32.
 hipError_t launch_select(const Geom& g, int k, const u16* Q, const double* kbar, int* sel,
                          unsigned* selmask, double* gap, void* ws, hipStream_t s) {
   double* qbar = (double*)ws;
   const int chunk = (int)select_chunk(g);
   unsigned* keys = (unsigned*)(qbar + (size_t)g.H * g.T * D);
   unsigned* ranks = keys + (size_t)chunk * g.T;
+  unsigned* info = ranks + (size_t)chunk * g.T;
   const int rounds = (g.T + TOPK_THREADS - 1) / TOPK_THREADS;
   auto topk = rounds <= 4    ? topk_kernel<1, 4>
               : rounds <= 16 ? topk_kernel<5, 16>
               : rounds <= 25 ? topk_kernel<17, 25>
                              : topk_kernel<26, TOPK_MAX_ROUNDS>;
+  auto resolve = rounds <= 4    ? topk_resolve_kernel<1, 4>
+                 : rounds <= 16 ? topk_resolve_kernel<5, 16>
+                 : rounds <= 25 ? topk_resolve_kernel<17, 25>
+                                : topk_resolve_kernel<26, TOPK_MAX_ROUNDS>;
   hipLaunchKernelGGL(qbar_kernel, dim3(g.T, g.H), dim3(64), 0, s, g, Q, qbar);
   for (int h = 0; h < g.H; ++h) {
     for (int t0 = 0; t0 < g.T; t0 += chunk) {
@@ -616,8 +679,11 @@ hipError_t launch_select(const Geom& g, int k, const u16* Q, const double* kbar,
       if (k > 0 && k < g.T)
         hipLaunchKernelGGL(scores_kernel, dim3((g.T + 63) / 64, (nq + 63) / 64), dim3(256), 0, s,
                            g, h, t0, nq, qbar, kbar, keys);
-      hipLaunchKernelGGL(topk, dim3(nq), dim3(TOPK_THREADS), 0, s, g, h, t0, k, keys, ranks, qbar,
-                         kbar, sel, selmask, gap);
+      hipLaunchKernelGGL(topk, dim3(nq), dim3(TOPK_THREADS), 0, s, g, h, t0, k, keys, info, sel, selmask,
+                         gap);
+      if (k > 0 && k < g.T)
+        hipLaunchKernelGGL(resolve, dim3(nq), dim3(TOPK_THREADS), 0, s, g, h, t0, k, keys, info, ranks,
+                           qbar, kbar, sel, selmask, gap);
     }
   }
   return hipGetLastError();

@@ -56,78 +56,129 @@ __device__ inline float key_f32(unsigned k) {
 }
 
 // Scores of query tiles [t0, t0+nq) of head h against every key tile:
-// out[tq][u] = (sum_d qbar[t0+tq][d] * kbar[u][d]) * 0.125, on the fp64
-// matrix cores. grid (ceil(T/64), ceil(nq/64)), block 256: a 64 x 64 tile,
-// wave w its 32 x 32 quarter (rows 32 (w >> 1), columns 32 (w & 1)) as 2 x 2
-// 16x16x4 MFMA tiles over the 16 steps of 4 channels. Both operands sit in
-// LDS row-major with a row stride of 68 doubles, so that a step's 64 lane
-// reads (16 rows x 4 channels) cover the 64 banks twice.
-constexpr int SC_LD = D + 4;
-__global__ void __launch_bounds__(256) scores_kernel(Geom g, int h, int t0, int nq,
+// out[tq][u] = key((sum_d qbar[t0+tq][d] * kbar[u][d]) * 0.125), the products
+// on the fp64 matrix cores, rounded to fp32 order keys on the way out.
+//
+// grid (key-tile ranges, ceil(nq/128)), block 512: a workgroup keeps a
+// block of 128 query rows in LDS and walks its range of 64-wide key tiles;
+// wave w computes the 32 x 32 part (rows 32 (w >> 1), columns 32 (w & 1)) of
+// each as 2 x 2 16x16x4 MFMA tiles over the 16 steps of 4 channels (two
+// waves per SIMD, so one's stores and waits run under the other's matrix
+// work). Key tiles
+// stream into two LDS buffers by async 16-byte global-to-LDS copies, one
+// tile ahead of the one being multiplied, so the copies run under the
+// matrix work. A key tile row is 32 16-byte chunks, chunk c stored at slot
+// c ^ (row % 16): the 16 rows that a step reads then fall on different
+// banks (in the query block a row stride of 68 doubles does that). A tile's
+// keys are stored while the next tile is multiplied, so the full wait at
+// the start of a tile finds only copies and stores issued a tile earlier.
+// Rows past the end repeat the last row (their scores are not stored).
+constexpr int SC_LD = D + 4;        // query block row stride (doubles)
+constexpr int SC_KT = 64 * D;       // one key tile (doubles)
+constexpr int SC_QB = 128;          // query rows per workgroup
+constexpr int SC_WAVES = SC_QB / 16;  // each 32 x 32 of the 128 x 64 block
+constexpr int SC_TARGET_WGS = 256;  // one workgroup per CU
+typedef void __attribute__((address_space(3))) sc_lds_void;
+
+__global__ void __launch_bounds__(SC_WAVES * 64) scores_kernel(Geom g, int h, int t0, int nq, int tiles_per_wg,
                                                      const double* __restrict__ qbar,
                                                      const double* __restrict__ kbar,
                                                      unsigned* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) double qs[64 * SC_LD];
-  __shared__ __attribute__((aligned(16))) double ks[64 * SC_LD];
+  __shared__ __attribute__((aligned(16))) double qs[SC_QB * SC_LD];
+  __shared__ __attribute__((aligned(1024))) double kt0[SC_KT];
+  __shared__ __attribute__((aligned(1024))) double kt1[SC_KT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int u0 = blockIdx.x * 64, q0 = blockIdx.y * 64;
+  const int q0 = blockIdx.y * SC_QB;
+  const int nut = (g.T + 63) / 64;
+  const int ut0 = blockIdx.x * tiles_per_wg, ut1 = min(nut, ut0 + tiles_per_wg);
   const double* qb = qbar + ((long long)h * g.T + t0) * D;
   const double* kb = kbar + (long long)h * g.T * D;
+  // key tile ut into dst: wave w's copy j fills slots (8j + w) * 64 + lane,
+  // that is row r = 2 (8j + w) + lane / 32, slot lane % 32
+  auto stage = [&](int ut, double* dst) {
+#pragma unroll
+    for (int j = 0; j < 32 / SC_WAVES; ++j) {
+      const int r = 2 * (SC_WAVES * j + wave) + (lane >> 5), slot = lane & 31;
+      const double* src = kb + (long long)min(ut * 64 + r, g.T - 1) * D + 2 * (slot ^ (r & 15));
+      __builtin_amdgcn_global_load_lds((const void*)src, (sc_lds_void*)(dst + (SC_WAVES * j + wave) * 128), 16, 0,
+                                       0);
+    }
+  };
+  if (ut0 < ut1) stage(ut0, kt0);
   {
-    // thread: row tid / 4, doubles 16 (tid % 4) .. +15 of both tiles; all
-    // sixteen 16-byte loads are issued before the first LDS write. Rows past
-    // the end repeat the last row (their outputs are not stored).
+    // the query block: thread row tid / 4, doubles 16 (tid % 4) .. +15
     const int r = tid >> 2, c0 = (tid & 3) * 16;
     const uint4* qsrc = (const uint4*)(qb + (long long)min(q0 + r, nq - 1) * D + c0);
-    const uint4* ksrc = (const uint4*)(kb + (long long)min(u0 + r, g.T - 1) * D + c0);
-    uint4 qv[8], kv[8];
+    uint4 qv[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      qv[c] = qsrc[c];
-      kv[c] = ksrc[c];
-    }
+    for (int c = 0; c < 8; ++c) qv[c] = qsrc[c];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      *(uint4*)(qs + r * SC_LD + c0 + 2 * c) = qv[c];
-      *(uint4*)(ks + r * SC_LD + c0 + 2 * c) = kv[c];
-    }
+    for (int c = 0; c < 8; ++c) *(uint4*)(qs + r * SC_LD + c0 + 2 * c) = qv[c];
   }
-  __syncthreads();
   const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
   const int m = lane & 15, kq = lane >> 4;
-  f64x4 acc[2][2];
+  // keys of the previous tile, stored while the next one is multiplied:
+  // pend[(i * 4 + r) * 2 + j] is query row wr + 16 i + 4 r + kq, key column
+  // wc + 16 j + m (the f64 MFMA's output element r of lane l is row 4 r + l / 16)
+  unsigned pend[16];
+  int pend_ut = -1;
+  auto flush = [&]() {
+    if (pend_ut < 0) return;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-  for (int s4 = 0; s4 < D / 4; ++s4) {
-    const int k = 4 * s4 + kq;
-    double a[2], b[2];
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      a[i] = qs[(wr + 16 * i + m) * SC_LD + k];
-      b[i] = ks[(wc + 16 * i + m) * SC_LD + k];
+        for (int j = 0; j < 2; ++j) {
+          const int q = q0 + wr + 16 * i + 4 * r + kq;
+          const int u = pend_ut * 64 + wc + 16 * j + m;
+          if (q < nq && u < g.T) out[(long long)q * g.T + u] = pend[(i * 4 + r) * 2 + j];
+        }
+  };
+  auto tile = [&](int ut, const double* cur, double* ahead) {
+    // this tile's copies (issued a tile ago) and the stores of two tiles ago
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();  // ... in every wave; the previous tile's buffer is free
+    if (ut + 1 < ut1) stage(ut + 1, ahead);
+    flush();
+    f64x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    // all 16 steps unrolled: with a loop the accumulators would be copied
+    // out of and back into the matrix registers, draining the pipe, each trip
+#pragma unroll
+    for (int s4 = 0; s4 < D / 4; ++s4) {
+      const int k = 4 * s4 + kq;
+      const int slot = ((k >> 1) ^ m) * 2 + (k & 1);  // key rows wc + 16 i + m: row % 16 = m
+      double a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = qs[(wr + 16 * i + m) * SC_LD + k];
+        b[i] = cur[(wc + 16 * i + m) * D + slot];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) pend[(i * 4 + r) * 2 + j] = f32_key((float)(acc[i][j][r] * 0.125));
+    pend_ut = ut;
+  };
+  // the loop over the two buffers, unrolled so that every LDS read names
+  // its buffer (and the compiler need not wait for copies into the other)
+  for (int ut = ut0; ut < ut1; ut += 2) {
+    tile(ut, kt0, kt1);
+    if (ut + 1 < ut1) tile(ut + 1, kt1, kt0);
   }
-  // acc[i][j][r]: query row wr + 16 i + 4 r + kq, key column wc + 16 j + m
-  // (the f64 MFMA's output element r of lane l is row 4 r + l / 16)
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int q = q0 + wr + 16 * i + 4 * r + kq;
-      if (q >= nq) continue;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int u = u0 + wc + 16 * j + m;
-        if (u < g.T) out[(long long)q * g.T + u] = f32_key((float)(acc[i][j][r] * 0.125));
-      }
-    }
+  flush();
 }
 
 constexpr int TOPK_THREADS = 1024;
@@ -676,9 +727,13 @@ hipError_t launch_select(const Geom& g, int k, const u16* Q, const double* kbar,
   for (int h = 0; h < g.H; ++h) {
     for (int t0 = 0; t0 < g.T; t0 += chunk) {
       const int nq = g.T - t0 < chunk ? g.T - t0 : chunk;
-      if (k > 0 && k < g.T)
-        hipLaunchKernelGGL(scores_kernel, dim3((g.T + 63) / 64, (nq + 63) / 64), dim3(256), 0, s,
-                           g, h, t0, nq, qbar, kbar, keys);
+      if (k > 0 && k < g.T) {
+        // about one workgroup per CU, each over an equal range of key tiles
+        const int nut = (g.T + 63) / 64, nqb = (nq + SC_QB - 1) / SC_QB;
+        const int per = (nut * nqb + SC_TARGET_WGS - 1) / SC_TARGET_WGS;
+        hipLaunchKernelGGL(scores_kernel, dim3((nut + per - 1) / per, nqb), dim3(SC_WAVES * 64), 0, s, g, h, t0, nq,
+                           per, qbar, kbar, keys);
+      }
       hipLaunchKernelGGL(topk, dim3(nq), dim3(TOPK_THREADS), 0, s, g, h, t0, k, keys, info, sel, selmask,
                          gap);
       if (k > 0 && k < g.T)

@@ -8,10 +8,11 @@
 // affine correction y = mu + W (o - mu) + b is applied to the output.
 //
 // Four kernels:
-//   linear_state  stream K and V once: phi(k) for 16 tokens per wave pass,
-//                 staged with V in LDS, then S += phi(K)^T V (bf16 MFMA,
-//                 fp32 accumulators) and z += phi(k); one partial per
-//                 workgroup (its waves added in a fixed order).
+//   linear_state  stream K and V once through per-wave LDS rings: phi(k)
+//                 for 16 tokens per group, written back in place, then
+//                 S += phi(K)^T V (bf16 MFMA on transposing LDS reads, fp32
+//                 accumulators) and z += phi(k); one partial per workgroup
+//                 (its waves added in a fixed order).
 //   linear_sum    fixed-order fp64 sum of the partials, one element per
 //                 thread over all of a head's partials;
 //   linear_fold   S' = S W^T split into bf16 high/low parts and
@@ -88,10 +89,12 @@ __device__ inline void token_pos(const Geom& g, const PosDiv& dv, long long tok,
 // Feature map of one token's 16 lane channels (x holds them, fp32, in
 // lane order). On return x holds phi(x) for those channels, or, with
 // NORMALIZE false, phi(x) times a positive per-token constant (enough where
-// phi only enters a ratio). `gained`: multiply by the RMSNorm gains.
+// phi only enters a ratio). `gained`: multiply by the RMSNorm gains. cr[i]
+// and cc[i] are the rotary {cos, sin} of channel pair 4g + i at the token's
+// patch row and column.
 template <bool NORMALIZE>
-__device__ inline void featurize16(float x[16], bool gained, const float gain[16], const float2* tab, int pr,
-                                   int pc, int g, float eps) {
+__device__ inline void featurize16_rot(float x[16], bool gained, const float gain[16], const float2 cr[4],
+                                       const float2 cc[4], float eps) {
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) ss += x[i] * x[i];
@@ -105,15 +108,12 @@ __device__ inline void featurize16(float x[16], bool gained, const float gain[16
   // rotary: pairs (i, i+4) for i in 0..3 (row) and 8..11 (column)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int j = 4 * g + i;
-    const float2 cr = tab[pr * 16 + j];
-    const float2 cc = tab[pc * 16 + j];
     const float a = x[i], b = x[i + 4];
-    x[i] = a * cr.x - b * cr.y;
-    x[i + 4] = b * cr.x + a * cr.y;
+    x[i] = a * cr[i].x - b * cr[i].y;
+    x[i + 4] = b * cr[i].x + a * cr[i].y;
     const float a2 = x[i + 8], b2 = x[i + 12];
-    x[i + 8] = a2 * cc.x - b2 * cc.y;
-    x[i + 12] = b2 * cc.x + a2 * cc.y;
+    x[i + 8] = a2 * cc[i].x - b2 * cc[i].y;
+    x[i + 12] = b2 * cc[i].x + a2 * cc[i].y;
   }
   float m = x[0];
 #pragma unroll
@@ -133,6 +133,19 @@ __device__ inline void featurize16(float x[16], bool gained, const float gain[16
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] *= inv;
   }
+}
+
+// The same with the rotary values read from the table tab[p][j] = {cos, sin}.
+template <bool NORMALIZE>
+__device__ inline void featurize16(float x[16], bool gained, const float gain[16], const float2* tab, int pr,
+                                   int pc, int g, float eps) {
+  float2 cr[4], cc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    cr[i] = tab[pr * 16 + 4 * g + i];
+    cc[i] = tab[pc * 16 + 4 * g + i];
+  }
+  featurize16_rot<NORMALIZE>(x, gained, gain, cr, cc, eps);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -187,15 +200,31 @@ __device__ inline void unpack16(const uint2 w[4], float x[16]) {
 
 // grid (nchunks, H), block 256. Partial p = chunk holds
 // S [64][64] (row a = phi channel, column c = value channel) then z [64].
-__global__ void __launch_bounds__(LIN_THREADS, 2) linear_state_kernel(
+//
+// Each wave streams its 16-token groups of K and V (group m: tokens
+// first + 64 m .. +15, first = t_begin + 16 w) through a private LDS ring of
+// ST_NB slots, ST_NB - 1 groups ahead, by async 16-byte copies; no workgroup
+// barrier in the loop. A slot holds the group's K rows then its V rows,
+// token-major, a 128-byte row as eight 16-byte chunks, chunk c of row r at
+// slot c ^ ls_swz(r) (both access patterns below then spread over the
+// banks). The K rows are read in the feature-map lane layout (one token per
+// 4 lanes), turned into phi(k) (bf16) and written back in place; then
+// S += phi^T V with 16 bf16 MFMAs (16x16x16, k = token) whose operands, 4
+// consecutive tokens of one channel per lane, come from transposing LDS
+// reads. The ring is read and written by inline asm that waits on LDS
+// only: as plain accesses the compiler would first wait for every copy in
+// flight into the ring. The workgroup adds its waves' states in wave order.
+constexpr int ST_NB = 4;       // LDS ring slots per wave
+constexpr int ST_SLOT = 4096;  // bytes per slot: 16 K rows, then 16 V rows
+__device__ inline int ls_swz(int r) { return (r ^ (r >> 2)) & 7; }
+typedef short st_v4s __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
     Geom g, LinParams P, const u16* __restrict__ K, const u16* __restrict__ V,
     const float* __restrict__ gk, float* __restrict__ partials, int nchunks, int tpw) {
   float2* tab = rope_tab;
-  // phi(k) and v of a wave's 32 tokens, channel-major ([channel][token],
-  // rows of 40 u16 = 80 bytes): an MFMA operand fragment (one channel, 8
-  // consecutive tokens) is one 16-byte read
-  __shared__ __attribute__((aligned(16))) u16 phis[LIN_WAVES][D][40];
-  __shared__ __attribute__((aligned(16))) u16 vals[LIN_WAVES][D][40];
+  __shared__ __attribute__((aligned(1024))) char sring[LIN_WAVES][ST_NB][ST_SLOT];
+  static_assert(sizeof(sring) >= LIN_STATE * sizeof(float), "the partial fits the rings");
   const int h = blockIdx.y, chunk = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, tl = lane & 15;
@@ -204,8 +233,6 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_state_kernel(
   float gain[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) gain[i] = gk ? gk[h * D + lane_channel(grp, i)] : 1.0f;
-  __syncthreads();
-
   f32x4 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -214,73 +241,124 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_state_kernel(
   float zacc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) zacc[i] = 0.f;
+  __syncthreads();  // the rotary table
 
   const long long t_begin = (long long)chunk * tpw;
   const long long t_end = min((long long)g.N, t_begin + tpw);
   const long long rs = (long long)g.H * D;
-  constexpr int STRIDE = 32 * LIN_WAVES;
-  // raw K and V of the wave's 32 tokens: this iteration's and the next's
-  // (requested one iteration ahead so the wave always has loads in flight)
-  uint2 kc[2][4], vc[2][4];
-  auto fetch = [&](long long t0, uint2 kr[2][4], uint2 vr[2][4]) {
+  const long long first = t_begin + 16 * wave;
+  const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
+  char* ring = &sring[wave][0][0];
+  // group m into slot m % ST_NB: copy j of each of K and V fills row
+  // 8j + lane/8, slot lane % 8 (chunk (lane % 8) ^ ls_swz(row)). Rows past
+  // t_end repeat the last token (their phi is zeroed). Every lane issues all
+  // four copies, so the wave's memory counter advances by 4 per group.
+  auto stage = [&](int m) {
+    const long long r0 = first + 64LL * m;
+    char* dst = ring + (m % ST_NB) * ST_SLOT;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const long long tok = t0 + pass * 16 + tl;
-      fetch16(K + tok * rs + h * D, grp, tok < t_end, kr[pass]);
-      fetch16(V + tok * rs + h * D, grp, tok < t_end, vr[pass]);
+    for (int j = 0; j < 2; ++j) {
+      const int r = 8 * j + (lane >> 3);
+      const long long tok = min(r0 + r, t_end - 1);
+      const long long off = (tok * rs + h * D) * 2 + (((lane & 7) ^ ls_swz(r)) << 4);
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)K + off), (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)V + off), (lin_lds_void*)(dst + 2048 + j * 1024), 16,
+                                       0, 0);
     }
   };
-  fetch(t_begin + wave * 32, kc, vc);
-  for (long long t0 = t_begin + wave * 32; t0 < t_end; t0 += STRIDE) {
-    uint2 kn[2][4], vn[2][4];
-    fetch(t0 + STRIDE, kn, vn);
+  for (int m = 0; m < ST_NB - 1 && m < n; ++m) stage(m);
+  for (int m = 0; m < n; ++m) {
+    // group m has landed once at most the newer groups' copies are pending
+    lin_wait_vm(4 * min(ST_NB - 2, n - 1 - m));
+    asm volatile("" ::: "memory");
+    const unsigned sb = (unsigned)(size_t)(ring + (m % ST_NB) * ST_SLOT);
+    // this lane's K row pieces: token tl, channels 16q + 4 grp .. +3 =
+    // chunk 2q + grp/2, half grp % 2
+    unsigned ka[4];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int slot = pass * 16 + tl;
-      const long long tok = t0 + slot;
-      float x[16];
-      unpack16(kc[pass], x);
-      int pr = 0, pc = 0;
-      if (tok < t_end) token_pos(g, dv, tok, pr, pc);
-      featurize16<true>(x, gk != nullptr, gain, tab, pr, pc, grp, P.eps);
-      if (tok >= t_end) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const unsigned pw = pack_bf16x2(x[i], x[i + 1]);  // round to nearest even
-        zacc[i] += __uint_as_float(pw << 16);
-        zacc[i + 1] += __uint_as_float(pw & 0xFFFF0000u);
-        phis[wave][lane_channel(grp, i)][slot] = (u16)(pw & 0xFFFFu);
-        phis[wave][lane_channel(grp, i + 1)][slot] = (u16)(pw >> 16);
-        const unsigned vw = (i & 2) ? vc[pass][i >> 2].y : vc[pass][i >> 2].x;  // raw bf16 values
-        vals[wave][lane_channel(grp, i)][slot] = (u16)(vw & 0xFFFFu);
-        vals[wave][lane_channel(grp, i + 1)][slot] = (u16)(vw >> 16);
-      }
+    for (int q = 0; q < 4; ++q) ka[q] = sb + tl * 128 + (((2 * q + (grp >> 1)) ^ ls_swz(tl)) << 4) + (grp & 1) * 8;
+    uint2 w4[4];
+    asm volatile(
+        "ds_read_b64 %0, %4\n\t"
+        "ds_read_b64 %1, %5\n\t"
+        "ds_read_b64 %2, %6\n\t"
+        "ds_read_b64 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w4[0]), "=&v"(w4[1]), "=&v"(w4[2]), "=&v"(w4[3])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3])
+        : "memory");
+    const long long tok = first + 64LL * m + tl;
+    float x[16];
+    unpack16(w4, x);
+    int pr = 0, pc = 0;
+    if (tok < t_end) token_pos(g, dv, tok, pr, pc);
+    // the rotary values of pairs 4 grp .. +3 at (pr, pc), by asm for the
+    // same reason as the ring (the table is an extern LDS array)
+    float2 cr[4], cc[4];
+    {
+      const unsigned tr0 = (unsigned)(size_t)(tab + pr * 16 + 4 * grp), tc0 = (unsigned)(size_t)(tab + pc * 16 + 4 * grp);
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:16\n\t"
+          "ds_read_b128 %2, %5\n\t"
+          "ds_read_b128 %3, %5 offset:16\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(*(float4*)&cr[0]), "=&v"(*(float4*)&cr[2]), "=&v"(*(float4*)&cc[0]), "=&v"(*(float4*)&cc[2])
+          : "v"(tr0), "v"(tc0)
+          : "memory");
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS writes done (single wave)
-    __builtin_amdgcn_wave_barrier();
-    // S[a][c] += sum_tok phi[tok][a] * v[tok][c]; k index = token
-    bf16x8 A[4], B[4];
+    featurize16_rot<true>(x, gk != nullptr, gain, cr, cc, P.eps);
+    if (tok >= t_end) {
 #pragma unroll
-    for (int ab = 0; ab < 4; ++ab) {
-      A[ab] = *(const bf16x8*)&phis[wave][ab * 16 + tl][8 * grp];
-      B[ab] = *(const bf16x8*)&vals[wave][ab * 16 + tl][8 * grp];
+      for (int i = 0; i < 16; ++i) x[i] = 0.f;
     }
+    uint2 pw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pw[q].x = pack_bf16x2(x[4 * q], x[4 * q + 1]);  // round to nearest even
+      pw[q].y = pack_bf16x2(x[4 * q + 2], x[4 * q + 3]);
+      zacc[4 * q + 0] += __uint_as_float(pw[q].x << 16);
+      zacc[4 * q + 1] += __uint_as_float(pw[q].x & 0xFFFF0000u);
+      zacc[4 * q + 2] += __uint_as_float(pw[q].y << 16);
+      zacc[4 * q + 3] += __uint_as_float(pw[q].y & 0xFFFF0000u);
+    }
+    // phi in place of the K rows, then the MFMA operands: lane i of each 16
+    // names row 4 grp + i/4, columns 16 b + 4 (i % 4) .. +3 of the phi (A)
+    // or V (B) rows, and receives column 16 b + i of rows 4 grp .. +3
+    unsigned ta[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int row = 4 * grp + (tl >> 2), col = 16 * b + 4 * (tl & 3);
+      ta[b] = sb + row * 128 + (((col >> 3) ^ ls_swz(row)) << 4) + (col & 4) * 2;
+    }
+    uint2 A[4], B[4];
+    asm volatile(
+        "ds_write_b64 %8, %12\n\t"
+        "ds_write_b64 %9, %13\n\t"
+        "ds_write_b64 %10, %14\n\t"
+        "ds_write_b64 %11, %15\n\t"
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %17\n\t"
+        "ds_read_b64_tr_b16 %2, %18\n\t"
+        "ds_read_b64_tr_b16 %3, %19\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %6, %18 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(A[0]), "=&v"(A[1]), "=&v"(A[2]), "=&v"(A[3]), "=&v"(B[0]), "=&v"(B[1]), "=&v"(B[2]), "=&v"(B[3])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(pw[0]), "v"(pw[1]), "v"(pw[2]), "v"(pw[3]),
+          "v"(ta[0]), "v"(ta[1]), "v"(ta[2]), "v"(ta[3])
+        : "memory");
+    // S[16 ab + 4 grp + r][16 cb + tl] += sum over the group's 16 tokens
 #pragma unroll
     for (int ab = 0; ab < 4; ++ab)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
-        acc[ab][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ab], B[cb], acc[ab][cb], 0, 0, 0);
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        kc[pass][q] = kn[pass][q];
-        vc[pass][q] = vn[pass][q];
-      }
+        acc[ab][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(st_v4s, A[ab]),
+                                                                 __builtin_bit_cast(st_v4s, B[cb]), acc[ab][cb], 0, 0,
+                                                                 0);
+    if (m + ST_NB - 1 < n) stage(m + ST_NB - 1);
   }
   // z: sum the 16 lanes of each channel group
 #pragma unroll
@@ -293,9 +371,8 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_state_kernel(
     zacc[i] = v;
   }
   // the workgroup's partial: the 4 waves' states added in wave order in LDS
-  // (over the feature staging area), then written once
-  float* red = (float*)&phis[0][0][0];
-  static_assert(sizeof(phis) >= LIN_STATE * sizeof(float), "partial fits the staging area");
+  // (over the rings, once every wave has left its loop), then written once
+  float* red = (float*)&sring[0][0][0];
   __syncthreads();
   for (int w = 0; w < LIN_WAVES; ++w) {
     if (wave == w) {

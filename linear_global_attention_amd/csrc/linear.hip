@@ -86,6 +86,20 @@ __device__ inline void token_pos(const Geom& g, const PosDiv& dv, long long tok,
   pc = special ? 0 : c;
 }
 
+// Sum / max of v over lane pairs (l, l ^ 16) or (l, l ^ 32) on the VALU
+// (v_permlane16/32_swap give each lane the pair in the same order, so both
+// lanes get the same bits), instead of a cross-lane LDS permute.
+__device__ inline float lin_pair16(float v, bool mx) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return mx ? fmaxf(a, b) : a + b;
+}
+__device__ inline float lin_pair32(float v, bool mx) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return mx ? fmaxf(a, b) : a + b;
+}
+
 // Feature map of one token's 16 lane channels (x holds them, fp32, in
 // lane order). On return x holds phi(x) for those channels, or, with
 // NORMALIZE false, phi(x) times a positive per-token constant (enough where
@@ -98,8 +112,7 @@ __device__ inline void featurize16_rot(float x[16], bool gained, const float gai
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) ss += x[i] * x[i];
-  ss += __shfl_xor(ss, 16, 64);
-  ss += __shfl_xor(ss, 32, 64);
+  ss = lin_pair32(lin_pair16(ss, false), false);
   const float r = __builtin_amdgcn_rsqf(ss * (1.0f / 64.0f) + eps);
   if (gained) {
 #pragma unroll
@@ -118,8 +131,7 @@ __device__ inline void featurize16_rot(float x[16], bool gained, const float gai
   float m = x[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) m = fmaxf(m, x[i]);
-  m = fmaxf(m, __shfl_xor(m, 16, 64));
-  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  m = lin_pair32(lin_pair16(m, true), true);
   const float sc = r * LOG2E, off = -m * sc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_exp2f(fmaf(x[i], sc, off));
@@ -127,8 +139,7 @@ __device__ inline void featurize16_rot(float x[16], bool gained, const float gai
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += x[i];
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
+    s = lin_pair32(lin_pair16(s, false), false);
     const float inv = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] *= inv;
@@ -566,8 +577,7 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
     bf16x8 Bk[2];
     Bk[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
     Bk[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
-    den += __shfl_xor(den, 16, 64);
-    den += __shfl_xor(den, 32, 64);
+    den = lin_pair32(lin_pair16(den, false), false);
     const float inv = __builtin_amdgcn_rcpf(den);
     f32x4 y[4];
 #pragma unroll

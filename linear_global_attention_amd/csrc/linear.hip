@@ -594,29 +594,40 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
     // The 16 x 128-byte output tile goes through this group's ring slot
     // (its queries are already in registers), swizzled as the input, so
     // that each row is stored whole: 8 lanes x 16 bytes per row.
+    // Written and read back in one asm block that waits on LDS only: as
+    // plain stores the compiler would first wait for every copy in flight
+    // into the ring.
     char* slot = ring + (m % AP_NB) * 2048;
+    uint2 w[4];
+    unsigned wa[4];
 #pragma unroll
     for (int eb = 0; eb < 4; ++eb) {
-      uint2 w;
-      w.x = pack_bf16x2(fmaf(y[eb][0], inv, bp[eb * 4 + 0]), fmaf(y[eb][1], inv, bp[eb * 4 + 1]));
-      w.y = pack_bf16x2(fmaf(y[eb][2], inv, bp[eb * 4 + 2]), fmaf(y[eb][3], inv, bp[eb * 4 + 3]));
+      w[eb].x = pack_bf16x2(fmaf(y[eb][0], inv, bp[eb * 4 + 0]), fmaf(y[eb][1], inv, bp[eb * 4 + 1]));
+      w[eb].y = pack_bf16x2(fmaf(y[eb][2], inv, bp[eb * 4 + 2]), fmaf(y[eb][3], inv, bp[eb * 4 + 3]));
       const int c = 2 * eb + (grp >> 1);
-      *(uint2*)(slot + tl * 128 + ((c ^ (tl & 7)) << 4) + (grp & 1) * 8) = w;
+      wa[eb] = (unsigned)(size_t)(slot + tl * 128 + ((c ^ (tl & 7)) << 4) + (grp & 1) * 8);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = 8 * j + (lane >> 3), c = lane & 7;
-      uint4 v;
-      {
-        const unsigned va = (unsigned)(size_t)(slot + r * 128 + ((c ^ (r & 7)) << 4));
-        typedef unsigned u4 __attribute__((ext_vector_type(4)));
-        u4 t;
-        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(t) : "v"(va) : "memory");
-        v = make_uint4(t[0], t[1], t[2], t[3]);
-      }
-      const long long otok = min(first + 64LL * m + r, t_end - 1);
-      *(uint4*)(out + otok * rs + h * D + c * 8) = v;
-    }
+    // row r = 8j + lane/8 of the tile, 16-byte column lane % 8, for j = 0, 1
+    const int rr = lane >> 3, rc = lane & 7;
+    const unsigned ra0 = (unsigned)(size_t)(slot + rr * 128 + ((rc ^ (rr & 7)) << 4));
+    const unsigned ra1 = (unsigned)(size_t)(slot + (rr + 8) * 128 + ((rc ^ ((rr + 8) & 7)) << 4));
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    u4 t0, t1;
+    asm volatile(
+        "ds_write_b64 %2, %6\n\t"
+        "ds_write_b64 %3, %7\n\t"
+        "ds_write_b64 %4, %8\n\t"
+        "ds_write_b64 %5, %9\n\t"
+        "ds_read_b128 %0, %10\n\t"
+        "ds_read_b128 %1, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t0), "=&v"(t1)
+        : "v"(wa[0]), "v"(wa[1]), "v"(wa[2]), "v"(wa[3]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(ra0),
+          "v"(ra1)
+        : "memory");
+    const long long otok0 = min(first + 64LL * m + rr, t_end - 1), otok1 = min(first + 64LL * m + rr + 8, t_end - 1);
+    *(uint4*)(out + otok0 * rs + h * D + rc * 8) = make_uint4(t0[0], t0[1], t0[2], t0[3]);
+    *(uint4*)(out + otok1 * rs + h * D + rc * 8) = make_uint4(t1[0], t1[1], t1[2], t1[3]);
     if (m + AP_NB - 1 < n) stage(m + AP_NB - 1);
   }
 }

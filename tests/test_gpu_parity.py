@@ -334,6 +334,36 @@ def test_selection_exact_ties():
     assert checked >= L.heads * tm.T // 2
 
 
+def test_selection_gap():
+    """The reported gap between the k-th and (k+1)-th ranked scores. Where
+    the two round to different fp32 values it comes from those fp32 values,
+    each within 2^-24 of its fp64 score, so it is within 2.5e-7 of the fp64
+    gap; where they round to the same value both are recomputed in fp64
+    (here: all-zero query tiles, whose scores all tie, gap 0)."""
+    L = zs.Layout(8, 1, 40, 40, heads=2)
+    y = 0.8
+    q, k, v = _inputs(L, seed=14)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    Qf = zs.bf16_to_f32(q).copy()
+    zero_tiles = (3, 77)
+    for t in zero_tiles:
+        Qf[tm.tokens[t]] = 0.0
+    q = zs.f32_to_bf16(Qf)
+    Q, K = widen(q), widen(k)
+    st = Stage(L, q, k, v, y)
+    st.select()
+    gap = st.bufs.gap().cpu().numpy()
+    worst = 0.0
+    for h in range(L.heads):
+        kbar, _, _ = osp.landmarks(K[:, h], K[:, h], tm)
+        _, _, gref = osp.select_tiles(Q[:, h], kbar, tm, y)
+        assert np.all(gap[h, list(zero_tiles)] == 0.0), gap[h, list(zero_tiles)]
+        err = np.abs(gap[h] - gref)
+        worst = max(worst, float(err.max()))
+        assert err.max() <= 2.5e-7, (h, int(err.argmax()), gap[h, err.argmax()], gref[err.argmax()])
+    log(f"gap: max |gpu - oracle| = {worst:.2e} over {L.heads * tm.T} rows")
+
+
 def test_selection_with_outlier_tiles():
     """A few key tiles scaled by 1e4 put their scores far outside the rest,
     so nearly all scores fall into one bin of the first score-uniform

@@ -364,6 +364,44 @@ def test_selection_gap():
     log(f"gap: max |gpu - oracle| = {worst:.2e} over {L.heads * tm.T} rows")
 
 
+@pytest.mark.parametrize("frames,heads", [(8, 2), (88, 1)], ids=["T200", "T2200"])
+def test_selection_fp32_tie_ranked_in_fp64(frames, heads):
+    """Every key token holds the same vector except channel 5, which is 0
+    but for the first token of tiles u < 256, set to a distinct small bf16
+    value eps_u = (1 + j/128) 2^-(20+e) (u = 128 e + j), and query channel 5
+    is 1 on every token. All tile scores then
+    round to one fp32 value (on most rows) while the perturbed ones differ in
+    fp64 by about 1e-12 relative (far above fp64 rounding) and the others tie
+    exactly, so the kept set is decided by the fp64 re-ranking of a tie group
+    that straddles the cut, ties cut by tile index; it must equal the
+    oracle's exactly on every row (no near-tie allowance). With 2,200 tiles
+    the group is ranked in two LDS chunks."""
+    L = zs.Layout(frames, 1, 40, 40, heads=heads)
+    y = 0.8
+    q, k, v = _inputs(L, seed=15)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    Kf = zs.bf16_to_f32(k).copy()
+    base = Kf[0].copy()  # [H][64]
+    base[:, 5] = 0.0
+    Kf[:] = base
+    for u in range(min(tm.T, 256)):
+        j, e = u % 128, u // 128
+        Kf[tm.tokens[u][0], :, 5] = (1.0 + j / 128.0) * 2.0 ** -(20 + e)
+    k = zs.f32_to_bf16(Kf)
+    assert np.array_equal(zs.bf16_to_f32(k), Kf)  # every value exact in bf16
+    # query channel 5 = 1 on every token: the perturbations weigh the same
+    # on every row (spacing >= 2^-28 / 512 between perturbed scores)
+    Qf = zs.bf16_to_f32(q).copy()
+    Qf[:, :, 5] = 1.0
+    q = zs.f32_to_bf16(Qf)
+    Q, K = widen(q), widen(k)
+    sel = Stage(L, q, k, v, y).select()
+    sel_ref, _ = _sel_ref(Q, K, tm, y)
+    diff = np.any(sel != sel_ref, axis=-1)
+    log(f"fp32 tie ranked in fp64: {int(diff.sum())} of {diff.size} rows differ")
+    assert not diff.any(), np.argwhere(diff)[:5]
+
+
 def test_selection_with_outlier_tiles():
     """A few key tiles scaled by 1e4 put their scores far outside the rest,
     so nearly all scores fall into one bin of the first score-uniform

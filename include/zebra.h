@@ -128,7 +128,8 @@ enum {
   ZEBRA_OP_SELECT = 2,
   ZEBRA_OP_SPARSE = 3,
   ZEBRA_OP_LINEAR = 4,
-  ZEBRA_OP_DENSE = 5
+  ZEBRA_OP_DENSE = 5,
+  ZEBRA_OP_AFFINE_STATS = 6
 };
 
 /* Pack K and V into tile-major order ("Speedup scales with the number of
@@ -183,6 +184,31 @@ zebra_status zebra_linear_attn(const zebra_args* a, zebra_stream stream);
  * v; writes kt, vt, ks, vs, kbar, vbar, logn, lm (it packs and builds the
  * per-tile key bounds first) and out; uses the workspace. */
 zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream);
+
+/* Statistics of the closed-form centred affine fit of a linear stage ("A
+ * closed-form fit avoids retraining from scratch": teacher softmax outputs
+ * and the converted linear outputs, accumulated over tokens and heads (and,
+ * over calls, scenes), for a regularised least-squares solve in fp64).
+ * o = a->out (the linear stage's output with no correction: W, b, mu NULL),
+ * t = teacher (same layout as q: bf16 [N][H][64]); both pooled over all
+ * N x H rows. Adds into stats, a device array of ZEBRA_AFFINE_STATS doubles
+ * that the caller zeroes before the first call: n, sum o [64], sum t [64],
+ * sum o o^T [64][64] (row-major), sum o t^T [64][64] (row a = o channel).
+ * Products are exact, summed in fp32 over a workgroup's tokens and in fp64
+ * across workgroups. Uses the workspace. */
+#define ZEBRA_AFFINE_STATS (1 + 2 * 64 + 2 * 64 * 64)
+zebra_status zebra_affine_stats(const zebra_args* a, const void* teacher, double* stats, zebra_stream stream);
+
+/* Host-only fp64 solve from those statistics (host copy, ZEBRA_AFFINE_STATS
+ * doubles): mu = mean o, b = mean t - mu, and W minimising
+ * sum |(t - mean t) - W (o - mu)|^2 + lambda |W|^2 with
+ * lambda = lambda_rel * trace(G) / 64, G the centred Gram of o:
+ * W^T = (G + lambda I)^-1 C, C = sum (o - mu)(t - mean t)^T (Cholesky).
+ * Writes W [64][64] (row = output channel), b [64], mu [64] as fp32, the
+ * form zebra_linear_attn takes per head (one fit shared by all heads).
+ * Errors: NULL pointers, lambda_rel < 0, n < 1, G + lambda I not positive
+ * definite (ZEBRA_ERR_INVALID_ARG). */
+zebra_status zebra_affine_solve(const double* stats, double lambda_rel, float* W, float* b, float* mu);
 
 /* Host-only argument check of operation `op` (ZEBRA_OP_*); no GPU call. */
 zebra_status zebra_validate(const zebra_args* a, int op);

@@ -25,12 +25,14 @@ LIB_PATH = os.path.join(_HERE, "libzebra.so")
 
 BUF = dict(KT=0, VT=1, KS=2, VS=3, KBAR=4, VBAR=5, LOGN=6, LM=7, SEL=8, SELMASK=9, GAP=10,
            WORKSPACE=11)
-OP = dict(PACK=0, LANDMARKS=1, SELECT=2, SPARSE=3, LINEAR=4, DENSE=5)
+OP = dict(PACK=0, LANDMARKS=1, SELECT=2, SPARSE=3, LINEAR=4, DENSE=5, AFFINE_STATS=6)
+AFFINE_STATS = 1 + 2 * 64 + 2 * 64 * 64  # doubles of the affine-fit statistics
 STATUS = {0: "ZEBRA_OK", 1: "ZEBRA_ERR_INVALID_ARG", 2: "ZEBRA_ERR_UNSUPPORTED",
           3: "ZEBRA_ERR_WORKSPACE", 4: "ZEBRA_ERR_HIP"}
 EXPORTS = ["zebra_pack_tiles", "zebra_landmarks", "zebra_select_tiles", "zebra_sparse_attn",
            "zebra_linear_attn", "zebra_dense_attn", "zebra_validate", "zebra_buffer_bytes",
-           "zebra_keep_count", "zebra_num_tiles", "zebra_last_error", "zebra_version"]
+           "zebra_keep_count", "zebra_num_tiles", "zebra_last_error", "zebra_version",
+           "zebra_affine_stats", "zebra_affine_solve"]
 
 
 class ZebraError(RuntimeError):
@@ -88,6 +90,10 @@ def _load() -> ctypes.CDLL:
     so.zebra_last_error.restype = ctypes.c_char_p
     so.zebra_version.argtypes = []
     so.zebra_version.restype = ctypes.c_char_p
+    so.zebra_affine_stats.argtypes = [P(Args), _vp, _vp, _vp]
+    so.zebra_affine_stats.restype = ctypes.c_int
+    so.zebra_affine_solve.argtypes = [_vp, ctypes.c_double, _vp, _vp, _vp]
+    so.zebra_affine_solve.restype = ctypes.c_int
     return so
 
 
@@ -242,6 +248,31 @@ def linear_attn(args: Args, stream=None):
 
 def dense_attn(args: Args, stream=None):
     _call(lib.zebra_dense_attn, args, stream)
+
+
+def affine_stats(args: Args, teacher, stats, stream=None):
+    """Adds the affine-fit statistics of o = args.out against `teacher`
+    (bf16 [N][H][64], a device tensor) into `stats` (fp64 device tensor of
+    AFFINE_STATS elements, zeroed by the caller before the first call)."""
+    st = lib.zebra_affine_stats(ctypes.byref(args), _ptr(teacher), _ptr(stats), _stream(stream))
+    if st != 0:
+        raise ZebraError(st, lib.zebra_last_error().decode())
+
+
+def affine_solve(stats, lambda_rel: float):
+    """fp64 host solve of the centred affine fit from the statistics (a
+    host float64 array of AFFINE_STATS elements): returns W [64][64], b [64],
+    mu [64] as float32 numpy arrays (one fit for all heads)."""
+    import numpy as np
+    s = np.ascontiguousarray(stats, dtype=np.float64)
+    assert s.shape == (AFFINE_STATS,), s.shape
+    W = np.zeros((64, 64), np.float32)
+    b = np.zeros(64, np.float32)
+    mu = np.zeros(64, np.float32)
+    st = lib.zebra_affine_solve(s.ctypes.data, float(lambda_rel), W.ctypes.data, b.ctypes.data, mu.ctypes.data)
+    if st != 0:
+        raise ZebraError(st, lib.zebra_last_error().decode())
+    return W, b, mu
 
 
 def sparse_stage(args: Args, stream=None):

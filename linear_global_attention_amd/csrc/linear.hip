@@ -632,6 +632,181 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
   }
 }
 
+// Statistics of the closed-form centred affine fit (Zebra3D pages, "A
+// closed-form fit avoids retraining from scratch": teacher outputs t and
+// linear outputs o accumulated over tokens and heads for a regularised
+// least-squares solve in fp64). grid (nchunks, H), block 256; partial p =
+// chunk of head h holds, in fp32: sum o [64], sum t [64], sum o o^T [64][64],
+// sum o t^T [64][64] over its tokens. The same per-wave rings as
+// linear_state (a slot holds 16 rows of o, then 16 rows of t) and the same
+// transposing reads; the sums come from MFMAs against an all-ones operand.
+constexpr int AF_PART = 2 * D + 2 * D * D;  // floats of one partial
+
+__global__ void __launch_bounds__(LIN_THREADS) affine_stats_kernel(Geom g, const u16* __restrict__ O,
+                                                                   const u16* __restrict__ Tt,
+                                                                   float* __restrict__ partials, int nchunks,
+                                                                   int tpw) {
+  __shared__ __attribute__((aligned(1024))) char sring[LIN_WAVES][ST_NB][ST_SLOT];
+  static_assert(sizeof(sring) >= AF_PART * sizeof(float), "the partial fits the rings");
+  const int h = blockIdx.y, chunk = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane >> 4, tl = lane & 15;
+  f32x4 aoo[4][4], aot[4][4], so[4], st[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    so[a] = st[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) aoo[a][c] = aot[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const st_v4s ones = __builtin_bit_cast(st_v4s, make_uint2(0x3F803F80u, 0x3F803F80u));  // bf16 1.0 x 4
+  const long long t_begin = (long long)chunk * tpw;
+  const long long t_end = min((long long)g.N, t_begin + tpw);
+  const long long rs = (long long)g.H * D;
+  const long long first = t_begin + 16 * wave;
+  const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
+  char* ring = &sring[wave][0][0];
+  // group m into slot m % ST_NB (as in linear_state): rows past t_end
+  // repeat the last token (every lane issues all four copies, so the wave's
+  // memory counter advances by 4 per group); those rows are zeroed in LDS
+  // before they are read.
+  auto stage = [&](int m) {
+    const long long r0 = first + 64LL * m;
+    char* dst = ring + (m % ST_NB) * ST_SLOT;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 8 * j + (lane >> 3);
+      const long long tok = min(r0 + r, t_end - 1);
+      const long long off = (tok * rs + h * D) * 2 + (((lane & 7) ^ ls_swz(r)) << 4);
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)O + off), (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)Tt + off), (lin_lds_void*)(dst + 2048 + j * 1024),
+                                       16, 0, 0);
+    }
+  };
+  for (int m = 0; m < ST_NB - 1 && m < n; ++m) stage(m);
+  for (int m = 0; m < n; ++m) {
+    lin_wait_vm(4 * min(ST_NB - 2, n - 1 - m));
+    asm volatile("" ::: "memory");
+    const unsigned sb = (unsigned)(size_t)(ring + (m % ST_NB) * ST_SLOT);
+    // rows of this group past t_end hold a repeated token: zero them (o and
+    // t) before the reads; lane (row tl, 16-byte chunk grp * 2 + half) pairs
+    const long long valid = t_end - (first + 64LL * m);
+    unsigned ta[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int row = 4 * grp + (tl >> 2), col = 16 * b + 4 * (tl & 3);
+      ta[b] = sb + row * 128 + (((col >> 3) ^ ls_swz(row)) << 4) + (col & 4) * 2;
+    }
+    uint2 A[4], B[4];
+    if (valid >= 16) {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8\n\t"
+          "ds_read_b64_tr_b16 %1, %9\n\t"
+          "ds_read_b64_tr_b16 %2, %10\n\t"
+          "ds_read_b64_tr_b16 %3, %11\n\t"
+          "ds_read_b64_tr_b16 %4, %8 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %5, %9 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %6, %10 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(A[0]), "=&v"(A[1]), "=&v"(A[2]), "=&v"(A[3]), "=&v"(B[0]), "=&v"(B[1]), "=&v"(B[2]), "=&v"(B[3])
+          : "v"(ta[0]), "v"(ta[1]), "v"(ta[2]), "v"(ta[3])
+          : "memory");
+    } else {
+      // the last, part-filled group: zero the rows past t_end first (lane
+      // l clears the 16-byte chunk l % 8 of row l / 8 + 8j of o and of t)
+      unsigned za[4];
+      uint2 zero = make_uint2(0u, 0u);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 8 * j + (lane >> 3);
+        za[2 * j] = sb + r * 128 + ((lane & 7) << 4);
+        za[2 * j + 1] = r >= valid ? 1u : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (za[2 * j + 1])
+          asm volatile(
+              "ds_write_b64 %0, %1\n\t"
+              "ds_write_b64 %0, %1 offset:8\n\t"
+              "ds_write_b64 %0, %1 offset:2048\n\t"
+              "ds_write_b64 %0, %1 offset:2056\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              :
+              : "v"(za[2 * j]), "v"(zero)
+              : "memory");
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8\n\t"
+          "ds_read_b64_tr_b16 %1, %9\n\t"
+          "ds_read_b64_tr_b16 %2, %10\n\t"
+          "ds_read_b64_tr_b16 %3, %11\n\t"
+          "ds_read_b64_tr_b16 %4, %8 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %5, %9 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %6, %10 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(A[0]), "=&v"(A[1]), "=&v"(A[2]), "=&v"(A[3]), "=&v"(B[0]), "=&v"(B[1]), "=&v"(B[2]), "=&v"(B[3])
+          : "v"(ta[0]), "v"(ta[1]), "v"(ta[2]), "v"(ta[3])
+          : "memory");
+    }
+    // A[b]: o of channels 16 b + i, B[b]: t of channels 16 b + i, for the 4
+    // tokens 4 grp .. +3 (k = token)
+#pragma unroll
+    for (int ab = 0; ab < 4; ++ab) {
+      const st_v4s oa = __builtin_bit_cast(st_v4s, A[ab]);
+      so[ab] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(oa, ones, so[ab], 0, 0, 0);
+      st[ab] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(st_v4s, B[ab]), ones, st[ab], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        aoo[ab][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(oa, __builtin_bit_cast(st_v4s, A[cb]), aoo[ab][cb], 0, 0, 0);
+        aot[ab][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(oa, __builtin_bit_cast(st_v4s, B[cb]), aot[ab][cb], 0, 0, 0);
+      }
+    }
+    if (m + ST_NB - 1 < n) stage(m + ST_NB - 1);
+  }
+  // the workgroup's partial: the 4 waves added in wave order in LDS (over
+  // the rings, once every wave has left its loop), then written once.
+  // MFMA 16x16 output: lane holds column tl, rows 4*grp + 0..3; the sums
+  // are in every column (all-ones operand), taken from column 0.
+  float* red = (float*)&sring[0][0][0];
+  __syncthreads();
+  for (int w = 0; w < LIN_WAVES; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int a = ab * 16 + 4 * grp + r;
+          if (tl == 0) {
+            red[a] = w == 0 ? so[ab][r] : red[a] + so[ab][r];
+            red[D + a] = w == 0 ? st[ab][r] : red[D + a] + st[ab][r];
+          }
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            float* e1 = &red[2 * D + a * D + cb * 16 + tl];
+            float* e2 = &red[2 * D + D * D + a * D + cb * 16 + tl];
+            *e1 = w == 0 ? aoo[ab][cb][r] : *e1 + aoo[ab][cb][r];
+            *e2 = w == 0 ? aot[ab][cb][r] : *e2 + aot[ab][cb][r];
+          }
+        }
+    }
+    __syncthreads();
+  }
+  float* out = partials + ((long long)h * nchunks + chunk) * AF_PART;
+  for (int e = threadIdx.x; e < AF_PART; e += LIN_THREADS) out[e] = red[e];
+}
+
+// grid (ceil(AF_PART / 256)), block 256: stats[1 + e] += the fixed-order
+// fp64 sum of element e over all nparts partials; stats[0] += n.
+__global__ void __launch_bounds__(256) affine_sum_kernel(const float* __restrict__ partials, int nparts,
+                                                         double n, double* __restrict__ stats) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e == 0) stats[0] += n;
+  if (e >= AF_PART) return;
+  double s = 0.0;
+  for (int p = 0; p < nparts; ++p) s += (double)partials[(long long)p * AF_PART + e];
+  stats[1 + e] += s;
+}
+
 // Tokens per workgroup (a multiple of 128), chosen so that the H x chunks
 // workgroups fill whole waves of LIN_RESIDENT: about 8,192 tokens, rounded
 // so that no last, part-filled wave of workgroups runs alone.
@@ -675,6 +850,21 @@ hipError_t launch_linear(const Geom& g, float eps, float base, const u16* Q, con
   hipLaunchKernelGGL(linear_fold_kernel, dim3(g.H), dim3(256), 0, s, (const double*)state, W, b, mu, sp, zb);
   hipLaunchKernelGGL(linear_apply_kernel, dim3(nch, g.H), dim3(LIN_THREADS), 0, s, g, P, Q, gq, sp,
                      zb, out, tpw);
+  return hipGetLastError();
+}
+
+size_t affine_workspace_bytes(const Geom& g) {
+  return (size_t)g.H * linear_chunks(g) * AF_PART * sizeof(float);
+}
+
+// Workspace: the partials [H][nchunks][AF_PART] fp32.
+hipError_t launch_affine_stats(const Geom& g, const u16* O, const u16* Tt, double* stats, void* ws,
+                               hipStream_t s) {
+  const int nch = linear_chunks(g), tpw = linear_tokens_per_wg(g);
+  float* parts = (float*)ws;
+  hipLaunchKernelGGL(affine_stats_kernel, dim3(nch, g.H), dim3(LIN_THREADS), 0, s, g, O, Tt, parts, nch, tpw);
+  hipLaunchKernelGGL(affine_sum_kernel, dim3((AF_PART + 255) / 256), dim3(256), 0, s, (const float*)parts,
+                     g.H * nch, (double)g.N * g.H, stats);
   return hipGetLastError();
 }
 

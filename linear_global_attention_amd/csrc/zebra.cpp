@@ -23,6 +23,8 @@ size_t linear_workspace_bytes(const Geom&);
 hipError_t launch_linear(const Geom&, float, float, const u16*, const u16*, const u16*,
                          const float*, const float*, const float*, const float*, const float*,
                          u16*, void*, hipStream_t);
+size_t affine_workspace_bytes(const Geom&);
+hipError_t launch_affine_stats(const Geom&, const u16*, const u16*, double*, void*, hipStream_t);
 }  // namespace zebra
 
 using namespace zebra;
@@ -104,9 +106,10 @@ size_t buf_bytes(const Geom& g, int64_t k, int which) {
     case ZEBRA_BUF_GAP: return H * T * sizeof(double);
     case ZEBRA_BUF_WORKSPACE: {
       size_t m = select_workspace_bytes(g);
-      const size_t b = linear_workspace_bytes(g), c = attn_workspace_bytes(g);
+      const size_t b = linear_workspace_bytes(g), c = attn_workspace_bytes(g), f = affine_workspace_bytes(g);
       if (b > m) m = b;
       if (c > m) m = c;
+      if (f > m) m = f;
       return m;
     }
     default: return 0;
@@ -202,6 +205,12 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
       NEED(a->workspace, "workspace");
       if (a->workspace_bytes < attn_workspace_bytes(g))
         return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_dense_attn");
+      break;
+    case ZEBRA_OP_AFFINE_STATS:
+      NEED(a->out, "out (the linear outputs)");
+      NEED(a->workspace, "workspace");
+      if (a->workspace_bytes < affine_workspace_bytes(g))
+        return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_affine_stats");
       break;
     default:
       return fail(ZEBRA_ERR_INVALID_ARG, "unknown operation");
@@ -323,6 +332,80 @@ zebra_status zebra_linear_attn(const zebra_args* a, zebra_stream stream) {
                                   (const u16*)a->v, a->W, a->b, a->mu, a->gq, a->gk,
                                   (u16*)a->out, a->workspace, (hipStream_t)stream),
                     "zebra_linear_attn");
+}
+
+zebra_status zebra_affine_stats(const zebra_args* a, const void* teacher, double* stats, zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_AFFINE_STATS, g, k);
+  if (s != ZEBRA_OK) return s;
+  if (!teacher) return fail(ZEBRA_ERR_INVALID_ARG, "teacher is NULL");
+  if (!stats) return fail(ZEBRA_ERR_INVALID_ARG, "stats is NULL");
+  return hip_result(launch_affine_stats(g, (const u16*)a->out, (const u16*)teacher, stats, a->workspace,
+                                        (hipStream_t)stream),
+                    "zebra_affine_stats");
+}
+
+zebra_status zebra_affine_solve(const double* stats, double lambda_rel, float* W, float* b, float* mu) {
+  if (!stats || !W || !b || !mu) return fail(ZEBRA_ERR_INVALID_ARG, "stats, W, b and mu must be non-NULL");
+  if (!(lambda_rel >= 0.0) || !isfinite(lambda_rel)) return fail(ZEBRA_ERR_INVALID_ARG, "lambda_rel must be >= 0");
+  const int d = D;
+  const double n = stats[0];
+  if (!(n >= 1.0)) return fail(ZEBRA_ERR_INVALID_ARG, "no samples accumulated");
+  const double* so = stats + 1;
+  const double* st = so + d;
+  const double* oo = st + d;
+  const double* ot = oo + d * d;
+  double m[D], tb[D];
+  for (int i = 0; i < d; ++i) {
+    m[i] = so[i] / n;
+    tb[i] = st[i] / n;
+  }
+  // centred Gram G = sum (o - m)(o - m)^T and cross term Cx = sum (o - m)(t - tb)^T
+  static thread_local double G[D * D], Cx[D * D];
+  double tr = 0.0;
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      G[i * d + j] = oo[i * d + j] - n * m[i] * m[j];
+      Cx[i * d + j] = ot[i * d + j] - n * m[i] * tb[j];
+    }
+  for (int i = 0; i < d; ++i) tr += G[i * d + i];
+  const double lam = lambda_rel * tr / d;
+  for (int i = 0; i < d; ++i) G[i * d + i] += lam;
+  // Cholesky G = L L^T (lower, in place)
+  for (int j = 0; j < d; ++j) {
+    double s = G[j * d + j];
+    for (int p = 0; p < j; ++p) s -= G[j * d + p] * G[j * d + p];
+    if (!(s > 0.0)) return fail(ZEBRA_ERR_INVALID_ARG, "Gram matrix (plus ridge) is not positive definite");
+    const double l = sqrt(s);
+    G[j * d + j] = l;
+    for (int i = j + 1; i < d; ++i) {
+      double t = G[i * d + j];
+      for (int p = 0; p < j; ++p) t -= G[i * d + p] * G[j * d + p];
+      G[i * d + j] = t / l;
+    }
+  }
+  // X = G^-1 Cx, column by column; W[c][a] = X[a][c]
+  for (int c = 0; c < d; ++c) {
+    double x[D];
+    for (int i = 0; i < d; ++i) {
+      double t = Cx[i * d + c];
+      for (int p = 0; p < i; ++p) t -= G[i * d + p] * x[p];
+      x[i] = t / G[i * d + i];
+    }
+    for (int i = d - 1; i >= 0; --i) {
+      double t = x[i];
+      for (int p = i + 1; p < d; ++p) t -= G[p * d + i] * x[p];
+      x[i] = t / G[i * d + i];
+    }
+    for (int a = 0; a < d; ++a) W[c * d + a] = (float)x[a];
+  }
+  for (int i = 0; i < d; ++i) {
+    b[i] = (float)(tb[i] - m[i]);
+    mu[i] = (float)m[i];
+  }
+  g_err.clear();
+  return ZEBRA_OK;
 }
 
 }  // extern "C"

@@ -459,3 +459,39 @@ def test_selection_tie_group_after_narrowing():
         checked += 1
     log(f"tie group: {checked} of {tm.T} rows checked")
     assert checked >= tm.T // 2
+
+
+# ------------------------------------------------------------- affine fit
+def test_affine_stats_and_fit():
+    """zebra_affine_stats against the oracle's statistics (pooled over all
+    N x H rows; 3,468 tokens leave a ragged last group), accumulation over
+    two calls, and the fit from the GPU statistics against the oracle's fit:
+    the corrected outputs agree to the stage tolerance."""
+    from gpu_helpers import dev
+    from oracle import affine as oaf
+    L = zs.Layout(6, 2, 24, 24, heads=2)
+    q, k, v = _inputs(L, seed=16)
+    o, t = q, k  # any two bf16 tensors of the output layout
+    st = Stage(L, q, k, v, 0.0)
+    st.out.copy_(dev(o))
+    teacher = dev(t)
+    stats = torch.zeros(zb.AFFINE_STATS, dtype=torch.float64, device="cuda")
+    zb.affine_stats(st.args(), teacher, stats)
+    torch.cuda.synchronize()
+    got = stats.cpu().numpy()
+    O, T = widen(o), widen(t)
+    ref = oaf.affine_stats(O, T)
+    assert got[0] == ref[0] == L.tokens * L.heads
+    err = np.abs(got - ref)
+    scale = np.abs(ref).max()
+    log(f"affine stats: max |gpu - oracle| = {err.max():.3e} (largest sum {scale:.3e})")
+    assert err.max() <= 1e-6 * scale + 1e-6, err.max()
+    zb.affine_stats(st.args(), teacher, stats)  # a second scene adds
+    torch.cuda.synchronize()
+    assert np.allclose(stats.cpu().numpy(), 2 * got, rtol=1e-12, atol=1e-9)
+    for lam in (0.0, 1e-3):
+        W, b, mu = zb.affine_solve(got, lam)
+        Wr, br, mur = oaf.affine_fit(ref, lam)
+        Y = oaf.apply_affine(O, W.astype(np.float64), b.astype(np.float64), mu.astype(np.float64))
+        Yr = oaf.apply_affine(O, Wr, br, mur)
+        close(Y, Yr, f"affine-corrected outputs (lambda_rel {lam})")

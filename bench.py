@@ -262,6 +262,29 @@ def main():
         "wall_s_timed_region": t_wall,
     }
 
+    # closed-form affine fit statistics (calibration, outside the step): the
+    # uncorrected linear output against the sparse stage's output as teacher,
+    # timed over 3 calls after one warm-up call; reads o and t once each
+    out_plain = torch.empty_like(qd)
+    zb.linear_attn(zb.make_args(zL, qd, kd, vd, out_plain, bufs, a.y))
+    stats = torch.zeros(zb.AFFINE_STATS, dtype=torch.float64, device="cuda")
+    args_f = zb.make_args(zL, qd, kd, vd, out_plain, bufs, a.y)
+    zb.affine_stats(args_f, out, stats)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        zb.affine_stats(args_f, out, stats)
+    e1.record()
+    torch.cuda.synchronize()
+    aff_ms = e0.elapsed_time(e1) / 3
+    aff_bytes = 2 * N * H * 64 * 2
+    result["roofline_affine_stats"] = {
+        "kernels": "affine_stats_kernel + affine_sum_kernel (zebra_affine_stats)", "bound": "hbm",
+        "achieved": aff_bytes / (aff_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": aff_bytes / (aff_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": aff_bytes,
+        "avg_launch_ms": aff_ms}
+    del out_plain, stats
+
     if not a.no_dense:
         log("dense baseline (one call)")
         args_d = zb.make_args(zL, qd, kd, vd, out, bufs, a.y)

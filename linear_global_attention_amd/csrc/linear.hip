@@ -795,15 +795,28 @@ __global__ void __launch_bounds__(LIN_THREADS) affine_stats_kernel(Geom g, const
   for (int e = threadIdx.x; e < AF_PART; e += LIN_THREADS) out[e] = red[e];
 }
 
-// grid (ceil(AF_PART / 256)), block 256: stats[1 + e] += the fixed-order
-// fp64 sum of element e over all nparts partials; stats[0] += n.
-__global__ void __launch_bounds__(256) affine_sum_kernel(const float* __restrict__ partials, int nparts,
-                                                         double n, double* __restrict__ stats) {
+// The partials are added in a fixed order in two levels: level 1, grid
+// (ceil(AF_PART / 256), AF_GROUPS), sums partials j, j + AF_GROUPS, ... into
+// group j (fp64); level 2, grid (ceil(AF_PART / 256)), adds the groups in
+// order into stats[1 + e], and n into stats[0].
+constexpr int AF_GROUPS = 64;
+
+__global__ void __launch_bounds__(256) affine_sum1_kernel(const float* __restrict__ partials, int nparts,
+                                                          double* __restrict__ groups) {
+  const int e = blockIdx.x * 256 + threadIdx.x, j = blockIdx.y;
+  if (e >= AF_PART) return;
+  double s = 0.0;
+  for (int p = j; p < nparts; p += AF_GROUPS) s += (double)partials[(long long)p * AF_PART + e];
+  groups[(long long)j * AF_PART + e] = s;
+}
+
+__global__ void __launch_bounds__(256) affine_sum2_kernel(const double* __restrict__ groups, double n,
+                                                          double* __restrict__ stats) {
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e == 0) stats[0] += n;
   if (e >= AF_PART) return;
   double s = 0.0;
-  for (int p = 0; p < nparts; ++p) s += (double)partials[(long long)p * AF_PART + e];
+  for (int j = 0; j < AF_GROUPS; ++j) s += groups[(long long)j * AF_PART + e];
   stats[1 + e] += s;
 }
 
@@ -854,17 +867,21 @@ hipError_t launch_linear(const Geom& g, float eps, float base, const u16* Q, con
 }
 
 size_t affine_workspace_bytes(const Geom& g) {
-  return (size_t)g.H * linear_chunks(g) * AF_PART * sizeof(float);
+  return (size_t)g.H * linear_chunks(g) * AF_PART * sizeof(float) + (size_t)AF_GROUPS * AF_PART * sizeof(double);
 }
 
-// Workspace: the partials [H][nchunks][AF_PART] fp32.
+// Workspace: the partials [H][nchunks][AF_PART] fp32, then the group sums
+// [AF_GROUPS][AF_PART] fp64.
 hipError_t launch_affine_stats(const Geom& g, const u16* O, const u16* Tt, double* stats, void* ws,
                                hipStream_t s) {
   const int nch = linear_chunks(g), tpw = linear_tokens_per_wg(g);
   float* parts = (float*)ws;
+  double* groups = (double*)(parts + (size_t)g.H * nch * AF_PART);
   hipLaunchKernelGGL(affine_stats_kernel, dim3(nch, g.H), dim3(LIN_THREADS), 0, s, g, O, Tt, parts, nch, tpw);
-  hipLaunchKernelGGL(affine_sum_kernel, dim3((AF_PART + 255) / 256), dim3(256), 0, s, (const float*)parts,
-                     g.H * nch, (double)g.N * g.H, stats);
+  hipLaunchKernelGGL(affine_sum1_kernel, dim3((AF_PART + 255) / 256, AF_GROUPS), dim3(256), 0, s,
+                     (const float*)parts, g.H * nch, groups);
+  hipLaunchKernelGGL(affine_sum2_kernel, dim3((AF_PART + 255) / 256), dim3(256), 0, s, (const double*)groups,
+                     (double)g.N * g.H, stats);
   return hipGetLastError();
 }
 

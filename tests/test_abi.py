@@ -107,3 +107,20 @@ def test_entry_points_fail_before_any_launch():
         assert fn(ctypes.byref(a), None) == 1
     with pytest.raises(zb.ZebraError, match="INVALID_ARG"):
         zb.pack_tiles(a, stream=0)
+
+
+def test_affine_entry_points_reject_on_host():
+    """zebra_affine_stats checks its arguments before any launch; the host
+    solve needs no GPU at all."""
+    L = zb.Layout(4, 5, 37, 37, 2)
+    a = _full_args(L, 0.5)
+    buf = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    f = zb.lib.zebra_affine_stats
+    assert f(ctypes.byref(a), None, buf, None) == 1 and "teacher" in zb.last_error()
+    assert f(ctypes.byref(a), buf, None, None) == 1 and "stats" in zb.last_error()
+    a.out = None
+    assert f(ctypes.byref(a), buf, buf, None) == 1 and "out" in zb.last_error()
+    a = _full_args(L, 0.5)
+    a.workspace_bytes = 16
+    assert f(ctypes.byref(a), buf, buf, None) == 3
+    assert zb.lib.zebra_affine_solve(None, 0.0, None, None, None) == 1

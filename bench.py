@@ -1,6 +1,6 @@
 """Benchmark of the global multi-view attention stage on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config c4]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config 1024views]
 
 Workload (default): 1,024 views of a VGGT-like backbone, 5 special tokens and
 37x37 patches per frame, 1,406,976 tokens, 16 heads, d = 64, bf16, seeded
@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=3)
     p.add_argument("--warmup", type=int, default=1)
-    p.add_argument("--config", default="c4")
+    p.add_argument("--config", default="1024views")
     p.add_argument("--y", type=float, default=0.8)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-dense", action="store_true")
@@ -90,7 +90,7 @@ def recorded_traffic(config: str, y: float):
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", "attn_traffic_1024views.md")
-    if config != "c4" or abs(y - 0.8) > 1e-12 or not os.path.exists(path):
+    if config != "1024views" or abs(y - 0.8) > 1e-12 or not os.path.exists(path):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), flags=re.S)
     if not m:
@@ -154,7 +154,7 @@ def cpu_baseline(L, q, k, v, y, seed):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on one GPU per process here; --gpus must be 1"}))
         sys.exit(2)
     import torch
     import linear_global_attention_amd as zb

@@ -24,7 +24,7 @@ from make_large import CASES, digest  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("case", ["c3", "c4"])
+@pytest.mark.parametrize("case", ["512views", "1024views"])
 def test_large_shape_sampled_rows(case):
     path = os.path.join(GOLDEN, f"{case}_rows.npz")
     d = np.load(path)

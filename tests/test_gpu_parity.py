@@ -38,7 +38,7 @@ def _sel_ref(Q, K, tm, y):
 
 # ------------------------------------------------------------- small, full
 EDGE = [
-    ("c0", zs.CONFIGS["c0"], 0.5),
+    ("2views_16x16", zs.CONFIGS["2views_16x16"], 0.5),
     ("partial-no-specials", zs.Layout(3, 0, 11, 13, heads=2), 0.3),
     ("partial-y0", zs.Layout(2, 3, 9, 17, heads=2), 0.0),
     ("partial-y1", zs.Layout(2, 3, 9, 17, heads=2), 1.0),
@@ -131,7 +131,7 @@ def test_landmark_of_identical_tile_equals_tile():
         assert np.array_equal(vbar[:, u], widen(v[tm.tokens[u][0]]).astype(np.float32))
 
 
-@pytest.mark.parametrize("name,L", [("c0", zs.CONFIGS["c0"]), ("partial", zs.Layout(3, 2, 11, 13, heads=2)),
+@pytest.mark.parametrize("name,L", [("2views_16x16", zs.CONFIGS["2views_16x16"]), ("partial", zs.Layout(3, 2, 11, 13, heads=2)),
                                     ("vggt-2view", zs.Layout(2, 5, 37, 37, heads=2))])
 def test_dense_full(name, L):
     q, k, v = _inputs(L, seed=4)
@@ -150,7 +150,7 @@ def test_y0_sparse_equals_dense_on_gpu():
     close(a, b, "y=0 sparse vs dense (GPU)")
 
 
-LIN = [("c0-identity", zs.CONFIGS["c0"], False),
+LIN = [("2views_16x16-identity", zs.CONFIGS["2views_16x16"], False),
        ("partial-affine", zs.Layout(3, 2, 11, 13, heads=2), True),
        ("vggt-2view-affine", zs.Layout(2, 5, 37, 37, heads=3), True)]
 
@@ -172,19 +172,19 @@ def test_linear_full(name, L, affine):
 
 
 # ------------------------------------------------------------- 32 views
-def test_c1_sparse_selection_and_rows():
-    L = zs.CONFIGS["c1"]
+def test_32views_sparse_selection_and_rows():
+    L = zs.CONFIGS["32views"]
     y = 0.8
-    log("c1: drawing inputs")
+    log("32 views: drawing inputs")
     q, k, v = _inputs(L, seed=0)
     Q, K, V = widen(q), widen(k), widen(v)
     tm = TileMap(L.frames, L.specials, L.rows, L.cols)
     st = Stage(L, q, k, v, y)
-    log("c1: GPU sparse stage")
+    log("32 views: GPU sparse stage")
     st.sparse()
     sel = st.bufs.sel().cpu().numpy()
     sel_ref, tie_ref = _sel_ref(Q, K, tm, y)
-    compare_selection(sel, sel_ref, tie_ref, "c1 selection (all 16x800 query tiles)")
+    compare_selection(sel, sel_ref, tie_ref, "32 views: selection (all 16x800 query tiles)")
     # every row of 40 seeded (head, query tile) pairs plus all special rows of 2 heads
     g = np.random.default_rng(0)
     rows = []
@@ -192,13 +192,13 @@ def test_c1_sparse_selection_and_rows():
         rows += [(int(h), int(tok)) for tok in tm.tokens[t]]
     rows += [(h, int(s)) for h in (0, 9) for s in tm.specials]
     rows = np.array(sorted(set(rows)), dtype=np.int64)
-    log(f"c1: oracle on {len(rows)} rows")
+    log(f"32 views: oracle on {len(rows)} rows")
     ref, _ = osp.sparse_rows(Q, K, V, tm, y, rows)
-    close(st.rows(rows), ref, "c1 sparse rows")
+    close(st.rows(rows), ref, "32 views: sparse rows")
 
 
-def test_c1_dense_and_linear_rows():
-    L = zs.CONFIGS["c1"]
+def test_32views_dense_and_linear_rows():
+    L = zs.CONFIGS["32views"]
     q, k, v = _inputs(L, seed=0)
     Q, K, V = widen(q), widen(k), widen(v)
     tm = TileMap(L.frames, L.specials, L.rows, L.cols)
@@ -206,51 +206,51 @@ def test_c1_dense_and_linear_rows():
     st = Stage(L, q, k, v, 0.0)
     st.dense()
     ref = np.stack([osp.dense_rows(Q[:, h], K[:, h], V[:, h], [t])[0] for h, t in rows])
-    close(st.rows(rows), ref, "c1 dense rows")
+    close(st.rows(rows), ref, "32 views: dense rows")
     W, b = zs.affine_params(L, seed=0)
     mu = (0.01 * np.random.default_rng(1).standard_normal((L.heads, 64))).astype(np.float32)
     st.linear(W, b, mu)
     ref = olin.linear_rows(Q, K, V, tm, rows, W, b, mu)
-    close(st.rows(rows), ref, "c1 linear rows")
+    close(st.rows(rows), ref, "32 views: linear rows")
 
 
-def test_c2_linear_full():
-    L = zs.CONFIGS["c2"]
-    log("c2: drawing inputs")
+def test_128views_linear_full():
+    L = zs.CONFIGS["128views"]
+    log("128 views: drawing inputs")
     q, k, v = _inputs(L, seed=0)
     Q, K, V = widen(q), widen(k), widen(v)
     tm = TileMap(L.frames, L.specials, L.rows, L.cols)
     W, b = zs.affine_params(L, seed=0)
-    log("c2: oracle mean output")
+    log("128 views: oracle mean output")
     mu = np.stack([olin.mean_output(Q[:, h], K[:, h], V[:, h], tm)
                    for h in range(L.heads)]).astype(np.float32)
     st = Stage(L, q, k, v, 0.0, sparse=False)
     out = bf16_host(st.linear(W, b, mu)).reshape(L.tokens, L.heads, 64)
-    log("c2: oracle linear stage")
+    log("128 views: oracle linear stage")
     ref = olin.linear_attention(Q, K, V, tm, W, b, mu)
-    close(out, ref, "c2 linear (all 175,872 x 16 rows)")
+    close(out, ref, "128 views: linear (all 175,872 x 16 rows)")
 
 
 @pytest.mark.parametrize("y", [0.6, 0.8, 0.95])
-def test_c1_special_rows_in_key_segments(y):
+def test_32views_special_rows_in_key_segments(y):
     """Special query rows see every key. The main kernel splits each special
     item's keys into about T/k segments (3, 5 and 8 at these y) and adds
     their partial sums afterwards. Every special row of two heads matches the
     oracle's dense rows, and sampled patch rows its sparse rows."""
-    L = zs.CONFIGS["c1"]
+    L = zs.CONFIGS["32views"]
     q, k, v = _inputs(L, seed=7)
     Q, K, V = widen(q), widen(k), widen(v)
     tm = TileMap(L.frames, L.specials, L.rows, L.cols)
-    log(f"c1: sparse stage y={y}")
+    log(f"32 views: sparse stage y={y}")
     st = Stage(L, q, k, v, y)
     st.sparse()
     heads = (3, 12)
     spec = np.array([(h, int(t)) for h in heads for t in tm.specials], dtype=np.int64)
     ref = np.concatenate([osp.dense_rows(Q[:, h], K[:, h], V[:, h], list(tm.specials)) for h in heads])
-    close(st.rows(spec), ref, f"c1 y={y} special rows ({len(spec)})")
+    close(st.rows(spec), ref, f"32 views y={y}: special rows ({len(spec)})")
     rows = zs.sample_rows(L, 256, seed=7, special_frames=0)
     ref, _ = osp.sparse_rows(Q, K, V, tm, y, rows)
-    close(st.rows(rows), ref, f"c1 y={y} sparse rows")
+    close(st.rows(rows), ref, f"32 views y={y}: sparse rows")
 
 
 def test_exact_fallback_rows():

@@ -58,9 +58,9 @@ def test_layout_counts_golden():
         assert sorted(np.concatenate(tm.tokens).tolist() + tm.specials.tolist()) == list(range(tm.N))
         if "y" in c:
             assert keep_count(c["y"], c["T"]) == c["k"], name
-    c4 = fx["configs"]["c4"]
-    assert c4["F"] * (c4["S"] + c4["R"] * c4["C"]) == c4["N"]
-    assert keep_count(c4["y"], c4["T"]) == c4["k"]
+    big = fx["configs"]["1024views"]
+    assert big["F"] * (big["S"] + big["R"] * big["C"]) == big["N"]
+    assert keep_count(big["y"], big["T"]) == big["k"]
 
 
 def test_keep_count_rounds_not_floors():

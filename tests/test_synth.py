@@ -16,7 +16,7 @@ def test_bf16_round_to_nearest_even():
 
 
 def test_deterministic_and_thread_independent():
-    L = zs.CONFIGS["c0"]
+    L = zs.CONFIGS["2views_16x16"]
     a = zs.stage_inputs(L, seed=0, threads=1)
     b = zs.stage_inputs(L, seed=0, threads=4)
     c = zs.stage_inputs(L, seed=1, threads=2)
@@ -46,7 +46,7 @@ def test_tile_centroid_model():
 
 
 def test_affine_and_rows():
-    L = zs.CONFIGS["c1"]
+    L = zs.CONFIGS["32views"]
     W, b = zs.affine_params(L, seed=0)
     assert W.shape == (16, 64, 64) and b.shape == (16, 64)
     assert np.abs(np.diagonal(W, axis1=1, axis2=2) - 1).max() < 0.05

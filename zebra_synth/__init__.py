@@ -66,11 +66,11 @@ class Layout:
 # Synthetic multi-view shapes: a 2-frame 16x16 toy stage, and VGGT-like
 # 37x37-patch frames with 5 special tokens at 32, 128, 512 and 1,024 views.
 CONFIGS = {
-    "c0": Layout(2, 5, 16, 16, heads=1),
-    "c1": Layout(32, 5, 37, 37),
-    "c2": Layout(128, 5, 37, 37),
-    "c3": Layout(512, 5, 37, 37),
-    "c4": Layout(1024, 5, 37, 37),
+    "2views_16x16": Layout(2, 5, 16, 16, heads=1),
+    "32views": Layout(32, 5, 37, 37),
+    "128views": Layout(128, 5, 37, 37),
+    "512views": Layout(512, 5, 37, 37),
+    "1024views": Layout(1024, 5, 37, 37),
 }
 
 

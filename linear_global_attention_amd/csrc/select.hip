@@ -27,18 +27,25 @@ __device__ inline long long tile_token_s(const Geom& g, int f, int tl, int s) {
   return (long long)f * g.tok_pf + g.S + (long long)r * g.C + c;
 }
 
-// grid (T, H), block 64: qbar[h][t][d] = mean over tile t's patch queries.
-__global__ void __launch_bounds__(64) qbar_kernel(Geom g, const u16* __restrict__ Q,
-                                                  double* __restrict__ qbar) {
-  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+// grid (ceil(T / 4), H), block 256: qbar[h][t][d] = mean over tile t's
+// patch queries, wave w for tile 4 blockIdx.x + w, lane d for channel d.
+// A tile holds at most 64 bf16 values (8-bit significands) per channel:
+// whenever they span less than 2^38 in magnitude (any ordinary data) every
+// partial sum and the total are exact in fp64, so the four independent
+// partial sums, which give the loads room to overlap, equal a serial sum.
+__global__ void __launch_bounds__(256) qbar_kernel(Geom g, const u16* __restrict__ Q,
+                                                   double* __restrict__ qbar) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), h = blockIdx.y, d = threadIdx.x & 63;
+  if (t >= g.T) return;
   const int f = t / g.tpf, tl = t - f * g.tpf;
   const int n = tile_n(g, tl);
-  double s = 0.0;
-  for (int i = 0; i < n; ++i) {
-    const long long tok = tile_token_s(g, f, tl, i);
-    s += (double)bf2f(Q[(tok * g.H + h) * D + d]);
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int i = 0; i < n; i += 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (i + j < n) s[j] += (double)bf2f(Q[(tile_token_s(g, f, tl, i + j) * g.H + h) * D + d]);
   }
-  qbar[((long long)h * g.T + t) * D + d] = s / n;
+  qbar[((long long)h * g.T + t) * D + d] = ((s[0] + s[1]) + (s[2] + s[3])) / n;
 }
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
@@ -723,7 +730,7 @@ hipError_t launch_select(const Geom& g, int k, const u16* Q, const double* kbar,
                  : rounds <= 16 ? topk_resolve_kernel<5, 16>
                  : rounds <= 25 ? topk_resolve_kernel<17, 25>
                                 : topk_resolve_kernel<26, TOPK_MAX_ROUNDS>;
-  hipLaunchKernelGGL(qbar_kernel, dim3(g.T, g.H), dim3(64), 0, s, g, Q, qbar);
+  hipLaunchKernelGGL(qbar_kernel, dim3((g.T + 3) / 4, g.H), dim3(256), 0, s, g, Q, qbar);
   for (int h = 0; h < g.H; ++h) {
     for (int t0 = 0; t0 < g.T; t0 += chunk) {
       const int nq = g.T - t0 < chunk ? g.T - t0 : chunk;

@@ -3,7 +3,7 @@ attention stage of a Zebra3D-style hybrid model.
 
 Argument marshalling only: every step runs in the HIP kernels behind the C
 ABI of include/zebra.h. PyTorch provides device memory and streams. The
-library must have been built (python -m linear_global_attention_amd.build);
+library must have been built (python linear_global_attention_amd/build.py);
 importing the binding raises if libzebra.so is missing, and every call
 raises ZebraError on a non-zero status. There is no CPU fallback.
 """
@@ -65,7 +65,7 @@ class Args(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m linear_global_attention_amd.build`")
+                          "`python linear_global_attention_amd/build.py`")
     # One HIP runtime per process: the torch wheel bundles its own
     # libamdhip64 (same soname as /opt/rocm's). Loading torch first makes
     # libzebra bind to that copy; loaded the other way round, the process

@@ -1,6 +1,6 @@
 """Build libzebra.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m linear_global_attention_amd.build
+    python linear_global_attention_amd/build.py
 
 Each source is compiled with hipcc for gfx950 into _build/, then linked into
 linear_global_attention_amd/libzebra.so next to this file.

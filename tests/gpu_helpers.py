@@ -82,9 +82,10 @@ class Stage:
         torch.cuda.synchronize()
         return self.out
 
-    def linear(self, W=None, b=None, mu=None):
+    def linear(self, W=None, b=None, mu=None, gq=None, gk=None, eps=1e-6, base=100.0):
         Wd, bd, md = dev_f32(W), dev_f32(b), dev_f32(mu)
-        zb.linear_attn(self.args(W=Wd, b=bd, mu=md))
+        gqd, gkd = dev_f32(gq), dev_f32(gk)
+        zb.linear_attn(self.args(W=Wd, b=bd, mu=md, gq=gqd, gk=gkd, rms_eps=eps, rope_base=base))
         torch.cuda.synchronize()
         return self.out
 
@@ -95,8 +96,34 @@ class Stage:
         return bf16_host(o)
 
 
-def compare_selection(sel_gpu: np.ndarray, sel_ref: np.ndarray, tie_ref: np.ndarray, what: str):
-    """Bit-exact kept-tile lists except on near-tie rows (reported)."""
+NEAR_TIE = 1e-6
+
+
+def valid_near_tie_list(kept: np.ndarray, scores: np.ndarray, k: int) -> None:
+    """Checks a kept-tile list of a near-tie row, where several lists are
+    correct. With a = the k-th and b = the (k+1)-th ranked oracle score and
+    band = [b - delta, a + delta], delta = 1e-6 max(|a|, |b|): the list holds
+    exactly k distinct tiles in ascending order, keeps every tile scoring
+    above the band and none scoring below it."""
+    kept = np.asarray(kept, dtype=np.int64)
+    T = scores.shape[0]
+    assert kept.shape == (k,), kept.shape
+    assert np.all(np.diff(kept) > 0), "not strictly ascending"
+    assert kept.min() >= 0 and kept.max() < T
+    order = np.lexsort((np.arange(T), -scores))
+    a, b = scores[order[k - 1]], scores[order[k]]
+    delta = NEAR_TIE * max(abs(a), abs(b), 1e-300)
+    must = np.flatnonzero(scores > a + delta)
+    never = np.flatnonzero(scores < b - delta)
+    assert np.isin(must, kept).all(), "a tile above the near-tie band was dropped"
+    assert not np.isin(never, kept).any(), "a tile below the near-tie band was kept"
+
+
+def compare_selection(sel_gpu: np.ndarray, sel_ref: np.ndarray, tie_ref: np.ndarray, what: str,
+                      scores=None):
+    """Bit-exact kept-tile lists except on near-tie rows, which are counted
+    and, given scores(h, t) -> the oracle's fp64 scores of that row, checked
+    for validity (valid_near_tie_list)."""
     assert sel_gpu.shape == sel_ref.shape, (sel_gpu.shape, sel_ref.shape)
     diff = np.any(sel_gpu != sel_ref, axis=-1)
     n_tie = int(tie_ref.sum())
@@ -104,4 +131,21 @@ def compare_selection(sel_gpu: np.ndarray, sel_ref: np.ndarray, tie_ref: np.ndar
     log(f"{what}: {diff.sum()} of {diff.size} rows differ, {n_tie} near-tie rows, "
         f"{bad.sum()} differing non-tie rows")
     assert not bad.any(), f"{what}: selection differs on {bad.sum()} non-tie rows"
+    if scores is not None:
+        for h, t in np.argwhere(tie_ref):
+            valid_near_tie_list(sel_gpu[h, t], scores(int(h), int(t)), sel_gpu.shape[-1])
+        log(f"{what}: {n_tie} near-tie rows valid")
     return dict(rows=int(diff.size), near_tie=n_tie, differ=int(diff.sum()))
+
+
+def oracle_scores(Q, K, tm, osp):
+    """scores(h, t): the oracle's fp64 tile scores qbar_t . kbar_u / 8 of
+    query tile t in head h (landmarks cached per head)."""
+    cache = {}
+
+    def f(h, t):
+        if h not in cache:
+            cache[h] = osp.landmarks(K[:, h], K[:, h], tm)[0]
+        qbar = Q[tm.tokens[t], h].sum(axis=0) / tm.n[t]
+        return cache[h] @ qbar / 8.0
+    return f

@@ -15,7 +15,9 @@ import pytest
 import torch
 
 import zebra_synth as zs
-from gpu_helpers import Stage, close, log
+from gpu_helpers import Stage, close, log, valid_near_tie_list, widen
+from oracle import sparse as osp
+from oracle.layout import TileMap
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 sys.path.insert(0, GOLDEN)
@@ -46,6 +48,16 @@ def test_large_shape_sampled_rows(case):
     log(f"{case} selection: {differ.sum()} of {len(sel_tiles)} sampled tiles differ, "
         f"{d['sel_tie'].sum()} near-tie, {bad.sum()} differing non-tie")
     assert not bad.any(), f"{case}: kept-tile lists differ on {bad.sum()} non-tie tiles"
+    # near-tie tiles: several lists are correct; the GPU's must be a valid one
+    # under the oracle's fp64 scores
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    for i in np.flatnonzero(d["sel_tie"]):
+        h, t = (int(x) for x in sel_tiles[i])
+        Kh = widen(k[:, h])
+        kbar = osp.landmarks(Kh, Kh, tm)[0]
+        qbar = widen(q[tm.tokens[t], h]).sum(axis=0) / tm.n[t]
+        valid_near_tie_list(sel[i], kbar @ qbar / 8.0, sel.shape[-1])
+    log(f"{case} selection: {int(d['sel_tie'].sum())} near-tie tiles hold valid lists")
     del st
     torch.cuda.empty_cache()
 

@@ -15,7 +15,7 @@ from oracle import linear as olin
 from oracle import sparse as osp
 from oracle.layout import TileMap, keep_count
 
-from gpu_helpers import Stage, bf16_host, close, compare_selection, log, widen
+from gpu_helpers import Stage, bf16_host, close, compare_selection, log, oracle_scores, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_sparse_stage_full(name, L, y):
     kk = keep_count(y, tm.T)
     if kk > 0:
         sel = st.bufs.sel().cpu().numpy()
-        compare_selection(sel, sel_ref, tie_ref, f"{name} selection")
+        compare_selection(sel, sel_ref, tie_ref, f"{name} selection", oracle_scores(Q, K, tm, osp))
         # the bitmap agrees with the lists
         mask = st.bufs.selmask().cpu().numpy().view(np.uint32)
         for h in range(L.heads):
@@ -171,6 +171,51 @@ def test_linear_full(name, L, affine):
     close(out, ref, f"{name} linear")
 
 
+GAINS = [("partial-gains", zs.Layout(3, 2, 11, 13, heads=2)),
+         ("vggt-2view-gains", zs.Layout(2, 5, 37, 37, heads=3))]
+
+
+@pytest.mark.parametrize("name,L", GAINS, ids=[x[0] for x in GAINS])
+def test_linear_gains_eps_base(name, L):
+    """zebra_linear_attn with per-head RMSNorm gains on Q and K (random, in
+    [0.5, 1.5)), eps = 1e-3 and rotary base 10,000, plus the per-head affine
+    correction: every row against the oracle at the same settings."""
+    q, k, v = _inputs(L, seed=17)
+    Q, K, V = widen(q), widen(k), widen(v)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    g = np.random.default_rng(17)
+    gq = (0.5 + g.random((L.heads, 64))).astype(np.float32)
+    gk = (0.5 + g.random((L.heads, 64))).astype(np.float32)
+    eps, base = 1e-3, 10000.0
+    W, b = zs.affine_params(L, seed=17)
+    mu = np.stack([olin.mean_output(Q[:, h], K[:, h], V[:, h], tm, gq[h], gk[h], eps, base)
+                   for h in range(L.heads)]).astype(np.float32)
+    st = Stage(L, q, k, v, 0.0, sparse=False)
+    out = bf16_host(st.linear(W, b, mu, gq, gk, eps, base)).reshape(L.tokens, L.heads, 64)
+    ref = olin.linear_attention(Q, K, V, tm, W, b, mu, gq, gk, eps, base)
+    close(out, ref, f"{name} linear with gains, eps {eps}, base {base}")
+    # the settings matter at this tolerance: defaults give another output
+    plain = olin.linear_attention(Q, K, V, tm, W, b, mu)
+    assert np.abs(plain - ref).max() > 5e-2
+
+
+def test_32views_linear_gains_rows():
+    L = zs.CONFIGS["32views"]
+    q, k, v = _inputs(L, seed=18)
+    Q, K, V = widen(q), widen(k), widen(v)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    g = np.random.default_rng(18)
+    gq = (0.5 + g.random((L.heads, 64))).astype(np.float32)
+    gk = (0.5 + g.random((L.heads, 64))).astype(np.float32)
+    W, b = zs.affine_params(L, seed=18)
+    mu = (0.01 * g.standard_normal((L.heads, 64))).astype(np.float32)
+    rows = zs.sample_rows(L, 512, seed=18, special_frames=2)
+    st = Stage(L, q, k, v, 0.0, sparse=False)
+    st.linear(W, b, mu, gq, gk, 1e-3, 10000.0)
+    ref = olin.linear_rows(Q, K, V, tm, rows, W, b, mu, gq, gk, 1e-3, 10000.0)
+    close(st.rows(rows), ref, "32 views: linear rows with gains, eps 1e-3, base 1e4")
+
+
 # ------------------------------------------------------------- 32 views
 def test_32views_sparse_selection_and_rows():
     L = zs.CONFIGS["32views"]
@@ -184,7 +229,8 @@ def test_32views_sparse_selection_and_rows():
     st.sparse()
     sel = st.bufs.sel().cpu().numpy()
     sel_ref, tie_ref = _sel_ref(Q, K, tm, y)
-    compare_selection(sel, sel_ref, tie_ref, "32 views: selection (all 16x800 query tiles)")
+    compare_selection(sel, sel_ref, tie_ref, "32 views: selection (all 16x800 query tiles)",
+                      oracle_scores(Q, K, tm, osp))
     # every row of 40 seeded (head, query tile) pairs plus all special rows of 2 heads
     g = np.random.default_rng(0)
     rows = []
@@ -418,7 +464,7 @@ def test_selection_with_outlier_tiles():
     Q, K = widen(q), widen(k)
     sel = Stage(L, q, k, v, y).select()
     sel_ref, tie_ref = _sel_ref(Q, K, tm, y)
-    r = compare_selection(sel, sel_ref, tie_ref, "outlier tiles selection")
+    r = compare_selection(sel, sel_ref, tie_ref, "outlier tiles selection", oracle_scores(Q, K, tm, osp))
     assert r["near_tie"] < r["rows"] // 10
 
 

@@ -160,6 +160,76 @@ def test_rows_and_mean_output():
     assert np.allclose(full.mean(axis=0), mu + b, atol=1e-13)
 
 
+def _brute_head(Q, K, V, tm, W, b, mu, gq, gk, eps, base):
+    """One head's corrected linear output written out token by token with
+    math-module scalars: RMSNorm with gain, the pair rotation by
+    p * base^(-j/16) per 32-channel half, the channel softmax, the O(N^2)
+    weighted sum and y_a = mu_a + b_a + sum_c W[a][c] (o_c - mu_c)."""
+    N, d = Q.shape
+    C = tm.C
+
+    def pos(t):
+        loc = t % tm.tpf
+        return (0, 0) if loc < tm.S else divmod(loc - tm.S, C)
+
+    def phi(x, g, t):
+        ms = sum(c * c for c in x) / d
+        r = math.sqrt(ms + eps)
+        xn = [x[c] / r * g[c] for c in range(d)]
+        out = list(xn)
+        for half, p in enumerate(pos(t)):
+            for j in range(16):
+                a = p * base ** (-j / 16)
+                lo, hi = xn[32 * half + j], xn[32 * half + 16 + j]
+                out[32 * half + j] = lo * math.cos(a) - hi * math.sin(a)
+                out[32 * half + 16 + j] = hi * math.cos(a) + lo * math.sin(a)
+        m = max(out)
+        e = [math.exp(c - m) for c in out]
+        s = sum(e)
+        return [c / s for c in e]
+
+    pk = [phi(K[j], gk, j) for j in range(N)]
+    Y = np.empty((N, d))
+    for i in range(N):
+        pq = phi(Q[i], gq, i)
+        w = [sum(pq[a] * pk[j][a] for a in range(d)) for j in range(N)]
+        den = sum(w)
+        o = [sum(w[j] * V[j][c] for j in range(N)) / den for c in range(d)]
+        Y[i] = [mu[a] + b[a] + sum(W[a][c] * (o[c] - mu[c]) for c in range(d)) for a in range(d)]
+    return Y
+
+
+def test_multi_head_wrapper_takes_each_heads_parameters():
+    """linear_attention and linear_rows with per-head W, b, mu, RMSNorm gains,
+    a non-default eps and rotary base: every head equals the scalar brute
+    force of that head with that head's parameters, and swapping the heads'
+    W (or gains) changes the result, so a per-head mix-up is caught."""
+    tm = TileMap(2, 1, 3, 5)
+    g = np.random.default_rng(8)
+    H, d = 2, 64
+    Q, K, V = g.standard_normal((3, tm.N, H, d))
+    W = np.eye(d)[None].repeat(H, 0) + 0.3 * g.standard_normal((H, d, d))
+    b = g.standard_normal((H, d))
+    mu = g.standard_normal((H, d))
+    gq = 0.5 + g.random((H, d))
+    gk = 0.5 + g.random((H, d))
+    eps, base = 1e-3, 10000.0
+    got = olin.linear_attention(Q, K, V, tm, W, b, mu, gq, gk, eps, base)
+    for h in range(H):
+        want = _brute_head(Q[:, h], K[:, h], V[:, h], tm, W[h], b[h], mu[h], gq[h], gk[h], eps, base)
+        assert np.abs(got[:, h] - want).max() < 1e-11, h
+    rows = np.array([[0, 3], [1, 0], [1, tm.N - 1]])
+    sub = olin.linear_rows(Q, K, V, tm, rows, W, b, mu, gq, gk, eps, base)
+    assert np.abs(sub - got[rows[:, 1], rows[:, 0]]).max() < 1e-13
+    swapped = olin.linear_attention(Q, K, V, tm, W[::-1], b, mu, gq, gk, eps, base)
+    assert np.abs(swapped - got).max() > 1e-2
+    swapped = olin.linear_attention(Q, K, V, tm, W, b, mu, gq[::-1], gk[::-1], eps, base)
+    assert np.abs(swapped - got).max() > 1e-4
+    # eps and base reach the result
+    assert np.abs(olin.linear_attention(Q, K, V, tm, W, b, mu, gq, gk, 1e-6, base) - got).max() > 1e-6
+    assert np.abs(olin.linear_attention(Q, K, V, tm, W, b, mu, gq, gk, eps, 100.0) - got).max() > 1e-4
+
+
 def test_pins_catch_planted_mistakes(monkeypatch):
     tm = TileMap(2, 2, 3, 4)
     g = np.random.default_rng(0)

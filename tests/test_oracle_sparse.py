@@ -172,6 +172,23 @@ def test_dense_matches_scipy_softmax():
     assert np.allclose(got, _scipy_dense(Q[:, 0], K[:, 0], V[:, 0]), atol=1e-13)
 
 
+def test_dense_attention_two_heads_match_scipy_per_head():
+    """The all-heads wrapper (the reference of the dense GPU tests): each
+    head's output equals scipy's softmax attention on that head's own
+    Q, K, V. 300 rows cross the wrapper's 256-row blocks; head 1's inputs
+    are scaled so that a head mix-up cannot go unnoticed."""
+    Q, K, V = _rand_qkv(300, 2, 64, 21)
+    Q[:, 1] *= 2.5
+    V[:, 1] += 3.0
+    got = osp.dense_attention(Q, K, V)
+    assert got.shape == (300, 2, 64)
+    for h in range(2):
+        want = _scipy_dense(Q[:, h], K[:, h], V[:, h])
+        assert np.abs(got[:, h] - want).max() < 1e-12, h
+    other = _scipy_dense(Q[:, 0], K[:, 0], V[:, 0])
+    assert np.abs(got[:, 1] - other).max() > 1.0
+
+
 @pytest.mark.parametrize("shape", [(2, 5, 16, 16), (3, 2, 11, 13)])
 def test_y0_is_dense(shape):
     tm = TileMap(*shape)

@@ -17,8 +17,12 @@
  * Conventions for every entry point
  *   - Sequence layout: F frames; each frame holds S special tokens then an
  *     R x C patch grid in row-major order; N = F*(S+R*C) tokens. Q, K, V and
- *     the output are contiguous bfloat16 arrays [N][H][64] (token, head,
- *     channel). Head dim d must be 64; 1 <= R, C <= 128; H >= 1.
+ *     the output are bfloat16 arrays indexed [token][head][channel]: element
+ *     (n, h, c) of q, k and v sits at n*tok_stride + h*head_stride + c, of
+ *     the output at n*out_tok_stride + h*out_head_stride + c (zebra_layout;
+ *     0 selects the contiguous [N][H][64] strides). The 64 channels of a
+ *     (token, head) row are contiguous. Head dim d must be 64; 1 <= R, C <=
+ *     128; H >= 1.
  *   - Tiles: tile u = f*tpf + a*ceil(C/8) + b (tpf = ceil(R/8)*ceil(C/8))
  *     covers patch rows [8a, min(8a+8,R)) and columns [8b, min(8b+8,C));
  *     n_u = its patch count; T = F*tpf tiles. Lower index wins score ties.
@@ -57,6 +61,18 @@ typedef struct {
   int32_t cols;      /* C, patch grid columns, 1..128 */
   int32_t heads;     /* H >= 1 */
   int32_t head_dim;  /* d, must be 64 */
+  /* Element strides of q, k, v (and the affine teacher) and of out, for
+   * callers whose Q/K/V are views of a fused projection output ("Linear-
+   * centered stages plus tile-sparse stages": the QKV projections are kept,
+   * so the operator reads their output in place). 0 selects the contiguous
+   * value (tok: heads*64, head: 64). Otherwise each must be a positive
+   * multiple of 8 elements (16 bytes) and at least 64; the pointers must be
+   * 16-byte aligned. Rows of different (token, head) pairs may not overlap
+   * in out, nor overlap q, k or v. */
+  int64_t tok_stride;
+  int64_t head_stride;
+  int64_t out_tok_stride;
+  int64_t out_head_stride;
 } zebra_layout;
 
 /* Opaque stream handle: a hipStream_t (NULL = the default stream). */

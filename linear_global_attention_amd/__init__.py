@@ -23,43 +23,16 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzebra.so")
 
-BUF = dict(KT=0, VT=1, KS=2, VS=3, KBAR=4, VBAR=5, LOGN=6, LM=7, SEL=8, SELMASK=9, GAP=10,
-           WORKSPACE=11)
-OP = dict(PACK=0, LANDMARKS=1, SELECT=2, SPARSE=3, LINEAR=4, DENSE=5, AFFINE_STATS=6)
-AFFINE_STATS = 1 + 2 * 64 + 2 * 64 * 64  # doubles of the affine-fit statistics
-STATUS = {0: "ZEBRA_OK", 1: "ZEBRA_ERR_INVALID_ARG", 2: "ZEBRA_ERR_UNSUPPORTED",
-          3: "ZEBRA_ERR_WORKSPACE", 4: "ZEBRA_ERR_HIP"}
-EXPORTS = ["zebra_pack_tiles", "zebra_landmarks", "zebra_select_tiles", "zebra_sparse_attn",
-           "zebra_linear_attn", "zebra_dense_attn", "zebra_validate", "zebra_buffer_bytes",
-           "zebra_keep_count", "zebra_num_tiles", "zebra_last_error", "zebra_version",
-           "zebra_affine_stats", "zebra_affine_solve"]
+from .abi import (AFFINE_STATS, BUF, EXPORTS, OP, STATUS, Args,  # noqa: E402,F401
+                  CLayout, declare as _declare)
+
+_Layout = CLayout
 
 
 class ZebraError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
         self.status = status
-
-
-class _Layout(ctypes.Structure):
-    _fields_ = [("frames", ctypes.c_int32), ("specials", ctypes.c_int32),
-                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
-                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
-
-
-_vp = ctypes.c_void_p
-
-
-class Args(ctypes.Structure):
-    """Mirror of zebra_args."""
-    _fields_ = [("L", _Layout), ("y", ctypes.c_double),
-                ("q", _vp), ("k", _vp), ("v", _vp), ("out", _vp),
-                ("W", _vp), ("b", _vp), ("mu", _vp), ("gq", _vp), ("gk", _vp),
-                ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
-                ("kt", _vp), ("vt", _vp), ("ks", _vp), ("vs", _vp),
-                ("kbar", _vp), ("vbar", _vp), ("logn", _vp), ("lm", _vp),
-                ("sel", _vp), ("selmask", _vp), ("gap", _vp),
-                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
 
 
 def _load() -> ctypes.CDLL:
@@ -71,30 +44,7 @@ def _load() -> ctypes.CDLL:
     # libzebra bind to that copy; loaded the other way round, the process
     # would hold two runtimes and the second one sees no device.
     import torch  # noqa: F401
-    so = ctypes.CDLL(LIB_PATH)
-    P = ctypes.POINTER
-    for name in ("zebra_pack_tiles", "zebra_landmarks", "zebra_select_tiles",
-                 "zebra_sparse_attn", "zebra_linear_attn", "zebra_dense_attn"):
-        f = getattr(so, name)
-        f.argtypes = [P(Args), _vp]
-        f.restype = ctypes.c_int
-    so.zebra_validate.argtypes = [P(Args), ctypes.c_int]
-    so.zebra_validate.restype = ctypes.c_int
-    so.zebra_buffer_bytes.argtypes = [P(_Layout), ctypes.c_double, ctypes.c_int]
-    so.zebra_buffer_bytes.restype = ctypes.c_size_t
-    so.zebra_keep_count.argtypes = [P(_Layout), ctypes.c_double]
-    so.zebra_keep_count.restype = ctypes.c_int64
-    so.zebra_num_tiles.argtypes = [P(_Layout)]
-    so.zebra_num_tiles.restype = ctypes.c_int64
-    so.zebra_last_error.argtypes = []
-    so.zebra_last_error.restype = ctypes.c_char_p
-    so.zebra_version.argtypes = []
-    so.zebra_version.restype = ctypes.c_char_p
-    so.zebra_affine_stats.argtypes = [P(Args), _vp, _vp, _vp]
-    so.zebra_affine_stats.restype = ctypes.c_int
-    so.zebra_affine_solve.argtypes = [_vp, ctypes.c_double, _vp, _vp, _vp]
-    so.zebra_affine_solve.restype = ctypes.c_int
-    return so
+    return _declare(ctypes.CDLL(LIB_PATH))
 
 
 lib = _load()
@@ -186,10 +136,54 @@ def _itemsize(dtype) -> int:
     return torch.empty((), dtype=dtype).element_size()
 
 
+def _rows_view(name, t, L: Layout):
+    """Checks a bf16 [N][H][64] tensor argument (int16 or bfloat16 storage,
+    on the GPU, 64 contiguous channels per row, 16-byte aligned) and returns
+    its (token, head) element strides."""
+    import torch
+    if t.dtype not in (torch.int16, torch.bfloat16):
+        raise ValueError(f"{name}: bf16 data expected (int16 or bfloat16 storage), got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: device tensor expected, got {t.device}")
+    if tuple(t.shape) != (L.tokens, L.heads, L.head_dim):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} is not [N][H][64] = "
+                         f"{(L.tokens, L.heads, L.head_dim)}")
+    if t.stride(2) != 1:
+        raise ValueError(f"{name}: the 64 channels of a row must be contiguous")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name}: data must be 16-byte aligned")
+    return t.stride(0), t.stride(1)
+
+
+def _f32(name, t, n):
+    import torch
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.device.type != "cuda" or not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name}: contiguous float32 device tensor of at least {n} elements expected")
+    return t
+
+
 def make_args(L, q=None, k=None, v=None, out=None, bufs: StageBuffers | None = None, y=0.0,
               W=None, b=None, mu=None, gq=None, gk=None, rms_eps=1e-6, rope_base=100.0) -> Args:
+    """Fills zebra_args from torch tensors after checking them: q, k, v and
+    out bf16 [N][H][64] (views with other token and head strides allowed,
+    e.g. slices of a fused QKV projection; q, k and v must share their
+    strides), W [H][64][64], b, mu, gq, gk [H][64] float32."""
+    Lp = _as_layout(L)
     a = Args()
-    a.L = _as_layout(L).c()
+    a.L = Lp.c()
+    strides = [(n, _rows_view(n, t, Lp)) for n, t in (("q", q), ("k", k), ("v", v)) if t is not None]
+    if strides:
+        if len({st for _, st in strides}) != 1:
+            raise ValueError("q, k and v must have the same token and head strides: "
+                             + ", ".join(f"{n} {st}" for n, st in strides))
+        a.L.tok_stride, a.L.head_stride = strides[0][1]
+    if out is not None:
+        a.L.out_tok_stride, a.L.out_head_stride = _rows_view("out", out, Lp)
+    H = Lp.heads
+    W, b, mu = _f32("W", W, H * 64 * 64), _f32("b", b, H * 64), _f32("mu", mu, H * 64)
+    gq, gk = _f32("gq", gq, H * 64), _f32("gk", gk, H * 64)
     a.y = float(y)
     a.q, a.k, a.v, a.out = _ptr(q), _ptr(k), _ptr(v), _ptr(out)
     a.W, a.b, a.mu, a.gq, a.gk = _ptr(W), _ptr(b), _ptr(mu), _ptr(gq), _ptr(gk)
@@ -246,14 +240,23 @@ def linear_attn(args: Args, stream=None):
     _call(lib.zebra_linear_attn, args, stream)
 
 
+
 def dense_attn(args: Args, stream=None):
     _call(lib.zebra_dense_attn, args, stream)
 
 
 def affine_stats(args: Args, teacher, stats, stream=None):
     """Adds the affine-fit statistics of o = args.out against `teacher`
-    (bf16 [N][H][64], a device tensor) into `stats` (fp64 device tensor of
-    AFFINE_STATS elements, zeroed by the caller before the first call)."""
+    (bf16 [N][H][64], a device tensor with the token and head strides of
+    args' q, k, v) into `stats` (fp64 device tensor of AFFINE_STATS
+    elements, zeroed by the caller before the first call)."""
+    import torch
+    Lp = Layout(args.L.frames, args.L.specials, args.L.rows, args.L.cols, args.L.heads, args.L.head_dim)
+    ts, hs = _rows_view("teacher", teacher, Lp)
+    if (args.L.tok_stride or Lp.heads * 64, args.L.head_stride or 64) != (ts, hs):
+        raise ValueError("teacher must have the token and head strides of q, k and v")
+    if stats.dtype != torch.float64 or stats.device.type != "cuda" or stats.numel() < AFFINE_STATS:
+        raise ValueError(f"stats: float64 device tensor of {AFFINE_STATS} elements expected")
     st = lib.zebra_affine_stats(ctypes.byref(args), _ptr(teacher), _ptr(stats), _stream(stream))
     if st != 0:
         raise ZebraError(st, lib.zebra_last_error().decode())

@@ -39,7 +39,39 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer build (device
+# code is compiled as usual): validation, tile geometry, buffer sizing and
+# the fp64 affine solve, exercised on the CPU by tests/test_sanitized_host.py.
+SAN_LIB = os.path.join(BUILD, "san", "libzebra_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+
+
+def _compile_in(src: str, outdir: str, extra) -> str:
+    obj = os.path.join(outdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    outdir = os.path.dirname(SAN_LIB)
+    os.makedirs(outdir, exist_ok=True)
+    with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda f: _compile_in(f, outdir, SAN_FLAGS), SOURCES))
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, "-shared-libasan", "-o", SAN_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
+def build(verbose: bool = False, sanitized: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
@@ -51,6 +83,8 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    if sanitized:
+        build_sanitized(verbose)
     return LIB
 
 

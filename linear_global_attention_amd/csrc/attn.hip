@@ -109,7 +109,6 @@ template <int G>
 __device__ __forceinline__ void load_queries(const Geom& g, const AttnArgs& A, const QueryGroups& qg, int h,
                                              unsigned slots, int lane, bf16x8 q[G][2]) {
   const int lg = lane >> 4, tl = lane & 15;
-  const long long rs = (long long)g.H * D;
 #pragma unroll
   for (int s = 0; s < G; ++s) {
     const int j = qg.row_block(s) * 16 + tl;
@@ -117,7 +116,7 @@ __device__ __forceinline__ void load_queries(const Geom& g, const AttnArgs& A, c
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (ok) w = *(const uint4*)(A.Q + qg.token(s, j) * rs + h * D + ds * 32 + 8 * lg);
+      if (ok) w = *(const uint4*)(A.Q + qg.token(s, j) * g.in_tok + h * g.in_head + ds * 32 + 8 * lg);
       q[s][ds] = __builtin_bit_cast(bf16x8, w);
     }
   }
@@ -546,7 +545,7 @@ __device__ __forceinline__ void store_slot(const Geom& g, const AttnArgs& A, con
   const float inv = 1.0f / xsum32(xsum16(l));
   const int j = qg.row_block(s) * 16 + tl;
   if (j < qg.rows(s)) {
-    u16* orow = A.O + qg.token(s, j) * ((long long)g.H * D) + h * D;
+    u16* orow = A.O + qg.token(s, j) * g.out_tok + h * g.out_head;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       uint2 wv;

@@ -115,7 +115,6 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) attn_exact_kernel(Geom g, Attn
   const int item = work - h * items_per_head;
   const QueryGroups qg(g, item, patch_items, G, wave);
   const bool sparse = A.sparse && qg.patch;
-  const long long rs = (long long)g.H * D;
   const u16* Kt16 = A.Kt + (long long)h * g.slots * D;
   const u16* Vt16 = A.Vt + (long long)h * g.slots * D;
   const u16* Ks16 = A.Ks + (long long)h * g.spec_pad * D;
@@ -136,7 +135,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) attn_exact_kernel(Geom g, Attn
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (ok) w = *(const uint4*)(A.Q + qg.token(s, j) * rs + h * D + ds * 32 + 8 * lg);
+      if (ok) w = *(const uint4*)(A.Q + qg.token(s, j) * g.in_tok + h * g.in_head + ds * 32 + 8 * lg);
       st.q[s][ds] = __builtin_bit_cast(bf16x8, w);
     }
     st.m[s] = M_INIT;
@@ -334,7 +333,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 1) attn_exact_kernel(Geom g, Attn
     const float inv = 1.0f / xsum32(xsum16(st.l[s]));
     const int j = qg.row_block(s) * 16 + tl;
     if (j < qg.rows(s)) {
-      u16* orow = A.O + qg.token(s, j) * rs + h * D;
+      u16* orow = A.O + qg.token(s, j) * g.out_tok + h * g.out_head;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         uint2 wv;

@@ -256,8 +256,7 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
 
   const long long t_begin = (long long)chunk * tpw;
   const long long t_end = min((long long)g.N, t_begin + tpw);
-  const long long rs = (long long)g.H * D;
-  const long long first = t_begin + 16 * wave;
+    const long long first = t_begin + 16 * wave;
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
   char* ring = &sring[wave][0][0];
   // group m into slot m % ST_NB: copy j of each of K and V fills row
@@ -271,7 +270,7 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
     for (int j = 0; j < 2; ++j) {
       const int r = 8 * j + (lane >> 3);
       const long long tok = min(r0 + r, t_end - 1);
-      const long long off = (tok * rs + h * D) * 2 + (((lane & 7) ^ ls_swz(r)) << 4);
+      const long long off = (tok * g.in_tok + h * g.in_head) * 2 + (((lane & 7) ^ ls_swz(r)) << 4);
       __builtin_amdgcn_global_load_lds((const void*)((const char*)K + off), (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)((const char*)V + off), (lin_lds_void*)(dst + 2048 + j * 1024), 16,
                                        0, 0);
@@ -507,8 +506,7 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
   __syncthreads();
   const long long t_begin = (long long)chunk * tpw;
   const long long t_end = min((long long)g.N, t_begin + tpw);
-  const long long rs = (long long)g.H * D;
-  // This wave's 16-token groups: m = 0..n-1, first token t_begin + 16 (wave + 4m).
+    // This wave's 16-token groups: m = 0..n-1, first token t_begin + 16 (wave + 4m).
   const long long first = t_begin + 16 * wave;
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
   char* ring = &qring[wave][0][0];
@@ -527,7 +525,7 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
       const int r = 8 * j + (lane >> 3);
       const long long tok = min(r0 + r, t_end - 1);
       const int c = (lane & 7) ^ (r & 7);
-      const char* src = (const char*)(Q + tok * rs + h * D) + c * 16;
+      const char* src = (const char*)(Q + tok * g.in_tok + h * g.in_head) + c * 16;
       __builtin_amdgcn_global_load_lds((const void*)src, (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
     }
   };
@@ -626,8 +624,8 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
           "v"(ra1)
         : "memory");
     const long long otok0 = min(first + 64LL * m + rr, t_end - 1), otok1 = min(first + 64LL * m + rr + 8, t_end - 1);
-    *(uint4*)(out + otok0 * rs + h * D + rc * 8) = make_uint4(t0[0], t0[1], t0[2], t0[3]);
-    *(uint4*)(out + otok1 * rs + h * D + rc * 8) = make_uint4(t1[0], t1[1], t1[2], t1[3]);
+    *(uint4*)(out + otok0 * g.out_tok + h * g.out_head + rc * 8) = make_uint4(t0[0], t0[1], t0[2], t0[3]);
+    *(uint4*)(out + otok1 * g.out_tok + h * g.out_head + rc * 8) = make_uint4(t1[0], t1[1], t1[2], t1[3]);
     if (m + AP_NB - 1 < n) stage(m + AP_NB - 1);
   }
 }
@@ -661,8 +659,7 @@ __global__ void __launch_bounds__(LIN_THREADS) affine_stats_kernel(Geom g, const
   const st_v4s ones = __builtin_bit_cast(st_v4s, make_uint2(0x3F803F80u, 0x3F803F80u));  // bf16 1.0 x 4
   const long long t_begin = (long long)chunk * tpw;
   const long long t_end = min((long long)g.N, t_begin + tpw);
-  const long long rs = (long long)g.H * D;
-  const long long first = t_begin + 16 * wave;
+    const long long first = t_begin + 16 * wave;
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
   char* ring = &sring[wave][0][0];
   // group m into slot m % ST_NB (as in linear_state): rows past t_end
@@ -676,9 +673,11 @@ __global__ void __launch_bounds__(LIN_THREADS) affine_stats_kernel(Geom g, const
     for (int j = 0; j < 2; ++j) {
       const int r = 8 * j + (lane >> 3);
       const long long tok = min(r0 + r, t_end - 1);
-      const long long off = (tok * rs + h * D) * 2 + (((lane & 7) ^ ls_swz(r)) << 4);
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)O + off), (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)Tt + off), (lin_lds_void*)(dst + 2048 + j * 1024),
+      const long long sw = ((lane & 7) ^ ls_swz(r)) << 4;
+      const long long offo = (tok * g.out_tok + h * g.out_head) * 2 + sw;  // o: the output's strides
+      const long long offt = (tok * g.in_tok + h * g.in_head) * 2 + sw;    // teacher: q's strides
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)O + offo), (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)Tt + offt), (lin_lds_void*)(dst + 2048 + j * 1024),
                                        16, 0, 0);
     }
   };

@@ -60,7 +60,6 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
   const int slot_in = tid >> 3;  // 0..31
   const int chunk = tid & 7;     // 8 channels each
   const int lane = tid & 63, wave = tid >> 6;
-  const long long rowstride = (long long)g.H * D;
   const int spec_blocks = g.spec_pad / KBLK;
 
   if (LMK && blockIdx.x >= (unsigned)(g.T + spec_blocks)) {  // padding landmark
@@ -110,8 +109,9 @@ __global__ void __launch_bounds__(256) pack_kernel(Geom g, const u16* __restrict
         const int i = (int)base_slot + s;  // special index = frame*S + s
         tok = (long long)(i / g.S) * g.tok_pf + (i % g.S);
       }
-      kv = *(const uint4*)(K + tok * rowstride + (long long)h * D + chunk * 8);
-      vv = *(const uint4*)(V + tok * rowstride + (long long)h * D + chunk * 8);
+      const long long row = tok * g.in_tok + (long long)h * g.in_head;
+      kv = *(const uint4*)(K + row + chunk * 8);
+      vv = *(const uint4*)(V + row + chunk * 8);
     }
     *(uint4*)(Kdst + (base_slot + s) * D + chunk * 8) = kv;
     const u16* pv = (const u16*)&vv;

@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(256) qbar_kernel(Geom g, const u16* __restrict
   for (int i = 0; i < n; i += 4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (i + j < n) s[j] += (double)bf2f(Q[(tile_token_s(g, f, tl, i + j) * g.H + h) * D + d]);
+      if (i + j < n) s[j] += (double)bf2f(Q[tile_token_s(g, f, tl, i + j) * g.in_tok + (long long)h * g.in_head + d]);
   }
   qbar[((long long)h * g.T + t) * D + d] = ((s[0] + s[1]) + (s[2] + s[3])) / n;
 }

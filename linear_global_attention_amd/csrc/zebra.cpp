@@ -1,6 +1,7 @@
 // libzebra host side: argument validation, tile geometry, buffer sizing and
 // kernel launches behind the C ABI declared in include/zebra.h.
 #include <math.h>
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -79,8 +80,21 @@ zebra_status make_geom(const zebra_layout* L, Geom& g) {
   g.nspec = (int)nspec;
   g.spec_pad = pad32(g.nspec);
   g.T_pad = pad32(g.T);
+  const long long rowdef = (long long)g.H * D;
+  const long long st[4] = {L->tok_stride, L->head_stride, L->out_tok_stride, L->out_head_stride};
+  for (int i = 0; i < 4; ++i)
+    if (st[i] != 0 && (st[i] < D || st[i] % 8 != 0 || st[i] > (1LL << 40)))
+      return fail(ZEBRA_ERR_INVALID_ARG, "strides must be 0 or multiples of 8 elements, at least 64");
+  g.in_tok = L->tok_stride ? L->tok_stride : rowdef;
+  g.in_head = L->head_stride ? L->head_stride : D;
+  g.out_tok = L->out_tok_stride ? L->out_tok_stride : rowdef;
+  g.out_head = L->out_head_stride ? L->out_head_stride : D;
   return ZEBRA_OK;
 }
+
+// 16-byte alignment of a caller's tensor pointer (the kernels move rows in
+// 16-byte pieces).
+bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u) != 0; }
 
 int64_t keep_count(const Geom& g, double y) {
   if (!(y >= 0.0 && y <= 1.0)) return -1;
@@ -118,7 +132,11 @@ size_t buf_bytes(const Geom& g, int64_t k, int which) {
 
 zebra_status check_common(const zebra_args* a, Geom& g) {
   if (!a) return fail(ZEBRA_ERR_INVALID_ARG, "args is NULL");
-  return make_geom(&a->L, g);
+  const zebra_status s = make_geom(&a->L, g);
+  if (s != ZEBRA_OK) return s;
+  if (misaligned(a->q) || misaligned(a->k) || misaligned(a->v) || misaligned(a->out))
+    return fail(ZEBRA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  return ZEBRA_OK;
 }
 
 #define NEED(ptr, name) \
@@ -340,6 +358,7 @@ zebra_status zebra_affine_stats(const zebra_args* a, const void* teacher, double
   zebra_status s = validate(a, ZEBRA_OP_AFFINE_STATS, g, k);
   if (s != ZEBRA_OK) return s;
   if (!teacher) return fail(ZEBRA_ERR_INVALID_ARG, "teacher is NULL");
+  if (misaligned(teacher)) return fail(ZEBRA_ERR_INVALID_ARG, "teacher must be 16-byte aligned");
   if (!stats) return fail(ZEBRA_ERR_INVALID_ARG, "stats is NULL");
   return hip_result(launch_affine_stats(g, (const u16*)a->out, (const u16*)teacher, stats, a->workspace,
                                         (hipStream_t)stream),

@@ -124,3 +124,37 @@ def test_affine_entry_points_reject_on_host():
     a.workspace_bytes = 16
     assert f(ctypes.byref(a), buf, buf, None) == 3
     assert zb.lib.zebra_affine_solve(None, 0.0, None, None, None) == 1
+
+
+def test_strides_and_alignment_checked_on_host():
+    """Token/head strides of q, k, v and out: 0 (contiguous) or positive
+    multiples of 8 elements, at least 64; tensor pointers 16-byte aligned."""
+    L = zb.Layout(4, 5, 37, 37, 2)
+    a = _full_args(L, 0.5)
+    a.L.tok_stride, a.L.head_stride = 3 * 2 * 64, 64  # a fused QKV projection
+    a.L.out_tok_stride, a.L.out_head_stride = 2 * 128, 128
+    for op in zb.OP:
+        assert zb.validate(a, op) == 0, op
+    for field, bad in (("tok_stride", 60), ("head_stride", 12), ("out_tok_stride", 100), ("out_head_stride", -64)):
+        b = _full_args(L, 0.5)
+        setattr(b.L, field, bad)
+        assert zb.validate(b, "LINEAR") == 1 and "stride" in zb.last_error(), field
+    b = _full_args(L, 0.5)
+    b.q = ctypes.c_void_p(0x1008)
+    assert zb.validate(b, "SPARSE") == 1 and "aligned" in zb.last_error()
+    # buffer sizes do not depend on the strides
+    Ls = zb.CLayout(4, 5, 37, 37, 2, 64, 384, 64, 256, 128) if hasattr(zb, "CLayout") else None
+    if Ls is not None:
+        assert zb.lib.zebra_buffer_bytes(ctypes.byref(Ls), 0.5, zb.BUF["KT"]) == zb.buffer_bytes(L, 0.5, "KT")
+
+
+def test_make_args_rejects_wrong_tensors():
+    import torch
+    L = zb.Layout(2, 1, 3, 5, 1)
+    x = torch.zeros((L.tokens, 1, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="bf16"):
+        zb.make_args(L, q=x)
+    with pytest.raises(ValueError, match="device"):
+        zb.make_args(L, q=x.to(torch.int16))
+    with pytest.raises(ValueError, match="float32"):
+        zb.make_args(L, W=torch.zeros(64 * 64, dtype=torch.float64))

@@ -216,6 +216,60 @@ def test_32views_linear_gains_rows():
     close(st.rows(rows), ref, "32 views: linear rows with gains, eps 1e-3, base 1e4")
 
 
+def test_fused_qkv_and_strided_output():
+    """Q, K and V as views of one fused projection output [N][3][H][64]
+    (token stride 3*H*64) and the output as every other 64-channel row of a
+    wider buffer (head stride 128): every entry point reads and writes
+    through the strides. Results equal the contiguous run's bit for bit (the
+    same kernels over the same values), the rows between the output views
+    stay untouched, and the sparse output is within tolerance of the oracle."""
+    from gpu_helpers import dev
+    L = zs.Layout(3, 2, 11, 13, heads=2)
+    y = 0.5
+    q, k, v = _inputs(L, seed=19)
+    N, H = L.tokens, L.heads
+    zL = zb.Layout(L.frames, L.specials, L.rows, L.cols, H)
+    W, b = zs.affine_params(L, seed=19)
+    mu = zs.calib_mean(L, seed=19)
+    Wd, bd, mud = (torch.from_numpy(x).cuda() for x in (W, b, mu))
+    st = Stage(L, q, k, v, y)
+    want_sparse = st.sparse().clone()
+    zb.linear_attn(st.args(W=Wd, b=bd, mu=mud))
+    torch.cuda.synchronize()
+    want_linear = st.out.clone()
+    want_dense = st.dense().clone()
+    stats_c = torch.zeros(zb.AFFINE_STATS, dtype=torch.float64, device="cuda")
+    st.out.copy_(want_linear)
+    zb.affine_stats(st.args(), st.v, stats_c)
+
+    qkv = torch.stack([dev(q), dev(k), dev(v)], dim=1)  # [N][3][H][64]
+    qv, kv, vv = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    wide = torch.full((N, H, 2, 64), 0x1234, dtype=torch.int16, device="cuda")
+    ov = wide[:, :, 1]
+    bufs = zb.StageBuffers(zL, y)
+    a = zb.make_args(zL, qv, kv, vv, ov, bufs, y)
+    assert (a.L.tok_stride, a.L.head_stride, a.L.out_tok_stride, a.L.out_head_stride) == (3 * H * 64, 64, H * 128, 128)
+    zb.sparse_stage(a)
+    torch.cuda.synchronize()
+    assert torch.equal(ov, want_sparse), "strided sparse stage differs from the contiguous one"
+    out = bf16_host(ov.contiguous()).reshape(N, H, 64)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    O_ref, _, _ = osp.sparse_attention(widen(q), widen(k), widen(v), tm, y)
+    close(out, O_ref, "fused-QKV strided sparse output")
+    zb.linear_attn(zb.make_args(zL, qv, kv, vv, ov, bufs, y, W=Wd, b=bd, mu=mud))
+    torch.cuda.synchronize()
+    assert torch.equal(ov, want_linear), "strided linear stage differs"
+    stats_s = torch.zeros(zb.AFFINE_STATS, dtype=torch.float64, device="cuda")
+    zb.affine_stats(zb.make_args(zL, qv, kv, vv, ov, bufs, y), vv, stats_s)
+    torch.cuda.synchronize()
+    assert torch.equal(stats_s, stats_c), "affine statistics through strides differ"
+    zb.dense_attn(zb.make_args(zL, qv, kv, vv, ov, bufs, y))
+    torch.cuda.synchronize()
+    assert torch.equal(ov, want_dense), "strided dense attention differs"
+    assert bool((wide[:, :, 0] == 0x1234).all()), "rows between the output views were written"
+    log("fused QKV / strided output: sparse, linear, affine statistics, dense bit-equal")
+
+
 # ------------------------------------------------------------- 32 views
 def test_32views_sparse_selection_and_rows():
     L = zs.CONFIGS["32views"]

@@ -56,3 +56,32 @@ def test_affine_and_rows():
     spec = rows[(rows[:, 1] % tpf) < L.specials]
     assert len(spec) >= 4 * 5 * 16
     assert np.array_equal(rows, zs.sample_rows(L, 2048, seed=0, special_frames=4))
+
+
+def test_device_generator_model_and_determinism():
+    """The torch-drawn variant (used where every stage of a long schedule
+    needs fresh inputs) follows the same tile-centroid model: keys of a block
+    share a centroid, queries follow the neighbouring frames' centroids,
+    specials and values are unit normal; it is deterministic per (seed,
+    stage) and bf16-rounded."""
+    import torch
+    L = zs.Layout(4, 5, 16, 16, heads=2)
+    q, k, v = zs.stage_inputs_device(L, seed=3, device="cpu")
+    q2, _, _ = zs.stage_inputs_device(L, seed=3, device="cpu")
+    q3, _, _ = zs.stage_inputs_device(L, seed=3, stage=1, device="cpu")
+    assert q.dtype == torch.int16 and q.shape == (L.tokens, 2, 64)
+    assert torch.equal(q, q2) and not torch.equal(q, q3)
+    f = lambda t: zs.bf16_to_f32(t.numpy().view(np.uint16)).astype(np.float64)  # noqa: E731
+    q, k, v = f(q), f(k), f(v)
+    tpf = L.tokens_per_frame
+    blk = [5 + r * 16 + c for r in range(8) for c in range(8)]
+    kk = k[blk, 0]
+    assert kk.std(axis=0).mean() < 0.7 and np.abs(kk.mean(axis=0)).mean() > 0.3
+    q1 = q[[tpf + x for x in blk], 0].mean(axis=0)
+    kc = 0.75 * (kk.mean(axis=0) + k[[2 * tpf + x for x in blk], 0].mean(axis=0))
+    assert np.corrcoef(q1, kc)[0, 1] > 0.95
+    assert abs(v.mean()) < 0.05 and abs(v.std() - 1) < 0.05
+    spec = q[[f * tpf + s for f in range(4) for s in range(5)]]
+    assert abs(spec.std() - 1) < 0.15
+    mu = zs.calib_mean(L, seed=3, stage=2)
+    assert mu.shape == (2, 64) and mu.dtype == np.float32 and np.abs(mu).max() < 0.06

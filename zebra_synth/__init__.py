@@ -37,12 +37,12 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = [
-    "Layout", "CONFIGS", "stage_inputs", "affine_params", "sample_rows",
-    "bf16_to_f32", "f32_to_bf16", "draw_threads",
+    "Layout", "CONFIGS", "stage_inputs", "stage_inputs_device", "affine_params", "calib_mean",
+    "sample_rows", "bf16_to_f32", "f32_to_bf16", "draw_threads",
 ]
 
 TOKEN_CHUNK = 2048
-_T_CENTROID, _T_Q, _T_K, _T_V, _T_W, _T_B, _T_ROWS = range(7)
+_T_CENTROID, _T_Q, _T_K, _T_V, _T_W, _T_B, _T_ROWS, _T_MU = range(8)
 
 
 @dataclass(frozen=True)
@@ -144,6 +144,44 @@ def stage_inputs(L: Layout, seed: int = 0, stage: int = 0, threads: int | None =
     with ThreadPoolExecutor(threads or draw_threads()) as ex:
         list(ex.map(work, range(nchunks)))
     return q, k, v
+
+
+def stage_inputs_device(L: Layout, seed: int = 0, stage: int = 0, device="cuda"):
+    """The same tile-centroid model drawn with torch's generator on `device`
+    (fast enough to give every stage of a long schedule fresh inputs). The
+    stream is torch's, keyed by (seed, stage, tensor), so the values differ
+    from stage_inputs'; anything checked against the oracle reads these
+    tensors' own bytes back. Returns (q, k, v) as int16 tensors [N][H][d]
+    holding bfloat16 bit patterns (round to nearest even)."""
+    import torch
+    H, d, F, S = L.heads, L.head_dim, L.frames, L.specials
+    blocks = -(-L.rows // 8) * -(-L.cols // 8)
+
+    def gen(tensor: int):
+        g = torch.Generator(device=device)
+        g.manual_seed((int(seed) * 1_000_003 + int(stage)) * 16 + tensor)
+        return g
+
+    cen = torch.randn((F, blocks, H, d), generator=gen(_T_CENTROID), device=device, dtype=torch.float32)
+    idx = torch.arange(F, device=device)
+    nb = (cen[(idx - 1) % F] + cen[(idx + 1) % F]) * 0.75
+    blk = torch.from_numpy(_block_of_patch(L)).to(device)
+    out = []
+    for tid in (_T_Q, _T_K, _T_V):
+        e = torch.randn((F, L.tokens_per_frame, H, d), generator=gen(tid), device=device, dtype=torch.float32)
+        if tid != _T_V:
+            e[:, S:] *= 0.5
+            e[:, S:] += (nb if tid == _T_Q else cen)[:, blk]
+        out.append(e.reshape(L.tokens, H, d).to(torch.bfloat16).view(torch.int16))
+        del e
+    return tuple(out)
+
+
+def calib_mean(L: Layout, seed: int = 0, stage: int = 0):
+    """A seeded stand-in for the calibration mean mu of the centred affine
+    correction, 0.01 * N(0, I) per head (float32 [H][d])."""
+    return (_rng(seed, stage, _T_MU, 0).standard_normal((L.heads, L.head_dim), dtype=np.float32)
+            * np.float32(0.01))
 
 
 def affine_params(L: Layout, seed: int = 0, stage: int = 0):

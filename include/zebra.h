@@ -195,6 +195,22 @@ zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream);
  * gq, gk; writes out. Uses the workspace. */
 zebra_status zebra_linear_attn(const zebra_args* a, zebra_stream stream);
 
+/* zebra_linear_attn for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same result, but the scratch they need (partial
+ * KV states, their sum and the folded state) lives in a static device array
+ * of ZEBRA_NOALLOC_SCRATCH_BYTES that the library holds on every device it
+ * runs on until the process ends; a->workspace is ignored. Reads q, k, v, W,
+ * b, mu, gq, gk; writes out. The caller passes inputs and outputs only.
+ * Calls no allocating routine (the first call on a device looks up the
+ * array's address once). Layouts needing more scratch than the maximum
+ * (about 1,300 views of 37x37 patches at 16 heads) are rejected with
+ * ZEBRA_ERR_WORKSPACE before any launch. Every call on a device shares that
+ * device's array: calls that overlap on one device (other streams, other
+ * threads) race and must be serialised by the caller. */
+#define ZEBRA_NOALLOC_SCRATCH_BYTES (64u << 20)
+zebra_status zebra_linear_attn_noalloc(const zebra_args* a, zebra_stream stream);
+
 /* Dense softmax attention of every token over all N keys ("Global attention
  * dominates runtime as views grow"): the measurement baseline. Reads q, k,
  * v; writes kt, vt, ks, vs, kbar, vbar, logn, lm (it packs and builds the

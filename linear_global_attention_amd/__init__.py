@@ -16,14 +16,14 @@ from dataclasses import dataclass
 __all__ = [
     "ZebraError", "lib", "Layout", "Args", "StageBuffers", "keep_count", "num_tiles",
     "buffer_bytes", "pack_tiles", "landmarks", "select_tiles", "sparse_attn", "linear_attn",
-    "dense_attn", "sparse_stage", "validate", "EXPORTS",
+    "dense_attn", "sparse_stage", "validate", "EXPORTS", "linear_attn_noalloc",
     "BUF", "OP",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzebra.so")
 
-from .abi import (AFFINE_STATS, BUF, EXPORTS, OP, STATUS, Args,  # noqa: E402,F401
+from .abi import (AFFINE_STATS, BUF, EXPORTS, NOALLOC_SCRATCH_BYTES, OP, STATUS, Args,  # noqa: E402,F401
                   CLayout, declare as _declare)
 
 _Layout = CLayout
@@ -238,6 +238,12 @@ def sparse_attn(args: Args, stream=None):
 
 def linear_attn(args: Args, stream=None):
     _call(lib.zebra_linear_attn, args, stream)
+
+
+def linear_attn_noalloc(args: Args, stream=None):
+    """zebra_linear_attn with the library's static device scratch in place
+    of args.workspace (for callers that cannot allocate)."""
+    _call(lib.zebra_linear_attn_noalloc, args, stream)
 
 
 

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/zebra.h"
@@ -237,6 +238,38 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
   return ZEBRA_OK;
 }
 
+zebra_status hip_result(hipError_t e, const char* what);
+
+// Device scratch of zebra_linear_attn_noalloc: the linear stage's partial KV
+// states, their fp64 sum and the folded state, in place of a workspace. One
+// copy per device, held until the process ends. Host code never passes
+// `scratch` itself to a kernel (on the host it names a stand-in, not device
+// memory): it takes the device address that hipGetSymbolAddress returns, once
+// per device, with that device current.
+static __device__ __align__(256) char scratch[ZEBRA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's scratch address (looked up on its first use).
+zebra_status device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_result(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(ZEBRA_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_result(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(ZEBRA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ZEBRA_OK;
+}
+
 zebra_status hip_result(hipError_t e, const char* what) {
   if (e != hipSuccess) {
     char buf[256];
@@ -350,6 +383,33 @@ zebra_status zebra_linear_attn(const zebra_args* a, zebra_stream stream) {
                                   (const u16*)a->v, a->W, a->b, a->mu, a->gq, a->gk,
                                   (u16*)a->out, a->workspace, (hipStream_t)stream),
                     "zebra_linear_attn");
+}
+
+zebra_status zebra_linear_attn_noalloc(const zebra_args* a, zebra_stream stream) {
+  Geom g;
+  zebra_status s = check_common(a, g);
+  if (s != ZEBRA_OK) return s;
+  NEED(a->q, "q");
+  NEED(a->k, "k");
+  NEED(a->v, "v");
+  NEED(a->out, "out");
+  const size_t need = linear_workspace_bytes(g);
+  if (need > (size_t)ZEBRA_NOALLOC_SCRATCH_BYTES) {
+    char buf[160];
+    snprintf(buf, sizeof buf, "zebra_linear_attn_noalloc: layout needs %zu scratch bytes, the maximum is %zu",
+             need, (size_t)ZEBRA_NOALLOC_SCRATCH_BYTES);
+    return fail(ZEBRA_ERR_WORKSPACE, buf);
+  }
+  void* ws = nullptr;
+  s = device_scratch(&ws);
+  if (s != ZEBRA_OK) return s;
+  g_err.clear();
+  const float eps = a->rms_eps > 0.f ? a->rms_eps : 1e-6f;
+  const float base = a->rope_base > 0.f ? a->rope_base : 100.0f;
+  return hip_result(launch_linear(g, eps, base, (const u16*)a->q, (const u16*)a->k,
+                                  (const u16*)a->v, a->W, a->b, a->mu, a->gq, a->gk,
+                                  (u16*)a->out, ws, (hipStream_t)stream),
+                    "zebra_linear_attn_noalloc");
 }
 
 zebra_status zebra_affine_stats(const zebra_args* a, const void* teacher, double* stats, zebra_stream stream) {

@@ -88,6 +88,8 @@ for op in (2, 3, 4, 5, 6):
 a = args(L, 0.5, fill=False)
 for name in abi.STAGE_CALLS:
     check(getattr(so, name)(ctypes.byref(a), None) == 1, name)
+big = args(layout(4096, 5, 37, 37, 16), 0.0)
+check(so.zebra_linear_attn_noalloc(ctypes.byref(big), None) == 3, "no-alloc scratch limit")
 check(so.zebra_affine_stats(ctypes.byref(args(L, 0.5)), None, None, None) == 1, "affine stats NULLs")
 # fp64 affine solve: recovers a planted map from exact statistics
 n, d = 5000, 64

@@ -126,6 +126,21 @@ def test_affine_entry_points_reject_on_host():
     assert zb.lib.zebra_affine_solve(None, 0.0, None, None, None) == 1
 
 
+def test_noalloc_linear_rejects_on_host():
+    """zebra_linear_attn_noalloc checks its pointers and that the layout's
+    scratch fits the library's static array before any GPU call."""
+    f = zb.lib.zebra_linear_attn_noalloc
+    big = zb.Layout(2048, 5, 37, 37, 16)  # about 100 MB of partial states
+    a = _full_args(big, 0.0)
+    assert f(ctypes.byref(a), None) == 3 and "scratch" in zb.last_error()
+    a = _full_args(zb.Layout(4, 5, 37, 37, 2), 0.0)
+    a.k = None
+    assert f(ctypes.byref(a), None) == 1 and "k" in zb.last_error()
+    a = _full_args(zb.Layout(4, 5, 37, 37, 2, head_dim=32), 0.0)
+    assert f(ctypes.byref(a), None) == 2
+    assert zb.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def test_strides_and_alignment_checked_on_host():
     """Token/head strides of q, k, v and out: 0 (contiguous) or positive
     multiples of 8 elements, at least 64; tensor pointers 16-byte aligned."""

@@ -259,6 +259,12 @@ def test_fused_qkv_and_strided_output():
     zb.linear_attn(zb.make_args(zL, qv, kv, vv, ov, bufs, y, W=Wd, b=bd, mu=mud))
     torch.cuda.synchronize()
     assert torch.equal(ov, want_linear), "strided linear stage differs"
+    an = zb.make_args(zL, qv, kv, vv, ov, bufs, y, W=Wd, b=bd, mu=mud)
+    an.workspace, an.workspace_bytes = None, 0
+    ov.fill_(0)
+    zb.linear_attn_noalloc(an)
+    torch.cuda.synchronize()
+    assert torch.equal(ov, want_linear), "strided no-alloc linear stage differs"
     stats_s = torch.zeros(zb.AFFINE_STATS, dtype=torch.float64, device="cuda")
     zb.affine_stats(zb.make_args(zL, qv, kv, vv, ov, bufs, y), vv, stats_s)
     torch.cuda.synchronize()
@@ -267,7 +273,7 @@ def test_fused_qkv_and_strided_output():
     torch.cuda.synchronize()
     assert torch.equal(ov, want_dense), "strided dense attention differs"
     assert bool((wide[:, :, 0] == 0x1234).all()), "rows between the output views were written"
-    log("fused QKV / strided output: sparse, linear, affine statistics, dense bit-equal")
+    log("fused QKV / strided output: sparse, linear, no-alloc linear, affine statistics, dense bit-equal")
 
 
 # ------------------------------------------------------------- 32 views

@@ -199,7 +199,7 @@ __device__ __forceinline__ void attend_block(MainState<SW>& st, unsigned us, con
 // is the initial value of the S^T accumulators.
 template <int SW>
 __device__ __forceinline__ void attend_landmarks(MainState<SW>& st, unsigned us, const char* kb, int lb,
-                                                 cmask_ptr mrow0, int nwords, int lane) {
+                                                 cmask_ptr mrow0, long long mstep, int lane) {
   bf16x8 kf[2][2], vf[4];
   load_kfrag(kb, 0, lane, kf);
   load_vfrag(kb + LDS_V, lane, vf);
@@ -209,7 +209,7 @@ __device__ __forceinline__ void attend_landmarks(MainState<SW>& st, unsigned us,
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
     if (!((us >> s) & 1u)) continue;
-    const unsigned kept = mrow0[(long long)s * nwords + lb];
+    const unsigned kept = mrow0[s * mstep + lb];
     f32x4 c0, c1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -242,7 +242,7 @@ struct FastItem {
 // record >> 8 is the group's index (head-major) in the flag array.
 __device__ __forceinline__ long long lane_record(const Geom& g, const QueryGroups& qg, int h, int s, int lane) {
   const FastItems fi(g);
-  const int gid = (qg.patch ? 0 : g.T) + qg.gid0 + s;
+  const int gid = (qg.patch ? 0 : g.T) + qg.tile(s);
   return (((long long)h * fi.groups_per_head + gid) * 4 + qg.row_block(s)) * 64 + lane;
 }
 
@@ -377,7 +377,7 @@ __global__ void __launch_bounds__(FWAVES * 64) attn_bound_kernel(Geom g, AttnArg
   const FastItem it(g, blockIdx.x);
   const int h = it.h;
   const FastItems fi(g);
-  const QueryGroups qg(g, it.item, fi.patch_items, G, simd, s0);  // this wave's SW slots
+  const QueryGroups qg(g, it.item, fi.patch_items, G, simd, s0, true);  // this wave's SW slots
   const u16* Kt16 = A.Kt + (long long)h * g.slots * D;
   const u16* Ks16 = A.Ks + (long long)h * g.spec_pad * D;
   const float kmax = sqrtf(__uint_as_float(kmax2[h])) * 1.01f;
@@ -443,7 +443,8 @@ __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int 
   const int local = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (local >= nunits) return;  // uniform per wave
   const Unit un(g, segs, unit0 + local);
-  const QueryGroups qgi(g, un.item, fi.patch_items, G, 0);
+  const QueryGroups qgi(g, un.item, fi.patch_items, G, 0, 0, true);
+  const long long mstep = (long long)qgi.stride * A.nwords;  // mask words between the item's groups
   const bool sparse = A.sparse && qgi.patch;
   int w0, w1;
   seg_words(A.nwords, segs, un.seg, w0, w1);
@@ -460,7 +461,7 @@ __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int 
       unsigned lm = 0u;
 #pragma unroll
       for (int s = 0; s < G; ++s)
-        if (w < w1 && ((valid >> s) & 1u) && mrow[(long long)s * A.nwords + w] != 0xFFFFFFFFu) lm |= 1u << s;
+        if (w < w1 && ((valid >> s) & 1u) && mrow[s * mstep + w] != 0xFFFFFFFFu) lm |= 1u << s;
       const unsigned long long bal = __ballot(lm != 0u);
       if (lm)
         out[base + __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u))] =
@@ -482,7 +483,7 @@ __global__ void __launch_bounds__(256) attn_plan_kernel(Geom g, AttnArgs A, int 
       unsigned v = 0u;
       if (on && ((valid >> s) & 1u)) {
         if (sparse) {
-          v = mrow[(long long)s * A.nwords + w];
+          v = mrow[s * mstep + w];
         } else {
           const int rem = g.T - w * 32;
           v = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
@@ -588,7 +589,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   const Unit un(g, segs, unit0 + blockIdx.x);
   const int h = un.h;
   const FastItems fi(g);
-  const QueryGroups qg(g, un.item, fi.patch_items, G, simd, s0);   // this wave's SW slots
+  const QueryGroups qg(g, un.item, fi.patch_items, G, simd, s0, true);   // this wave's SW slots
   const bool sparse = A.sparse && qg.patch;
   const u16* Kt16 = A.Kt + (long long)h * g.slots * D;
   const u16* Vt16 = A.Vt + (long long)h * g.slots * D;
@@ -613,10 +614,11 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   ZEBRA_VMCNT(0);
 
   const char* lmh = (const char*)A.LM + (long long)h * g.T_pad * LM_BYTES_PER_TILE;
-  // kept-tile bitmap row of this wave's slot s: mrow0 + s * nwords (patch
-  // groups are consecutive query tiles)
+  // kept-tile bitmap row of this wave's slot s: mrow0 + s * mstep (the
+  // item's groups are stride tiles apart)
   const cmask_ptr mrow0 =
       (cmask_ptr)(sparse ? A.selmask + ((long long)h * g.T + qg.gid0) * A.nwords : A.selmask);
+  const long long mstep = (long long)qg.stride * A.nwords;
   const int nlb = g.T_pad / KBLK;
 
   // This unit's plan: `count` entries, in chunks of PLAN_CHUNK that each
@@ -687,7 +689,7 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
   auto consume_lm = [&](const Item& it, const char* kb) {
     if (it.kind() != KIND_LANDMARK) return;
     const unsigned us = (it.users() >> s0) & slots;
-    if (us) attend_landmarks<SW>(st, us, kb, it.index(), mrow0, A.nwords, lane);
+    if (us) attend_landmarks<SW>(st, us, kb, it.index(), mrow0, mstep, lane);
   };
   auto consume = [&](const Item& it, const char* kb) {
     const unsigned us = (it.users() >> s0) & slots;
@@ -732,8 +734,8 @@ __global__ void __launch_bounds__(FWAVES * 64, FOCC) attn_main_kernel(Geom g, At
 #pragma unroll
     for (int s = 0; s < SW; ++s) {
       if (!((slots >> s) & 1u)) continue;
-      const int t = qg.gid0 + s;
-      if ((mrow0[(long long)s * A.nwords + (t >> 5)] >> (t & 31)) & 1u) continue;
+      const int t = qg.tile(s);
+      if ((mrow0[s * mstep + (t >> 5)] >> (t & 31)) & 1u) continue;
       const int j = qg.row_block(s) * 16 + tl_a;
       const bool okrow = j < qg.rows(s);
       const long long slot = qg.own_slot(s, j);
@@ -777,7 +779,7 @@ __global__ void __launch_bounds__(FWAVES * 64) attn_special_combine_kernel(Geom 
   const int simd = wave & 3, s0 = (wave >> 2) * SW;
   const FastItems fi(g);
   const int h = blockIdx.x / fi.spec_items, si = blockIdx.x - h * fi.spec_items;
-  const QueryGroups qg(g, fi.patch_items + si, fi.patch_items, G, simd, s0);
+  const QueryGroups qg(g, fi.patch_items + si, fi.patch_items, G, simd, s0, true);
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
     if (qg.row_block(s) * 16 >= qg.rows(s)) continue;  // uniform

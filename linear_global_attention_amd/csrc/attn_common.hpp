@@ -152,28 +152,47 @@ __device__ __forceinline__ unsigned lane_valid_mask(int nvalid, int lane) {
 }
 
 // The query groups of one work item (G groups), seen from one wave that
-// holds slots i = 0.. for groups s = s0 + i. Patch item: query tiles
-// gid0..gid0+G-1; special item: groups of 64 special rows. Row block j (16
-// rows) of group s belongs to the wave with `wave` == (s + j) % 4 (the SIMD
-// index when two waves share a SIMD).
+// holds slots i = 0.. for groups s = s0 + i; slot i is group tile(i) =
+// gid0 + i * stride. Patch item: G query tiles, either consecutive ones
+// (stride 1) or, with by_position, the tiles at one tile position in G
+// consecutive frames (stride = tiles per frame: the same image region seen
+// from neighbouring views keeps similar key tiles, so the item's groups
+// share more of the tiles it stages); special item: groups of 64 special
+// rows. Row block j (16 rows) of group s belongs to the wave with `wave` ==
+// (s + j) % 4 (the SIMD index when two waves share a SIMD).
 struct QueryGroups {
   const Geom& g;
   bool patch;
   int gid0;
+  int stride;
   int wave;
   int s0;
-  __device__ QueryGroups(const Geom& g_, int item, int patch_items, int G, int wave_, int s0_ = 0)
-      : g(g_), patch(item < patch_items),
-        gid0((item < patch_items ? item * G : (item - patch_items) * G) + s0_), wave(wave_), s0(s0_) {}
+  __device__ QueryGroups(const Geom& g_, int item, int patch_items, int G, int wave_, int s0_ = 0,
+                         bool by_position = false)
+      : g(g_), patch(item < patch_items), wave(wave_), s0(s0_) {
+    if (!patch) {
+      gid0 = (item - patch_items) * G + s0_;
+      stride = 1;
+    } else if (by_position) {
+      const int nfb = (g.F + G - 1) / G;  // frame blocks per tile position
+      const int u = item / nfb, b = item - u * nfb;
+      gid0 = (b * G + s0_) * g.tpf + u;
+      stride = g.tpf;
+    } else {
+      gid0 = item * G + s0_;
+      stride = 1;
+    }
+  }
+  __device__ int tile(int s) const { return gid0 + s * stride; }
   __device__ int rows(int s) const {
-    const int id = gid0 + s;
+    const int id = tile(s);
     if (patch) return id < g.T ? tile_n(g, id % g.tpf) : 0;
     return max(0, min(64, g.nspec - id * 64));
   }
   __device__ int row_block(int s) const { return (wave - s0 - s) & 3; }
   // token index of row j of group s
   __device__ long long token(int s, int j) const {
-    const int id = gid0 + s;
+    const int id = tile(s);
     if (patch) {
       const int f = id / g.tpf, tl = id - f * g.tpf;
       const int a = tl / g.tc, b = tl - a * g.tc;
@@ -186,7 +205,7 @@ struct QueryGroups {
   }
   // packed slot of the row's own key (in Kt/Vt for patch rows, Ks/Vs else)
   __device__ long long own_slot(int s, int j) const {
-    const int id = gid0 + s;
+    const int id = tile(s);
     if (patch) {
       const int f = id / g.tpf, tl = id - f * g.tpf;
       return (long long)f * g.slots_pf + tile_off(g, tl) + j;
@@ -208,12 +227,13 @@ struct ItemCounts {
 };
 
 // Work items of the fast kernels (FG groups each), per head: the special
-// items first, then the patch items. Groups of a head: T patch query tiles,
-// then ceil(nspec/64) special groups.
+// items first, then the patch items (grouped by tile position: FG
+// consecutive frames at one tile position). Groups of a head: T patch query
+// tiles, then ceil(nspec/64) special groups.
 struct FastItems {
   int spec_items, patch_items, per_head, total, groups_per_head;
   __host__ __device__ explicit FastItems(const Geom& g) {
-    patch_items = (g.T + FG - 1) / FG;
+    patch_items = g.tpf * ((g.F + FG - 1) / FG);
     const int sg = (g.nspec + 63) / 64;
     spec_items = (sg + FG - 1) / FG;
     per_head = spec_items + patch_items;

@@ -145,7 +145,8 @@ enum {
   ZEBRA_OP_SPARSE = 3,
   ZEBRA_OP_LINEAR = 4,
   ZEBRA_OP_DENSE = 5,
-  ZEBRA_OP_AFFINE_STATS = 6
+  ZEBRA_OP_AFFINE_STATS = 6,
+  ZEBRA_OP_COVERAGE = 7
 };
 
 /* Pack K and V into tile-major order ("Speedup scales with the number of
@@ -216,6 +217,25 @@ zebra_status zebra_linear_attn_noalloc(const zebra_args* a, zebra_stream stream)
  * v; writes kt, vt, ks, vs, kbar, vbar, logn, lm (it packs and builds the
  * per-tile key bounds first) and out; uses the workspace. */
 zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream);
+
+/* Attention-mass coverage diagnostic of a tile-sparse stage ("Sensitive
+ * stages also concentrate their attention": stages are profiled by how
+ * concentrated their attention mass is, and sparse selection covers most
+ * of it where softmax matters). For every head and patch query tile t,
+ * averaged over the tile's rows i:
+ *   coverage[h][t] = share of row i's DENSE softmax mass (all N keys,
+ *                    logits q.k/8) that falls on the tokens of the key
+ *                    tiles t kept;
+ *   lm_error[h][t] = 1 - L_i/E_i, E_i the exact mass of the omitted tiles'
+ *                    tokens and L_i the mass their landmarks give them
+ *                    (n_u exp(q.kbar_u/8), kbar rounded to bf16 as the
+ *                    sparse kernel uses it); 0 if no tile is omitted. In
+ *                    [0, 1) by Jensen's inequality (up to rounding).
+ * Reads q, kt, ks, lm (zebra_pack_tiles with the landmark buffers, or
+ * zebra_landmarks) and selmask (zebra_select_tiles at the stage's y);
+ * writes coverage and lm_error, device float32 [H][T]. Dense work: two
+ * passes of Q.K^T over every key. */
+zebra_status zebra_coverage(const zebra_args* a, float* coverage, float* lm_error, zebra_stream stream);
 
 /* Statistics of the closed-form centred affine fit of a linear stage ("A
  * closed-form fit avoids retraining from scratch": teacher softmax outputs

@@ -268,6 +268,21 @@ def affine_stats(args: Args, teacher, stats, stream=None):
         raise ZebraError(st, lib.zebra_last_error().decode())
 
 
+def coverage(args: Args, cov, lm_error, stream=None):
+    """Attention-mass coverage of the kept tiles and landmark error of the
+    omitted ones per (head, query tile), into float32 device tensors
+    cov, lm_error of H*T elements. Needs the packed keys, landmarks and the
+    kept-tile bitmap of args' stage (pack_tiles and select_tiles first)."""
+    import torch
+    n = args.L.heads * num_tiles(Layout(args.L.frames, args.L.specials, args.L.rows, args.L.cols, args.L.heads))
+    for name, t in (("cov", cov), ("lm_error", lm_error)):
+        if t.dtype != torch.float32 or t.device.type != "cuda" or not t.is_contiguous() or t.numel() < n:
+            raise ValueError(f"{name}: contiguous float32 device tensor of {n} elements expected")
+    st = lib.zebra_coverage(ctypes.byref(args), _ptr(cov), _ptr(lm_error), _stream(stream))
+    if st != 0:
+        raise ZebraError(st, lib.zebra_last_error().decode())
+
+
 def affine_solve(stats, lambda_rel: float):
     """fp64 host solve of the centred affine fit from the statistics (a
     host float64 array of AFFINE_STATS elements): returns W [64][64], b [64],

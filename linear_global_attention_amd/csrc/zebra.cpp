@@ -27,6 +27,8 @@ hipError_t launch_linear(const Geom&, float, float, const u16*, const u16*, cons
                          u16*, void*, hipStream_t);
 size_t affine_workspace_bytes(const Geom&);
 hipError_t launch_affine_stats(const Geom&, const u16*, const u16*, double*, void*, hipStream_t);
+hipError_t launch_coverage(const Geom&, const u16*, const u16*, const u16*, const u16*, const unsigned*, float*,
+                           float*, hipStream_t);
 }  // namespace zebra
 
 using namespace zebra;
@@ -231,6 +233,14 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
       if (a->workspace_bytes < affine_workspace_bytes(g))
         return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_affine_stats");
       break;
+    case ZEBRA_OP_COVERAGE:
+      if (k < 0) return fail(ZEBRA_ERR_INVALID_ARG, "y must lie in [0, 1]");
+      NEED(a->q, "q");
+      NEED(a->kt, "kt");
+      NEED(a->ks, "ks");
+      NEED(a->lm, "lm");
+      NEED(a->selmask, "selmask");
+      break;
     default:
       return fail(ZEBRA_ERR_INVALID_ARG, "unknown operation");
   }
@@ -410,6 +420,17 @@ zebra_status zebra_linear_attn_noalloc(const zebra_args* a, zebra_stream stream)
                                   (const u16*)a->v, a->W, a->b, a->mu, a->gq, a->gk,
                                   (u16*)a->out, ws, (hipStream_t)stream),
                     "zebra_linear_attn_noalloc");
+}
+
+zebra_status zebra_coverage(const zebra_args* a, float* coverage, float* lm_error, zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_COVERAGE, g, k);
+  if (s != ZEBRA_OK) return s;
+  if (!coverage || !lm_error) return fail(ZEBRA_ERR_INVALID_ARG, "coverage and lm_error must be non-NULL");
+  return hip_result(launch_coverage(g, (const u16*)a->q, (const u16*)a->kt, (const u16*)a->ks, (const u16*)a->lm,
+                                    (const unsigned*)a->selmask, coverage, lm_error, (hipStream_t)stream),
+                    "zebra_coverage");
 }
 
 zebra_status zebra_affine_stats(const zebra_args* a, const void* teacher, double* stats, zebra_stream stream) {

@@ -17,6 +17,9 @@ float64; bf16 inputs are widened exactly before use.
              attention with landmarks, special keys/rows and the self key,
              and dense softmax attention ("Linear-centered stages plus
              tile-sparse stages"; "Global attention dominates runtime").
+  coverage.py  attention-mass coverage of the kept tiles and the landmark
+             error of the omitted ones, per query tile ("Sensitive stages
+             also concentrate their attention").
   linear.py  RMSNorm, 2D rotary, channel-softmax feature map, linear
              attention and the centred affine output correction
              ("Speedup scales with the number of input views" for the fused
@@ -28,4 +31,4 @@ other than itself (brute force, closed forms, invariants, hand-derived
 golden fixtures). The exact outputs at the synthetic 32..1,024-view shapes
 are not printed anywhere on the pages; only those invariants pin them.
 """
-from . import layout, sparse, linear  # noqa: F401
+from . import layout, sparse, linear, coverage  # noqa: F401

@@ -276,6 +276,84 @@ def test_fused_qkv_and_strided_output():
     log("fused QKV / strided output: sparse, linear, no-alloc linear, affine statistics, dense bit-equal")
 
 
+COV = [("2views_16x16", zs.CONFIGS["2views_16x16"], 0.5), ("partial", zs.Layout(3, 2, 11, 13, heads=2), 0.3),
+       ("partial-y0", zs.Layout(2, 3, 9, 17, heads=2), 0.0), ("partial-y1", zs.Layout(2, 3, 9, 17, heads=2), 1.0),
+       ("vggt-2view", zs.Layout(2, 5, 37, 37, heads=2), 0.8)]
+COV_TOL = 1e-4     # coverage: fp32 sums of exactly computed logits
+# Landmark error: the kernel's landmark keys are kbar rounded to bf16 (as the
+# sparse kernel uses them), the oracle's are fp64 means. Rounding moves each
+# element by at most 2^-9 of itself, so a landmark logit moves by at most
+# b = |q| |kbar| 2^-9 / 8 (Cauchy-Schwarz) and the landmark mass by a factor
+# within e^(+-b); the error 1 - L/E then moves by at most e^b - 1 (L <= E).
+# Each tile is held to that bound (b from its largest |q| and the head's
+# largest |kbar|), and the mean deviation to 5e-3.
+LMERR_MEAN = 5e-3
+
+
+def _lm_bound(Q_h, K_h, tm, tiles):
+    """e^b - 1 per query tile, b = max |q| * max |kbar| * 2^-9 / 8."""
+    kb = np.array([K_h[tm.tokens[u]].mean(axis=0) for u in range(tm.T)])
+    kmax = np.linalg.norm(kb, axis=1).max()
+    qn = np.array([np.linalg.norm(Q_h[tm.tokens[t]], axis=1).max() for t in tiles])
+    return np.expm1(qn * kmax * 2.0 ** -9 / 8.0)
+
+
+def _coverage_gpu(st):
+    a = st.args()
+    zb.pack_tiles(a)
+    zb.select_tiles(a)
+    H, T = st.L.heads, st.bufs.T
+    cov = torch.empty(H * T, dtype=torch.float32, device="cuda")
+    err = torch.empty_like(cov)
+    zb.coverage(a, cov, err)
+    torch.cuda.synchronize()
+    return cov.view(H, T).cpu().numpy().astype(np.float64), err.view(H, T).cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("name,L,y", COV, ids=[c[0] for c in COV])
+def test_coverage_full(name, L, y):
+    """zebra_coverage against the oracle on every (head, query tile)."""
+    from oracle import coverage as ocov
+    q, k, v = _inputs(L, seed=20)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    cov, err = _coverage_gpu(Stage(L, q, k, v, y))
+    rc, re = ocov.coverage(widen(q), widen(k), tm, y)
+    dc, de = np.abs(cov - rc), np.abs(err - re)
+    bound = np.stack([_lm_bound(widen(q[:, h]), widen(k[:, h]), tm, range(tm.T)) for h in range(L.heads)])
+    log(f"{name} coverage: max |gpu - oracle| {dc.max():.2e}; landmark error: max {de.max():.2e}, "
+        f"mean {de.mean():.2e}, largest share of its bound {(de / bound).max():.2f} "
+        f"(coverage mean {rc.mean():.3f}, landmark error mean {re.mean():.3f})")
+    assert dc.max() <= COV_TOL and np.all(de <= bound) and de.mean() <= LMERR_MEAN
+    if y == 1.0:
+        assert np.all(cov == 0.0)
+    if y == 0.0:
+        assert np.all(err == 0.0)
+
+
+def test_32views_coverage_sampled_tiles():
+    from oracle import coverage as ocov
+    L = zs.CONFIGS["32views"]
+    y = 0.8
+    q, k, v = _inputs(L, seed=21)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    cov, err = _coverage_gpu(Stage(L, q, k, v, y))
+    g = np.random.default_rng(21)
+    worst_c = worst_e = 0.0
+    de = []
+    for h in (0, 7, 15):
+        tiles = np.sort(g.choice(tm.T, 12, replace=False))
+        rc, re = ocov.coverage_head(widen(q[:, h]), widen(k[:, h]), tm, y, query_tiles=tiles)
+        worst_c = max(worst_c, float(np.abs(cov[h, tiles] - rc).max()))
+        d = np.abs(err[h, tiles] - re)
+        assert np.all(d <= _lm_bound(widen(q[:, h]), widen(k[:, h]), tm, tiles)), h
+        de.append(d)
+    de = np.concatenate(de)
+    log(f"32 views coverage (36 sampled tiles): max |gpu - oracle| {worst_c:.2e}, landmark error max {de.max():.2e} "
+        f"mean {de.mean():.2e}; mean coverage {cov.mean():.3f}, mean landmark error {err.mean():.3f}")
+    assert worst_c <= COV_TOL and de.mean() <= LMERR_MEAN
+    assert np.all((cov > 0) & (cov < 1)) and np.all(err > -1e-4) and np.all(err < 1)
+
+
 # ------------------------------------------------------------- 32 views
 def test_32views_sparse_selection_and_rows():
     L = zs.CONFIGS["32views"]

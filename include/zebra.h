@@ -146,7 +146,9 @@ enum {
   ZEBRA_OP_LINEAR = 4,
   ZEBRA_OP_DENSE = 5,
   ZEBRA_OP_AFFINE_STATS = 6,
-  ZEBRA_OP_COVERAGE = 7
+  ZEBRA_OP_COVERAGE = 7,
+  ZEBRA_OP_PROLOGUE = 8,
+  ZEBRA_OP_FRAME = 9
 };
 
 /* Pack K and V into tile-major order ("Speedup scales with the number of
@@ -217,6 +219,26 @@ zebra_status zebra_linear_attn_noalloc(const zebra_args* a, zebra_stream stream)
  * v; writes kt, vt, ks, vs, kbar, vbar, logn, lm (it packs and builds the
  * per-tile key bounds first) and out; uses the workspace. */
 zebra_status zebra_dense_attn(const zebra_args* a, zebra_stream stream);
+
+/* Query/key prologue of a tile-sparse (or frame-wise) stage ("Linear-
+ * centered stages plus tile-sparse stages": conversion keeps the
+ * normalisation layers and positional encoding): for every token and head,
+ * x -> RoPE2D(RMSNorm(x)) exactly as the linear stage applies it (per-head
+ * RMSNorm over the 64 channels with eps a->rms_eps and gains a->gq / a->gk,
+ * then the pair (j, j+16) of channels [0,32) turned by the patch row and of
+ * [32,64) by the column, angle p * base^(-j/16), base a->rope_base, special
+ * tokens at (0,0)). Reads q and k; writes q_out and k_out (bf16, device,
+ * with the token and head strides of q, k and v, so that they can stand in
+ * for q and k in the next call; each may equal its input). */
+zebra_status zebra_qk_prologue(const zebra_args* a, void* q_out, void* k_out, zebra_stream stream);
+
+/* Frame-wise softmax attention ("Global attention dominates runtime as
+ * views grow": the backbones alternate frame-wise attention with global
+ * attention): every token of a frame, special or patch, attends with
+ * logits q.k/8 to all tokens of its own frame and no other. Reads q, k, v;
+ * packs K/V into kt, vt, ks, vs first (as zebra_pack_tiles, without
+ * landmarks); writes out. At most 65,535 frames. */
+zebra_status zebra_frame_attn(const zebra_args* a, zebra_stream stream);
 
 /* Attention-mass coverage diagnostic of a tile-sparse stage ("Sensitive
  * stages also concentrate their attention": stages are profiled by how

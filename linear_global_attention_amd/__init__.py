@@ -188,6 +188,11 @@ def make_args(L, q=None, k=None, v=None, out=None, bufs: StageBuffers | None = N
     a.q, a.k, a.v, a.out = _ptr(q), _ptr(k), _ptr(v), _ptr(out)
     a.W, a.b, a.mu, a.gq, a.gk = _ptr(W), _ptr(b), _ptr(mu), _ptr(gq), _ptr(gk)
     a.rms_eps, a.rope_base = float(rms_eps), float(rope_base)
+    # The struct holds bare device addresses: keep the tensors they point
+    # into alive for as long as the struct, so that a temporary passed here
+    # is not freed (and its memory handed to the next allocation) before
+    # the kernels that read it have run.
+    a._keep = (q, k, v, out, W, b, mu, gq, gk, bufs)
     if bufs is not None:
         t = bufs.t
         g = lambda n: _ptr(t[n]) if n in t else None  # noqa: E731
@@ -264,6 +269,27 @@ def affine_stats(args: Args, teacher, stats, stream=None):
     if stats.dtype != torch.float64 or stats.device.type != "cuda" or stats.numel() < AFFINE_STATS:
         raise ValueError(f"stats: float64 device tensor of {AFFINE_STATS} elements expected")
     st = lib.zebra_affine_stats(ctypes.byref(args), _ptr(teacher), _ptr(stats), _stream(stream))
+    if st != 0:
+        raise ZebraError(st, lib.zebra_last_error().decode())
+
+
+def frame_attn(args: Args, stream=None):
+    """Frame-wise softmax attention of args.q over the keys of each token's
+    own frame, into args.out (packs K/V into args' buffers first)."""
+    _call(lib.zebra_frame_attn, args, stream)
+
+
+def qk_prologue(args: Args, q_out, k_out, stream=None):
+    """RoPE2D(RMSNorm(.)) of args.q and args.k (gains args.gq, args.gk,
+    args.rms_eps, args.rope_base) into q_out and k_out: bf16 device tensors
+    with the token and head strides of args' q, k and v (they may be q and k
+    themselves)."""
+    Lp = Layout(args.L.frames, args.L.specials, args.L.rows, args.L.cols, args.L.heads, args.L.head_dim)
+    want = (args.L.tok_stride or Lp.heads * 64, args.L.head_stride or 64)
+    for name, t in (("q_out", q_out), ("k_out", k_out)):
+        if _rows_view(name, t, Lp) != want:
+            raise ValueError(f"{name} must have the token and head strides of q, k and v {want}")
+    st = lib.zebra_qk_prologue(ctypes.byref(args), _ptr(q_out), _ptr(k_out), _stream(stream))
     if st != 0:
         raise ZebraError(st, lib.zebra_last_error().decode())
 

@@ -27,6 +27,9 @@ hipError_t launch_linear(const Geom&, float, float, const u16*, const u16*, cons
                          u16*, void*, hipStream_t);
 size_t affine_workspace_bytes(const Geom&);
 hipError_t launch_affine_stats(const Geom&, const u16*, const u16*, double*, void*, hipStream_t);
+hipError_t launch_qk_prologue(const Geom&, const u16*, const float*, float, float, u16*, hipStream_t);
+hipError_t launch_frame_attn(const Geom&, const u16*, const u16*, const u16*, const u16*, const u16*, u16*,
+                             hipStream_t);
 hipError_t launch_coverage(const Geom&, const u16*, const u16*, const u16*, const u16*, const unsigned*, float*,
                            float*, hipStream_t);
 }  // namespace zebra
@@ -233,6 +236,21 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
       if (a->workspace_bytes < affine_workspace_bytes(g))
         return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_affine_stats");
       break;
+    case ZEBRA_OP_PROLOGUE:
+      NEED(a->q, "q");
+      NEED(a->k, "k");
+      break;
+    case ZEBRA_OP_FRAME:
+      if (g.F > 65535) return fail(ZEBRA_ERR_UNSUPPORTED, "frame-wise attention supports at most 65535 frames");
+      NEED(a->q, "q");
+      NEED(a->k, "k");
+      NEED(a->v, "v");
+      NEED(a->out, "out");
+      NEED(a->kt, "kt");
+      NEED(a->vt, "vt");
+      NEED(a->ks, "ks");
+      NEED(a->vs, "vs");
+      break;
     case ZEBRA_OP_COVERAGE:
       if (k < 0) return fail(ZEBRA_ERR_INVALID_ARG, "y must lie in [0, 1]");
       NEED(a->q, "q");
@@ -420,6 +438,36 @@ zebra_status zebra_linear_attn_noalloc(const zebra_args* a, zebra_stream stream)
                                   (const u16*)a->v, a->W, a->b, a->mu, a->gq, a->gk,
                                   (u16*)a->out, ws, (hipStream_t)stream),
                     "zebra_linear_attn_noalloc");
+}
+
+zebra_status zebra_qk_prologue(const zebra_args* a, void* q_out, void* k_out, zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_PROLOGUE, g, k);
+  if (s != ZEBRA_OK) return s;
+  if (!q_out || !k_out) return fail(ZEBRA_ERR_INVALID_ARG, "q_out and k_out must be non-NULL");
+  if (misaligned(q_out) || misaligned(k_out)) return fail(ZEBRA_ERR_INVALID_ARG, "q_out and k_out must be 16-byte aligned");
+  const float eps = a->rms_eps > 0.f ? a->rms_eps : 1e-6f;
+  const float base = a->rope_base > 0.f ? a->rope_base : 100.0f;
+  s = hip_result(launch_qk_prologue(g, (const u16*)a->q, a->gq, eps, base, (u16*)q_out, (hipStream_t)stream),
+                 "zebra_qk_prologue (q)");
+  if (s != ZEBRA_OK) return s;
+  return hip_result(launch_qk_prologue(g, (const u16*)a->k, a->gk, eps, base, (u16*)k_out, (hipStream_t)stream),
+                    "zebra_qk_prologue (k)");
+}
+
+zebra_status zebra_frame_attn(const zebra_args* a, zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_FRAME, g, k);
+  if (s != ZEBRA_OK) return s;
+  s = hip_result(launch_pack(g, (const u16*)a->k, (const u16*)a->v, (u16*)a->kt, (u16*)a->vt, (u16*)a->ks,
+                             (u16*)a->vs, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream),
+                 "zebra_frame_attn (pack)");
+  if (s != ZEBRA_OK) return s;
+  return hip_result(launch_frame_attn(g, (const u16*)a->q, (const u16*)a->k, (const u16*)a->v, (const u16*)a->kt,
+                                      (const u16*)a->vt, (u16*)a->out, (hipStream_t)stream),
+                    "zebra_frame_attn");
 }
 
 zebra_status zebra_coverage(const zebra_args* a, float* coverage, float* lm_error, zebra_stream stream) {

@@ -20,6 +20,10 @@ float64; bf16 inputs are widened exactly before use.
   coverage.py  attention-mass coverage of the kept tiles and the landmark
              error of the omitted ones, per query tile ("Sensitive stages
              also concentrate their attention").
+  block.py   frame-wise attention, and the RMSNorm + 2D-rotary prologue of
+             the queries and keys of a sparse stage ("Global attention
+             dominates runtime as views grow"; "Linear-centered stages plus
+             tile-sparse stages").
   linear.py  RMSNorm, 2D rotary, channel-softmax feature map, linear
              attention and the centred affine output correction
              ("Speedup scales with the number of input views" for the fused
@@ -31,4 +35,4 @@ other than itself (brute force, closed forms, invariants, hand-derived
 golden fixtures). The exact outputs at the synthetic 32..1,024-view shapes
 are not printed anywhere on the pages; only those invariants pin them.
 """
-from . import layout, sparse, linear, coverage  # noqa: F401
+from . import layout, sparse, linear, coverage, block  # noqa: F401

@@ -15,7 +15,7 @@ from oracle import linear as olin
 from oracle import sparse as osp
 from oracle.layout import TileMap, keep_count
 
-from gpu_helpers import Stage, bf16_host, close, compare_selection, log, oracle_scores, widen
+from gpu_helpers import Stage, bf16_host, close, compare_selection, dev_f32, log, oracle_scores, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -352,6 +352,98 @@ def test_32views_coverage_sampled_tiles():
         f"mean {de.mean():.2e}; mean coverage {cov.mean():.3f}, mean landmark error {err.mean():.3f}")
     assert worst_c <= COV_TOL and de.mean() <= LMERR_MEAN
     assert np.all((cov > 0) & (cov < 1)) and np.all(err > -1e-4) and np.all(err < 1)
+
+
+PRO = [("partial-defaults", zs.Layout(3, 2, 11, 13, heads=2), None, 1e-6, 100.0),
+       ("partial-gains", zs.Layout(3, 2, 11, 13, heads=2), 17, 1e-3, 1000.0),
+       ("vggt-2view", zs.Layout(2, 5, 37, 37, heads=3), 18, 1e-6, 100.0)]
+
+
+@pytest.mark.parametrize("name,L,gseed,eps,base", PRO, ids=[p[0] for p in PRO])
+def test_qk_prologue(name, L, gseed, eps, base):
+    """zebra_qk_prologue against the oracle's RoPE2D(RMSNorm(.)) rounded to
+    bf16: every element within one bf16 step (fp32 on the GPU against fp64
+    before the same rounding), and in place into a fused QKV buffer."""
+    from gpu_helpers import dev
+    from oracle import block as ob
+    q, k, v = _inputs(L, seed=22)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    gq = gk = None
+    if gseed is not None:
+        g = np.random.default_rng(gseed)
+        gq = (0.5 + g.random((L.heads, 64))).astype(np.float32)
+        gk = (0.5 + g.random((L.heads, 64))).astype(np.float32)
+    st = Stage(L, q, k, v, 0.0, sparse=False)
+    a = st.args(gq=dev_f32(gq), gk=dev_f32(gk), rms_eps=eps, rope_base=base)
+    qo, ko = torch.empty_like(st.q), torch.empty_like(st.k)
+    zb.qk_prologue(a, qo, ko)
+    torch.cuda.synchronize()
+    for got, x, gain, nm in ((qo, q, gq, "q"), (ko, k, gk, "k")):
+        ref = ob.round_bf16(ob.prologue(widen(x), tm, gain, eps, base))
+        got = bf16_host(got).reshape(ref.shape)
+        # One bf16 step of the result, but at least 2^-18: a rotated pair
+        # lo*c - hi*s can cancel to a value far below its O(1) products
+        # (the normalised rows have RMS 1, times gains < 1.5), and the fp32
+        # rounding of those products and of the fp32 cos/sin table (a few
+        # 2^-24 each) then exceeds a bf16 step of the small result.
+        ulp = 2.0 ** (np.frexp(np.maximum(np.abs(ref), 1e-30))[1] - 8)
+        err = np.abs(got - ref)
+        bad = err > np.maximum(ulp, 2.0 ** -18)
+        log(f"{name} prologue {nm}: {int((got != ref).sum())} of {got.size} values differ from the rounded oracle, "
+            f"{int((err > ulp).sum())} by more than one bf16 step, largest such error {float(err[err > ulp].max(initial=0)):.2e}")
+        assert not bad.any()
+    # in place, inside a fused [N][3][H][64] buffer
+    qkv = torch.stack([dev(q), dev(k), dev(v)], dim=1)
+    zL = zb.Layout(L.frames, L.specials, L.rows, L.cols, L.heads)
+    af = zb.make_args(zL, qkv[:, 0], qkv[:, 1], qkv[:, 2], None, None, 0.0, gq=dev_f32(gq), gk=dev_f32(gk),
+                      rms_eps=eps, rope_base=base)
+    zb.qk_prologue(af, qkv[:, 0], qkv[:, 1])
+    torch.cuda.synchronize()
+    assert torch.equal(qkv[:, 0], qo) and torch.equal(qkv[:, 1], ko) and torch.equal(qkv[:, 2], dev(v))
+
+
+FRAME = [("2views_16x16", zs.CONFIGS["2views_16x16"]), ("partial", zs.Layout(3, 2, 11, 13, heads=2)),
+         ("no-specials", zs.Layout(3, 0, 9, 9, heads=2)), ("vggt-2view", zs.Layout(2, 5, 37, 37, heads=2)),
+         ("40-specials", zs.Layout(2, 40, 5, 7, heads=1))]
+
+
+@pytest.mark.parametrize("name,L", FRAME, ids=[f[0] for f in FRAME])
+def test_frame_attn_full(name, L):
+    from oracle import block as ob
+    q, k, v = _inputs(L, seed=23)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    st = Stage(L, q, k, v, 0.0, sparse=False)
+    zb.frame_attn(st.args())
+    torch.cuda.synchronize()
+    out = bf16_host(st.out).reshape(L.tokens, L.heads, 64)
+    close(out, ob.frame_attention(widen(q), widen(k), widen(v), tm), f"{name} frame-wise attention")
+
+
+def test_alternating_block_32views():
+    """One frame-wise stage, then a tile-sparse global stage (y = 0.8) whose
+    queries and keys first pass the prologue, on 32 views: sampled rows of
+    each step against the oracle taking the same steps (the prologue output
+    rounded to bf16, where the selector decides from it)."""
+    from oracle import block as ob
+    L = zs.CONFIGS["32views"]
+    y = 0.8
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    rows = zs.sample_rows(L, 384, seed=24, special_frames=1)
+    q, k, v = _inputs(L, seed=24, stage=0)
+    st = Stage(L, q, k, v, y)
+    zb.frame_attn(st.args())
+    torch.cuda.synchronize()
+    Q, K, V = widen(q), widen(k), widen(v)
+    ref = np.stack([ob.frame_attention_head(Q[:, h], K[:, h], V[:, h], tm)[t] for h, t in rows])
+    close(st.rows(rows), ref, "32 views: frame-wise stage (sampled rows)")
+    q2, k2, v2 = _inputs(L, seed=24, stage=1)
+    st2 = Stage(L, q2, k2, v2, y)
+    zb.qk_prologue(st2.args(), st2.q, st2.k)  # in place
+    st2.sparse()
+    Qp = ob.round_bf16(ob.prologue(widen(q2), tm))
+    Kp = ob.round_bf16(ob.prologue(widen(k2), tm))
+    ref2, _ = osp.sparse_rows(Qp, Kp, widen(v2), tm, y, rows)
+    close(st2.rows(rows), ref2, "32 views: prologue + sparse global stage (sampled rows)")
 
 
 # ------------------------------------------------------------- 32 views

@@ -24,6 +24,11 @@ float64; bf16 inputs are widened exactly before use.
              the queries and keys of a sparse stage ("Global attention
              dominates runtime as views grow"; "Linear-centered stages plus
              tile-sparse stages").
+  backward.py  gradients of the linear and the tile-sparse stages with
+             respect to Q, K and V: the chain rule of linear.py and
+             sparse.py taken back step by step ("A closed-form fit avoids
+             retraining from scratch": the optional training stage after
+             conversion).
   linear.py  RMSNorm, 2D rotary, channel-softmax feature map, linear
              attention and the centred affine output correction
              ("Speedup scales with the number of input views" for the fused
@@ -35,4 +40,4 @@ other than itself (brute force, closed forms, invariants, hand-derived
 golden fixtures). The exact outputs at the synthetic 32..1,024-view shapes
 are not printed anywhere on the pages; only those invariants pin them.
 """
-from . import layout, sparse, linear, coverage, block  # noqa: F401
+from . import layout, sparse, linear, coverage, block, backward  # noqa: F401

@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-schedule", action="store_true")
+    p.add_argument("--no-backward", action="store_true")
     p.add_argument("--dense-reps", type=int, default=5)
     p.add_argument("--rows-per-stage", type=int, default=32)
     p.add_argument("--calib-copy-gb", type=float, default=0.0,
@@ -119,6 +120,13 @@ def recorded_linear_traffic(config: str):
     if config != "1024views":
         return None
     return _recorded("linear_traffic_1024views.md", "traffic_bytes_per_call")
+
+
+def recorded_linear_bwd_traffic(config: str):
+    """HBM-side bytes of one zebra_linear_attn_bwd call at 1,024 views."""
+    if config != "1024views":
+        return None
+    return _recorded("linear_bwd_1024views.md", "traffic_bytes_per_call")
 
 
 # ----------------------------------------------------------------- oracle pool
@@ -483,6 +491,32 @@ def main():
         "frac": aff_bytes / (aff_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": aff_bytes,
         "avg_launch_ms": aff_ms}
     del out_plain, stats
+
+    if not a.no_backward:
+        # backward of the linear stage (gradients of q, k, v for a training
+        # stage after conversion): a seeded synthetic bf16 output gradient,
+        # 3 calls after one warm-up call. Algorithmic bytes: read q, k, v and
+        # dout once, write dq, dk, dv once.
+        log("linear-stage backward (3 calls)")
+        dyd = zs.stage_inputs_device(L, seed=a.seed + 1, stage=0)[0]
+        gq_, gk_, gv_ = (torch.empty_like(qd) for _ in range(3))
+        args_b = zb.make_args(zL, qd, kd, vd, out_lin, bufs, a.y, W=Wd)
+        zb.linear_attn_bwd(args_b, dyd, gq_, gk_, gv_)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            zb.linear_attn_bwd(args_b, dyd, gq_, gk_, gv_)
+        e1.record()
+        torch.cuda.synchronize()
+        bwd_ms = e0.elapsed_time(e1) / 3
+        bwd_bytes = 7 * N * H * 64 * 2
+        result["roofline_linear_bwd"] = {
+            "kernels": ("linear_bwd_state + linear_bwd_query + linear_bwd_key, with two fp64 sums and "
+                        "two operand folds (zebra_linear_attn_bwd)"), "bound": "hbm",
+            "achieved": bwd_bytes / (bwd_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": bwd_bytes,
+            "avg_launch_ms": bwd_ms, "traffic": recorded_linear_bwd_traffic(a.config)}
+        del dyd, gq_, gk_, gv_, args_b
 
     dms = None
     if not a.no_dense:

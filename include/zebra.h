@@ -148,7 +148,8 @@ enum {
   ZEBRA_OP_AFFINE_STATS = 6,
   ZEBRA_OP_COVERAGE = 7,
   ZEBRA_OP_PROLOGUE = 8,
-  ZEBRA_OP_FRAME = 9
+  ZEBRA_OP_FRAME = 9,
+  ZEBRA_OP_LINEAR_BWD = 10
 };
 
 /* Pack K and V into tile-major order ("Speedup scales with the number of
@@ -197,6 +198,24 @@ zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream);
  * phi(q_i)^T z; out_i = mu + W (o_i - mu) + b. Reads q, k, v, W, b, mu,
  * gq, gk; writes out. Uses the workspace. */
 zebra_status zebra_linear_attn(const zebra_args* a, zebra_stream stream);
+
+/* Backward of zebra_linear_attn ("A closed-form fit avoids retraining from
+ * scratch": an optional training stage after the conversion fine-tunes the
+ * converted model, so gradients flow back through its linear stages). For
+ * out as zebra_linear_attn computes it, writes the gradients of
+ * sum(dout * out) with respect to q, k and v. W, gq, gk, rms_eps and
+ * rope_base are constants of the backward; b and mu do not change it and
+ * are not read. dout: bf16, device, with the output's token and head
+ * strides (a->L.out_tok_stride, out_head_stride); dq, dk, dv: bf16, device,
+ * with q's strides, overlapping none of q, k, v and dout. All four 16-byte
+ * aligned. Reads q, k, v, W, gq, gk; uses the workspace (the forward's KV
+ * state, the gradient of that state, their partial sums). fp32 arithmetic;
+ * products with the KV state and its gradient run on MFMA with both
+ * operands split into bf16 high and low parts; sums over tokens in fp32
+ * within a workgroup and in fp64 across workgroups; each gradient is
+ * rounded once to bf16 (nearest even). */
+zebra_status zebra_linear_attn_bwd(const zebra_args* a, const void* dout, void* dq, void* dk, void* dv,
+                                   zebra_stream stream);
 
 /* zebra_linear_attn for callers that cannot allocate memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc):

@@ -294,6 +294,24 @@ def qk_prologue(args: Args, q_out, k_out, stream=None):
         raise ZebraError(st, lib.zebra_last_error().decode())
 
 
+def linear_attn_bwd(args: Args, dout, dq, dk, dv, stream=None):
+    """Gradients of sum(dout * out) for the linear stage of args (q, k, v,
+    W, gq, gk, rms_eps, rope_base; b and mu do not enter) into dq, dk, dv.
+    dout: bf16 device tensor with the strides of args' out; dq, dk, dv: bf16
+    device tensors with the strides of args' q, k and v."""
+    Lp = Layout(args.L.frames, args.L.specials, args.L.rows, args.L.cols, args.L.heads, args.L.head_dim)
+    want_in = (args.L.tok_stride or Lp.heads * 64, args.L.head_stride or 64)
+    want_out = (args.L.out_tok_stride or Lp.heads * 64, args.L.out_head_stride or 64)
+    if _rows_view("dout", dout, Lp) != want_out:
+        raise ValueError(f"dout must have the token and head strides of out {want_out}")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if _rows_view(name, t, Lp) != want_in:
+            raise ValueError(f"{name} must have the token and head strides of q, k and v {want_in}")
+    st = lib.zebra_linear_attn_bwd(ctypes.byref(args), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream))
+    if st != 0:
+        raise ZebraError(st, lib.zebra_last_error().decode())
+
+
 def coverage(args: Args, cov, lm_error, stream=None):
     """Attention-mass coverage of the kept tiles and landmark error of the
     omitted ones per (head, query tile), into float32 device tensors

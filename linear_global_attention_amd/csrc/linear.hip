@@ -25,147 +25,9 @@
 // Each rotary pair (j, j+16) therefore sits in one lane; channel sums need
 // two cross-lane steps. For the apply MFMA the reduction index a runs over
 // these channels in lane order, so S'^T is stored column-permuted to match.
-#include "common.hpp"
+#include "linear_common.hpp"
 
 namespace zebra {
-
-constexpr int LIN_THREADS = 256;
-constexpr int LIN_WAVES = LIN_THREADS / 64;
-constexpr int LIN_RESIDENT = 512;  // workgroups resident at once: 256 CUs x 2
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr int LIN_STATE = D * D + D;  // floats of one partial state: S [64][64] then z [64]
-
-struct LinParams {
-  float eps;
-  float base;
-};
-
-__device__ inline int lane_channel(int g, int i) { return (i >> 2) * 16 + 4 * g + (i & 3); }
-
-// Rotary table in dynamic LDS, max(R, C) * 16 entries (rope_table_bytes).
-extern __shared__ float2 rope_tab[];
-inline size_t rope_table_bytes(const Geom& g) { return (size_t)(g.R > g.C ? g.R : g.C) * 16 * sizeof(float2); }
-
-// cos/sin of p * base^(-j/16) for p < npos, j < 16, in LDS: tab[p][j] = {c, s}
-__device__ inline void build_rope_table(float2* tab, int npos, float base) {
-  for (int i = threadIdx.x; i < npos * 16; i += blockDim.x) {
-    const int p = i >> 4, j = i & 15;
-    const double ang = (double)p * pow((double)base, -(double)j / 16.0);
-    double s, c;
-    sincos(ang, &s, &c);
-    tab[i] = make_float2((float)c, (float)s);
-  }
-}
-
-// Reciprocals for token -> (frame, patch row, patch column) without integer
-// division: quotients from a rounded reciprocal, then one exact correction.
-struct PosDiv {
-  double inv_tpf;  // 1 / tokens per frame
-  float inv_c;     // 1 / patch columns
-  __device__ explicit PosDiv(const Geom& g) : inv_tpf(1.0 / (double)g.tok_pf), inv_c(1.0f / (float)g.C) {}
-};
-
-// Rotary position of token tok: (patch row, patch column), specials (0, 0).
-__device__ inline void token_pos(const Geom& g, const PosDiv& dv, long long tok, int& pr, int& pc) {
-  long long f = (long long)((double)tok * dv.inv_tpf);
-  long long loc = tok - f * g.tok_pf;
-  if (loc < 0) loc += g.tok_pf;
-  else if (loc >= g.tok_pf) loc -= g.tok_pf;
-  const int p = max((int)loc - g.S, 0);  // p < 2^14: exact in fp32
-  int r = (int)((float)p * dv.inv_c);
-  int c = p - r * g.C;
-  if (c < 0) {
-    --r;
-    c += g.C;
-  } else if (c >= g.C) {
-    ++r;
-    c -= g.C;
-  }
-  const bool special = loc < g.S;
-  pr = special ? 0 : r;
-  pc = special ? 0 : c;
-}
-
-// Sum / max of v over lane pairs (l, l ^ 16) or (l, l ^ 32) on the VALU
-// (v_permlane16/32_swap give each lane the pair in the same order, so both
-// lanes get the same bits), instead of a cross-lane LDS permute.
-__device__ inline float lin_pair16(float v, bool mx) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return mx ? fmaxf(a, b) : a + b;
-}
-__device__ inline float lin_pair32(float v, bool mx) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return mx ? fmaxf(a, b) : a + b;
-}
-
-// Feature map of one token's 16 lane channels (x holds them, fp32, in
-// lane order). On return x holds phi(x) for those channels, or, with
-// NORMALIZE false, phi(x) times a positive per-token constant (enough where
-// phi only enters a ratio). `gained`: multiply by the RMSNorm gains. cr[i]
-// and cc[i] are the rotary {cos, sin} of channel pair 4g + i at the token's
-// patch row and column.
-template <bool NORMALIZE>
-__device__ inline void featurize16_rot(float x[16], bool gained, const float gain[16], const float2 cr[4],
-                                       const float2 cc[4], float eps) {
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) ss += x[i] * x[i];
-  ss = lin_pair32(lin_pair16(ss, false), false);
-  const float r = __builtin_amdgcn_rsqf(ss * (1.0f / 64.0f) + eps);
-  if (gained) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] *= gain[i];
-  }
-  // rotary: pairs (i, i+4) for i in 0..3 (row) and 8..11 (column)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = x[i], b = x[i + 4];
-    x[i] = a * cr[i].x - b * cr[i].y;
-    x[i + 4] = b * cr[i].x + a * cr[i].y;
-    const float a2 = x[i + 8], b2 = x[i + 12];
-    x[i + 8] = a2 * cc[i].x - b2 * cc[i].y;
-    x[i + 12] = b2 * cc[i].x + a2 * cc[i].y;
-  }
-  float m = x[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) m = fmaxf(m, x[i]);
-  m = lin_pair32(lin_pair16(m, true), true);
-  const float sc = r * LOG2E, off = -m * sc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_exp2f(fmaf(x[i], sc, off));
-  if (NORMALIZE) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s += x[i];
-    s = lin_pair32(lin_pair16(s, false), false);
-    const float inv = __builtin_amdgcn_rcpf(s);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] *= inv;
-  }
-}
-
-// The same with the rotary values read from the table tab[p][j] = {cos, sin}.
-template <bool NORMALIZE>
-__device__ inline void featurize16(float x[16], bool gained, const float gain[16], const float2* tab, int pr,
-                                   int pc, int g, float eps) {
-  float2 cr[4], cc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    cr[i] = tab[pr * 16 + 4 * g + i];
-    cc[i] = tab[pc * 16 + 4 * g + i];
-  }
-  featurize16_rot<NORMALIZE>(x, gained, gain, cr, cc, eps);
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-// two floats -> packed bf16 (hardware round to nearest even), a in the low half
-__device__ inline unsigned pack_bf16x2(float a, float b) {
-  const f32x2_t f = {a, b};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2_t));
-}
 
 typedef void __attribute__((address_space(3))) lin_lds_void;
 constexpr int AP_NB = 6;  // LDS ring slots per wave in linear_apply
@@ -192,22 +54,6 @@ __device__ inline void lin_wait_vm(int n) {
   }
 }
 static_assert(6 * (AP_NB - 2) <= 24, "lin_wait_vm covers the pending counts of linear_apply");
-
-// The lane's 16 channels of one bf16 row, raw (4 x 8 bytes); zeros past the end.
-__device__ inline void fetch16(const u16* row, int g, bool ok, uint2 w[4]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) w[q] = ok ? *(const uint2*)(row + q * 16 + 4 * g) : make_uint2(0u, 0u);
-}
-
-__device__ inline void unpack16(const uint2 w[4], float x[16]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    x[q * 4 + 0] = __uint_as_float(w[q].x << 16);
-    x[q * 4 + 1] = __uint_as_float(w[q].x & 0xFFFF0000u);
-    x[q * 4 + 2] = __uint_as_float(w[q].y << 16);
-    x[q * 4 + 3] = __uint_as_float(w[q].y & 0xFFFF0000u);
-  }
-}
 
 // grid (nchunks, H), block 256. Partial p = chunk holds
 // S [64][64] (row a = phi channel, column c = value channel) then z [64].
@@ -410,16 +256,21 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
   for (int e = threadIdx.x; e < LIN_STATE; e += LIN_THREADS) out[e] = red[e];
 }
 
-// grid (ceil(LIN_STATE / 256), H), block 256: fixed-order fp64 sum of the
-// per-wave partial states of a head, one element per thread.
+// grid (ceil(LIN_STATE / 256), H, LIN_SUM_PARTS), block 256: fixed-order
+// fp64 sums of the per-workgroup partial states of a head, one element per
+// thread, each z-slice over its own contiguous quarter of the partials (the
+// fold adds the quarters in order). Four chains of loads per element instead
+// of one long one.
 __global__ void __launch_bounds__(256) linear_sum_kernel(const float* __restrict__ partials, int nparts,
                                                          double* __restrict__ state) {
-  const int h = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  const int h = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x, part = blockIdx.z;
   if (e >= LIN_STATE) return;
+  const int p0 = (int)((long long)nparts * part / LIN_SUM_PARTS);
+  const int p1 = (int)((long long)nparts * (part + 1) / LIN_SUM_PARTS);
   const float* base = partials + (long long)h * nparts * LIN_STATE + e;
   double s = 0.0;
-  for (int p = 0; p < nparts; ++p) s += (double)base[(long long)p * LIN_STATE];
-  state[(long long)h * LIN_STATE + e] = s;
+  for (int p = p0; p < p1; ++p) s += (double)base[(long long)p * LIN_STATE];
+  state[((long long)h * LIN_SUM_PARTS + part) * LIN_STATE + e] = s;
 }
 
 // grid (H), block 256. Folds the affine correction into the state: writes
@@ -430,9 +281,18 @@ __global__ void __launch_bounds__(256) linear_fold_kernel(const double* __restri
                                                           const float* __restrict__ mu, u16* __restrict__ sp,
                                                           float* __restrict__ zb) {
   __shared__ double S[D][D + 1];
+  __shared__ double zs[D];
   const int h = blockIdx.x, tid = threadIdx.x;
-  const double* st = state + (long long)h * LIN_STATE;
-  for (int e = tid; e < D * D; e += 256) S[e / D][e % D] = st[e];
+  const double* st = state + (long long)h * LIN_SUM_PARTS * LIN_STATE;
+  for (int e = tid; e < LIN_STATE; e += 256) {
+    double v = 0.0;
+#pragma unroll
+    for (int q = 0; q < LIN_SUM_PARTS; ++q) v += st[(long long)q * LIN_STATE + e];
+    if (e < D * D)
+      S[e / D][e % D] = v;
+    else
+      zs[e - D * D] = v;
+  }
   __syncthreads();
   const float* Wh = W ? W + (long long)h * D * D : nullptr;
   u16* hi = sp + (long long)h * 2 * D * D;
@@ -455,7 +315,7 @@ __global__ void __launch_bounds__(256) linear_fold_kernel(const double* __restri
   }
   float* zo = zb + (long long)h * 2 * D;
   if (tid < D) {
-    zo[tid] = (float)st[D * D + tid];
+    zo[tid] = (float)zs[tid];
     // b' = mu - W mu + b
     double wm = 0.0, m_e = mu ? (double)mu[h * D + tid] : 0.0;
     if (mu) {
@@ -838,12 +698,28 @@ int linear_chunks(const Geom& g) {
 
 size_t linear_workspace_bytes(const Geom& g) {
   const size_t parts = (size_t)g.H * linear_chunks(g) * LIN_STATE * sizeof(float);
-  const size_t state = (size_t)g.H * LIN_STATE * sizeof(double);
+  const size_t state = (size_t)g.H * LIN_SUM_PARTS * LIN_STATE * sizeof(double);
   const size_t red = (size_t)g.H * (2 * D * D * sizeof(u16) + 2 * D * sizeof(float));
   return parts + state + red;
 }
 
-// Workspace: partials, the summed states fp64 [H][LIN_STATE], then Sp
+void launch_linear_sum(const Geom& g, const float* parts, int nch, double* quarters, hipStream_t s) {
+  hipLaunchKernelGGL(linear_sum_kernel, dim3((LIN_STATE + 255) / 256, g.H, LIN_SUM_PARTS), dim3(256), 0, s, parts,
+                     nch, quarters);
+}
+
+// S = phi(K)^T V and z = sum phi(k) of every head: per-workgroup partials
+// [H][linear_chunks][LIN_STATE] fp32, then their fixed-order fp64 sums in
+// quarters [H][LIN_SUM_PARTS][LIN_STATE].
+void launch_linear_kv_state(const Geom& g, LinParams P, const u16* K, const u16* V, const float* gk, float* parts,
+                            double* quarters, hipStream_t s) {
+  const int nch = linear_chunks(g), tpw = linear_tokens_per_wg(g);
+  hipLaunchKernelGGL(linear_state_kernel, dim3(nch, g.H), dim3(LIN_THREADS), rope_table_bytes(g), s, g, P, K, V, gk,
+                     parts, nch, tpw);
+  launch_linear_sum(g, parts, nch, quarters, s);
+}
+
+// Workspace: partials, the summed quarters fp64 [H][LIN_SUM_PARTS][LIN_STATE], then Sp
 // [H][2][64][64] bf16, then zb [H][2][64] fp32.
 hipError_t launch_linear(const Geom& g, float eps, float base, const u16* Q, const u16* K,
                          const u16* V, const float* W, const float* b, const float* mu,
@@ -851,14 +727,10 @@ hipError_t launch_linear(const Geom& g, float eps, float base, const u16* Q, con
   const int nch = linear_chunks(g), tpw = linear_tokens_per_wg(g);
   float* parts = (float*)ws;
   double* state = (double*)(parts + (size_t)g.H * nch * LIN_STATE);
-  u16* sp = (u16*)(state + (size_t)g.H * LIN_STATE);
+  u16* sp = (u16*)(state + (size_t)g.H * LIN_SUM_PARTS * LIN_STATE);
   float* zb = (float*)(sp + (size_t)g.H * 2 * D * D);
   LinParams P{eps, base};
-  const size_t tb = rope_table_bytes(g);
-  hipLaunchKernelGGL(linear_state_kernel, dim3(nch, g.H), dim3(LIN_THREADS), tb, s, g, P, K, V, gk,
-                     parts, nch, tpw);
-  hipLaunchKernelGGL(linear_sum_kernel, dim3((LIN_STATE + 255) / 256, g.H), dim3(256), 0, s,
-                     (const float*)parts, nch, state);
+  launch_linear_kv_state(g, P, K, V, gk, parts, state, s);
   hipLaunchKernelGGL(linear_fold_kernel, dim3(g.H), dim3(256), 0, s, (const double*)state, W, b, mu, sp, zb);
   hipLaunchKernelGGL(linear_apply_kernel, dim3(nch, g.H), dim3(LIN_THREADS), 0, s, g, P, Q, gq, sp,
                      zb, out, tpw);

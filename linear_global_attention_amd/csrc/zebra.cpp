@@ -22,6 +22,9 @@ hipError_t launch_select(const Geom&, int, const u16*, const double*, int*, unsi
 hipError_t launch_attn(const Geom&, const AttnArgs&, void*, hipStream_t);
 size_t attn_workspace_bytes(const Geom&);
 size_t linear_workspace_bytes(const Geom&);
+size_t linear_bwd_workspace_bytes(const Geom&);
+hipError_t launch_linear_bwd(const Geom&, float, float, const u16*, const u16*, const u16*, const float*,
+                             const float*, const float*, const u16*, u16*, u16*, u16*, void*, hipStream_t);
 hipError_t launch_linear(const Geom&, float, float, const u16*, const u16*, const u16*,
                          const float*, const float*, const float*, const float*, const float*,
                          u16*, void*, hipStream_t);
@@ -127,6 +130,8 @@ size_t buf_bytes(const Geom& g, int64_t k, int which) {
     case ZEBRA_BUF_WORKSPACE: {
       size_t m = select_workspace_bytes(g);
       const size_t b = linear_workspace_bytes(g), c = attn_workspace_bytes(g), f = affine_workspace_bytes(g);
+      const size_t lb = linear_bwd_workspace_bytes(g);
+      if (lb > m) m = lb;
       if (b > m) m = b;
       if (c > m) m = c;
       if (f > m) m = f;
@@ -250,6 +255,14 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
       NEED(a->vt, "vt");
       NEED(a->ks, "ks");
       NEED(a->vs, "vs");
+      break;
+    case ZEBRA_OP_LINEAR_BWD:
+      NEED(a->q, "q");
+      NEED(a->k, "k");
+      NEED(a->v, "v");
+      NEED(a->workspace, "workspace");
+      if (a->workspace_bytes < linear_bwd_workspace_bytes(g))
+        return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_linear_attn_bwd");
       break;
     case ZEBRA_OP_COVERAGE:
       if (k < 0) return fail(ZEBRA_ERR_INVALID_ARG, "y must lie in [0, 1]");
@@ -411,6 +424,23 @@ zebra_status zebra_linear_attn(const zebra_args* a, zebra_stream stream) {
                                   (const u16*)a->v, a->W, a->b, a->mu, a->gq, a->gk,
                                   (u16*)a->out, a->workspace, (hipStream_t)stream),
                     "zebra_linear_attn");
+}
+
+zebra_status zebra_linear_attn_bwd(const zebra_args* a, const void* dout, void* dq, void* dk, void* dv,
+                                   zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_LINEAR_BWD, g, k);
+  if (s != ZEBRA_OK) return s;
+  if (!dout || !dq || !dk || !dv) return fail(ZEBRA_ERR_INVALID_ARG, "dout, dq, dk and dv must be non-NULL");
+  if (misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv))
+    return fail(ZEBRA_ERR_INVALID_ARG, "dout, dq, dk and dv must be 16-byte aligned");
+  const float eps = a->rms_eps > 0.f ? a->rms_eps : 1e-6f;
+  const float base = a->rope_base > 0.f ? a->rope_base : 100.0f;
+  return hip_result(launch_linear_bwd(g, eps, base, (const u16*)a->q, (const u16*)a->k, (const u16*)a->v, a->W,
+                                      a->gq, a->gk, (const u16*)dout, (u16*)dq, (u16*)dk, (u16*)dv, a->workspace,
+                                      (hipStream_t)stream),
+                    "zebra_linear_attn_bwd");
 }
 
 zebra_status zebra_linear_attn_noalloc(const zebra_args* a, zebra_stream stream) {

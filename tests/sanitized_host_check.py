@@ -68,7 +68,7 @@ for F, S, R, C, H in [(1, 0, 1, 1, 1), (2, 5, 16, 16, 1), (3, 2, 11, 13, 2), (10
         check(so.zebra_buffer_bytes(ctypes.byref(L), 0.5, 99) == 0, "unknown buffer")
 # validation of every operation, good and bad arguments
 L = layout(4, 5, 37, 37, 2)
-for op in range(7):
+for op in sorted(abi.OP.values()):
     check(so.zebra_validate(ctypes.byref(args(L, 0.5)), op) == 0, f"op {op} accepts")
     check(so.zebra_validate(ctypes.byref(args(L, 0.5, fill=False)), op) == 1, f"op {op} rejects NULLs")
 check(so.zebra_validate(ctypes.byref(args(L, 0.5)), 42) == 1, "unknown op")
@@ -82,7 +82,7 @@ a.q = ctypes.c_void_p(0x1004)
 check(so.zebra_validate(ctypes.byref(a), 3) == 1, "misaligned q")
 a = args(L, 0.5)
 a.workspace_bytes = 1
-for op in (2, 3, 4, 5, 6):
+for op in (2, 3, 4, 5, 6, abi.OP["LINEAR_BWD"]):
     check(so.zebra_validate(ctypes.byref(a), op) == 3, f"small workspace op {op}")
 # every entry point fails on the host before any launch
 a = args(L, 0.5, fill=False)
@@ -91,6 +91,11 @@ for name in abi.STAGE_CALLS:
 big = args(layout(4096, 5, 37, 37, 16), 0.0)
 check(so.zebra_linear_attn_noalloc(ctypes.byref(big), None) == 3, "no-alloc scratch limit")
 check(so.zebra_affine_stats(ctypes.byref(args(L, 0.5)), None, None, None) == 1, "affine stats NULLs")
+g4 = [ctypes.c_void_p(0x9000 + 0x100 * i) for i in range(4)]
+check(so.zebra_linear_attn_bwd(ctypes.byref(args(L, 0.5)), None, g4[1], g4[2], g4[3], None) == 1, "bwd NULL dout")
+check(so.zebra_linear_attn_bwd(ctypes.byref(args(L, 0.5)), g4[0], g4[1], ctypes.c_void_p(0x9208), g4[3], None) == 1,
+      "bwd misaligned dk")
+check(so.zebra_linear_attn_bwd(ctypes.byref(args(L, 0.5, fill=False)), *g4, None) == 1, "bwd NULL q")
 # fp64 affine solve: recovers a planted map from exact statistics
 n, d = 5000, 64
 o = g.standard_normal((n, d))

@@ -134,7 +134,8 @@ enum {
   ZEBRA_BUF_SEL = 8,
   ZEBRA_BUF_SELMASK = 9,
   ZEBRA_BUF_GAP = 10,
-  ZEBRA_BUF_WORKSPACE = 11  /* enough for every entry point below */
+  ZEBRA_BUF_WORKSPACE = 11,     /* enough for every entry point below but zebra_sparse_attn_bwd */
+  ZEBRA_BUF_BWD_WORKSPACE = 12  /* enough for every entry point, zebra_sparse_attn_bwd included */
 };
 
 /* Operation codes for zebra_validate. */
@@ -149,7 +150,8 @@ enum {
   ZEBRA_OP_COVERAGE = 7,
   ZEBRA_OP_PROLOGUE = 8,
   ZEBRA_OP_FRAME = 9,
-  ZEBRA_OP_LINEAR_BWD = 10
+  ZEBRA_OP_LINEAR_BWD = 10,
+  ZEBRA_OP_SPARSE_BWD = 11
 };
 
 /* Pack K and V into tile-major order ("Speedup scales with the number of
@@ -189,6 +191,30 @@ zebra_status zebra_select_tiles(const zebra_args* a, zebra_stream stream);
  * special rows, whose keys are split into segments. Launches one kernel
  * pair per round of as many workgroups as the device holds at once. */
 zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream);
+
+/* Backward of zebra_sparse_attn ("A closed-form fit avoids retraining from
+ * scratch": an optional training stage after the conversion fine-tunes the
+ * converted model, so gradients flow back through its tile-sparse stages).
+ * For out as zebra_sparse_attn computes it at a->y, writes the gradients of
+ * sum(dout * out) with respect to q, k and v. The tile selection passes no
+ * gradient: the kept tiles are the forward's (sel, selmask). A landmark is
+ * the mean of its tile, so each token of an omitted tile receives 1/n_u of
+ * the landmark's key and value gradients (ln n_u is a constant); the
+ * landmarks enter at full precision (kbar fp64 and vbar fp32, each as bf16
+ * high and low parts; log2 n_u from lm). Reads q, k, v, kbar, vbar, lm, sel,
+ * selmask,
+ * i.e. call it after zebra_pack_tiles (with landmarks) and
+ * zebra_select_tiles on the same q, k, v and y, and nothing that overwrites
+ * them in between. dout: bf16, device, with the output's token and head
+ * strides; dq, dk, dv: bf16, device, with q's strides, overlapping none of
+ * the inputs. All four 16-byte aligned. The workspace must hold
+ * ZEBRA_BUF_BWD_WORKSPACE bytes (per-row log-sum-exp and D, the transposed
+ * kept-tile bitmap, partial gradients of the special keys and landmarks).
+ * fp32 arithmetic with bf16 MFMA operands: logits and dP exact products
+ * summed in fp32, P and the logit gradients rounded to bf16 for the
+ * gradient products; each gradient rounded once to bf16. */
+zebra_status zebra_sparse_attn_bwd(const zebra_args* a, const void* dout, void* dq, void* dk, void* dv,
+                                   zebra_stream stream);
 
 /* Linear attention with the centred affine correction. For each head:
  * phi(x) = softmax over the 64 channels of RoPE2D(RMSNorm(x)) (channels

@@ -93,7 +93,8 @@ class StageBuffers:
     """Device buffers of one stage shape (torch uint8 tensors sized by
     zebra_buffer_bytes). `gap` is allocated only if asked for."""
 
-    def __init__(self, L, y: float, device="cuda", with_gap: bool = True, sparse: bool = True):
+    def __init__(self, L, y: float, device="cuda", with_gap: bool = True, sparse: bool = True,
+                 backward: bool = False):
         import torch
         self.L, self.y = _as_layout(L), float(y)
         names = ["KT", "VT", "KS", "VS", "WORKSPACE"]
@@ -101,7 +102,8 @@ class StageBuffers:
             names += ["KBAR", "VBAR", "LOGN", "LM", "SEL", "SELMASK"] + (["GAP"] if with_gap else [])
         self.t = {}
         for n in names:
-            nb = buffer_bytes(self.L, self.y, n)
+            # backward: a workspace large enough for zebra_sparse_attn_bwd too
+            nb = buffer_bytes(self.L, self.y, "BWD_WORKSPACE" if (n == "WORKSPACE" and backward) else n)
             self.t[n] = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
         self.k = keep_count(self.L, self.y)
         self.T = num_tiles(self.L)
@@ -308,6 +310,26 @@ def linear_attn_bwd(args: Args, dout, dq, dk, dv, stream=None):
         if _rows_view(name, t, Lp) != want_in:
             raise ValueError(f"{name} must have the token and head strides of q, k and v {want_in}")
     st = lib.zebra_linear_attn_bwd(ctypes.byref(args), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream))
+    if st != 0:
+        raise ZebraError(st, lib.zebra_last_error().decode())
+
+
+def sparse_attn_bwd(args: Args, dout, dq, dk, dv, stream=None):
+    """Gradients of sum(dout * out) for the tile-sparse stage of args (the
+    kept tiles and landmarks of args' buffers, from pack_tiles and
+    select_tiles on the same inputs) into dq, dk, dv. dout: bf16 device
+    tensor with the strides of args' out; dq, dk, dv: bf16 device tensors
+    with the strides of args' q, k and v. args' workspace must be sized for
+    the backward (StageBuffers(..., backward=True))."""
+    Lp = Layout(args.L.frames, args.L.specials, args.L.rows, args.L.cols, args.L.heads, args.L.head_dim)
+    want_in = (args.L.tok_stride or Lp.heads * 64, args.L.head_stride or 64)
+    want_out = (args.L.out_tok_stride or Lp.heads * 64, args.L.out_head_stride or 64)
+    if _rows_view("dout", dout, Lp) != want_out:
+        raise ValueError(f"dout must have the token and head strides of out {want_out}")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if _rows_view(name, t, Lp) != want_in:
+            raise ValueError(f"{name} must have the token and head strides of q, k and v {want_in}")
+    st = lib.zebra_sparse_attn_bwd(ctypes.byref(args), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream))
     if st != 0:
         raise ZebraError(st, lib.zebra_last_error().decode())
 

@@ -9,9 +9,9 @@ from __future__ import annotations
 import ctypes
 
 BUF = dict(KT=0, VT=1, KS=2, VS=3, KBAR=4, VBAR=5, LOGN=6, LM=7, SEL=8, SELMASK=9, GAP=10,
-           WORKSPACE=11)
+           WORKSPACE=11, BWD_WORKSPACE=12)
 OP = dict(PACK=0, LANDMARKS=1, SELECT=2, SPARSE=3, LINEAR=4, DENSE=5, AFFINE_STATS=6, COVERAGE=7, PROLOGUE=8, FRAME=9,
-          LINEAR_BWD=10)
+          LINEAR_BWD=10, SPARSE_BWD=11)
 AFFINE_STATS = 1 + 2 * 64 + 2 * 64 * 64  # doubles of the affine-fit statistics
 NOALLOC_SCRATCH_BYTES = 64 << 20
 STATUS = {0: "ZEBRA_OK", 1: "ZEBRA_ERR_INVALID_ARG", 2: "ZEBRA_ERR_UNSUPPORTED",
@@ -20,7 +20,8 @@ EXPORTS = ["zebra_pack_tiles", "zebra_landmarks", "zebra_select_tiles", "zebra_s
            "zebra_linear_attn", "zebra_dense_attn", "zebra_validate", "zebra_buffer_bytes",
            "zebra_keep_count", "zebra_num_tiles", "zebra_last_error", "zebra_version",
            "zebra_affine_stats", "zebra_affine_solve", "zebra_linear_attn_noalloc", "zebra_coverage",
-           "zebra_qk_prologue", "zebra_frame_attn", "zebra_linear_attn_bwd"]
+           "zebra_qk_prologue", "zebra_frame_attn", "zebra_linear_attn_bwd",
+           "zebra_sparse_attn_bwd"]
 STAGE_CALLS = ("zebra_pack_tiles", "zebra_landmarks", "zebra_select_tiles", "zebra_sparse_attn",
                "zebra_linear_attn", "zebra_dense_attn", "zebra_linear_attn_noalloc",
                "zebra_frame_attn")
@@ -74,6 +75,8 @@ def declare(so: ctypes.CDLL) -> ctypes.CDLL:
     so.zebra_qk_prologue.restype = ctypes.c_int
     so.zebra_linear_attn_bwd.argtypes = [P(Args), _vp, _vp, _vp, _vp, _vp]
     so.zebra_linear_attn_bwd.restype = ctypes.c_int
+    so.zebra_sparse_attn_bwd.argtypes = [P(Args), _vp, _vp, _vp, _vp, _vp]
+    so.zebra_sparse_attn_bwd.restype = ctypes.c_int
     so.zebra_coverage.argtypes = [P(Args), _vp, _vp, _vp]
     so.zebra_coverage.restype = ctypes.c_int
     so.zebra_affine_solve.argtypes = [_vp, ctypes.c_double, _vp, _vp, _vp]

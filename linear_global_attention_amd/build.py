@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzebra.so")
 SOURCES = ["zebra.cpp", "pack.hip", "select.hip", "attn.hip", "attn_exact.hip", "linear.hip", "coverage.hip", "block.hip",
-           "linear_bwd.hip"]
+           "linear_bwd.hip", "sparse_bwd.hip"]
 ARCH = os.environ.get("ZEBRA_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

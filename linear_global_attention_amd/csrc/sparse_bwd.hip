@@ -1,0 +1,776 @@
+// Backward of the tile-sparse attention stage for gfx950: dq, dk and dv
+// from dout, for the stage zebra_sparse_attn computes.
+//
+// Zebra3D pages, "A closed-form fit avoids retraining from scratch": an
+// optional training stage after conversion fine-tunes the converted model,
+// which needs gradients through its tile-sparse stages. "Linear-centered
+// stages plus tile-sparse stages" defines the forward: a patch row of query
+// tile t attends to every token of the tiles t kept, to the mean-key/value
+// landmark of every omitted tile (logit q.kbar_u/8 + ln n_u), to every
+// special token, and to its own key when t itself is not kept; special rows
+// attend to every token. The selection passes no gradient (the kept tiles
+// are those of the forward); a landmark hands 1/n_u of its gradient to each
+// token of its tile.
+//
+// With l_ij the logits, P = softmax, dP_ij = dout_i . v_j and
+// D_i = sum_j P_ij dP_ij, the logit gradients are dS_ij = P_ij (dP_ij - D_i)
+// and dq_i = sum_j dS_ij k_j / 8, dk_j = sum_i dS_ij q_i / 8,
+// dv_j = sum_i P_ij dout_i.
+//
+// Kernels, in stream order (per head; rows and keys addressed through the
+// strides of q, k, v and dout):
+//   sbwd_rows<STATS>  query-major: every row's log2-sum-exp2 of its logits
+//                     (log2 units) and D, in one pass over its visible keys
+//                     (each lane keeps running partials over its own keys,
+//                     merged at the end: P stays exact fp32).
+//   sbwd_rows<DQ>     query-major again: dS in fp32, dq += K dS on MFMA
+//                     (K^T fragments from transposing LDS reads), plus the
+//                     self key; writes dq.
+//   sbwd_transpose    the kept-tile bitmap transposed: for every key tile,
+//                     the query tiles that keep it (32 x 32 bit blocks by
+//                     ballot).
+//   sbwd_keys<GLOBAL> key-major over special keys and landmarks, 64 per
+//                     workgroup, against every query row (landmarks masked
+//                     where the row's tile keeps them), in row chunks:
+//                     partial dk, dv per chunk.
+//   sbwd_reduce       fixed-order sums of those partials: dk, dv of the
+//                     special tokens; the landmark gradients.
+//   sbwd_keys<TILE>   key-major over the tokens of each key tile, against
+//                     the query tiles that keep it and every special row,
+//                     plus the self key and 1/n of the tile's landmark
+//                     gradient; writes dk, dv.
+// Per 32-key (query-major) or 32-row (key-major) block and wave: 4 MFMAs for
+// the logits, 4 for dP, 4 or 8 for the gradient products
+// (v_mfma_f32_16x16x32_bf16; P and dS enter as bf16). Landmarks enter at
+// full precision (the fp64 mean keys and fp32 mean values, each as bf16
+// high and low parts: two MFMAs where a token key takes one).
+#include "common.hpp"
+
+namespace zebra {
+
+constexpr int SB_THREADS = 256;                      // 4 waves, 16 rows or keys each
+constexpr float SB_C = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
+constexpr int SB_CHUNKS = 8;                         // row chunks of the global-key pass
+
+typedef void __attribute__((address_space(3))) sb_lds_void;
+typedef short sb_v4s __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- rows and units
+
+// A query unit: patch tile t (< T), or special-row unit T + s (64 special
+// rows each). Rows of a unit and the token of its row j.
+__device__ inline int unit_rows(const Geom& g, int unit) {
+  if (unit < g.T) return tile_n(g, unit - frame_of_tile(g, unit) * g.tpf);
+  return min(64, g.nspec - (unit - g.T) * 64);
+}
+
+__device__ inline long long unit_token(const Geom& g, int unit, int j) {
+  if (unit < g.T) {
+    const int f = frame_of_tile(g, unit), tl = unit - f * g.tpf;
+    const int a = tl / g.tc, b = tl - a * g.tc;
+    const int tw = tile_w(g, tl);
+    const int jr = j / tw;
+    const int r = TILE * a + jr, c = TILE * b + (j - jr * tw);
+    return (long long)f * g.tok_pf + g.S + (long long)r * g.C + c;
+  }
+  const int i = (unit - g.T) * 64 + j;
+  const int f = i / g.S;
+  return (long long)f * g.tok_pf + (i - f * g.S);
+}
+
+__device__ inline long long special_token(const Geom& g, int i) {
+  const int f = i / g.S;
+  return (long long)f * g.tok_pf + (i - f * g.S);
+}
+
+__device__ inline int num_units(const Geom& g) { return g.T + (g.nspec + 63) / 64; }
+
+// ---------------------------------------------------------------- LDS tiles
+// A tile of 32 rows x 64 bf16 channels (4 KB), the 16-byte chunk c of row
+// r stored at chunk c ^ (r % 8): the 16 lanes of an A-operand read (16 rows,
+// one chunk column) and of a transposing read (4 rows x 4 pieces) spread
+// over the banks.
+__device__ inline int sb_off(int r, int ch) { return r * D + ((((ch >> 3) ^ (r & 7))) << 3) + (ch & 7); }
+
+// A operand rows 16 h + lane%16, channels 32 ks + 8 (lane/16) .. +7
+__device__ inline bf16x8 row_frag(const u16* t, int h, int ks, int lane) {
+  const int r = 16 * h + (lane & 15);
+  return *(const bf16x8*)(t + sb_off(r, 32 * ks + 8 * (lane >> 4)));
+}
+
+// A operand of the transposed tile: rows = channels 16 cb + lane%16, k-slots
+// 8 g + j = tile rows 4 g + j (j < 4) and 16 + 4 g + j - 4 (j >= 4), g = lane/16.
+__device__ inline bf16x8 col_frag(const u16* t, int cb, int lane) {
+  typedef __attribute__((address_space(3))) sb_v4s lds_v4s;
+  const int i = lane & 15, g = lane >> 4;
+  const int ch = 16 * cb + 4 * (i & 3);
+  const sb_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + sb_off(4 * g + (i >> 2), ch)));
+  const sb_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + sb_off(16 + 4 * g + (i >> 2), ch)));
+  typedef short sb_v8s __attribute__((ext_vector_type(8)));
+  const sb_v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ inline unsigned sb_pack(float a, float b) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 f = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, b2));
+}
+
+// 8 lane values (the lane's two 4-row halves) as a bf16 B operand
+__device__ inline bf16x8 pack8(const float v[8]) {
+  return __builtin_bit_cast(bf16x8, make_uint4(sb_pack(v[0], v[1]), sb_pack(v[2], v[3]), sb_pack(v[4], v[5]),
+                                               sb_pack(v[6], v[7])));
+}
+
+// Sum / max over the 4 lanes l, l^16, l^32, l^48 that hold one row's or
+// key's pieces.
+__device__ inline float sb_sum4(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float sb_max4(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// 16 bytes (8 channels) at element offset `off` of a bf16 tensor; zeros
+// when !ok
+__device__ inline uint4 ld16(const u16* base, long long off, bool ok) {
+  return ok ? *(const uint4*)(base + off) : make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct SbArgs {
+  const u16* Q;
+  const u16* K;
+  const u16* V;
+  const u16* dO;
+  const u16* LM;          // landmark key blocks (row 32: fp32 log2 n)
+  const double* kbar;     // [H][T][64] exact landmark keys
+  const float* vbar;      // [H][T][64] landmark values
+  const int* sel;         // [H][T][keep] kept tiles, ascending
+  const unsigned* selmask;   // [H][T][nw] bit u of word u/32: t keeps u
+  unsigned* selT;            // [H][T][nw] bit t of word t/32: t keeps u
+  float* lse;             // [H][N] log2-sum-exp2 of the row's logits (log2 units)
+  float* dsum;            // [H][N] D
+  float* part;            // [SB_CHUNKS][H][nspec_pad + T_pad][2][64] partial dk, dv of global keys
+  float* lgrad;           // [H][T][2][64] landmark dk, dv
+  u16* dQ;
+  u16* dK;
+  u16* dV;
+  int keep, nw;
+  long long o_tok, o_head;  // dout strides
+};
+
+__device__ inline const char* lm_kblock(const Geom& g, const u16* LM, int h, int b) {
+  return (const char*)LM + (long long)h * g.T_pad * LM_BYTES_PER_TILE + (long long)b * LM_KEY_BLOCK;
+}
+
+// ---------------------------------------------------------------- query-major passes
+
+enum { SB_STATS = 0, SB_DQ = 1 };
+
+// 8 fp32 values as bf16 high parts and low parts (the rounding remainders)
+__device__ inline void split8(const float v[8], uint4& hi, uint4& lo) {
+  unsigned h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = sb_pack(v[2 * i], v[2 * i + 1]);
+    l[i] = sb_pack(v[2 * i] - __uint_as_float(h[i] << 16), v[2 * i + 1] - __uint_as_float(h[i] & 0xFFFF0000u));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// Channels c8 .. c8 + 7 of landmark u: the exact mean key (fp64) and value
+// (fp32), each as bf16 high and low parts.
+__device__ inline void landmark_parts(const Geom& g, const SbArgs& A, int h, int u, int c8, uint4& khi, uint4& klo,
+                                      uint4& vhi, uint4& vlo) {
+  const double* kr = A.kbar + ((long long)h * g.T + u) * D + c8;
+  const float4* vr = (const float4*)(A.vbar + ((long long)h * g.T + u) * D + c8);
+  float kv[8], vv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kv[i] = (float)kr[i];
+  const float4 a = vr[0], b = vr[1];
+  vv[0] = a.x;
+  vv[1] = a.y;
+  vv[2] = a.z;
+  vv[3] = a.w;
+  vv[4] = b.x;
+  vv[5] = b.y;
+  vv[6] = b.z;
+  vv[7] = b.w;
+  split8(kv, khi, klo);
+  split8(vv, vhi, vlo);
+}
+
+// Stages key block `blk` of one of three kinds into sK, sV and the per-key
+// logit bias (log2 units) sB:
+//   0: keys 32 hb .. of tile u (hb = blk & 1, u = blk >> 1), bias 0;
+//   1: special keys 32 blk ..;
+//   2: landmarks 32 blk .., bias log2 n_u, -inf where `mask` has the bit;
+//      the exact means as bf16 high parts in sK, sV and low parts in sK2,
+//      sV2 (the landmarks are means of similar tiles, so the query gradient
+//      is a small remainder of their sum, which a single rounding swamps).
+// Keys past the end: zero rows, bias -inf. Every thread calls it.
+__device__ inline void stage_key_block(const Geom& g, const SbArgs& A, int h, int kind, int blk, unsigned mask,
+                                       u16* sK, u16* sV, u16* sK2, u16* sV2, float* sB) {
+  const int tid = threadIdx.x, key = tid >> 3, c = tid & 7;
+  uint4 kw = make_uint4(0u, 0u, 0u, 0u), vw = kw;
+  float bias = -INFINITY;
+  if (kind == 2) {
+    const int u = 32 * blk + key;
+    uint4 kl = make_uint4(0u, 0u, 0u, 0u), vl = kl;
+    if (u < g.T) {
+      landmark_parts(g, A, h, u, 8 * c, kw, kl, vw, vl);
+      const char* kb = lm_kblock(g, A.LM, h, blk);
+      bias = ((mask >> key) & 1u) ? -INFINITY : ((const float*)(kb + LM_LOG2N_ROW * 128))[key];
+    }
+    *(uint4*)(sK2 + sb_off(key, 8 * c)) = kl;
+    *(uint4*)(sV2 + sb_off(key, 8 * c)) = vl;
+  } else {
+    long long tok = -1;
+    if (kind == 0) {
+      const int u = blk >> 1, j = 32 * (blk & 1) + key;
+      if (j < unit_rows(g, u)) tok = unit_token(g, u, j);
+    } else {
+      const int i = 32 * blk + key;
+      if (i < g.nspec) tok = special_token(g, i);
+    }
+    if (tok >= 0) {
+      const long long row = tok * g.in_tok + (long long)h * g.in_head;
+      kw = *(const uint4*)(A.K + row + 8 * c);
+      vw = *(const uint4*)(A.V + row + 8 * c);
+      bias = 0.f;
+    }
+  }
+  *(uint4*)(sK + sb_off(key, 8 * c)) = kw;
+  *(uint4*)(sV + sb_off(key, 8 * c)) = vw;
+  if (c == 0) sB[key] = bias;
+}
+
+// grid (units, H), block 256: one query unit (up to 64 rows, 16 per wave).
+template <int MODE>
+__global__ void __launch_bounds__(SB_THREADS) sbwd_rows_kernel(Geom g, SbArgs A) {
+  __shared__ __attribute__((aligned(16))) u16 sK[32 * D], sV[32 * D], sK2[32 * D], sV2[32 * D];
+  __shared__ __attribute__((aligned(16))) float sB[32];
+  const int unit = blockIdx.x, h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lg = lane >> 4, tl = lane & 15;
+  const bool patch = unit < g.T;
+  const int nrows = unit_rows(g, unit);
+  const int j = 16 * wave + tl;  // this lane's row of the unit
+  const bool valid = j < nrows;
+  const long long tok = valid ? unit_token(g, unit, j) : 0;
+  const long long qrow = tok * g.in_tok + (long long)h * g.in_head;
+  const long long orow = tok * A.o_tok + (long long)h * A.o_head;
+  bf16x8 qb[2], ob[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    qb[ks] = __builtin_bit_cast(bf16x8, ld16(A.Q, qrow + 32 * ks + 8 * lg, valid));
+    ob[ks] = __builtin_bit_cast(bf16x8, ld16(A.dO, orow + 32 * ks + 8 * lg, valid));
+  }
+  // per-lane partials (STATS) or the row's statistics (DQ)
+  float m = -1e30f, l = 0.f, dsm = 0.f;
+  float lse2 = 0.f, Drow = 0.f;
+  if (MODE == SB_DQ && valid) {
+    lse2 = A.lse[(long long)h * g.N + tok];
+    Drow = A.dsum[(long long)h * g.N + tok];
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto block = [&](int kind, int blk, unsigned mask) {
+    __syncthreads();  // the previous block's reads are done
+    stage_key_block(g, A, h, kind, blk, mask, sK, sV, sK2, sV2, sB);
+    __syncthreads();
+    f32x4 s[2], dp[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[hh] = s[hh];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(sK, hh, ks, lane), qb[ks], s[hh], 0, 0, 0);
+        dp[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(sV, hh, ks, lane), ob[ks], dp[hh], 0, 0, 0);
+        if (kind == 2) {
+          s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(sK2, hh, ks, lane), qb[ks], s[hh], 0, 0, 0);
+          dp[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(sV2, hh, ks, lane), ob[ks], dp[hh], 0, 0, 0);
+        }
+      }
+    }
+    // lane (row tl, group lg) holds keys 4 lg + r and 16 + 4 lg + r
+    const float4 b0 = *(const float4*)(sB + 4 * lg), b1 = *(const float4*)(sB + 16 + 4 * lg);
+    const float bias[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    float x[8], d[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = fmaf(s[i >> 2][i & 3], SB_C, bias[i]);
+      d[i] = dp[i >> 2][i & 3];
+    }
+    if (MODE == SB_STATS) {
+      float mx = m;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, x[i]);
+      const float sc = __builtin_amdgcn_exp2f(m - mx);
+      l *= sc;
+      dsm *= sc;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(x[i] - mx);
+        l += p;
+        dsm = fmaf(p, d[i], dsm);
+      }
+      m = mx;
+    } else {
+      float ds[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ds[i] = valid ? __builtin_amdgcn_exp2f(x[i] - lse2) * (d[i] - Drow) : 0.f;
+      const bf16x8 dsb = pack8(ds);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(sK, cb, lane), dsb, acc[cb], 0, 0, 0);
+        if (kind == 2)
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(sK2, cb, lane), dsb, acc[cb], 0, 0, 0);
+      }
+    }
+  };
+
+  const int hw = (long long)h * g.T;
+  if (patch) {
+    const int* kept = A.sel + ((long long)h * g.T + unit) * A.keep;
+    for (int i = 0; i < A.keep; ++i) {
+      const int u = kept[i];
+      block(0, 2 * u, 0u);
+      if (unit_rows(g, u) > 32) block(0, 2 * u + 1, 0u);
+    }
+  } else {
+    for (int u = 0; u < g.T; ++u) {
+      block(0, 2 * u, 0u);
+      if (unit_rows(g, u) > 32) block(0, 2 * u + 1, 0u);
+    }
+  }
+  for (int b = 0; b < (g.nspec + 31) / 32; ++b) block(1, b, 0u);
+  (void)hw;
+  bool self = false;
+  if (patch) {
+    const unsigned* mrow = A.selmask + ((long long)h * g.T + unit) * A.nw;
+    for (int b = 0; b < g.T_pad / 32; ++b) block(2, b, b < A.nw ? mrow[b] : 0xFFFFFFFFu);
+    self = ((mrow[unit >> 5] >> (unit & 31)) & 1u) == 0;
+  }
+  // the self key (a patch row whose own tile is not kept): its logit and
+  // dP from the lane's 16 channels, summed over the row's 4 lanes
+  float xs = -INFINITY, dps = 0.f;
+  if (self) {
+    const u16* kr = A.K + qrow;
+    const u16* vr = A.V + qrow;
+    float sq = 0.f, sd = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 kw = ld16(kr, 32 * ks + 8 * lg, valid), vw = ld16(vr, 32 * ks + 8 * lg, valid);
+      const uint4 qw = __builtin_bit_cast(uint4, qb[ks]), ow = __builtin_bit_cast(uint4, ob[ks]);
+      const unsigned qa[4] = {qw.x, qw.y, qw.z, qw.w}, ka[4] = {kw.x, kw.y, kw.z, kw.w};
+      const unsigned oa[4] = {ow.x, ow.y, ow.z, ow.w}, va[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sq = fmaf(__uint_as_float(qa[e] << 16), __uint_as_float(ka[e] << 16), sq);
+        sq = fmaf(__uint_as_float(qa[e] & 0xFFFF0000u), __uint_as_float(ka[e] & 0xFFFF0000u), sq);
+        sd = fmaf(__uint_as_float(oa[e] << 16), __uint_as_float(va[e] << 16), sd);
+        sd = fmaf(__uint_as_float(oa[e] & 0xFFFF0000u), __uint_as_float(va[e] & 0xFFFF0000u), sd);
+      }
+    }
+    xs = sb_sum4(sq) * SB_C;
+    dps = sb_sum4(sd);
+  }
+  if (MODE == SB_STATS) {
+    if (self && lg == 0) {  // one of the row's 4 lanes counts the self key
+      const float mx = fmaxf(m, xs), sc = __builtin_amdgcn_exp2f(m - mx), p = __builtin_amdgcn_exp2f(xs - mx);
+      l = l * sc + p;
+      dsm = dsm * sc + p * dps;
+      m = mx;
+    }
+    const float M = sb_max4(m);
+    const float sc = __builtin_amdgcn_exp2f(m - M);
+    const float L = sb_sum4(l * sc), Dn = sb_sum4(dsm * sc);
+    if (valid && lg == 0) {
+      A.lse[(long long)h * g.N + tok] = M + __log2f(L);
+      A.dsum[(long long)h * g.N + tok] = Dn / L;
+    }
+  } else {
+    // dq of row j (lane tl): channels 16 cb + 4 lg + r, times 1/8, plus the
+    // self key's dS k / 8
+    const float dss = self ? __builtin_amdgcn_exp2f(xs - lse2) * (dps - Drow) : 0.f;
+    if (valid) {
+      u16* out = A.dQ + qrow;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int ch = 16 * cb + 4 * lg;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[cb][r];
+        if (self) {
+          const uint2 kw = *(const uint2*)(A.K + qrow + ch);
+          v[0] = fmaf(dss, __uint_as_float(kw.x << 16), v[0]);
+          v[1] = fmaf(dss, __uint_as_float(kw.x & 0xFFFF0000u), v[1]);
+          v[2] = fmaf(dss, __uint_as_float(kw.y << 16), v[2]);
+          v[3] = fmaf(dss, __uint_as_float(kw.y & 0xFFFF0000u), v[3]);
+        }
+        *(uint2*)(out + ch) = make_uint2(sb_pack(v[0] * 0.125f, v[1] * 0.125f), sb_pack(v[2] * 0.125f, v[3] * 0.125f));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- transposed selection
+
+// grid (ceil(nw / 2), nw, H), block 64: two 32 x 32 bit blocks per wave.
+// Lane i of half b' reads word [t = 32 a + i][wb] of the kept bitmap; the
+// ballot of bit j over the half is word [u = 32 wb + j][a] of the transposed
+// bitmap.
+__global__ void __launch_bounds__(64) sbwd_transpose_kernel(Geom g, const unsigned* __restrict__ selmask,
+                                                            unsigned* __restrict__ selT, int nw) {
+  const int lane = threadIdx.x, half = lane >> 5, i = lane & 31;
+  const int wb = 2 * blockIdx.x + half, a = blockIdx.y, h = blockIdx.z;
+  const int t = 32 * a + i;
+  unsigned w = 0u;
+  if (wb < nw && t < g.T) w = selmask[((long long)h * g.T + t) * nw + wb];
+  unsigned mine = 0u;
+#pragma unroll 4
+  for (int j = 0; j < 32; ++j) {
+    const unsigned long long b = __ballot((w >> j) & 1u);
+    const unsigned col = half ? (unsigned)(b >> 32) : (unsigned)b;
+    if (i == j) mine = col;
+  }
+  const int u = 32 * wb + i;
+  if (wb < nw && u < g.T) selT[((long long)h * g.T + u) * nw + a] = mine;
+}
+
+// ---------------------------------------------------------------- key-major passes
+
+enum { SB_TILE = 0, SB_SPEC = 1, SB_LMK = 2 };
+
+// grid:
+//   TILE (T, H):                 keys = the tokens of tile blockIdx.x
+//   SPEC (ceil(nspec/64), H, SB_CHUNKS), LMK (ceil(T/64), H, SB_CHUNKS):
+//                                keys = 64 special keys or landmarks, rows =
+//                                chunk blockIdx.z of the query units
+// Wave w owns keys 16 w .. 16 w + 15 (lane tl: key 16 w + tl).
+template <int MODE>
+__global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A) {
+  __shared__ __attribute__((aligned(16))) u16 sQ[32 * D], sO[32 * D];
+  __shared__ __attribute__((aligned(16))) float sL[32], sD[32];
+  const int kb = blockIdx.x, h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lg = lane >> 4, tl = lane & 15;
+  const int key = 16 * wave + tl;
+  // this lane's key: its K and V rows as B operands, and its logit bias
+  bool kvalid;
+  long long ktok = 0;
+  int lmk = 0;
+  float kbias = 0.f;
+  bf16x8 kfrag[2], vfrag[2], kfrag2[2], vfrag2[2];  // *2: low parts (landmarks only)
+  if (MODE == SB_TILE) {
+    kvalid = key < unit_rows(g, kb);
+    if (kvalid) ktok = unit_token(g, kb, key);
+  } else if (MODE == SB_SPEC) {
+    const int i = 64 * kb + key;
+    kvalid = i < g.nspec;
+    if (kvalid) ktok = special_token(g, i);
+  } else {
+    lmk = 64 * kb + key;
+    kvalid = lmk < g.T;
+  }
+  if (MODE == SB_LMK) {
+    const char* blk = lm_kblock(g, A.LM, h, lmk >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 kw = make_uint4(0u, 0u, 0u, 0u), vw = kw, kl = kw, vl = kw;
+      if (kvalid) landmark_parts(g, A, h, lmk, 32 * ks + 8 * lg, kw, kl, vw, vl);
+      kfrag[ks] = __builtin_bit_cast(bf16x8, kw);
+      vfrag[ks] = __builtin_bit_cast(bf16x8, vw);
+      kfrag2[ks] = __builtin_bit_cast(bf16x8, kl);
+      vfrag2[ks] = __builtin_bit_cast(bf16x8, vl);
+    }
+    kbias = kvalid ? ((const float*)(blk + LM_LOG2N_ROW * 128))[lmk & 31] : -INFINITY;
+  } else {
+    const long long row = ktok * g.in_tok + (long long)h * g.in_head;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      kfrag[ks] = __builtin_bit_cast(bf16x8, ld16(A.K, row + 32 * ks + 8 * lg, kvalid));
+      vfrag[ks] = __builtin_bit_cast(bf16x8, ld16(A.V, row + 32 * ks + 8 * lg, kvalid));
+    }
+    kbias = kvalid ? 0.f : -INFINITY;
+  }
+  f32x4 dk[4], dv[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) dk[cb] = dv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // rows 32 hb .. 32 hb + 31 of query unit t against the workgroup's keys;
+  // `bias` is this lane's key bias for the unit (-inf: not visible)
+  auto rows = [&](int t, int hb, float bias) {
+    __syncthreads();  // the previous rows' reads are done
+    {
+      const int tid = threadIdx.x, r = tid >> 3, c = tid & 7;
+      const int jr = 32 * hb + r;
+      const bool ok = jr < unit_rows(g, t);
+      const long long tk = ok ? unit_token(g, t, jr) : 0;
+      *(uint4*)(sQ + sb_off(r, 8 * c)) = ld16(A.Q, tk * g.in_tok + (long long)h * g.in_head + 8 * c, ok);
+      *(uint4*)(sO + sb_off(r, 8 * c)) = ld16(A.dO, tk * A.o_tok + (long long)h * A.o_head + 8 * c, ok);
+      if (c == 0) {
+        sL[r] = ok ? A.lse[(long long)h * g.N + tk] : INFINITY;
+        sD[r] = ok ? A.dsum[(long long)h * g.N + tk] : 0.f;
+      }
+    }
+    __syncthreads();
+    f32x4 s[2], dp[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[hh] = s[hh];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 qa = row_frag(sQ, hh, ks, lane), oa = row_frag(sO, hh, ks, lane);
+        s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kfrag[ks], s[hh], 0, 0, 0);
+        dp[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vfrag[ks], dp[hh], 0, 0, 0);
+        if (MODE == SB_LMK) {
+          s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kfrag2[ks], s[hh], 0, 0, 0);
+          dp[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vfrag2[ks], dp[hh], 0, 0, 0);
+        }
+      }
+    }
+    // lane (key tl, group lg) holds rows 4 lg + r and 16 + 4 lg + r
+    const float4 l0 = *(const float4*)(sL + 4 * lg), l1 = *(const float4*)(sL + 16 + 4 * lg);
+    const float4 d0 = *(const float4*)(sD + 4 * lg), d1 = *(const float4*)(sD + 16 + 4 * lg);
+    const float lse[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+    const float Dr[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    float p[8], ds[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(fmaf(s[i >> 2][i & 3], SB_C, bias) - lse[i]);
+      ds[i] = p[i] * (dp[i >> 2][i & 3] - Dr[i]);
+    }
+    const bf16x8 pb = pack8(p), dsb = pack8(ds);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      dv[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(sO, cb, lane), pb, dv[cb], 0, 0, 0);
+      dk[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(sQ, cb, lane), dsb, dk[cb], 0, 0, 0);
+    }
+  };
+  auto unit = [&](int t, float bias) {
+    rows(t, 0, bias);
+    if (unit_rows(g, t) > 32) rows(t, 1, bias);
+  };
+
+  const int nunits = num_units(g);
+  if (MODE == SB_TILE) {
+    // the query tiles that keep this tile, then every special-row unit
+    const unsigned* trow = A.selT + ((long long)h * g.T + kb) * A.nw;
+    for (int w = 0; w < A.nw; ++w) {
+      unsigned bits = (unsigned)__builtin_amdgcn_readfirstlane((int)trow[w]);
+      while (bits) {
+        const int t = 32 * w + __builtin_ctz(bits);
+        bits &= bits - 1u;
+        unit(t, kbias);
+      }
+    }
+    for (int t = g.T; t < nunits; ++t) unit(t, kbias);
+  } else {
+    const int lastu = MODE == SB_LMK ? g.T : nunits;  // special rows see no landmark
+    const int c = blockIdx.z;
+    const int t0 = (int)((long long)lastu * c / SB_CHUNKS), t1 = (int)((long long)lastu * (c + 1) / SB_CHUNKS);
+    for (int t = t0; t < t1; ++t) {
+      float bias = kbias;
+      if (MODE == SB_LMK && kvalid) {
+        const unsigned wd = A.selmask[((long long)h * g.T + t) * A.nw + (lmk >> 5)];
+        if ((wd >> (lmk & 31)) & 1u) bias = -INFINITY;
+      }
+      unit(t, bias);
+    }
+  }
+
+  // lane (key tl, group lg) holds channels 16 cb + 4 lg + r of dk (x 1/8 to
+  // come) and dv
+  if (MODE == SB_TILE) {
+    if (!kvalid) return;
+    float vk[16], vv[16];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        vk[4 * cb + r] = dk[cb][r];
+        vv[4 * cb + r] = dv[cb][r];
+      }
+    const long long row = ktok * g.in_tok + (long long)h * g.in_head;
+    // the self key: a row of this tile whose tile is not kept attends to its
+    // own key (row `key` of unit kb is token ktok)
+    const bool self = ((A.selmask[((long long)h * g.T + kb) * A.nw + (kb >> 5)] >> (kb & 31)) & 1u) == 0;
+    if (self) {
+      const long long orow = ktok * A.o_tok + (long long)h * A.o_head;
+      float qv[16], ov[16], kv[16], vw[16];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int ch = 16 * cb + 4 * lg;
+        const uint2 a = *(const uint2*)(A.Q + row + ch), b = *(const uint2*)(A.dO + orow + ch);
+        const uint2 c = *(const uint2*)(A.K + row + ch), d = *(const uint2*)(A.V + row + ch);
+        const unsigned aa[2] = {a.x, a.y}, bb[2] = {b.x, b.y}, cc[2] = {c.x, c.y}, dd[2] = {d.x, d.y};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          qv[4 * cb + 2 * e] = __uint_as_float(aa[e] << 16);
+          qv[4 * cb + 2 * e + 1] = __uint_as_float(aa[e] & 0xFFFF0000u);
+          ov[4 * cb + 2 * e] = __uint_as_float(bb[e] << 16);
+          ov[4 * cb + 2 * e + 1] = __uint_as_float(bb[e] & 0xFFFF0000u);
+          kv[4 * cb + 2 * e] = __uint_as_float(cc[e] << 16);
+          kv[4 * cb + 2 * e + 1] = __uint_as_float(cc[e] & 0xFFFF0000u);
+          vw[4 * cb + 2 * e] = __uint_as_float(dd[e] << 16);
+          vw[4 * cb + 2 * e + 1] = __uint_as_float(dd[e] & 0xFFFF0000u);
+        }
+      }
+      float sq = 0.f, sd = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sq = fmaf(qv[i], kv[i], sq);
+        sd = fmaf(ov[i], vw[i], sd);
+      }
+      sq = sb_sum4(sq);
+      sd = sb_sum4(sd);
+      const float ps = __builtin_amdgcn_exp2f(sq * SB_C - A.lse[(long long)h * g.N + ktok]);
+      const float dss = ps * (sd - A.dsum[(long long)h * g.N + ktok]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        vk[i] = fmaf(dss, qv[i], vk[i]);
+        vv[i] = fmaf(ps, ov[i], vv[i]);
+      }
+    }
+    // 1/n of the tile's landmark gradient (already scaled like dk: the
+    // landmark pass stores sum dS q, without the 1/8)
+    const float invn = 1.0f / (float)unit_rows(g, kb);
+    const float* lgk = A.lgrad + ((long long)h * g.T + kb) * 2 * D;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int ch = 16 * cb + 4 * lg;
+      const float4 a = *(const float4*)(lgk + ch), b = *(const float4*)(lgk + D + ch);
+      vk[4 * cb] = fmaf(a.x, invn, vk[4 * cb]);
+      vk[4 * cb + 1] = fmaf(a.y, invn, vk[4 * cb + 1]);
+      vk[4 * cb + 2] = fmaf(a.z, invn, vk[4 * cb + 2]);
+      vk[4 * cb + 3] = fmaf(a.w, invn, vk[4 * cb + 3]);
+      vv[4 * cb] = fmaf(b.x, invn, vv[4 * cb]);
+      vv[4 * cb + 1] = fmaf(b.y, invn, vv[4 * cb + 1]);
+      vv[4 * cb + 2] = fmaf(b.z, invn, vv[4 * cb + 2]);
+      vv[4 * cb + 3] = fmaf(b.w, invn, vv[4 * cb + 3]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int ch = 16 * cb + 4 * lg;
+      *(uint2*)(A.dK + row + ch) = make_uint2(sb_pack(vk[4 * cb] * 0.125f, vk[4 * cb + 1] * 0.125f),
+                                             sb_pack(vk[4 * cb + 2] * 0.125f, vk[4 * cb + 3] * 0.125f));
+      *(uint2*)(A.dV + row + ch) =
+          make_uint2(sb_pack(vv[4 * cb], vv[4 * cb + 1]), sb_pack(vv[4 * cb + 2], vv[4 * cb + 3]));
+    }
+  } else {
+    // partial sums of this chunk: global key index (specials first, then
+    // landmarks), [2][64] each
+    const int gk = MODE == SB_SPEC ? 64 * kb + key : g.spec_pad + lmk;
+    const int nglob = g.spec_pad + g.T_pad;
+    float* pp = A.part + (((long long)blockIdx.z * g.H + h) * nglob + gk) * 2 * D;
+    if (kvalid) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int ch = 16 * cb + 4 * lg;
+        *(float4*)(pp + ch) = make_float4(dk[cb][0], dk[cb][1], dk[cb][2], dk[cb][3]);
+        *(float4*)(pp + D + ch) = make_float4(dv[cb][0], dv[cb][1], dv[cb][2], dv[cb][3]);
+      }
+    }
+  }
+}
+
+// grid (ceil((nspec + T) / 2), H), block 128: the partials of one global key
+// per 64 threads (one channel each), summed over the chunks in order. A
+// special key's sums are its dk (x 1/8) and dv; a landmark's go to lgrad.
+__global__ void __launch_bounds__(128) sbwd_reduce_kernel(Geom g, SbArgs A) {
+  const int h = blockIdx.y, ch = threadIdx.x & 63;
+  const int i = 2 * blockIdx.x + (threadIdx.x >> 6);
+  if (i >= g.nspec + g.T) return;
+  const int gk = i < g.nspec ? i : g.spec_pad + (i - g.nspec);
+  const int nglob = g.spec_pad + g.T_pad;
+  float sk = 0.f, sv = 0.f;
+  for (int c = 0; c < SB_CHUNKS; ++c) {
+    const float* pp = A.part + (((long long)c * g.H + h) * nglob + gk) * 2 * D;
+    sk += pp[ch];
+    sv += pp[D + ch];
+  }
+  if (i < g.nspec) {
+    const long long row = special_token(g, i) * g.in_tok + (long long)h * g.in_head;
+    A.dK[row + ch] = f2bf(sk * 0.125f);
+    A.dV[row + ch] = f2bf(sv);
+  } else {
+    float* lgk = A.lgrad + ((long long)h * g.T + (i - g.nspec)) * 2 * D;
+    lgk[ch] = sk;
+    lgk[D + ch] = sv;
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+size_t sparse_bwd_workspace_bytes(const Geom& g) {
+  const size_t nw = (size_t)(g.T + 31) / 32;
+  const size_t stats = (size_t)2 * g.H * g.N * sizeof(float);
+  const size_t selT = (size_t)g.H * g.T * nw * sizeof(unsigned);
+  const size_t part = (size_t)SB_CHUNKS * g.H * (g.spec_pad + g.T_pad) * 2 * D * sizeof(float);
+  const size_t lgrad = (size_t)g.H * g.T * 2 * D * sizeof(float);
+  return stats + selT + part + lgrad + 256 * 4;
+}
+
+// Workspace: lse [H][N], dsum [H][N] fp32; selT [H][T][nw]; the global-key
+// partials [SB_CHUNKS][H][spec_pad + T_pad][2][64] fp32; lgrad [H][T][2][64].
+hipError_t launch_sparse_bwd(const Geom& g, int keep, const u16* Q, const u16* K, const u16* V, const u16* dO,
+                             long long o_tok, long long o_head, const u16* LM, const double* kbar,
+                             const float* vbar, const int* sel,
+                             const unsigned* selmask, u16* dQ, u16* dK, u16* dV, void* ws, hipStream_t s) {
+  const int nw = (g.T + 31) / 32;
+  auto align = [](char* p) { return (char*)(((uintptr_t)p + 255) & ~(uintptr_t)255); };
+  char* p = align((char*)ws);
+  SbArgs A;
+  A.Q = Q;
+  A.K = K;
+  A.V = V;
+  A.dO = dO;
+  A.LM = LM;
+  A.kbar = kbar;
+  A.vbar = vbar;
+  A.sel = sel;
+  A.selmask = selmask;
+  A.lse = (float*)p;
+  A.dsum = A.lse + (size_t)g.H * g.N;
+  p = align((char*)(A.dsum + (size_t)g.H * g.N));
+  A.selT = (unsigned*)p;
+  p = align((char*)(A.selT + (size_t)g.H * g.T * nw));
+  A.part = (float*)p;
+  p = align((char*)(A.part + (size_t)SB_CHUNKS * g.H * (g.spec_pad + g.T_pad) * 2 * D));
+  A.lgrad = (float*)p;
+  A.dQ = dQ;
+  A.dK = dK;
+  A.dV = dV;
+  A.keep = keep;
+  A.nw = nw;
+  A.o_tok = o_tok;
+  A.o_head = o_head;
+  const int nunits = g.T + (g.nspec + 63) / 64;
+  hipLaunchKernelGGL(sbwd_rows_kernel<SB_STATS>, dim3(nunits, g.H), dim3(SB_THREADS), 0, s, g, A);
+  hipLaunchKernelGGL(sbwd_rows_kernel<SB_DQ>, dim3(nunits, g.H), dim3(SB_THREADS), 0, s, g, A);
+  hipLaunchKernelGGL(sbwd_transpose_kernel, dim3((nw + 1) / 2, nw, g.H), dim3(64), 0, s, g, selmask, A.selT, nw);
+  if (g.nspec > 0)
+    hipLaunchKernelGGL(sbwd_keys_kernel<SB_SPEC>, dim3((g.nspec + 63) / 64, g.H, SB_CHUNKS), dim3(SB_THREADS), 0, s,
+                       g, A);
+  hipLaunchKernelGGL(sbwd_keys_kernel<SB_LMK>, dim3((g.T + 63) / 64, g.H, SB_CHUNKS), dim3(SB_THREADS), 0, s, g, A);
+  hipLaunchKernelGGL(sbwd_reduce_kernel, dim3((g.nspec + g.T + 1) / 2, g.H), dim3(128), 0, s, g, A);
+  hipLaunchKernelGGL(sbwd_keys_kernel<SB_TILE>, dim3(g.T, g.H), dim3(SB_THREADS), 0, s, g, A);
+  return hipGetLastError();
+}
+
+}  // namespace zebra

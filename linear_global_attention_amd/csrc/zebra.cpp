@@ -23,6 +23,10 @@ hipError_t launch_attn(const Geom&, const AttnArgs&, void*, hipStream_t);
 size_t attn_workspace_bytes(const Geom&);
 size_t linear_workspace_bytes(const Geom&);
 size_t linear_bwd_workspace_bytes(const Geom&);
+size_t sparse_bwd_workspace_bytes(const Geom&);
+hipError_t launch_sparse_bwd(const Geom&, int, const u16*, const u16*, const u16*, const u16*, long long, long long,
+                             const u16*, const double*, const float*, const int*, const unsigned*, u16*, u16*, u16*,
+                             void*, hipStream_t);
 hipError_t launch_linear_bwd(const Geom&, float, float, const u16*, const u16*, const u16*, const float*,
                              const float*, const float*, const u16*, u16*, u16*, u16*, void*, hipStream_t);
 hipError_t launch_linear(const Geom&, float, float, const u16*, const u16*, const u16*,
@@ -136,6 +140,10 @@ size_t buf_bytes(const Geom& g, int64_t k, int which) {
       if (c > m) m = c;
       if (f > m) m = f;
       return m;
+    }
+    case ZEBRA_BUF_BWD_WORKSPACE: {
+      const size_t w = buf_bytes(g, k, ZEBRA_BUF_WORKSPACE), sb = sparse_bwd_workspace_bytes(g);
+      return sb > w ? sb : w;
     }
     default: return 0;
   }
@@ -263,6 +271,21 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
       NEED(a->workspace, "workspace");
       if (a->workspace_bytes < linear_bwd_workspace_bytes(g))
         return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_linear_attn_bwd");
+      break;
+    case ZEBRA_OP_SPARSE_BWD:
+      if (k < 0) return fail(ZEBRA_ERR_INVALID_ARG, "y must lie in [0, 1]");
+      if (g.T > 32768) return fail(ZEBRA_ERR_UNSUPPORTED, "the sparse backward supports at most 32768 tiles");
+      NEED(a->q, "q");
+      NEED(a->k, "k");
+      NEED(a->v, "v");
+      NEED(a->lm, "lm");
+      NEED(a->kbar, "kbar");
+      NEED(a->vbar, "vbar");
+      NEED(a->sel, "sel");
+      NEED(a->selmask, "selmask");
+      NEED(a->workspace, "workspace");
+      if (a->workspace_bytes < sparse_bwd_workspace_bytes(g))
+        return fail(ZEBRA_ERR_WORKSPACE, "workspace too small for zebra_sparse_attn_bwd (ZEBRA_BUF_BWD_WORKSPACE)");
       break;
     case ZEBRA_OP_COVERAGE:
       if (k < 0) return fail(ZEBRA_ERR_INVALID_ARG, "y must lie in [0, 1]");
@@ -441,6 +464,22 @@ zebra_status zebra_linear_attn_bwd(const zebra_args* a, const void* dout, void* 
                                       a->gq, a->gk, (const u16*)dout, (u16*)dq, (u16*)dk, (u16*)dv, a->workspace,
                                       (hipStream_t)stream),
                     "zebra_linear_attn_bwd");
+}
+
+zebra_status zebra_sparse_attn_bwd(const zebra_args* a, const void* dout, void* dq, void* dk, void* dv,
+                                   zebra_stream stream) {
+  Geom g;
+  int64_t k;
+  zebra_status s = validate(a, ZEBRA_OP_SPARSE_BWD, g, k);
+  if (s != ZEBRA_OK) return s;
+  if (!dout || !dq || !dk || !dv) return fail(ZEBRA_ERR_INVALID_ARG, "dout, dq, dk and dv must be non-NULL");
+  if (misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv))
+    return fail(ZEBRA_ERR_INVALID_ARG, "dout, dq, dk and dv must be 16-byte aligned");
+  return hip_result(launch_sparse_bwd(g, (int)k, (const u16*)a->q, (const u16*)a->k, (const u16*)a->v,
+                                      (const u16*)dout, g.out_tok, g.out_head, (const u16*)a->lm, a->kbar, a->vbar,
+                                      (const int*)a->sel, (const unsigned*)a->selmask, (u16*)dq, (u16*)dk, (u16*)dv,
+                                      a->workspace, (hipStream_t)stream),
+                    "zebra_sparse_attn_bwd");
 }
 
 zebra_status zebra_linear_attn_noalloc(const zebra_args* a, zebra_stream stream) {

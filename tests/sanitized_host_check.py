@@ -33,7 +33,7 @@ def args(L, y, fill=True):
         for i, f in enumerate(["q", "k", "v", "out", "kt", "vt", "ks", "vs", "kbar", "vbar", "logn",
                                "lm", "sel", "selmask", "workspace"]):
             setattr(a, f, ctypes.c_void_p(0x1000 * (i + 1)))
-        a.workspace_bytes = so.zebra_buffer_bytes(ctypes.byref(L), y, abi.BUF["WORKSPACE"])
+        a.workspace_bytes = so.zebra_buffer_bytes(ctypes.byref(L), y, abi.BUF["BWD_WORKSPACE"])
     return a
 
 
@@ -62,7 +62,7 @@ for F, S, R, C, H in [(1, 0, 1, 1, 1), (2, 5, 16, 16, 1), (3, 2, 11, 13, 2), (10
         for y in (0.0, 0.2, 0.5, 0.8, 1.0, 0.3333):
             k = so.zebra_keep_count(ctypes.byref(L), y)
             check(k == max(0, min(T, round((1 - y) * T))), f"keep count {y}")
-            for w in range(12):
+            for w in range(len(abi.BUF)):
                 so.zebra_buffer_bytes(ctypes.byref(L), y, w)
         check(so.zebra_keep_count(ctypes.byref(L), 1.5) == -1, "y > 1")
         check(so.zebra_buffer_bytes(ctypes.byref(L), 0.5, 99) == 0, "unknown buffer")
@@ -82,7 +82,7 @@ a.q = ctypes.c_void_p(0x1004)
 check(so.zebra_validate(ctypes.byref(a), 3) == 1, "misaligned q")
 a = args(L, 0.5)
 a.workspace_bytes = 1
-for op in (2, 3, 4, 5, 6, abi.OP["LINEAR_BWD"]):
+for op in (2, 3, 4, 5, 6, abi.OP["LINEAR_BWD"], abi.OP["SPARSE_BWD"]):
     check(so.zebra_validate(ctypes.byref(a), op) == 3, f"small workspace op {op}")
 # every entry point fails on the host before any launch
 a = args(L, 0.5, fill=False)
@@ -96,6 +96,10 @@ check(so.zebra_linear_attn_bwd(ctypes.byref(args(L, 0.5)), None, g4[1], g4[2], g
 check(so.zebra_linear_attn_bwd(ctypes.byref(args(L, 0.5)), g4[0], g4[1], ctypes.c_void_p(0x9208), g4[3], None) == 1,
       "bwd misaligned dk")
 check(so.zebra_linear_attn_bwd(ctypes.byref(args(L, 0.5, fill=False)), *g4, None) == 1, "bwd NULL q")
+check(so.zebra_sparse_attn_bwd(ctypes.byref(args(L, 0.5)), None, g4[1], g4[2], g4[3], None) == 1, "sparse bwd NULL dout")
+check(so.zebra_sparse_attn_bwd(ctypes.byref(args(L, 1.5)), *g4, None) == 1, "sparse bwd y > 1")
+check(so.zebra_buffer_bytes(ctypes.byref(L), 0.5, abi.BUF["BWD_WORKSPACE"]) >=
+      so.zebra_buffer_bytes(ctypes.byref(L), 0.5, abi.BUF["WORKSPACE"]), "backward workspace covers the forward's")
 # fp64 affine solve: recovers a planted map from exact statistics
 n, d = 5000, 64
 o = g.standard_normal((n, d))

@@ -70,7 +70,7 @@ def _full_args(L, y):
     for i, f in enumerate(["q", "k", "v", "out", "kt", "vt", "ks", "vs", "kbar", "vbar", "logn",
                            "lm", "sel", "selmask", "workspace"]):
         setattr(a, f, _fake(i + 1))
-    a.workspace_bytes = zb.buffer_bytes(L, y, "WORKSPACE")
+    a.workspace_bytes = zb.buffer_bytes(L, y, "BWD_WORKSPACE")
     return a
 
 

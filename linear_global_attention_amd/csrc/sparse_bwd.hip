@@ -209,56 +209,118 @@ __device__ inline void landmark_parts(const Geom& g, const SbArgs& A, int h, int
   split8(vv, vhi, vlo);
 }
 
-// Stages key block `blk` of one of three kinds into sK, sV and the per-key
-// logit bias (log2 units) sB:
-//   0: keys 32 hb .. of tile u (hb = blk & 1, u = blk >> 1), bias 0;
-//   1: special keys 32 blk ..;
-//   2: landmarks 32 blk .., bias log2 n_u, -inf where `mask` has the bit;
-//      the exact means as bf16 high parts in sK, sV and low parts in sK2,
-//      sV2 (the landmarks are means of similar tiles, so the query gradient
-//      is a small remainder of their sum, which a single rounding swamps).
-// Keys past the end: zero rows, bias -inf. Every thread calls it.
-__device__ inline void stage_key_block(const Geom& g, const SbArgs& A, int h, int kind, int blk, unsigned mask,
-                                       u16* sK, u16* sV, u16* sK2, u16* sV2, float* sB) {
-  const int tid = threadIdx.x, key = tid >> 3, c = tid & 7;
-  uint4 kw = make_uint4(0u, 0u, 0u, 0u), vw = kw;
-  float bias = -INFINITY;
-  if (kind == 2) {
-    const int u = 32 * blk + key;
-    uint4 kl = make_uint4(0u, 0u, 0u, 0u), vl = kl;
-    if (u < g.T) {
-      landmark_parts(g, A, h, u, 8 * c, kw, kl, vw, vl);
-      const char* kb = lm_kblock(g, A.LM, h, blk);
-      bias = ((mask >> key) & 1u) ? -INFINITY : ((const float*)(kb + LM_LOG2N_ROW * 128))[key];
-    }
-    *(uint4*)(sK2 + sb_off(key, 8 * c)) = kl;
-    *(uint4*)(sV2 + sb_off(key, 8 * c)) = vl;
-  } else {
+// One thread's share of a 64-key token or special block, loaded ahead of
+// its use: keys tid / 8 and 32 + tid / 8, channels 8 (tid % 8) .. +7 of K
+// and V (bf16), and their logit biases (log2 units: 0, or -inf for keys
+// past the end).
+struct KeyFetch {
+  uint4 k[2], v[2];
+  float bias[2];
+};
+
+// Key block `blk` of kind 0 (the keys of tile blk) or kind 1 (special keys
+// 64 blk ..).
+__device__ inline void fetch_key_block(const Geom& g, const SbArgs& A, int h, int kind, int blk, KeyFetch& f) {
+  const int tid = threadIdx.x, c = tid & 7;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int key = (tid >> 3) + 32 * e;
+    f.k[e] = f.v[e] = make_uint4(0u, 0u, 0u, 0u);
+    f.bias[e] = -INFINITY;
     long long tok = -1;
     if (kind == 0) {
-      const int u = blk >> 1, j = 32 * (blk & 1) + key;
-      if (j < unit_rows(g, u)) tok = unit_token(g, u, j);
+      if (key < unit_rows(g, blk)) tok = unit_token(g, blk, key);
     } else {
-      const int i = 32 * blk + key;
+      const int i = 64 * blk + key;
       if (i < g.nspec) tok = special_token(g, i);
     }
     if (tok >= 0) {
       const long long row = tok * g.in_tok + (long long)h * g.in_head;
-      kw = *(const uint4*)(A.K + row + 8 * c);
-      vw = *(const uint4*)(A.V + row + 8 * c);
-      bias = 0.f;
+      f.k[e] = *(const uint4*)(A.K + row + 8 * c);
+      f.v[e] = *(const uint4*)(A.V + row + 8 * c);
+      f.bias[e] = 0.f;
     }
   }
-  *(uint4*)(sK + sb_off(key, 8 * c)) = kw;
-  *(uint4*)(sV + sb_off(key, 8 * c)) = vw;
-  if (c == 0) sB[key] = bias;
+}
+
+// Writes a fetched share into the 64-row LDS tiles (keys past the end: zero
+// rows, bias -inf).
+__device__ inline void commit_key_block(const KeyFetch& f, u16* sK, u16* sV, float* sB) {
+  const int tid = threadIdx.x, c = tid & 7;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int key = (tid >> 3) + 32 * e;
+    *(uint4*)(sK + sb_off(key, 8 * c)) = f.k[e];
+    *(uint4*)(sV + sb_off(key, 8 * c)) = f.v[e];
+    if (c == 0) sB[key] = f.bias[e];
+  }
+}
+
+// One thread's share of landmark block b (landmarks 32 b ..): the 8 fp64
+// mean-key values and 8 fp32 mean values of landmark 32 b + tid / 8,
+// channels 8 (tid % 8) .., and its bias log2 n_u (-inf past the last tile or
+// where `mask` has its bit: the row's tile keeps it).
+struct LandmarkFetch {
+  uint4 k[4], v[2];
+  float bias;
+};
+
+__device__ inline void fetch_landmark_block(const Geom& g, const SbArgs& A, int h, int b, unsigned mask,
+                                            LandmarkFetch& f) {
+  const int tid = threadIdx.x, key = tid >> 3, c = tid & 7;
+  const int u = 32 * b + key;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.k[i] = make_uint4(0u, 0u, 0u, 0u);
+  f.v[0] = f.v[1] = make_uint4(0u, 0u, 0u, 0u);
+  f.bias = -INFINITY;
+  if (u < g.T) {
+    const uint4* kr = (const uint4*)(A.kbar + ((long long)h * g.T + u) * D + 8 * c);
+    const uint4* vr = (const uint4*)(A.vbar + ((long long)h * g.T + u) * D + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.k[i] = kr[i];
+    f.v[0] = vr[0];
+    f.v[1] = vr[1];
+    const char* kb = lm_kblock(g, A.LM, h, b);
+    f.bias = ((mask >> key) & 1u) ? -INFINITY : ((const float*)(kb + LM_LOG2N_ROW * 128))[key];
+  }
+}
+
+// The landmarks as bf16 high parts into sK, sV and low parts into sK2, sV2
+// (the landmarks are means of similar tiles, so the query gradient is a
+// small remainder of their sum, which a single rounding would swamp).
+__device__ inline void commit_landmark_block(const LandmarkFetch& f, u16* sK, u16* sV, u16* sK2, u16* sV2,
+                                             float* sB) {
+  const int tid = threadIdx.x, key = tid >> 3, c = tid & 7;
+  float kv[8], vv[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double2 d2 = __builtin_bit_cast(double2, f.k[i]);
+    kv[2 * i] = (float)d2.x;
+    kv[2 * i + 1] = (float)d2.y;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float4 v4 = __builtin_bit_cast(float4, f.v[i]);
+    vv[4 * i] = v4.x;
+    vv[4 * i + 1] = v4.y;
+    vv[4 * i + 2] = v4.z;
+    vv[4 * i + 3] = v4.w;
+  }
+  uint4 kh, kl, vh, vl;
+  split8(kv, kh, kl);
+  split8(vv, vh, vl);
+  *(uint4*)(sK + sb_off(key, 8 * c)) = kh;
+  *(uint4*)(sV + sb_off(key, 8 * c)) = vh;
+  *(uint4*)(sK2 + sb_off(key, 8 * c)) = kl;
+  *(uint4*)(sV2 + sb_off(key, 8 * c)) = vl;
+  if (c == 0) sB[key] = f.bias;
 }
 
 // grid (units, H), block 256: one query unit (up to 64 rows, 16 per wave).
 template <int MODE>
-__global__ void __launch_bounds__(SB_THREADS) sbwd_rows_kernel(Geom g, SbArgs A) {
-  __shared__ __attribute__((aligned(16))) u16 sK[32 * D], sV[32 * D], sK2[32 * D], sV2[32 * D];
-  __shared__ __attribute__((aligned(16))) float sB[32];
+__global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs A) {
+  __shared__ __attribute__((aligned(16))) u16 sK[64 * D], sV[64 * D], sK2[64 * D], sV2[64 * D];
+  __shared__ __attribute__((aligned(16))) float sB[64];
   const int unit = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lg = lane >> 4, tl = lane & 15;
@@ -286,10 +348,13 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_rows_kernel(Geom g, SbArgs A)
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto block = [&](int kind, int blk, unsigned mask) {
-    __syncthreads();  // the previous block's reads are done
-    stage_key_block(g, A, h, kind, blk, mask, sK, sV, sK2, sV2, sB);
-    __syncthreads();
+  // 32 staged keys (rows 32 sub .. of the LDS tiles) against the wave's rows
+  auto block = [&](int kind, int sub) {
+    const u16* tK = sK + sub * 32 * D;
+    const u16* tV = sV + sub * 32 * D;
+    const u16* tK2 = sK2 + sub * 32 * D;
+    const u16* tV2 = sV2 + sub * 32 * D;
+    const float* tB = sB + 32 * sub;
     f32x4 s[2], dp[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -297,16 +362,16 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_rows_kernel(Geom g, SbArgs A)
       dp[hh] = s[hh];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(sK, hh, ks, lane), qb[ks], s[hh], 0, 0, 0);
-        dp[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(sV, hh, ks, lane), ob[ks], dp[hh], 0, 0, 0);
+        s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(tK, hh, ks, lane), qb[ks], s[hh], 0, 0, 0);
+        dp[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(tV, hh, ks, lane), ob[ks], dp[hh], 0, 0, 0);
         if (kind == 2) {
-          s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(sK2, hh, ks, lane), qb[ks], s[hh], 0, 0, 0);
-          dp[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(sV2, hh, ks, lane), ob[ks], dp[hh], 0, 0, 0);
+          s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(tK2, hh, ks, lane), qb[ks], s[hh], 0, 0, 0);
+          dp[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(tV2, hh, ks, lane), ob[ks], dp[hh], 0, 0, 0);
         }
       }
     }
     // lane (row tl, group lg) holds keys 4 lg + r and 16 + 4 lg + r
-    const float4 b0 = *(const float4*)(sB + 4 * lg), b1 = *(const float4*)(sB + 16 + 4 * lg);
+    const float4 b0 = *(const float4*)(tB + 4 * lg), b1 = *(const float4*)(tB + 16 + 4 * lg);
     const float bias[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
     float x[8], d[8];
 #pragma unroll
@@ -335,35 +400,71 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_rows_kernel(Geom g, SbArgs A)
       const bf16x8 dsb = pack8(ds);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(sK, cb, lane), dsb, acc[cb], 0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(tK, cb, lane), dsb, acc[cb], 0, 0, 0);
         if (kind == 2)
-          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(sK2, cb, lane), dsb, acc[cb], 0, 0, 0);
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(tK2, cb, lane), dsb, acc[cb], 0, 0, 0);
       }
     }
   };
 
-  const int hw = (long long)h * g.T;
-  if (patch) {
-    const int* kept = A.sel + ((long long)h * g.T + unit) * A.keep;
-    for (int i = 0; i < A.keep; ++i) {
-      const int u = kept[i];
-      block(0, 2 * u, 0u);
-      if (unit_rows(g, u) > 32) block(0, 2 * u + 1, 0u);
+  // The unit's key blocks in order, 64 keys each: its kept tiles (all tiles
+  // for special rows), the special keys, then (patch rows) the landmarks.
+  // Token and special blocks are fetched into registers one block ahead,
+  // so that their loads overlap the previous block's work.
+  const int* kept = A.sel + ((long long)h * g.T + unit) * A.keep;
+  const unsigned* mrow = A.selmask + ((long long)h * g.T + (patch ? unit : 0)) * A.nw;
+  const int ntb = patch ? A.keep : g.T, nsb = (g.nspec + 63) / 64, nlb = patch ? (g.T + 63) / 64 : 0;
+  const int nblk = ntb + nsb;
+  auto desc = [&](int i, int& kind, int& blk) {
+    if (i < ntb) {
+      kind = 0;
+      blk = patch ? kept[i] : i;
+    } else {
+      kind = 1;
+      blk = i - ntb;
     }
-  } else {
-    for (int u = 0; u < g.T; ++u) {
-      block(0, 2 * u, 0u);
-      if (unit_rows(g, u) > 32) block(0, 2 * u + 1, 0u);
+  };
+  {
+    KeyFetch f;
+    if (nblk > 0) {
+      int kind, blk;
+      desc(0, kind, blk);
+      fetch_key_block(g, A, h, kind, blk, f);
+    }
+    for (int i = 0; i < nblk; ++i) {
+      int kind, blk;
+      desc(i, kind, blk);
+      __syncthreads();  // the previous block's reads are done
+      commit_key_block(f, sK, sV, sB);
+      if (i + 1 < nblk) {
+        int kn, bn;
+        desc(i + 1, kn, bn);
+        fetch_key_block(g, A, h, kn, bn, f);
+      }
+      __syncthreads();
+      block(kind, 0);
+      if (kind == 0 ? unit_rows(g, blk) > 32 : 64 * blk + 32 < g.nspec) block(kind, 1);
     }
   }
-  for (int b = 0; b < (g.nspec + 31) / 32; ++b) block(1, b, 0u);
-  (void)hw;
+  // landmark blocks (patch rows), staged as they come: fetching them ahead
+  // would hold their larger fp64 / fp32 loads in registers through every
+  // token block
+  for (int b = 0; b < nlb; ++b) {
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int b32 = 2 * b + sub;
+      LandmarkFetch lf;
+      fetch_landmark_block(g, A, h, b32, b32 < A.nw ? mrow[b32] : ~0u, lf);
+      commit_landmark_block(lf, sK + sub * 32 * D, sV + sub * 32 * D, sK2 + sub * 32 * D, sV2 + sub * 32 * D,
+                            sB + 32 * sub);
+    }
+    __syncthreads();
+    block(2, 0);
+    if (64 * b + 32 < g.T) block(2, 1);
+  }
   bool self = false;
-  if (patch) {
-    const unsigned* mrow = A.selmask + ((long long)h * g.T + unit) * A.nw;
-    for (int b = 0; b < g.T_pad / 32; ++b) block(2, b, b < A.nw ? mrow[b] : 0xFFFFFFFFu);
-    self = ((mrow[unit >> 5] >> (unit & 31)) & 1u) == 0;
-  }
+  if (patch) self = ((mrow[unit >> 5] >> (unit & 31)) & 1u) == 0;
   // the self key (a patch row whose own tile is not kept): its logit and
   // dP from the lane's 16 channels, summed over the row's 4 lanes
   float xs = -INFINITY, dps = 0.f;
@@ -511,23 +612,46 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A)
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) dk[cb] = dv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // rows 32 hb .. 32 hb + 31 of query unit t against the workgroup's keys;
-  // `bias` is this lane's key bias for the unit (-inf: not visible)
-  auto rows = [&](int t, int hb, float bias) {
-    __syncthreads();  // the previous rows' reads are done
-    {
-      const int tid = threadIdx.x, r = tid >> 3, c = tid & 7;
-      const int jr = 32 * hb + r;
-      const bool ok = jr < unit_rows(g, t);
-      const long long tk = ok ? unit_token(g, t, jr) : 0;
-      *(uint4*)(sQ + sb_off(r, 8 * c)) = ld16(A.Q, tk * g.in_tok + (long long)h * g.in_head + 8 * c, ok);
-      *(uint4*)(sO + sb_off(r, 8 * c)) = ld16(A.dO, tk * A.o_tok + (long long)h * A.o_head + 8 * c, ok);
-      if (c == 0) {
-        sL[r] = ok ? A.lse[(long long)h * g.N + tk] : INFINITY;
-        sD[r] = ok ? A.dsum[(long long)h * g.N + tk] : 0.f;
-      }
+  // One thread's share of rows 32 hb .. +31 of query unit t (row tid / 8,
+  // channels 8 (tid % 8) .. +7), loaded one step ahead of its use, and the
+  // lane's landmark mask word of the unit.
+  struct RowFetch {
+    uint4 q, o;
+    float lse, d;
+    unsigned mw;
+  };
+  auto fetch_rows = [&](int t, int hb, RowFetch& f) {
+    const int tid = threadIdx.x, r = tid >> 3, c = tid & 7;
+    const int jr = 32 * hb + r;
+    const bool ok = jr < unit_rows(g, t);
+    const long long tk = ok ? unit_token(g, t, jr) : 0;
+    f.q = ld16(A.Q, tk * g.in_tok + (long long)h * g.in_head + 8 * c, ok);
+    f.o = ld16(A.dO, tk * A.o_tok + (long long)h * A.o_head + 8 * c, ok);
+    f.lse = INFINITY;
+    f.d = 0.f;
+    if (ok && c == 0) {
+      f.lse = A.lse[(long long)h * g.N + tk];
+      f.d = A.dsum[(long long)h * g.N + tk];
     }
-    __syncthreads();
+    f.mw = 0u;
+    if (MODE == SB_LMK && kvalid) f.mw = A.selmask[((long long)h * g.T + t) * A.nw + (lmk >> 5)];
+  };
+  auto commit_rows = [&](const RowFetch& f) {
+    const int tid = threadIdx.x, r = tid >> 3, c = tid & 7;
+    *(uint4*)(sQ + sb_off(r, 8 * c)) = f.q;
+    *(uint4*)(sO + sb_off(r, 8 * c)) = f.o;
+    if (c == 0) {
+      sL[r] = f.lse;
+      sD[r] = f.d;
+    }
+  };
+  // the staged rows against the workgroup's keys; `bias` is this lane's key
+  // bias for the unit (-inf: not visible)
+  auto rows = [&](float bias) {
+    const u16* tQ = sQ;
+    const u16* tO = sO;
+    const float* tL = sL;
+    const float* tD = sD;
     f32x4 s[2], dp[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -535,7 +659,7 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A)
       dp[hh] = s[hh];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 qa = row_frag(sQ, hh, ks, lane), oa = row_frag(sO, hh, ks, lane);
+        const bf16x8 qa = row_frag(tQ, hh, ks, lane), oa = row_frag(tO, hh, ks, lane);
         s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kfrag[ks], s[hh], 0, 0, 0);
         dp[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vfrag[ks], dp[hh], 0, 0, 0);
         if (MODE == SB_LMK) {
@@ -545,8 +669,8 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A)
       }
     }
     // lane (key tl, group lg) holds rows 4 lg + r and 16 + 4 lg + r
-    const float4 l0 = *(const float4*)(sL + 4 * lg), l1 = *(const float4*)(sL + 16 + 4 * lg);
-    const float4 d0 = *(const float4*)(sD + 4 * lg), d1 = *(const float4*)(sD + 16 + 4 * lg);
+    const float4 l0 = *(const float4*)(tL + 4 * lg), l1 = *(const float4*)(tL + 16 + 4 * lg);
+    const float4 d0 = *(const float4*)(tD + 4 * lg), d1 = *(const float4*)(tD + 16 + 4 * lg);
     const float lse[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
     const float Dr[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
     float p[8], ds[8];
@@ -558,40 +682,61 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A)
     const bf16x8 pb = pack8(p), dsb = pack8(ds);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      dv[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(sO, cb, lane), pb, dv[cb], 0, 0, 0);
-      dk[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(sQ, cb, lane), dsb, dk[cb], 0, 0, 0);
+      dv[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(tO, cb, lane), pb, dv[cb], 0, 0, 0);
+      dk[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(col_frag(tQ, cb, lane), dsb, dk[cb], 0, 0, 0);
     }
   };
-  auto unit = [&](int t, float bias) {
-    rows(t, 0, bias);
-    if (unit_rows(g, t) > 32) rows(t, 1, bias);
-  };
-
+  // The (unit, half) steps in order. TILE: the query tiles that keep this
+  // tile (set bits of its transposed-bitmap row), then every special-row
+  // unit; SPEC / LMK: the units of this chunk (no special rows for LMK).
   const int nunits = num_units(g);
+  const unsigned* trow = A.selT + ((long long)h * g.T + (MODE == SB_TILE ? kb : 0)) * A.nw;
+  int w = 0, tcur = -1;
+  unsigned bits = 0u;
+  int t0 = 0, t1 = 0;
   if (MODE == SB_TILE) {
-    // the query tiles that keep this tile, then every special-row unit
-    const unsigned* trow = A.selT + ((long long)h * g.T + kb) * A.nw;
-    for (int w = 0; w < A.nw; ++w) {
-      unsigned bits = (unsigned)__builtin_amdgcn_readfirstlane((int)trow[w]);
-      while (bits) {
-        const int t = 32 * w + __builtin_ctz(bits);
-        bits &= bits - 1u;
-        unit(t, kbias);
-      }
-    }
-    for (int t = g.T; t < nunits; ++t) unit(t, kbias);
+    bits = A.nw > 0 ? (unsigned)__builtin_amdgcn_readfirstlane((int)trow[0]) : 0u;
   } else {
     const int lastu = MODE == SB_LMK ? g.T : nunits;  // special rows see no landmark
     const int c = blockIdx.z;
-    const int t0 = (int)((long long)lastu * c / SB_CHUNKS), t1 = (int)((long long)lastu * (c + 1) / SB_CHUNKS);
-    for (int t = t0; t < t1; ++t) {
-      float bias = kbias;
-      if (MODE == SB_LMK && kvalid) {
-        const unsigned wd = A.selmask[((long long)h * g.T + t) * A.nw + (lmk >> 5)];
-        if ((wd >> (lmk & 31)) & 1u) bias = -INFINITY;
-      }
-      unit(t, bias);
+    t0 = (int)((long long)lastu * c / SB_CHUNKS);
+    t1 = (int)((long long)lastu * (c + 1) / SB_CHUNKS);
+  }
+  // the unit after tcur, or -1
+  auto next_unit = [&]() -> int {
+    if (MODE != SB_TILE) {
+      if (tcur < 0) return t0 < t1 ? t0 : -1;
+      return tcur + 1 < t1 ? tcur + 1 : -1;
     }
+    if (tcur >= g.T) return tcur + 1 < nunits ? tcur + 1 : -1;  // the special-row units
+    while (bits == 0u && w + 1 < A.nw) bits = (unsigned)__builtin_amdgcn_readfirstlane((int)trow[++w]);
+    if (bits) {
+      const int t = 32 * w + __builtin_ctz(bits);
+      bits &= bits - 1u;
+      return t;
+    }
+    return g.T < nunits ? g.T : -1;
+  };
+  int tn = next_unit(), hn = 0;
+  RowFetch f;
+  if (tn >= 0) fetch_rows(tn, 0, f);
+  while (tn >= 0) {
+    const int t = tn, hb = hn;
+    // the step after (t, hb)
+    if (hb == 0 && unit_rows(g, t) > 32) {
+      hn = 1;
+    } else {
+      tcur = t;
+      tn = next_unit();
+      hn = 0;
+    }
+    float bias = kbias;
+    if (MODE == SB_LMK && ((f.mw >> (lmk & 31)) & 1u)) bias = -INFINITY;
+    __syncthreads();  // the previous rows' reads are done
+    commit_rows(f);
+    if (tn >= 0) fetch_rows(tn, hn, f);
+    __syncthreads();
+    rows(bias);
   }
 
   // lane (key tl, group lg) holds channels 16 cb + 4 lg + r of dk (x 1/8 to

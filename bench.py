@@ -19,6 +19,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -516,7 +517,31 @@ def main():
             "achieved": bwd_bytes / (bwd_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": bwd_bytes,
             "avg_launch_ms": bwd_ms, "traffic": recorded_linear_bwd_traffic(a.config)}
-        del dyd, gq_, gk_, gv_, args_b
+        del args_b
+        # backward of the tile-sparse stage on the step's kept tiles and
+        # landmarks (the stage buffers still hold them), with a workspace
+        # sized for it; one call. Algorithmic work: 10 x 64 flops per
+        # visible (row, key) pair (the logits, dP, dV, dK and dQ products),
+        # 2.5 times the forward's 4 x 64.
+        log("tile-sparse backward (1 call)")
+        ws = torch.empty(zb.buffer_bytes(zL, a.y, "BWD_WORKSPACE"), dtype=torch.uint8, device="cuda")
+        args_sb = zb.make_args(zL, qd, kd, vd, out, bufs, a.y)
+        args_sb.workspace = ctypes.c_void_p(ws.data_ptr())
+        args_sb.workspace_bytes = ws.numel()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        zb.sparse_attn_bwd(args_sb, dyd, gq_, gk_, gv_)
+        e1.record()
+        torch.cuda.synchronize()
+        sb_ms = e0.elapsed_time(e1)
+        sb_flops = 10 * 64 * pairs
+        result["roofline_sparse_bwd"] = {
+            "kernels": ("sbwd_rows (statistics, dq), sbwd_transpose, sbwd_keys (special keys, landmarks, kept "
+                        "tiles), sbwd_reduce (zebra_sparse_attn_bwd)"), "bound": "mfma",
+            "achieved": sb_flops / (sb_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": sb_flops / (sb_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "algorithmic_flops": sb_flops,
+            "avg_launch_ms": sb_ms, "vs_forward_sparse_attn": sb_ms / att_ms}
+        del dyd, gq_, gk_, gv_, args_sb, ws
 
     dms = None
     if not a.no_dense:

@@ -275,6 +275,7 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
     case ZEBRA_OP_SPARSE_BWD:
       if (k < 0) return fail(ZEBRA_ERR_INVALID_ARG, "y must lie in [0, 1]");
       if (g.T > 32768) return fail(ZEBRA_ERR_UNSUPPORTED, "the sparse backward supports at most 32768 tiles");
+      if (g.N >= (1LL << 31)) return fail(ZEBRA_ERR_UNSUPPORTED, "the sparse backward supports fewer than 2^31 tokens");
       NEED(a->q, "q");
       NEED(a->k, "k");
       NEED(a->v, "v");

@@ -155,10 +155,13 @@ __device__ __forceinline__ unsigned lane_valid_mask(int nvalid, int lane) {
 // holds slots i = 0.. for groups s = s0 + i; slot i is group tile(i) =
 // gid0 + i * stride. Patch item: G query tiles, either consecutive ones
 // (stride 1) or, with by_position, the tiles at one tile position in G
-// consecutive frames (stride = tiles per frame: the same image region seen
-// from neighbouring views keeps similar key tiles, so the item's groups
-// share more of the tiles it stages); special item: groups of 64 special
-// rows. Row block j (16 rows) of group s belongs to the wave with `wave` ==
+// frames of the same parity, two apart (stride = two frames' tiles: the
+// same image region seen from nearby views keeps similar key tiles, so the
+// item's groups share more of the tiles it stages; on the tile-centroid
+// inputs a query tile's kept set overlaps most with the one two frames
+// away, whose neighbouring frames it shares). Items per tile position: two
+// per 2G frames (even and odd frames), the last pair possibly short. Special
+// item: groups of 64 special rows. Row block j (16 rows) of group s belongs to the wave with `wave` ==
 // (s + j) % 4 (the SIMD index when two waves share a SIMD).
 struct QueryGroups {
   const Geom& g;
@@ -174,10 +177,10 @@ struct QueryGroups {
       gid0 = (item - patch_items) * G + s0_;
       stride = 1;
     } else if (by_position) {
-      const int nfb = (g.F + G - 1) / G;  // frame blocks per tile position
+      const int nfb = 2 * ((g.F + 2 * G - 1) / (2 * G));  // items per tile position
       const int u = item / nfb, b = item - u * nfb;
-      gid0 = (b * G + s0_) * g.tpf + u;
-      stride = g.tpf;
+      gid0 = ((b >> 1) * 2 * G + (b & 1) + 2 * s0_) * g.tpf + u;
+      stride = 2 * g.tpf;
     } else {
       gid0 = item * G + s0_;
       stride = 1;
@@ -233,7 +236,7 @@ struct ItemCounts {
 struct FastItems {
   int spec_items, patch_items, per_head, total, groups_per_head;
   __host__ __device__ explicit FastItems(const Geom& g) {
-    patch_items = g.tpf * ((g.F + FG - 1) / FG);
+    patch_items = g.tpf * 2 * ((g.F + 2 * FG - 1) / (2 * FG));
     const int sg = (g.nspec + 63) / 64;
     spec_items = (sg + FG - 1) / FG;
     per_head = spec_items + patch_items;

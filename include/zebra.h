@@ -184,7 +184,11 @@ zebra_status zebra_select_tiles(const zebra_args* a, zebra_stream stream);
  * of every kept tile, the landmark of every omitted tile (logit
  * q.kbar_u/8 + ln n_u, value vbar_u), every special key, and its own key
  * when tile t itself is not kept. Special rows: dense over all N keys.
- * Reads q, kt, vt, ks, vs, lm, logn, selmask; writes out. Uses the workspace:
+ * Reads q, kt, vt, ks, vs, lm, logn, selmask; writes out. The padding slots
+ * of kt, vt, ks and vs must hold zeros, as zebra_pack_tiles writes them (a
+ * padding key then contributes nothing). Products use bf16 operands with
+ * fp32 accumulation; the queries are scaled by log2(e)/8 and rounded to bf16
+ * before the key products. Uses the workspace:
  * per-row softmax offsets, one flag per query tile (rows whose cheap logit
  * bound is too loose are recomputed with an exact online softmax), the
  * staging plans of one round of work units, and fp32 partial outputs of the

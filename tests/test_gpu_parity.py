@@ -45,6 +45,10 @@ EDGE = [
     ("one-tile", zs.Layout(1, 2, 8, 8, heads=1), 0.5),
     ("one-small-tile", zs.Layout(1, 1, 3, 5, heads=1), 0.7),
     ("vggt-2view", zs.Layout(2, 5, 37, 37, heads=2), 0.8),
+    # 13 frames: the attention groups query tiles of one tile position in
+    # frames of one parity, five at a time (frames 0, 2, .., 8 | 1, 3, .., 9 |
+    # 10, 12 | 11), so the last groups are short
+    ("partial-13frames", zs.Layout(13, 2, 9, 11, heads=2), 0.6),
 ]
 
 

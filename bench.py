@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-schedule", action="store_true")
     p.add_argument("--no-backward", action="store_true")
+    p.add_argument("--no-full-small", action="store_true",
+                   help="skip the full oracle runs on the 2-view and 32-view workloads")
     p.add_argument("--dense-reps", type=int, default=5)
     p.add_argument("--rows-per-stage", type=int, default=32)
     p.add_argument("--calib-copy-gb", type=float, default=0.0,
@@ -231,6 +233,78 @@ def _job_stage_check(layout, meta, kind, y, toks, W=None, b=None, mu=None):
         return _job_sparse_rows(layout, meta, y, toks, lm)[1]
     _, (S, z) = _job_linear_state(layout, meta)
     return _job_linear_rows(layout, meta, toks, S, z, W, b, mu)[1]
+
+
+def _job_full_head(layout, meta, y):
+    """The oracle on every row of one head: the tile-sparse stage at y (patch
+    and special rows) and the linear stage (no affine correction)."""
+    from oracle import linear as olin
+    from oracle import sparse as osp
+    from oracle.layout import TileMap
+    d = _attach(meta)
+    tm = TileMap(*layout)
+    Q, K, V = (_widen(d[n])[:, None] for n in ("q", "k", "v"))
+    t0 = time.perf_counter()
+    out_s, sel, _ = osp.sparse_attention(Q, K, V, tm, y)
+    t1 = time.perf_counter()
+    out_l = olin.linear_attention(Q, K, V, tm)
+    t2 = time.perf_counter()
+    return t1 - t0, t2 - t1, out_s[:, 0], sel[0] if sel.ndim == 3 else sel, out_l[:, 0]
+
+
+def full_small(pool, workers, zb, zs, torch, seed):
+    """The fp64 oracle run in full (every row of every head) on the two small
+    workloads, 2 views of 16x16 patches (1 head, y = 0.5) and 32 views of
+    37x37 patches (16 heads, y = 0.8), one head per worker process, and the
+    GPU's outputs of the same stages compared with it on every row (rows of
+    query tiles whose kept-tile list differs from the oracle's, near-ties,
+    are counted and left out)."""
+    res = {}
+    for name, y in (("2views_16x16", 0.5), ("32views", 0.8)):
+        L = zs.CONFIGS[name]
+        N, H = L.tokens, L.heads
+        q, k, v = zs.stage_inputs(L, seed=seed)
+        zL = zb.Layout(L.frames, L.specials, L.rows, L.cols, H)
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda")  # noqa: E731
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        out_s, out_l = torch.empty_like(qd), torch.empty_like(qd)
+        bufs = zb.StageBuffers(zL, y)
+        zb.sparse_stage(zb.make_args(zL, qd, kd, vd, out_s, bufs, y))
+        zb.linear_attn(zb.make_args(zL, qd, kd, vd, out_l, bufs, y))
+        torch.cuda.synchronize()
+        got_s = zs.bf16_to_f32(out_s.cpu().numpy().view(np.uint16)).reshape(N, H, 64).astype(np.float64)
+        got_l = zs.bf16_to_f32(out_l.cpu().numpy().view(np.uint16)).reshape(N, H, 64).astype(np.float64)
+        sel_gpu = bufs.sel().cpu().numpy()
+        layout = (L.frames, L.specials, L.rows, L.cols)
+        shs = [Shared(q=q[:, h], k=k[:, h], v=v[:, h]) for h in range(H)]
+        try:
+            t0 = time.perf_counter()
+            futs = [pool.submit(_job_full_head, layout, sh.meta, y) for sh in shs]
+            rs = [f.result() for f in futs]
+            wall = time.perf_counter() - t0
+        finally:
+            for sh in shs:
+                sh.close()
+        from oracle.layout import TileMap
+        tm = TileMap(*layout)
+        es, el, skipped = [], [], 0
+        for h, (_, _, ref_s, sel_ref, ref_l) in enumerate(rs):
+            ok_tile = np.array([np.array_equal(sel_gpu[h, t], sel_ref[t]) for t in range(tm.T)])
+            rows = np.ones(N, dtype=bool)
+            rows[tm.tile_of >= 0] = ok_tile[tm.tile_of[tm.tile_of >= 0]]
+            skipped += int((~rows).sum())
+            es.append(np.abs(got_s[rows, h] - ref_s[rows]))
+            el.append(np.abs(got_l[:, h] - ref_l))
+        es, el = np.concatenate(es), np.concatenate(el)
+        cpu_s = sum(r[0] + r[1] for r in rs)
+        res[name] = {"tokens": N, "heads": H, "y": y, "oracle_wall_s": wall, "processes": workers,
+                     "oracle_cpu_s": cpu_s, "oracle_tokens_per_s": N / wall,
+                     "sparse_max_abs": float(es.max()), "sparse_mean_abs": float(es.mean()),
+                     "sparse_rows_checked": int(es.shape[0]), "sparse_rows_near_tie": skipped,
+                     "linear_max_abs": float(el.max()), "linear_mean_abs": float(el.mean())}
+        del qd, kd, vd, out_s, out_l, bufs
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(pool, workers, L, q, k, v, y, seed):
@@ -615,6 +689,9 @@ def main():
             sch["speedup_vs_dense"] = 24 * dms / total
             result["speedup_vs_dense"]["schedule_0.7L/0.8S_24_stages"] = 24 * dms / total
         result["schedule"] = sch
+    if not a.no_cpu and not a.no_full_small:
+        log(f"oracle in full on the 2-view and 32-view workloads ({workers} processes)")
+        result["oracle_full_small"] = full_small(pool, workers, zb, zs, torch, a.seed)
     if pool is not None:
         pool.shutdown()
     print(json.dumps(result), flush=True)

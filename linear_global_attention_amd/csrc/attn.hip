@@ -154,15 +154,6 @@ __device__ __forceinline__ void load_queries(const Geom& g, const AttnArgs& A, c
   }
 }
 
-__device__ __forceinline__ void qk(const bf16x8 q[2], const bf16x8 kf[2][2], f32x4& s0, f32x4& s1) {
-  s0 = f32x4{0.f, 0.f, 0.f, 0.f};
-  s1 = s0;
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][0], q[0], s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][0], q[0], s1, 0, 0, 0);
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][1], q[1], s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][1], q[1], s1, 0, 0, 0);
-}
-
 // p = exp2(s) for the lane's 8 keys of a 32-key block (s already in log2
 // units with the row's offset applied)
 __device__ __forceinline__ void probs(const f32x4& s0, const f32x4& s1, float p[8]) {
@@ -238,9 +229,9 @@ __device__ __forceinline__ void attend_block(MainState<SW>& st, unsigned us, con
 }
 
 // The landmark block lb (landmarks of tiles 32lb..32lb+31) for every user
-// slot: logit q.kbar/8 + ln n_u, value vbar_u. The landmark term log2(n_u)/C
-// (-inf past the last tile, and -inf for the tiles the slot's group kept)
-// is the initial value of the S^T accumulators.
+// slot: logit q.kbar/8 + ln n_u, value vbar_u. In log2 units the landmark
+// term log2(n_u) - M (-inf past the last tile, and -inf for the tiles the
+// slot's group kept) is the initial value of the S^T accumulators.
 template <int SW>
 __device__ __forceinline__ void attend_landmarks(MainState<SW>& st, unsigned us, const char* kb, int lb,
                                                  cmask_ptr mrow0, long long mstep, int lane) {

@@ -47,7 +47,7 @@
 // channels][32] with keys permuted by value_pos). Row sums use the
 // bf16-rounded p that P.V sees, through one more MFMA whose A operand is 1
 // for real keys and 0 for the zero padding of a tile's last block. The bf16
-// rounding of C q changes a logit by at most 2^-9 of |C q . k| per channel
+// rounding of C q changes a logit by at most 2^-8 of |C q_c k_c| per channel
 // term (measured: 8.3e-4 against 7.6e-4 max-abs at 1,024 views), and saves
 // the per-score multiply-add that used to sit between the MFMAs.
 // LDS layouts are XOR-swizzled at 16-byte granularity (keys: column ^ key%8,

@@ -65,12 +65,14 @@ static_assert(6 * (AP_NB - 2) <= 24, "lin_wait_vm covers the pending counts of l
 // token-major, a 128-byte row as eight 16-byte chunks, chunk c of row r at
 // slot c ^ ls_swz(r) (both access patterns below then spread over the
 // banks). The K rows are read in the feature-map lane layout (one token per
-// 4 lanes), turned into phi(k) (bf16) and written back in place; then
-// S += phi^T V with 16 bf16 MFMAs (16x16x16, k = token) whose operands, 4
-// consecutive tokens of one channel per lane, come from transposing LDS
-// reads. The ring is read and written by inline asm that waits on LDS
-// only: as plain accesses the compiler would first wait for every copy in
-// flight into the ring. The workgroup adds its waves' states in wave order.
+// 4 lanes), turned into phi(k) (bf16) and written back in place; transposing
+// LDS reads then give the MFMA operands, 4 consecutive tokens of one channel
+// per lane. Every two groups, S += phi^T V and z += phi^T 1 take 20 bf16
+// MFMAs (16x16x32, k = the two groups' 32 tokens; the all-ones operand gives
+// z from the same bf16 phi as S). The ring is read and written by inline asm
+// that waits on LDS only: as plain accesses the compiler would first wait
+// for every copy in flight into the ring. The workgroup adds its waves'
+// states in wave order.
 constexpr int ST_NB = 4;       // LDS ring slots per wave
 constexpr int ST_SLOT = 4096;  // bytes per slot: 16 K rows, then 16 V rows
 __device__ inline int ls_swz(int r) { return (r ^ (r >> 2)) & 7; }
@@ -95,35 +97,66 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float zacc[16];
+  f32x4 zacc[4];  // z[16 ab + 4 grp + r] in zacc[ab][r] (every column alike)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) zacc[i] = 0.f;
+  for (int a = 0; a < 4; ++a) zacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint2 ones2 = make_uint2(0x3F803F80u, 0x3F803F80u);
   __syncthreads();  // the rotary table
 
   const long long t_begin = (long long)chunk * tpw;
   const long long t_end = min((long long)g.N, t_begin + tpw);
-    const long long first = t_begin + 16 * wave;
+  const long long first = t_begin + 16 * __builtin_amdgcn_readfirstlane(wave);
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
   char* ring = &sring[wave][0][0];
   // group m into slot m % ST_NB: copy j of each of K and V fills row
   // 8j + lane/8, slot lane % 8 (chunk (lane % 8) ^ ls_swz(row)). Rows past
   // t_end repeat the last token (their phi is zeroed). Every lane issues all
   // four copies, so the wave's memory counter advances by 4 per group.
+  // byte offset of this lane's piece of copy j within a group whose first
+  // token is at offset zero; a whole group then only adds a uniform base
+  long long loff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * j + (lane >> 3);
+    loff[j] = ((long long)r * g.in_tok + (long long)h * g.in_head) * 2 + (((lane & 7) ^ ls_swz(r)) << 4);
+  }
+  const long long gstep = 64LL * g.in_tok * 2;
   auto stage = [&](int m) {
     const long long r0 = first + 64LL * m;
     char* dst = ring + (m % ST_NB) * ST_SLOT;
+    if (r0 + 15 < t_end) {
+      const long long base = r0 * g.in_tok * 2;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = 8 * j + (lane >> 3);
-      const long long tok = min(r0 + r, t_end - 1);
-      const long long off = (tok * g.in_tok + h * g.in_head) * 2 + (((lane & 7) ^ ls_swz(r)) << 4);
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)K + off), (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)V + off), (lin_lds_void*)(dst + 2048 + j * 1024), 16,
-                                       0, 0);
+      for (int j = 0; j < 2; ++j) {
+        __builtin_amdgcn_global_load_lds((const void*)((const char*)K + base + loff[j]), (lin_lds_void*)(dst + j * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)((const char*)V + base + loff[j]),
+                                         (lin_lds_void*)(dst + 2048 + j * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 8 * j + (lane >> 3);
+        const long long tok = min(r0 + r, t_end - 1);
+        const long long off = (tok * g.in_tok + h * g.in_head) * 2 + (((lane & 7) ^ ls_swz(r)) << 4);
+        __builtin_amdgcn_global_load_lds((const void*)((const char*)K + off), (lin_lds_void*)(dst + j * 1024), 16, 0,
+                                         0);
+        __builtin_amdgcn_global_load_lds((const void*)((const char*)V + off), (lin_lds_void*)(dst + 2048 + j * 1024),
+                                         16, 0, 0);
+      }
     }
   };
   for (int m = 0; m < ST_NB - 1 && m < n; ++m) stage(m);
-  for (int m = 0; m < n; ++m) {
+  int loc;  // position within its frame of this lane's token of the current group
+  {
+    const long long t0 = first + tl;
+    long long f = (long long)((double)t0 * dv.inv_tpf);
+    long long l0 = t0 - f * g.tok_pf;
+    if (l0 < 0) l0 += g.tok_pf;
+    else if (l0 >= g.tok_pf) l0 -= g.tok_pf;
+    loc = (int)l0;
+  }
+  auto group = [&](int m, uint2 (&A)[4], uint2 (&B)[4]) {
     // group m has landed once at most the newer groups' copies are pending
     lin_wait_vm(4 * min(ST_NB - 2, n - 1 - m));
     asm volatile("" ::: "memory");
@@ -146,8 +179,26 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
     const long long tok = first + 64LL * m + tl;
     float x[16];
     unpack16(w4, x);
+    // patch row and column of the token at `loc` in its frame; loc then
+    // steps to this lane's token of the next group
     int pr = 0, pc = 0;
-    if (tok < t_end) token_pos(g, dv, tok, pr, pc);
+    {
+      const int p = max(loc - g.S, 0);
+      int r = (int)((float)p * dv.inv_c);
+      int c = p - r * g.C;
+      if (c < 0) {
+        --r;
+        c += g.C;
+      } else if (c >= g.C) {
+        ++r;
+        c -= g.C;
+      }
+      const bool live = loc >= g.S && tok < t_end;
+      pr = live ? r : 0;
+      pc = live ? c : 0;
+      loc += 64;
+      while (loc >= g.tok_pf) loc -= g.tok_pf;
+    }
     // the rotary values of pairs 4 grp .. +3 at (pr, pc), by asm for the
     // same reason as the ring (the table is an extern LDS array)
     float2 cr[4], cc[4];
@@ -173,10 +224,6 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
     for (int q = 0; q < 4; ++q) {
       pw[q].x = pack_bf16x2(x[4 * q], x[4 * q + 1]);  // round to nearest even
       pw[q].y = pack_bf16x2(x[4 * q + 2], x[4 * q + 3]);
-      zacc[4 * q + 0] += __uint_as_float(pw[q].x << 16);
-      zacc[4 * q + 1] += __uint_as_float(pw[q].x & 0xFFFF0000u);
-      zacc[4 * q + 2] += __uint_as_float(pw[q].y << 16);
-      zacc[4 * q + 3] += __uint_as_float(pw[q].y & 0xFFFF0000u);
     }
     // phi in place of the K rows, then the MFMA operands: lane i of each 16
     // names row 4 grp + i/4, columns 16 b + 4 (i % 4) .. +3 of the phi (A)
@@ -187,7 +234,6 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
       const int row = 4 * grp + (tl >> 2), col = 16 * b + 4 * (tl & 3);
       ta[b] = sb + row * 128 + (((col >> 3) ^ ls_swz(row)) << 4) + (col & 4) * 2;
     }
-    uint2 A[4], B[4];
     asm volatile(
         "ds_write_b64 %8, %12\n\t"
         "ds_write_b64 %9, %13\n\t"
@@ -206,25 +252,29 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
         : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(pw[0]), "v"(pw[1]), "v"(pw[2]), "v"(pw[3]),
           "v"(ta[0]), "v"(ta[1]), "v"(ta[2]), "v"(ta[3])
         : "memory");
-    // S[16 ab + 4 grp + r][16 cb + tl] += sum over the group's 16 tokens
+    if (m + ST_NB - 1 < n) stage(m + ST_NB - 1);
+  };
+  const uint4 ones4 = make_uint4(ones2.x, ones2.y, ones2.x, ones2.y);
+  for (int m = 0; m < n; m += 2) {
+    uint2 A0[4], B0[4], A1[4], B1[4];
+    group(m, A0, B0);
+    if (m + 1 < n) {
+      group(m + 1, A1, B1);
+    } else {
 #pragma unroll
-    for (int ab = 0; ab < 4; ++ab)
+      for (int i = 0; i < 4; ++i) A1[i] = B1[i] = make_uint2(0u, 0u);
+    }
+    // S[16 ab + 4 grp + r][16 cb + tl] += sum over the two groups' 32 tokens
+    // (k = 8 grp + j: token 4 grp + j of group m for j < 4, of group m + 1 else)
+#pragma unroll
+    for (int ab = 0; ab < 4; ++ab) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(A0[ab].x, A0[ab].y, A1[ab].x, A1[ab].y));
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
-        acc[ab][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(st_v4s, A[ab]),
-                                                                 __builtin_bit_cast(st_v4s, B[cb]), acc[ab][cb], 0, 0,
-                                                                 0);
-    if (m + ST_NB - 1 < n) stage(m + ST_NB - 1);
-  }
-  // z: sum the 16 lanes of each channel group
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float v = zacc[i];
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    v += __shfl_xor(v, 8, 64);
-    zacc[i] = v;
+        acc[ab][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, __builtin_bit_cast(bf16x8, make_uint4(B0[cb].x, B0[cb].y, B1[cb].x, B1[cb].y)), acc[ab][cb], 0, 0, 0);
+      zacc[ab] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, ones4), zacc[ab], 0, 0, 0);
+    }
   }
   // the workgroup's partial: the 4 waves' states added in wave order in LDS
   // (over the rings, once every wave has left its loop), then written once
@@ -244,10 +294,12 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
           }
       if (tl == 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float* e = &red[D * D + lane_channel(grp, i)];
-          *e = w == 0 ? zacc[i] : *e + zacc[i];
-        }
+        for (int ab = 0; ab < 4; ++ab)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float* e = &red[D * D + ab * 16 + 4 * grp + r];
+            *e = w == 0 ? zacc[ab][r] : *e + zacc[ab][r];
+          }
       }
     }
     __syncthreads();
@@ -367,7 +419,7 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
   const long long t_begin = (long long)chunk * tpw;
   const long long t_end = min((long long)g.N, t_begin + tpw);
     // This wave's 16-token groups: m = 0..n-1, first token t_begin + 16 (wave + 4m).
-  const long long first = t_begin + 16 * wave;
+  const long long first = t_begin + 16 * __builtin_amdgcn_readfirstlane(wave);
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
   char* ring = &qring[wave][0][0];
   // Stage group m's 16 Q rows (2 KB) into ring slot m % AP_NB: two async
@@ -377,18 +429,44 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
   // with the same value: every lane issues every load and store, so the
   // wave's memory counter advances by exactly 2 per group staged and 2 per
   // group stored.
+  // byte offsets of this lane's copy pieces and output pieces within a
+  // group whose first token is at offset zero (rows 8j + l/8, 16-byte
+  // column l%8, swizzled for the loads)
+  long long qoff[2], ooff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * j + (lane >> 3);
+    qoff[j] = ((long long)r * g.in_tok + (long long)h * g.in_head) * 2 + (((lane & 7) ^ (r & 7)) << 4);
+    ooff[j] = ((long long)r * g.out_tok + (long long)h * g.out_head) * 2 + (lane & 7) * 16;
+  }
   auto stage = [&](int m) {
     const long long r0 = first + 64LL * m;
     char* dst = ring + (m % AP_NB) * 2048;
+    if (r0 + 15 < t_end) {
+      const char* base = (const char*)Q + r0 * g.in_tok * 2;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = 8 * j + (lane >> 3);
-      const long long tok = min(r0 + r, t_end - 1);
-      const int c = (lane & 7) ^ (r & 7);
-      const char* src = (const char*)(Q + tok * g.in_tok + h * g.in_head) + c * 16;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
+      for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(base + qoff[j]), (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 8 * j + (lane >> 3);
+        const long long tok = min(r0 + r, t_end - 1);
+        const int c = (lane & 7) ^ (r & 7);
+        const char* src = (const char*)(Q + tok * g.in_tok + h * g.in_head) + c * 16;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
+      }
     }
   };
+  int loc;  // position within its frame of this lane's token of group m
+  {
+    const long long t0 = first + tl;
+    long long f = (long long)((double)t0 * dv.inv_tpf);
+    long long l0 = t0 - f * g.tok_pf;
+    if (l0 < 0) l0 += g.tok_pf;
+    else if (l0 >= g.tok_pf) l0 -= g.tok_pf;
+    loc = (int)l0;
+  }
   for (int m = 0; m < AP_NB - 1 && m < n; ++m) stage(m);
   for (int m = 0; m < n; ++m) {
     // group m has landed once at most `later` newer memory operations of
@@ -417,11 +495,29 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
           : "v"(qa[0]), "v"(qa[1]), "v"(qa[2]), "v"(qa[3])
           : "memory");
     }
-    const long long tok = min(first + 64LL * m + tl, t_end - 1);
+    const long long r0 = first + 64LL * m;
+    const bool whole = r0 + 15 < t_end;  // no row of the group past t_end
     float x[16];
     unpack16(qr, x);
     int pr = 0, pc = 0;
-    token_pos(g, dv, tok, pr, pc);
+    if (whole) {
+      const int p = max(loc - g.S, 0);
+      int r = (int)((float)p * dv.inv_c);
+      int c = p - r * g.C;
+      if (c < 0) {
+        --r;
+        c += g.C;
+      } else if (c >= g.C) {
+        ++r;
+        c -= g.C;
+      }
+      pr = loc >= g.S ? r : 0;
+      pc = loc >= g.S ? c : 0;
+    } else {
+      token_pos(g, dv, min(r0 + tl, t_end - 1), pr, pc);
+    }
+    loc += 64;
+    while (loc >= g.tok_pf) loc -= g.tok_pf;
     // phi(q) enters o = phi(q)^T S' / phi(q)^T z only as a ratio
     featurize16<false>(x, gq != nullptr, gain, tab, pr, pc, grp, P.eps);
     unsigned pw[8];
@@ -483,9 +579,15 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
         : "v"(wa[0]), "v"(wa[1]), "v"(wa[2]), "v"(wa[3]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(ra0),
           "v"(ra1)
         : "memory");
-    const long long otok0 = min(first + 64LL * m + rr, t_end - 1), otok1 = min(first + 64LL * m + rr + 8, t_end - 1);
-    *(uint4*)(out + otok0 * g.out_tok + h * g.out_head + rc * 8) = make_uint4(t0[0], t0[1], t0[2], t0[3]);
-    *(uint4*)(out + otok1 * g.out_tok + h * g.out_head + rc * 8) = make_uint4(t1[0], t1[1], t1[2], t1[3]);
+    if (whole) {
+      char* ob = (char*)out + r0 * g.out_tok * 2;
+      *(uint4*)(ob + ooff[0]) = make_uint4(t0[0], t0[1], t0[2], t0[3]);
+      *(uint4*)(ob + ooff[1]) = make_uint4(t1[0], t1[1], t1[2], t1[3]);
+    } else {
+      const long long otok0 = min(r0 + rr, t_end - 1), otok1 = min(r0 + rr + 8, t_end - 1);
+      *(uint4*)(out + otok0 * g.out_tok + h * g.out_head + rc * 8) = make_uint4(t0[0], t0[1], t0[2], t0[3]);
+      *(uint4*)(out + otok1 * g.out_tok + h * g.out_head + rc * 8) = make_uint4(t1[0], t1[1], t1[2], t1[3]);
+    }
     if (m + AP_NB - 1 < n) stage(m + AP_NB - 1);
   }
 }
@@ -496,11 +598,15 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
 // least-squares solve in fp64). grid (nchunks, H), block 256; partial p =
 // chunk of head h holds, in fp32: sum o [64], sum t [64], sum o o^T [64][64],
 // sum o t^T [64][64] over its tokens. The same per-wave rings as
-// linear_state (a slot holds 16 rows of o, then 16 rows of t) and the same
-// transposing reads; the sums come from MFMAs against an all-ones operand.
+// linear_state (a slot holds 16 rows of o, then 16 rows of t), the same
+// transposing reads and the same 16x16x32 MFMAs over pairs of groups; the
+// sums come from MFMAs against an all-ones operand, and of the symmetric
+// o o^T only the blocks on and above the diagonal are accumulated.
 constexpr int AF_PART = 2 * D + 2 * D * D;  // floats of one partial
+// index of block (ab, cb), ab <= cb < 4, in the upper triangle, row by row
+#define AF_TRI(ab, cb) ((ab) * 4 - (ab) * ((ab) - 1) / 2 + (cb) - (ab))
 
-__global__ void __launch_bounds__(LIN_THREADS) affine_stats_kernel(Geom g, const u16* __restrict__ O,
+__global__ void __launch_bounds__(LIN_THREADS, 2) affine_stats_kernel(Geom g, const u16* __restrict__ O,
                                                                    const u16* __restrict__ Tt,
                                                                    float* __restrict__ partials, int nchunks,
                                                                    int tpw) {
@@ -509,40 +615,66 @@ __global__ void __launch_bounds__(LIN_THREADS) affine_stats_kernel(Geom g, const
   const int h = blockIdx.y, chunk = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, tl = lane & 15;
-  f32x4 aoo[4][4], aot[4][4], so[4], st[4];
+  // o o^T is symmetric: only its blocks ab <= cb are accumulated, in
+  // aoo[AF_TRI(ab, cb)]
+  f32x4 aoo[10], aot[4][4], so[4], st[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     so[a] = st[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) aoo[a][c] = aot[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 4; ++c) aot[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const st_v4s ones = __builtin_bit_cast(st_v4s, make_uint2(0x3F803F80u, 0x3F803F80u));  // bf16 1.0 x 4
+#pragma unroll
+  for (int i = 0; i < 10; ++i) aoo[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   const long long t_begin = (long long)chunk * tpw;
   const long long t_end = min((long long)g.N, t_begin + tpw);
-    const long long first = t_begin + 16 * wave;
+  const long long first = t_begin + 16 * __builtin_amdgcn_readfirstlane(wave);
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
   char* ring = &sring[wave][0][0];
   // group m into slot m % ST_NB (as in linear_state): rows past t_end
   // repeat the last token (every lane issues all four copies, so the wave's
   // memory counter advances by 4 per group); those rows are zeroed in LDS
   // before they are read.
+  // byte offsets of this lane's pieces of copy j (o: the output's strides,
+  // teacher: q's strides) within a group whose first token is at offset 0
+  long long ooff[2], toff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * j + (lane >> 3);
+    const long long sw = ((lane & 7) ^ ls_swz(r)) << 4;
+    ooff[j] = ((long long)r * g.out_tok + (long long)h * g.out_head) * 2 + sw;
+    toff[j] = ((long long)r * g.in_tok + (long long)h * g.in_head) * 2 + sw;
+  }
   auto stage = [&](int m) {
     const long long r0 = first + 64LL * m;
     char* dst = ring + (m % ST_NB) * ST_SLOT;
+    if (r0 + 15 < t_end) {
+      const char* ob = (const char*)O + r0 * g.out_tok * 2;
+      const char* tb = (const char*)Tt + r0 * g.in_tok * 2;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = 8 * j + (lane >> 3);
-      const long long tok = min(r0 + r, t_end - 1);
-      const long long sw = ((lane & 7) ^ ls_swz(r)) << 4;
-      const long long offo = (tok * g.out_tok + h * g.out_head) * 2 + sw;  // o: the output's strides
-      const long long offt = (tok * g.in_tok + h * g.in_head) * 2 + sw;    // teacher: q's strides
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)O + offo), (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)Tt + offt), (lin_lds_void*)(dst + 2048 + j * 1024),
-                                       16, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        __builtin_amdgcn_global_load_lds((const void*)(ob + ooff[j]), (lin_lds_void*)(dst + j * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(tb + toff[j]), (lin_lds_void*)(dst + 2048 + j * 1024), 16, 0,
+                                         0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 8 * j + (lane >> 3);
+        const long long tok = min(r0 + r, t_end - 1);
+        const long long sw = ((lane & 7) ^ ls_swz(r)) << 4;
+        const long long offo = (tok * g.out_tok + h * g.out_head) * 2 + sw;
+        const long long offt = (tok * g.in_tok + h * g.in_head) * 2 + sw;
+        __builtin_amdgcn_global_load_lds((const void*)((const char*)O + offo), (lin_lds_void*)(dst + j * 1024), 16, 0,
+                                         0);
+        __builtin_amdgcn_global_load_lds((const void*)((const char*)Tt + offt), (lin_lds_void*)(dst + 2048 + j * 1024),
+                                         16, 0, 0);
+      }
     }
   };
   for (int m = 0; m < ST_NB - 1 && m < n; ++m) stage(m);
-  for (int m = 0; m < n; ++m) {
+  auto group = [&](int m, uint2 (&A)[4], uint2 (&B)[4]) {
     lin_wait_vm(4 * min(ST_NB - 2, n - 1 - m));
     asm volatile("" ::: "memory");
     const unsigned sb = (unsigned)(size_t)(ring + (m % ST_NB) * ST_SLOT);
@@ -555,7 +687,6 @@ __global__ void __launch_bounds__(LIN_THREADS) affine_stats_kernel(Geom g, const
       const int row = 4 * grp + (tl >> 2), col = 16 * b + 4 * (tl & 3);
       ta[b] = sb + row * 128 + (((col >> 3) ^ ls_swz(row)) << 4) + (col & 4) * 2;
     }
-    uint2 A[4], B[4];
     if (valid >= 16) {
       asm volatile(
           "ds_read_b64_tr_b16 %0, %8\n\t"
@@ -607,20 +738,36 @@ __global__ void __launch_bounds__(LIN_THREADS) affine_stats_kernel(Geom g, const
           : "v"(ta[0]), "v"(ta[1]), "v"(ta[2]), "v"(ta[3])
           : "memory");
     }
-    // A[b]: o of channels 16 b + i, B[b]: t of channels 16 b + i, for the 4
-    // tokens 4 grp .. +3 (k = token)
+    if (m + ST_NB - 1 < n) stage(m + ST_NB - 1);
+  };
+  for (int m = 0; m < n; m += 2) {
+    uint2 A0[4], B0[4], A1[4], B1[4];
+    group(m, A0, B0);
+    if (m + 1 < n) {
+      group(m + 1, A1, B1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) A1[i] = B1[i] = make_uint2(0u, 0u);
+    }
+    // oa[b]: o of channels 16 b + i, tb[b]: t of channels 16 b + i, for the
+    // 8 tokens k = 8 grp + j (token 4 grp + j of group m for j < 4, of group
+    // m + 1 else)
+    bf16x8 oa[4], tb[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      oa[b] = __builtin_bit_cast(bf16x8, make_uint4(A0[b].x, A0[b].y, A1[b].x, A1[b].y));
+      tb[b] = __builtin_bit_cast(bf16x8, make_uint4(B0[b].x, B0[b].y, B1[b].x, B1[b].y));
+    }
 #pragma unroll
     for (int ab = 0; ab < 4; ++ab) {
-      const st_v4s oa = __builtin_bit_cast(st_v4s, A[ab]);
-      so[ab] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(oa, ones, so[ab], 0, 0, 0);
-      st[ab] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(st_v4s, B[ab]), ones, st[ab], 0, 0, 0);
+      so[ab] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[ab], ones, so[ab], 0, 0, 0);
+      st[ab] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tb[ab], ones, st[ab], 0, 0, 0);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        aoo[ab][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(oa, __builtin_bit_cast(st_v4s, A[cb]), aoo[ab][cb], 0, 0, 0);
-        aot[ab][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(oa, __builtin_bit_cast(st_v4s, B[cb]), aot[ab][cb], 0, 0, 0);
+        if (cb >= ab) aoo[AF_TRI(ab, cb)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[ab], oa[cb], aoo[AF_TRI(ab, cb)], 0, 0, 0);
+        aot[ab][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[ab], tb[cb], aot[ab][cb], 0, 0, 0);
       }
     }
-    if (m + ST_NB - 1 < n) stage(m + ST_NB - 1);
   }
   // the workgroup's partial: the 4 waves added in wave order in LDS (over
   // the rings, once every wave has left its loop), then written once.
@@ -641,10 +788,19 @@ __global__ void __launch_bounds__(LIN_THREADS) affine_stats_kernel(Geom g, const
           }
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
-            float* e1 = &red[2 * D + a * D + cb * 16 + tl];
             float* e2 = &red[2 * D + D * D + a * D + cb * 16 + tl];
-            *e1 = w == 0 ? aoo[ab][cb][r] : *e1 + aoo[ab][cb][r];
             *e2 = w == 0 ? aot[ab][cb][r] : *e2 + aot[ab][cb][r];
+            if (cb >= ab) {
+              // element (a, c) of o o^T and, off the diagonal blocks, (c, a)
+              const float v = aoo[AF_TRI(ab, cb)][r];
+              const int c = cb * 16 + tl;
+              float* e1 = &red[2 * D + a * D + c];
+              *e1 = w == 0 ? v : *e1 + v;
+              if (cb > ab) {
+                float* e1t = &red[2 * D + c * D + a];
+                *e1t = w == 0 ? v : *e1t + v;
+              }
+            }
           }
         }
     }

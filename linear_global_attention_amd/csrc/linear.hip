@@ -120,7 +120,6 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
     const int r = 8 * j + (lane >> 3);
     loff[j] = ((long long)r * g.in_tok + (long long)h * g.in_head) * 2 + (((lane & 7) ^ ls_swz(r)) << 4);
   }
-  const long long gstep = 64LL * g.in_tok * 2;
   auto stage = [&](int m) {
     const long long r0 = first + 64LL * m;
     char* dst = ring + (m % ST_NB) * ST_SLOT;
@@ -147,15 +146,7 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
     }
   };
   for (int m = 0; m < ST_NB - 1 && m < n; ++m) stage(m);
-  int loc;  // position within its frame of this lane's token of the current group
-  {
-    const long long t0 = first + tl;
-    long long f = (long long)((double)t0 * dv.inv_tpf);
-    long long l0 = t0 - f * g.tok_pf;
-    if (l0 < 0) l0 += g.tok_pf;
-    else if (l0 >= g.tok_pf) l0 -= g.tok_pf;
-    loc = (int)l0;
-  }
+  int loc = token_loc(g, dv, first + tl);  // frame position of this lane's token of the current group
   auto group = [&](int m, uint2 (&A)[4], uint2 (&B)[4]) {
     // group m has landed once at most the newer groups' copies are pending
     lin_wait_vm(4 * min(ST_NB - 2, n - 1 - m));
@@ -179,26 +170,12 @@ __global__ void __launch_bounds__(LIN_THREADS) linear_state_kernel(
     const long long tok = first + 64LL * m + tl;
     float x[16];
     unpack16(w4, x);
-    // patch row and column of the token at `loc` in its frame; loc then
-    // steps to this lane's token of the next group
+    // rotary position of the token (rows past t_end: (0, 0), their phi is
+    // zeroed); loc then steps to this lane's token of the next group
     int pr = 0, pc = 0;
-    {
-      const int p = max(loc - g.S, 0);
-      int r = (int)((float)p * dv.inv_c);
-      int c = p - r * g.C;
-      if (c < 0) {
-        --r;
-        c += g.C;
-      } else if (c >= g.C) {
-        ++r;
-        c -= g.C;
-      }
-      const bool live = loc >= g.S && tok < t_end;
-      pr = live ? r : 0;
-      pc = live ? c : 0;
-      loc += 64;
-      while (loc >= g.tok_pf) loc -= g.tok_pf;
-    }
+    loc_pos(g, dv, loc, pr, pc);
+    if (tok >= t_end) pr = pc = 0;
+    loc = loc_step64(g, loc);
     // the rotary values of pairs 4 grp .. +3 at (pr, pc), by asm for the
     // same reason as the ring (the table is an extern LDS array)
     float2 cr[4], cc[4];
@@ -458,15 +435,7 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
       }
     }
   };
-  int loc;  // position within its frame of this lane's token of group m
-  {
-    const long long t0 = first + tl;
-    long long f = (long long)((double)t0 * dv.inv_tpf);
-    long long l0 = t0 - f * g.tok_pf;
-    if (l0 < 0) l0 += g.tok_pf;
-    else if (l0 >= g.tok_pf) l0 -= g.tok_pf;
-    loc = (int)l0;
-  }
+  int loc = token_loc(g, dv, first + tl);  // frame position of this lane's token of group m
   for (int m = 0; m < AP_NB - 1 && m < n; ++m) stage(m);
   for (int m = 0; m < n; ++m) {
     // group m has landed once at most `later` newer memory operations of
@@ -500,24 +469,10 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_apply_kernel(
     float x[16];
     unpack16(qr, x);
     int pr = 0, pc = 0;
-    if (whole) {
-      const int p = max(loc - g.S, 0);
-      int r = (int)((float)p * dv.inv_c);
-      int c = p - r * g.C;
-      if (c < 0) {
-        --r;
-        c += g.C;
-      } else if (c >= g.C) {
-        ++r;
-        c -= g.C;
-      }
-      pr = loc >= g.S ? r : 0;
-      pc = loc >= g.S ? c : 0;
-    } else {
-      token_pos(g, dv, min(r0 + tl, t_end - 1), pr, pc);
-    }
-    loc += 64;
-    while (loc >= g.tok_pf) loc -= g.tok_pf;
+    // rows past t_end repeat the last token, so they take its position
+    if (whole) loc_pos(g, dv, loc, pr, pc);
+    else token_pos(g, dv, min(r0 + tl, t_end - 1), pr, pc);
+    loc = loc_step64(g, loc);
     // phi(q) enters o = phi(q)^T S' / phi(q)^T z only as a ratio
     featurize16<false>(x, gq != nullptr, gain, tab, pr, pc, grp, P.eps);
     unsigned pw[8];

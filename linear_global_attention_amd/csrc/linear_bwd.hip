@@ -368,7 +368,7 @@ __device__ inline void write_partial(const f32x4 X[4][4], float x[16], float* re
 // phi(k): the backward works with S - z m^T, a remainder far smaller than S,
 // which the forward's single bf16 rounding of phi(k) would swamp. Writes the
 // partial [S [64][64], z [64]].
-__global__ void __launch_bounds__(LIN_THREADS, 3) linear_bwd_state_kernel(
+__global__ void __launch_bounds__(LIN_THREADS, 2) linear_bwd_state_kernel(
     Geom g, LinParams P, const u16* __restrict__ K, const u16* __restrict__ V, const float* __restrict__ gk,
     float* __restrict__ partials, int nchunks, int tpw) {
   __shared__ __attribute__((aligned(16))) float2 tab[MAX_GRID * RT_STRIDE];
@@ -395,18 +395,31 @@ __global__ void __launch_bounds__(LIN_THREADS, 3) linear_bwd_state_kernel(
   const long long t_end = min((long long)g.N, t_begin + tpw);
   const long long first = t_begin + 16 * wave;
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
+  // the rows of the next group are loaded while this group is processed
+  auto fetch = [&](int m, uint2 (&a)[4], uint2 (&b)[4]) {
+    const long long tk = min(first + 64LL * m + tl, t_end - 1);
+    const long long row = tk * g.in_tok + (long long)h * g.in_head;
+    fetch16(K + row, grp, true, a);
+    fetch16(V + row, grp, true, b);
+  };
+  uint2 nk[4], nv[4];
+  if (n > 0) fetch(0, nk, nv);
+  int loc = token_loc(g, dv, first + tl);  // frame position of this lane's token of group m
   for (int m = 0; m < n; ++m) {
     const long long tok = first + 64LL * m + tl;
     const bool valid = tok < t_end;
-    const long long tk = valid ? tok : t_end - 1;
-    const long long row = tk * g.in_tok + (long long)h * g.in_head;
     uint2 wk[4], wv[4];
-    fetch16(K + row, grp, true, wk);
-    fetch16(V + row, grp, true, wv);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wk[i] = nk[i];
+      wv[i] = nv[i];
+    }
+    if (m + 1 < n) fetch(m + 1, nk, nv);
     RowFwd R;
     unpack16(wk, R.x);
     int pr = 0, pc = 0;
-    token_pos(g, dv, tk, pr, pc);
+    loc_pos(g, dv, loc, pr, pc);  // rows past t_end: masked, any position serves
+    loc = loc_step64(g, loc);
     float gain[16];
     lds16(sgain, grp, gain);
     row_forward(R, tab, gk != nullptr, gain, pr, pc, grp, P.eps);
@@ -465,17 +478,30 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_bwd_query_kernel(
   const long long t_end = min((long long)g.N, t_begin + tpw);
   const long long first = t_begin + 16 * wave;
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
+  // the rows of the next group are loaded while this group is processed
+  auto fetch = [&](int m, uint2 (&a)[4], uint2 (&b)[4]) {
+    const long long tk = min(first + 64LL * m + tl, t_end - 1);
+    fetch16(Q + tk * g.in_tok + (long long)h * g.in_head, grp, true, a);
+    fetch16(dY + tk * g.out_tok + (long long)h * g.out_head, grp, true, b);
+  };
+  uint2 nq[4], nd[4];
+  if (n > 0) fetch(0, nq, nd);
+  int loc = token_loc(g, dv, first + tl);  // frame position of this lane's token of group m
   for (int m = 0; m < n; ++m) {
     const long long tok = first + 64LL * m + tl;
     const bool valid = tok < t_end;
-    const long long tk = valid ? tok : t_end - 1;
     uint2 wq[4], wd[4];
-    fetch16(Q + tk * g.in_tok + (long long)h * g.in_head, grp, true, wq);
-    fetch16(dY + tk * g.out_tok + (long long)h * g.out_head, grp, true, wd);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wq[i] = nq[i];
+      wd[i] = nd[i];
+    }
+    if (m + 1 < n) fetch(m + 1, nq, nd);
     RowFwd R;
     unpack16(wq, R.x);
     int pr = 0, pc = 0;
-    token_pos(g, dv, tk, pr, pc);
+    loc_pos(g, dv, loc, pr, pc);  // rows past t_end: masked, any position serves
+    loc = loc_step64(g, loc);
     float gain[16], zl[16];
     lds16(sgain, grp, gain);
     row_forward(R, tab, gq != nullptr, gain, pr, pc, grp, P.eps);
@@ -548,21 +574,34 @@ __global__ void __launch_bounds__(LIN_THREADS, 3) linear_bwd_key_kernel(
   const long long t_end = min((long long)g.N, t_begin + tpw);
   const long long first = t_begin + 16 * wave;
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
+  // the rows of the next group are loaded while this group is processed
+  auto fetch = [&](int m, uint2 (&a)[4], uint2 (&b)[4]) {
+    const long long tk = min(first + 64LL * m + tl, t_end - 1);
+    const long long row = tk * g.in_tok + (long long)h * g.in_head;
+    fetch16(K + row, grp, true, a);
+    fetch16(V + row, grp, true, b);
+  };
+  uint2 nk[4], nv[4];
+  if (n > 0) fetch(0, nk, nv);
+  int loc = token_loc(g, dv, first + tl);  // frame position of this lane's token of group m
   for (int m = 0; m < n; ++m) {
     const long long tok = first + 64LL * m + tl;
     const bool valid = tok < t_end;
-    const long long tk = valid ? tok : t_end - 1;
-    const long long row = tk * g.in_tok + (long long)h * g.in_head;
     // the operand fragments are read from LDS where they are used, not
     // hoisted out of the loop into 128 registers
     asm volatile("" ::: "memory");
     uint2 wk[4], wv[4];
-    fetch16(K + row, grp, true, wk);
-    fetch16(V + row, grp, true, wv);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wk[i] = nk[i];
+      wv[i] = nv[i];
+    }
+    if (m + 1 < n) fetch(m + 1, nk, nv);
     RowFwd R;
     unpack16(wk, R.x);
     int pr = 0, pc = 0;
-    token_pos(g, dv, tk, pr, pc);
+    loc_pos(g, dv, loc, pr, pc);  // rows past t_end: masked, any position serves
+    loc = loc_step64(g, loc);
     float gain[16];
     lds16(sgain, grp, gain);
     row_forward(R, tab, gk != nullptr, gain, pr, pc, grp, P.eps);

@@ -48,13 +48,19 @@ struct PosDiv {
   __device__ explicit PosDiv(const Geom& g) : inv_tpf(1.0 / (double)g.tok_pf), inv_c(1.0f / (float)g.C) {}
 };
 
-// Rotary position of token tok: (patch row, patch column), specials (0, 0).
-__device__ inline void token_pos(const Geom& g, const PosDiv& dv, long long tok, int& pr, int& pc) {
-  long long f = (long long)((double)tok * dv.inv_tpf);
+// Position of token tok within its frame, 0 <= loc < tokens per frame.
+__device__ inline int token_loc(const Geom& g, const PosDiv& dv, long long tok) {
+  const long long f = (long long)((double)tok * dv.inv_tpf);
   long long loc = tok - f * g.tok_pf;
   if (loc < 0) loc += g.tok_pf;
   else if (loc >= g.tok_pf) loc -= g.tok_pf;
-  const int p = max((int)loc - g.S, 0);  // p < 2^14: exact in fp32
+  return (int)loc;
+}
+
+// Rotary position (patch row, patch column) of the token at frame position
+// loc; specials (0, 0).
+__device__ inline void loc_pos(const Geom& g, const PosDiv& dv, int loc, int& pr, int& pc) {
+  const int p = max(loc - g.S, 0);  // p < 2^14: exact in fp32
   int r = (int)((float)p * dv.inv_c);
   int c = p - r * g.C;
   if (c < 0) {
@@ -67,6 +73,18 @@ __device__ inline void token_pos(const Geom& g, const PosDiv& dv, long long tok,
   const bool special = loc < g.S;
   pr = special ? 0 : r;
   pc = special ? 0 : c;
+}
+
+// Rotary position of token tok.
+__device__ inline void token_pos(const Geom& g, const PosDiv& dv, long long tok, int& pr, int& pc) {
+  loc_pos(g, dv, token_loc(g, dv, tok), pr, pc);
+}
+
+// Frame position of the token 64 further on (a wave's next 16-token group).
+__device__ inline int loc_step64(const Geom& g, int loc) {
+  loc += 64;
+  while (loc >= g.tok_pf) loc -= g.tok_pf;
+  return loc;
 }
 
 // Sum / max of v over lane pairs (l, l ^ 16) or (l, l ^ 32) on the VALU

@@ -112,7 +112,8 @@ CASES = [("partial", zs.Layout(3, 2, 11, 13, heads=2), False, False),
          ("partial-affine-gains", zs.Layout(3, 2, 11, 13, heads=2), True, False),
          ("vggt-2view-affine", zs.Layout(2, 5, 37, 37, heads=3), True, False),
          ("no-specials-fused", zs.Layout(3, 0, 9, 9, heads=2), True, True),
-         ("vggt-2view-fused", zs.Layout(2, 5, 37, 37, heads=3), False, True)]
+         ("vggt-2view-fused", zs.Layout(2, 5, 37, 37, heads=3), False, True),
+         ("tiny-frames-affine-gains", zs.Layout(40, 1, 3, 4, heads=2), True, False)]
 
 
 @pytest.mark.parametrize("name,L,affine,fused", CASES, ids=[c[0] for c in CASES])

@@ -156,7 +156,10 @@ def test_y0_sparse_equals_dense_on_gpu():
 
 LIN = [("2views_16x16-identity", zs.CONFIGS["2views_16x16"], False),
        ("partial-affine", zs.Layout(3, 2, 11, 13, heads=2), True),
-       ("vggt-2view-affine", zs.Layout(2, 5, 37, 37, heads=3), True)]
+       ("vggt-2view-affine", zs.Layout(2, 5, 37, 37, heads=3), True),
+       # 13 tokens per frame: a wave's next 16-token group lies several
+       # frames on, so the stepped frame positions wrap more than once
+       ("tiny-frames-affine", zs.Layout(40, 1, 3, 4, heads=2), True)]
 
 
 @pytest.mark.parametrize("name,L,affine", LIN, ids=[x[0] for x in LIN])

@@ -213,7 +213,8 @@ zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream);
  * strides; dq, dk, dv: bf16, device, with q's strides, overlapping none of
  * the inputs. All four 16-byte aligned. The workspace must hold
  * ZEBRA_BUF_BWD_WORKSPACE bytes (per-row log-sum-exp and D, the transposed
- * kept-tile bitmap, partial gradients of the special keys and landmarks).
+ * kept-tile bitmap, partial gradients of the special keys and landmarks,
+ * the landmarks' bf16 high and low parts).
  * At most 32,768 tiles and fewer than 2^31 tokens (ZEBRA_ERR_UNSUPPORTED).
  * fp32 arithmetic with bf16 MFMA operands: logits and dP exact products
  * summed in fp32, P and the logit gradients rounded to bf16 for the

@@ -19,6 +19,8 @@
 //
 // Kernels, in stream order (per head; rows and keys addressed through the
 // strides of q, k, v and dout):
+//   sbwd_lmparts      the landmarks' bf16 high and low parts, once, in the
+//                     layout the query-major passes stage them in.
 //   sbwd_rows<STATS>  query-major: every row's log2-sum-exp2 of its logits
 //                     (log2 units) and D, in one pass over its visible keys
 //                     (each lane keeps running partials over its own keys,
@@ -54,6 +56,7 @@ constexpr int SB_CHUNKS = 8;                         // row chunks of the global
 
 typedef void __attribute__((address_space(3))) sb_lds_void;
 typedef short sb_v4s __attribute__((ext_vector_type(4)));
+typedef void __attribute__((address_space(3))) sb_lds_void;
 
 // ---------------------------------------------------------------- rows and units
 
@@ -160,6 +163,7 @@ struct SbArgs {
   float* dsum;            // [H][N] D
   float* part;            // [SB_CHUNKS][H][nspec_pad + T_pad][2][64] partial dk, dv of global keys
   float* lgrad;           // [H][T][2][64] landmark dk, dv
+  u16* lmp;               // [H][ceil(T/64)][4][64][64] landmark bf16 parts (sbwd_lmparts_kernel)
   u16* dQ;
   u16* dK;
   u16* dV;
@@ -209,6 +213,28 @@ __device__ inline void landmark_parts(const Geom& g, const SbArgs& A, int h, int
   split8(vv, vhi, vlo);
 }
 
+// grid (ceil(T / 64), H), block 256: the bf16 high and low parts of the
+// exact mean keys and values of landmarks 64 b .. 64 b + 63 (zero rows past
+// the last tile), laid out as the query-major passes hold a landmark block
+// in LDS: [K high, V high, K low, V low], each 64 rows at sb_off. Those
+// passes then copy a block into LDS as it is, with no conversion.
+__global__ void __launch_bounds__(256) sbwd_lmparts_kernel(Geom g, SbArgs A, int nlb) {
+  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int r = tid >> 2, u = 64 * b + r;
+  u16* dst = A.lmp + ((long long)h * nlb + b) * 4 * 64 * D;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c8 = 16 * (tid & 3) + 8 * i;
+    uint4 khi = make_uint4(0u, 0u, 0u, 0u), klo = khi, vhi = khi, vlo = khi;
+    if (u < g.T) landmark_parts(g, A, h, u, c8, khi, klo, vhi, vlo);
+    const int off = sb_off(r, c8);
+    *(uint4*)(dst + off) = khi;
+    *(uint4*)(dst + 64 * D + off) = vhi;
+    *(uint4*)(dst + 2 * 64 * D + off) = klo;
+    *(uint4*)(dst + 3 * 64 * D + off) = vlo;
+  }
+}
+
 // One thread's share of a 64-key token or special block, loaded ahead of
 // its use: keys tid / 8 and 32 + tid / 8, channels 8 (tid % 8) .. +7 of K
 // and V (bf16), and their logit biases (log2 units: 0, or -inf for keys
@@ -254,66 +280,6 @@ __device__ inline void commit_key_block(const KeyFetch& f, u16* sK, u16* sV, flo
     *(uint4*)(sV + sb_off(key, 8 * c)) = f.v[e];
     if (c == 0) sB[key] = f.bias[e];
   }
-}
-
-// One thread's share of landmark block b (landmarks 32 b ..): the 8 fp64
-// mean-key values and 8 fp32 mean values of landmark 32 b + tid / 8,
-// channels 8 (tid % 8) .., and its bias log2 n_u (-inf past the last tile or
-// where `mask` has its bit: the row's tile keeps it).
-struct LandmarkFetch {
-  uint4 k[4], v[2];
-  float bias;
-};
-
-__device__ inline void fetch_landmark_block(const Geom& g, const SbArgs& A, int h, int b, unsigned mask,
-                                            LandmarkFetch& f) {
-  const int tid = threadIdx.x, key = tid >> 3, c = tid & 7;
-  const int u = 32 * b + key;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.k[i] = make_uint4(0u, 0u, 0u, 0u);
-  f.v[0] = f.v[1] = make_uint4(0u, 0u, 0u, 0u);
-  f.bias = -INFINITY;
-  if (u < g.T) {
-    const uint4* kr = (const uint4*)(A.kbar + ((long long)h * g.T + u) * D + 8 * c);
-    const uint4* vr = (const uint4*)(A.vbar + ((long long)h * g.T + u) * D + 8 * c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.k[i] = kr[i];
-    f.v[0] = vr[0];
-    f.v[1] = vr[1];
-    const char* kb = lm_kblock(g, A.LM, h, b);
-    f.bias = ((mask >> key) & 1u) ? -INFINITY : ((const float*)(kb + LM_LOG2N_ROW * 128))[key];
-  }
-}
-
-// The landmarks as bf16 high parts into sK, sV and low parts into sK2, sV2
-// (the landmarks are means of similar tiles, so the query gradient is a
-// small remainder of their sum, which a single rounding would swamp).
-__device__ inline void commit_landmark_block(const LandmarkFetch& f, u16* sK, u16* sV, u16* sK2, u16* sV2,
-                                             float* sB) {
-  const int tid = threadIdx.x, key = tid >> 3, c = tid & 7;
-  float kv[8], vv[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const double2 d2 = __builtin_bit_cast(double2, f.k[i]);
-    kv[2 * i] = (float)d2.x;
-    kv[2 * i + 1] = (float)d2.y;
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float4 v4 = __builtin_bit_cast(float4, f.v[i]);
-    vv[4 * i] = v4.x;
-    vv[4 * i + 1] = v4.y;
-    vv[4 * i + 2] = v4.z;
-    vv[4 * i + 3] = v4.w;
-  }
-  uint4 kh, kl, vh, vl;
-  split8(kv, kh, kl);
-  split8(vv, vh, vl);
-  *(uint4*)(sK + sb_off(key, 8 * c)) = kh;
-  *(uint4*)(sV + sb_off(key, 8 * c)) = vh;
-  *(uint4*)(sK2 + sb_off(key, 8 * c)) = kl;
-  *(uint4*)(sV2 + sb_off(key, 8 * c)) = vl;
-  if (c == 0) sB[key] = f.bias;
 }
 
 // grid (units, H), block 256: one query unit (up to 64 rows, 16 per wave).
@@ -446,22 +412,31 @@ __global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs
       if (kind == 0 ? unit_rows(g, blk) > 32 : 64 * blk + 32 < g.nspec) block(kind, 1);
     }
   }
-  // landmark blocks (patch rows), staged as they come: fetching them ahead
-  // would hold their larger fp64 / fp32 loads in registers through every
-  // token block
-  for (int b = 0; b < nlb; ++b) {
-    __syncthreads();
+  // landmark blocks (patch rows): their precomputed bf16 parts copied into
+  // the LDS tiles as they are (async 16-byte copies, wave w one part), and
+  // the row's biases (log2 n_u; -inf past the last tile or where the row's
+  // tile keeps it)
+  {
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    u16* dpart = wu == 0 ? sK : wu == 1 ? sV : wu == 2 ? sK2 : sV2;
+    for (int b = 0; b < nlb; ++b) {
+      __syncthreads();  // the previous block's reads are done
+      const u16* src = A.lmp + (((long long)h * nlb + b) * 4 + wu) * 64 * D + 8 * lane;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int b32 = 2 * b + sub;
-      LandmarkFetch lf;
-      fetch_landmark_block(g, A, h, b32, b32 < A.nw ? mrow[b32] : ~0u, lf);
-      commit_landmark_block(lf, sK + sub * 32 * D, sV + sub * 32 * D, sK2 + sub * 32 * D, sV2 + sub * 32 * D,
-                            sB + 32 * sub);
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 512 * i), (sb_lds_void*)(dpart + 512 * i), 16, 0, 0);
+      if (threadIdx.x < 64) {
+        const int t = threadIdx.x, b32 = 2 * b + (t >> 5), key = t & 31;
+        float bias = -INFINITY;
+        if (64 * b + t < g.T && !(((b32 < A.nw ? mrow[b32] : ~0u) >> key) & 1u))
+          bias = ((const float*)(lm_kblock(g, A.LM, h, b32) + LM_LOG2N_ROW * 128))[key];
+        sB[t] = bias;
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+      __syncthreads();
+      block(2, 0);
+      if (64 * b + 32 < g.T) block(2, 1);
     }
-    __syncthreads();
-    block(2, 0);
-    if (64 * b + 32 < g.T) block(2, 1);
   }
   bool self = false;
   if (patch) self = ((mrow[unit >> 5] >> (unit & 31)) & 1u) == 0;
@@ -868,11 +843,13 @@ size_t sparse_bwd_workspace_bytes(const Geom& g) {
   const size_t selT = (size_t)g.H * g.T * nw * sizeof(unsigned);
   const size_t part = (size_t)SB_CHUNKS * g.H * (g.spec_pad + g.T_pad) * 2 * D * sizeof(float);
   const size_t lgrad = (size_t)g.H * g.T * 2 * D * sizeof(float);
-  return stats + selT + part + lgrad + 256 * 4;
+  const size_t lmp = (size_t)g.H * ((g.T + 63) / 64) * 4 * 64 * D * sizeof(u16);
+  return stats + selT + part + lgrad + lmp + 256 * 5;
 }
 
 // Workspace: lse [H][N], dsum [H][N] fp32; selT [H][T][nw]; the global-key
-// partials [SB_CHUNKS][H][spec_pad + T_pad][2][64] fp32; lgrad [H][T][2][64].
+// partials [SB_CHUNKS][H][spec_pad + T_pad][2][64] fp32; lgrad [H][T][2][64];
+// the landmark parts [H][ceil(T / 64)][4][64][64] bf16.
 hipError_t launch_sparse_bwd(const Geom& g, int keep, const u16* Q, const u16* K, const u16* V, const u16* dO,
                              long long o_tok, long long o_head, const u16* LM, const double* kbar,
                              const float* vbar, const int* sel,
@@ -898,6 +875,8 @@ hipError_t launch_sparse_bwd(const Geom& g, int keep, const u16* Q, const u16* K
   A.part = (float*)p;
   p = align((char*)(A.part + (size_t)SB_CHUNKS * g.H * (g.spec_pad + g.T_pad) * 2 * D));
   A.lgrad = (float*)p;
+  p = align((char*)(A.lgrad + (size_t)g.H * g.T * 2 * D));
+  A.lmp = (u16*)p;
   A.dQ = dQ;
   A.dK = dK;
   A.dV = dV;
@@ -906,6 +885,7 @@ hipError_t launch_sparse_bwd(const Geom& g, int keep, const u16* Q, const u16* K
   A.o_tok = o_tok;
   A.o_head = o_head;
   const int nunits = g.T + (g.nspec + 63) / 64;
+  hipLaunchKernelGGL(sbwd_lmparts_kernel, dim3((g.T + 63) / 64, g.H), dim3(256), 0, s, g, A, (g.T + 63) / 64);
   hipLaunchKernelGGL(sbwd_rows_kernel<SB_STATS>, dim3(nunits, g.H), dim3(SB_THREADS), 0, s, g, A);
   hipLaunchKernelGGL(sbwd_rows_kernel<SB_DQ>, dim3(nunits, g.H), dim3(SB_THREADS), 0, s, g, A);
   hipLaunchKernelGGL(sbwd_transpose_kernel, dim3((nw + 1) / 2, nw, g.H), dim3(64), 0, s, g, selmask, A.selT, nw);

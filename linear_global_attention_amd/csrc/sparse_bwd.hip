@@ -235,58 +235,11 @@ __global__ void __launch_bounds__(256) sbwd_lmparts_kernel(Geom g, SbArgs A, int
   }
 }
 
-// One thread's share of a 64-key token or special block, loaded ahead of
-// its use: keys tid / 8 and 32 + tid / 8, channels 8 (tid % 8) .. +7 of K
-// and V (bf16), and their logit biases (log2 units: 0, or -inf for keys
-// past the end).
-struct KeyFetch {
-  uint4 k[2], v[2];
-  float bias[2];
-};
-
-// Key block `blk` of kind 0 (the keys of tile blk) or kind 1 (special keys
-// 64 blk ..).
-__device__ inline void fetch_key_block(const Geom& g, const SbArgs& A, int h, int kind, int blk, KeyFetch& f) {
-  const int tid = threadIdx.x, c = tid & 7;
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int key = (tid >> 3) + 32 * e;
-    f.k[e] = f.v[e] = make_uint4(0u, 0u, 0u, 0u);
-    f.bias[e] = -INFINITY;
-    long long tok = -1;
-    if (kind == 0) {
-      if (key < unit_rows(g, blk)) tok = unit_token(g, blk, key);
-    } else {
-      const int i = 64 * blk + key;
-      if (i < g.nspec) tok = special_token(g, i);
-    }
-    if (tok >= 0) {
-      const long long row = tok * g.in_tok + (long long)h * g.in_head;
-      f.k[e] = *(const uint4*)(A.K + row + 8 * c);
-      f.v[e] = *(const uint4*)(A.V + row + 8 * c);
-      f.bias[e] = 0.f;
-    }
-  }
-}
-
-// Writes a fetched share into the 64-row LDS tiles (keys past the end: zero
-// rows, bias -inf).
-__device__ inline void commit_key_block(const KeyFetch& f, u16* sK, u16* sV, float* sB) {
-  const int tid = threadIdx.x, c = tid & 7;
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int key = (tid >> 3) + 32 * e;
-    *(uint4*)(sK + sb_off(key, 8 * c)) = f.k[e];
-    *(uint4*)(sV + sb_off(key, 8 * c)) = f.v[e];
-    if (c == 0) sB[key] = f.bias[e];
-  }
-}
-
 // grid (units, H), block 256: one query unit (up to 64 rows, 16 per wave).
 template <int MODE>
 __global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs A) {
   __shared__ __attribute__((aligned(16))) u16 sK[64 * D], sV[64 * D], sK2[64 * D], sV2[64 * D];
-  __shared__ __attribute__((aligned(16))) float sB[64];
+  __shared__ __attribute__((aligned(16))) float sB[64], sB2[64];
   const int unit = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lg = lane >> 4, tl = lane & 15;
@@ -315,12 +268,12 @@ __global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs
   for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // 32 staged keys (rows 32 sub .. of the LDS tiles) against the wave's rows
-  auto block = [&](int kind, int sub) {
-    const u16* tK = sK + sub * 32 * D;
-    const u16* tV = sV + sub * 32 * D;
+  auto block = [&](int kind, int sub, const u16* bK, const u16* bV, const float* bB) {
+    const u16* tK = bK + sub * 32 * D;
+    const u16* tV = bV + sub * 32 * D;
     const u16* tK2 = sK2 + sub * 32 * D;
     const u16* tV2 = sV2 + sub * 32 * D;
-    const float* tB = sB + 32 * sub;
+    const float* tB = bB + 32 * sub;
     f32x4 s[2], dp[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -375,8 +328,6 @@ __global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs
 
   // The unit's key blocks in order, 64 keys each: its kept tiles (all tiles
   // for special rows), the special keys, then (patch rows) the landmarks.
-  // Token and special blocks are fetched into registers one block ahead,
-  // so that their loads overlap the previous block's work.
   const int* kept = A.sel + ((long long)h * g.T + unit) * A.keep;
   const unsigned* mrow = A.selmask + ((long long)h * g.T + (patch ? unit : 0)) * A.nw;
   const int ntb = patch ? A.keep : g.T, nsb = (g.nspec + 63) / 64, nlb = patch ? (g.T + 63) / 64 : 0;
@@ -390,34 +341,56 @@ __global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs
       blk = i - ntb;
     }
   };
-  {
-    KeyFetch f;
-    if (nblk > 0) {
-      int kind, blk;
-      desc(0, kind, blk);
-      fetch_key_block(g, A, h, kind, blk, f);
+  // Token and special blocks go into LDS by async 16-byte copies, one block
+  // ahead, alternating between two buffers: (sK, sV, sB) and (sK2, sV2,
+  // sB2), the landmark low-part tiles, which are free until the landmark
+  // blocks. The loop is unrolled over the two buffers so that every LDS
+  // access names its array and the compiler sees that the fragment reads
+  // miss the copies in flight. One barrier per block.
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  auto block_keys = [&](int kind, int blk) { return kind == 0 ? unit_rows(g, blk) : min(64, g.nspec - 64 * blk); };
+  // (kind, blk) of block i come back to the caller, which hands them to
+  // compute: a second read of the kept-tile list there would be a memory
+  // load issued after the next block's copies, and waiting for it would
+  // wait for them too
+  auto issue = [&](int i, u16* bK, u16* bV, float* bB, int& kind, int& blk) __attribute__((always_inline)) {
+    desc(i, kind, blk);
+    const int nk = block_keys(kind, blk);
+    // wave w copies rows 16 w + 8 j + lane / 8, source chunk (lane % 8) ^
+    // (row % 8), so that LDS holds the sb_off layout; rows past the last
+    // key repeat it (their bias is -inf, so they add exact zeros)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r0 = 16 * wu + 8 * j, r = r0 + (lane >> 3), rr = min(r, nk - 1);
+      const long long tok = kind == 0 ? unit_token(g, blk, rr) : special_token(g, 64 * blk + rr);
+      const long long src = tok * g.in_tok + (long long)h * g.in_head + 8 * ((lane & 7) ^ (r & 7));
+      __builtin_amdgcn_global_load_lds((const void*)(A.K + src), (sb_lds_void*)(bK + r0 * D), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(A.V + src), (sb_lds_void*)(bV + r0 * D), 16, 0, 0);
     }
-    for (int i = 0; i < nblk; ++i) {
-      int kind, blk;
-      desc(i, kind, blk);
-      __syncthreads();  // the previous block's reads are done
-      commit_key_block(f, sK, sV, sB);
-      if (i + 1 < nblk) {
-        int kn, bn;
-        desc(i + 1, kn, bn);
-        fetch_key_block(g, A, h, kn, bn, f);
-      }
-      __syncthreads();
-      block(kind, 0);
-      if (kind == 0 ? unit_rows(g, blk) > 32 : 64 * blk + 32 < g.nspec) block(kind, 1);
-    }
+    if (threadIdx.x < 64) bB[threadIdx.x] = (int)threadIdx.x < nk ? 0.f : -INFINITY;
+  };
+  auto compute = [&](int kind, int blk, const u16* bK, const u16* bV, const float* bB) __attribute__((always_inline)) {
+    block(kind, 0, bK, bV, bB);
+    if (block_keys(kind, blk) > 32) block(kind, 1, bK, bV, bB);
+  };
+  int k0 = 0, b0 = 0, k1 = 0, b1 = 0;  // (kind, blk) of the block in each buffer
+  if (nblk > 0) issue(0, sK, sV, sB, k0, b0);
+  for (int i = 0; i < nblk; i += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of block i have landed
+    __syncthreads();  // ... in every wave, and block i - 1 is read
+    if (i + 1 < nblk) issue(i + 1, sK2, sV2, sB2, k1, b1);
+    compute(k0, b0, sK, sV, sB);
+    if (i + 1 >= nblk) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (i + 2 < nblk) issue(i + 2, sK, sV, sB, k0, b0);
+    compute(k1, b1, sK2, sV2, sB2);
   }
   // landmark blocks (patch rows): their precomputed bf16 parts copied into
   // the LDS tiles as they are (async 16-byte copies, wave w one part), and
   // the row's biases (log2 n_u; -inf past the last tile or where the row's
   // tile keeps it)
   {
-    const int wu = __builtin_amdgcn_readfirstlane(wave);
     u16* dpart = wu == 0 ? sK : wu == 1 ? sV : wu == 2 ? sK2 : sV2;
     for (int b = 0; b < nlb; ++b) {
       __syncthreads();  // the previous block's reads are done
@@ -434,8 +407,8 @@ __global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
       __syncthreads();
-      block(2, 0);
-      if (64 * b + 32 < g.T) block(2, 1);
+      block(2, 0, sK, sV, sB);
+      if (64 * b + 32 < g.T) block(2, 1, sK, sV, sB);
     }
   }
   bool self = false;

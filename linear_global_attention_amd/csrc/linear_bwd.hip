@@ -264,6 +264,31 @@ __device__ inline void mat_times(const bf16x8* Mhi, const bf16x8* Mlo, const bf1
   }
 }
 
+// Swizzle of the 16-byte chunks of row r in a wave's 16-row staging tile.
+__device__ inline int lb_swz(int r) { return (r ^ (r >> 2)) & 7; }
+
+// A group's 16 output rows, given in the feature-map lane layout (lane
+// (tl, grp): token tl, channels ch(grp, i) in v), stored as bf16 through the
+// wave's 2 KB LDS tile xs so that 8 lanes write each 128-byte row whole:
+// lane l stores chunk l % 8 of rows l / 8 and 8 + l / 8 (rows of tokens at
+// or past t_end, i.e. r >= valid, are not stored).
+__device__ inline void lb_store_rows(u16* xs, const float v[16], int lane, u16* out0, long long tok_stride,
+                                     int valid) {
+  const int grp = lane >> 4, tl = lane & 15;
+  __builtin_amdgcn_wave_barrier();  // the tile's previous reads come first
+#pragma unroll
+  for (int q = 0; q < 4; ++q)  // channels 16 q + 4 grp .. +3: chunk 2 q + grp / 2, half grp % 2
+    *(uint2*)(xs + tl * D + (((2 * q + (grp >> 1)) ^ lb_swz(tl)) << 3) + (grp & 1) * 4) =
+        make_uint2(pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3]));
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * j + (lane >> 3);
+    const uint4 c = *(const uint4*)(xs + r * D + (((lane & 7) ^ lb_swz(r)) << 3));
+    if (r < valid) *(uint4*)(out0 + r * tok_stride + (lane & 7) * 8) = c;
+  }
+}
+
 // The lane's 16 channels of a bf16 row (ch(grp, i), i = 4q + j at
 // 16q + 4grp + j) as 4 x 8 bytes.
 __device__ inline void store16(u16* row, int grp, const float v[16]) {
@@ -551,8 +576,9 @@ __global__ void __launch_bounds__(LIN_THREADS, 3) linear_bwd_key_kernel(
     Geom g, LinParams P, const u16* __restrict__ K, const u16* __restrict__ V, const float* __restrict__ gk,
     const u16* __restrict__ ops, const float* __restrict__ dzv, const float* __restrict__ mean,
     u16* __restrict__ dK, u16* __restrict__ dV, int tpw) {
-  __shared__ __attribute__((aligned(16))) float2 tab[MAX_GRID * RT_STRIDE];
+  float2* tab = rope_tab;  // max(R, C) * RT_STRIDE entries (dynamic LDS)
   __shared__ __attribute__((aligned(16))) u16 sops[LB_OPS];
+  __shared__ __attribute__((aligned(16))) u16 sxo[LIN_WAVES][16 * D];  // per wave: a group's output rows
   const int h = blockIdx.y, chunk = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, tl = lane & 15;
@@ -585,8 +611,6 @@ __global__ void __launch_bounds__(LIN_THREADS, 3) linear_bwd_key_kernel(
   if (n > 0) fetch(0, nk, nv);
   int loc = token_loc(g, dv, first + tl);  // frame position of this lane's token of group m
   for (int m = 0; m < n; ++m) {
-    const long long tok = first + 64LL * m + tl;
-    const bool valid = tok < t_end;
     // the operand fragments are read from LDS where they are used, not
     // hoisted out of the loop into 128 registers
     asm volatile("" ::: "memory");
@@ -613,7 +637,10 @@ __global__ void __launch_bounds__(LIN_THREADS, 3) linear_bwd_key_kernel(
     mat_times(F, F + 8 * 64, uh, ul, lane, acc);
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[i] = acc[i >> 2][i & 3];
-    if (valid) store16(dV + tok * g.in_tok + (long long)h * g.in_head, grp, o);
+    const int nvalid = (int)min(16LL, t_end - (first + 64LL * m));  // rows of the group before t_end
+    u16* xo = &sxo[__builtin_amdgcn_readfirstlane(wave)][0];
+    const long long orow0 = (first + 64LL * m) * g.in_tok + (long long)h * g.in_head;
+    lb_store_rows(xo, o, lane, dV + orow0, g.in_tok, nvalid);
     // dphi(k) = dS (v - m) + dzt
     unpack16(wv, o);
     {
@@ -629,7 +656,7 @@ __global__ void __launch_bounds__(LIN_THREADS, 3) linear_bwd_key_kernel(
     for (int i = 0; i < 16; ++i) o[i] += acc[i >> 2][i & 3];
     lds16(sgain, grp, gain);
     row_backward(R, o, gk != nullptr, gain);
-    if (valid) store16(dK + tok * g.in_tok + (long long)h * g.in_head, grp, o);
+    lb_store_rows(xo, o, lane, dK + orow0, g.in_tok, nvalid);
   }
 }
 
@@ -664,7 +691,8 @@ hipError_t launch_linear_bwd(const Geom& g, float eps, float base, const u16* Q,
                      (const u16*)opsq, (const float*)zq, dQ, parts, nch, tpw);
   launch_linear_sum(g, parts, nch, quarters, s);
   hipLaunchKernelGGL(linear_bwd_ops_kernel, dim3(g.H), dim3(256), 0, s, (const double*)quarters, W, 0, opsk, dzk, nullptr);
-  hipLaunchKernelGGL(linear_bwd_key_kernel, dim3(nch, g.H), dim3(LIN_THREADS), 0, s, g, P, K, V, gk,
+  hipLaunchKernelGGL(linear_bwd_key_kernel, dim3(nch, g.H), dim3(LIN_THREADS),
+                     (size_t)max(g.R, g.C) * RT_STRIDE * sizeof(float2), s, g, P, K, V, gk,
                      (const u16*)opsk, (const float*)dzk, (const float*)mean, dK, dV, tpw);
   return hipGetLastError();
 }

@@ -267,12 +267,28 @@ __device__ inline void mat_times(const bf16x8* Mhi, const bf16x8* Mlo, const bf1
 // Swizzle of the 16-byte chunks of row r in a wave's 16-row staging tile.
 __device__ inline int lb_swz(int r) { return (r ^ (r >> 2)) & 7; }
 
+// A group's 16 bf16 rows, loaded as whole 16-byte chunks (lane l: chunk
+// l % 8 of row l / 8 in c0, of row 8 + l / 8 in c1), into the feature-map
+// lane layout through the wave's 2 KB LDS tile xs: w[q] = channels
+// 16 q + 4 grp .. +3 of token tl, the pieces unpack16 takes.
+__device__ __forceinline__ void lb_relayout(u16* xs, uint4 c0, uint4 c1, int lane, uint2 w[4]) {
+  const int grp = lane >> 4, tl = lane & 15;
+  __builtin_amdgcn_wave_barrier();  // the tile's previous reads come first
+  const int r0 = lane >> 3, r1 = 8 + (lane >> 3);
+  *(uint4*)(xs + r0 * D + (((lane & 7) ^ lb_swz(r0)) << 3)) = c0;
+  *(uint4*)(xs + r1 * D + (((lane & 7) ^ lb_swz(r1)) << 3)) = c1;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < 4; ++q)  // channels 16 q + 4 grp .. +3: chunk 2 q + grp / 2, half grp % 2
+    w[q] = *(const uint2*)(xs + tl * D + (((2 * q + (grp >> 1)) ^ lb_swz(tl)) << 3) + (grp & 1) * 4);
+}
+
 // A group's 16 output rows, given in the feature-map lane layout (lane
 // (tl, grp): token tl, channels ch(grp, i) in v), stored as bf16 through the
 // wave's 2 KB LDS tile xs so that 8 lanes write each 128-byte row whole:
 // lane l stores chunk l % 8 of rows l / 8 and 8 + l / 8 (rows of tokens at
 // or past t_end, i.e. r >= valid, are not stored).
-__device__ inline void lb_store_rows(u16* xs, const float v[16], int lane, u16* out0, long long tok_stride,
+__device__ __forceinline__ void lb_store_rows(u16* xs, const float v[16], int lane, u16* out0, long long tok_stride,
                                      int valid) {
   const int grp = lane >> 4, tl = lane & 15;
   __builtin_amdgcn_wave_barrier();  // the tile's previous reads come first
@@ -421,25 +437,27 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_bwd_state_kernel(
   const long long first = t_begin + 16 * wave;
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
   // the rows of the next group are loaded while this group is processed
-  auto fetch = [&](int m, uint2 (&a)[4], uint2 (&b)[4]) {
-    const long long tk = min(first + 64LL * m + tl, t_end - 1);
-    const long long row = tk * g.in_tok + (long long)h * g.in_head;
-    fetch16(K + row, grp, true, a);
-    fetch16(V + row, grp, true, b);
+  // as whole 16-byte chunks (rows l / 8 and 8 + l / 8, chunk l % 8), put
+  // into the lane layout through the first scratch tile
+  uint4 nk0, nk1, nv0, nv1;
+  auto fetch = [&](int m) __attribute__((always_inline)) {
+    const long long t0 = min(first + 64LL * m + (lane >> 3), t_end - 1);
+    const long long t1 = min(first + 64LL * m + 8 + (lane >> 3), t_end - 1);
+    const long long c = (long long)h * g.in_head + (lane & 7) * 8;
+    nk0 = *(const uint4*)(K + t0 * g.in_tok + c);
+    nv0 = *(const uint4*)(V + t0 * g.in_tok + c);
+    nk1 = *(const uint4*)(K + t1 * g.in_tok + c);
+    nv1 = *(const uint4*)(V + t1 * g.in_tok + c);
   };
-  uint2 nk[4], nv[4];
-  if (n > 0) fetch(0, nk, nv);
+  if (n > 0) fetch(0);
   int loc = token_loc(g, dv, first + tl);  // frame position of this lane's token of group m
   for (int m = 0; m < n; ++m) {
     const long long tok = first + 64LL * m + tl;
     const bool valid = tok < t_end;
     uint2 wk[4], wv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wk[i] = nk[i];
-      wv[i] = nv[i];
-    }
-    if (m + 1 < n) fetch(m + 1, nk, nv);
+    lb_relayout(xs, nk0, nk1, lane, wk);
+    lb_relayout(xs, nv0, nv1, lane, wv);
+    if (m + 1 < n) fetch(m + 1);
     RowFwd R;
     unpack16(wk, R.x);
     int pr = 0, pc = 0;
@@ -504,24 +522,27 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_bwd_query_kernel(
   const long long first = t_begin + 16 * wave;
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
   // the rows of the next group are loaded while this group is processed
-  auto fetch = [&](int m, uint2 (&a)[4], uint2 (&b)[4]) {
-    const long long tk = min(first + 64LL * m + tl, t_end - 1);
-    fetch16(Q + tk * g.in_tok + (long long)h * g.in_head, grp, true, a);
-    fetch16(dY + tk * g.out_tok + (long long)h * g.out_head, grp, true, b);
+  // as whole 16-byte chunks (rows l / 8 and 8 + l / 8, chunk l % 8), put
+  // into the lane layout through the first scratch tile
+  uint4 nq0, nq1, nd0, nd1;
+  auto fetch = [&](int m) __attribute__((always_inline)) {
+    const long long t0 = min(first + 64LL * m + (lane >> 3), t_end - 1);
+    const long long t1 = min(first + 64LL * m + 8 + (lane >> 3), t_end - 1);
+    const long long cq = (long long)h * g.in_head + (lane & 7) * 8, cd = (long long)h * g.out_head + (lane & 7) * 8;
+    nq0 = *(const uint4*)(Q + t0 * g.in_tok + cq);
+    nd0 = *(const uint4*)(dY + t0 * g.out_tok + cd);
+    nq1 = *(const uint4*)(Q + t1 * g.in_tok + cq);
+    nd1 = *(const uint4*)(dY + t1 * g.out_tok + cd);
   };
-  uint2 nq[4], nd[4];
-  if (n > 0) fetch(0, nq, nd);
+  if (n > 0) fetch(0);
   int loc = token_loc(g, dv, first + tl);  // frame position of this lane's token of group m
   for (int m = 0; m < n; ++m) {
     const long long tok = first + 64LL * m + tl;
     const bool valid = tok < t_end;
     uint2 wq[4], wd[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wq[i] = nq[i];
-      wd[i] = nd[i];
-    }
-    if (m + 1 < n) fetch(m + 1, nq, nd);
+    lb_relayout(xs, nq0, nq1, lane, wq);
+    lb_relayout(xs, nd0, nd1, lane, wd);
+    if (m + 1 < n) fetch(m + 1);
     RowFwd R;
     unpack16(wq, R.x);
     int pr = 0, pc = 0;
@@ -601,26 +622,27 @@ __global__ void __launch_bounds__(LIN_THREADS, 3) linear_bwd_key_kernel(
   const long long first = t_begin + 16 * wave;
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
   // the rows of the next group are loaded while this group is processed
-  auto fetch = [&](int m, uint2 (&a)[4], uint2 (&b)[4]) {
-    const long long tk = min(first + 64LL * m + tl, t_end - 1);
-    const long long row = tk * g.in_tok + (long long)h * g.in_head;
-    fetch16(K + row, grp, true, a);
-    fetch16(V + row, grp, true, b);
+  uint4 nk0, nk1, nv0, nv1;
+  auto fetch = [&](int m) __attribute__((always_inline)) {
+    const long long t0 = min(first + 64LL * m + (lane >> 3), t_end - 1);
+    const long long t1 = min(first + 64LL * m + 8 + (lane >> 3), t_end - 1);
+    const long long c = (long long)h * g.in_head + (lane & 7) * 8;
+    nk0 = *(const uint4*)(K + t0 * g.in_tok + c);
+    nv0 = *(const uint4*)(V + t0 * g.in_tok + c);
+    nk1 = *(const uint4*)(K + t1 * g.in_tok + c);
+    nv1 = *(const uint4*)(V + t1 * g.in_tok + c);
   };
-  uint2 nk[4], nv[4];
-  if (n > 0) fetch(0, nk, nv);
+  if (n > 0) fetch(0);
+  u16* xo = &sxo[__builtin_amdgcn_readfirstlane(wave)][0];
   int loc = token_loc(g, dv, first + tl);  // frame position of this lane's token of group m
   for (int m = 0; m < n; ++m) {
     // the operand fragments are read from LDS where they are used, not
     // hoisted out of the loop into 128 registers
     asm volatile("" ::: "memory");
     uint2 wk[4], wv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wk[i] = nk[i];
-      wv[i] = nv[i];
-    }
-    if (m + 1 < n) fetch(m + 1, nk, nv);
+    lb_relayout(xo, nk0, nk1, lane, wk);
+    lb_relayout(xo, nv0, nv1, lane, wv);
+    if (m + 1 < n) fetch(m + 1);
     RowFwd R;
     unpack16(wk, R.x);
     int pr = 0, pc = 0;
@@ -638,7 +660,6 @@ __global__ void __launch_bounds__(LIN_THREADS, 3) linear_bwd_key_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[i] = acc[i >> 2][i & 3];
     const int nvalid = (int)min(16LL, t_end - (first + 64LL * m));  // rows of the group before t_end
-    u16* xo = &sxo[__builtin_amdgcn_readfirstlane(wave)][0];
     const long long orow0 = (first + 64LL * m) * g.in_tok + (long long)h * g.in_head;
     lb_store_rows(xo, o, lane, dV + orow0, g.in_tok, nvalid);
     // dphi(k) = dS (v - m) + dzt

@@ -522,27 +522,24 @@ __global__ void __launch_bounds__(LIN_THREADS, 2) linear_bwd_query_kernel(
   const long long first = t_begin + 16 * wave;
   const int n = first < t_end ? (int)((t_end - first + 16 * LIN_WAVES - 1) / (16 * LIN_WAVES)) : 0;
   // the rows of the next group are loaded while this group is processed
-  // as whole 16-byte chunks (rows l / 8 and 8 + l / 8, chunk l % 8), put
-  // into the lane layout through the first scratch tile
-  uint4 nq0, nq1, nd0, nd1;
-  auto fetch = [&](int m) __attribute__((always_inline)) {
-    const long long t0 = min(first + 64LL * m + (lane >> 3), t_end - 1);
-    const long long t1 = min(first + 64LL * m + 8 + (lane >> 3), t_end - 1);
-    const long long cq = (long long)h * g.in_head + (lane & 7) * 8, cd = (long long)h * g.out_head + (lane & 7) * 8;
-    nq0 = *(const uint4*)(Q + t0 * g.in_tok + cq);
-    nd0 = *(const uint4*)(dY + t0 * g.out_tok + cd);
-    nq1 = *(const uint4*)(Q + t1 * g.in_tok + cq);
-    nd1 = *(const uint4*)(dY + t1 * g.out_tok + cd);
+  auto fetch = [&](int m, uint2 (&a)[4], uint2 (&b)[4]) {
+    const long long tk = min(first + 64LL * m + tl, t_end - 1);
+    fetch16(Q + tk * g.in_tok + (long long)h * g.in_head, grp, true, a);
+    fetch16(dY + tk * g.out_tok + (long long)h * g.out_head, grp, true, b);
   };
-  if (n > 0) fetch(0);
+  uint2 nq[4], nd[4];
+  if (n > 0) fetch(0, nq, nd);
   int loc = token_loc(g, dv, first + tl);  // frame position of this lane's token of group m
   for (int m = 0; m < n; ++m) {
     const long long tok = first + 64LL * m + tl;
     const bool valid = tok < t_end;
     uint2 wq[4], wd[4];
-    lb_relayout(xs, nq0, nq1, lane, wq);
-    lb_relayout(xs, nd0, nd1, lane, wd);
-    if (m + 1 < n) fetch(m + 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wq[i] = nq[i];
+      wd[i] = nd[i];
+    }
+    if (m + 1 < n) fetch(m + 1, nq, nd);
     RowFwd R;
     unpack16(wq, R.x);
     int pr = 0, pc = 0;

@@ -168,8 +168,12 @@ __device__ inline unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2_t));
 }
 
-// The lane's 16 channels, given as 4 bf16 pieces (w[q]: channels
-// 16 q + 4 g .. +3), as fp32 in lane order.
+// The lane's 16 channels of one bf16 row, raw (4 x 8 bytes); zeros past the end.
+__device__ inline void fetch16(const u16* row, int g, bool ok, uint2 w[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w[q] = ok ? *(const uint2*)(row + q * 16 + 4 * g) : make_uint2(0u, 0u);
+}
+
 __device__ inline void unpack16(const uint2 w[4], float x[16]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {

@@ -256,13 +256,46 @@ __global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs
     qb[ks] = __builtin_bit_cast(bf16x8, ld16(A.Q, qrow + 32 * ks + 8 * lg, valid));
     ob[ks] = __builtin_bit_cast(bf16x8, ld16(A.dO, orow + 32 * ks + 8 * lg, valid));
   }
-  // per-lane partials (STATS) or the row's statistics (DQ)
-  float m = -1e30f, l = 0.f, dsm = 0.f;
+  // The row's own key: its logit xs and dP (from the lane's 16 channels,
+  // summed over the row's 4 lanes). A patch row always sees its own token
+  // (in its kept tile or as the self key) and a special row sees every
+  // token, so xs is at most the row's largest logit.
+  float xs, dps;
+  {
+    const u16* kr = A.K + qrow;
+    const u16* vr = A.V + qrow;
+    float sq = 0.f, sd = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 kw = ld16(kr, 32 * ks + 8 * lg, valid), vw = ld16(vr, 32 * ks + 8 * lg, valid);
+      const uint4 qw = __builtin_bit_cast(uint4, qb[ks]), ow = __builtin_bit_cast(uint4, ob[ks]);
+      const unsigned qa[4] = {qw.x, qw.y, qw.z, qw.w}, ka[4] = {kw.x, kw.y, kw.z, kw.w};
+      const unsigned oa[4] = {ow.x, ow.y, ow.z, ow.w}, va[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sq = fmaf(__uint_as_float(qa[e] << 16), __uint_as_float(ka[e] << 16), sq);
+        sq = fmaf(__uint_as_float(qa[e] & 0xFFFF0000u), __uint_as_float(ka[e] & 0xFFFF0000u), sq);
+        sd = fmaf(__uint_as_float(oa[e] << 16), __uint_as_float(va[e] << 16), sd);
+        sd = fmaf(__uint_as_float(oa[e] & 0xFFFF0000u), __uint_as_float(va[e] & 0xFFFF0000u), sd);
+      }
+    }
+    xs = sb_sum4(sq) * SB_C;
+    dps = sb_sum4(sd);
+  }
+  // STATS: per-lane partials over the lane's keys, relative to a running
+  // offset m (log2 units) that starts at the own logit and only moves up.
+  // DQ: the row's statistics, which enter as the initial values of the
+  // logit and dP accumulators (-lse / C and -D), so that a logit leaves the
+  // MFMAs with the row's log-sum-exp taken off and dP with D taken off.
+  // Rows past the unit's end have zero q, dout and statistics, so their dS
+  // is exactly zero and reaches only their own (unwritten) dq column.
+  float m = valid ? xs : 64.f, l = 0.f, dsm = 0.f;  // (past the end: no logit reaches m)
   float lse2 = 0.f, Drow = 0.f;
   if (MODE == SB_DQ && valid) {
     lse2 = A.lse[(long long)h * g.N + tok];
     Drow = A.dsum[(long long)h * g.N + tok];
   }
+  const float soff_dq = -lse2 * (1.0f / SB_C), doff_dq = -Drow;
   f32x4 acc[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -274,11 +307,13 @@ __global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs
     const u16* tK2 = sK2 + sub * 32 * D;
     const u16* tV2 = sV2 + sub * 32 * D;
     const float* tB = bB + 32 * sub;
+    const float so = MODE == SB_STATS ? -m * (1.0f / SB_C) : soff_dq;
+    const float dpo = MODE == SB_STATS ? 0.f : doff_dq;
     f32x4 s[2], dp[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[hh] = s[hh];
+      s[hh] = f32x4{so, so, so, so};
+      dp[hh] = f32x4{dpo, dpo, dpo, dpo};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         s[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(tK, hh, ks, lane), qb[ks], s[hh], 0, 0, 0);
@@ -299,23 +334,31 @@ __global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs
       d[i] = dp[i >> 2][i & 3];
     }
     if (MODE == SB_STATS) {
-      float mx = m;
+      // x = logit - m. The offset moves only when some lane of the wave
+      // sees a logit above its own m (a wave-uniform branch, taken on a
+      // few percent of the blocks); the other lanes shift by zero.
+      float bm = x[0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, x[i]);
-      const float sc = __builtin_amdgcn_exp2f(m - mx);
-      l *= sc;
-      dsm *= sc;
+      for (int i = 1; i < 8; ++i) bm = fmaxf(bm, x[i]);
+      if (__builtin_amdgcn_ballot_w64(bm > 0.f)) {
+        const float sh = fmaxf(bm, 0.f), sc = __builtin_amdgcn_exp2f(-sh);
+        m += sh;
+        l *= sc;
+        dsm *= sc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] -= sh;
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(x[i] - mx);
+        const float p = __builtin_amdgcn_exp2f(x[i]);
         l += p;
         dsm = fmaf(p, d[i], dsm);
       }
-      m = mx;
     } else {
+      // x = logit - lse, d = dP - D
       float ds[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ds[i] = valid ? __builtin_amdgcn_exp2f(x[i] - lse2) * (d[i] - Drow) : 0.f;
+      for (int i = 0; i < 8; ++i) ds[i] = __builtin_amdgcn_exp2f(x[i]) * d[i];
       const bf16x8 dsb = pack8(ds);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
@@ -411,32 +454,10 @@ __global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs
       if (64 * b + 32 < g.T) block(2, 1, sK, sV, sB);
     }
   }
+  // the self key: a patch row whose own tile is not kept attends to its
+  // own key (logit xs, dP dps from above)
   bool self = false;
   if (patch) self = ((mrow[unit >> 5] >> (unit & 31)) & 1u) == 0;
-  // the self key (a patch row whose own tile is not kept): its logit and
-  // dP from the lane's 16 channels, summed over the row's 4 lanes
-  float xs = -INFINITY, dps = 0.f;
-  if (self) {
-    const u16* kr = A.K + qrow;
-    const u16* vr = A.V + qrow;
-    float sq = 0.f, sd = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint4 kw = ld16(kr, 32 * ks + 8 * lg, valid), vw = ld16(vr, 32 * ks + 8 * lg, valid);
-      const uint4 qw = __builtin_bit_cast(uint4, qb[ks]), ow = __builtin_bit_cast(uint4, ob[ks]);
-      const unsigned qa[4] = {qw.x, qw.y, qw.z, qw.w}, ka[4] = {kw.x, kw.y, kw.z, kw.w};
-      const unsigned oa[4] = {ow.x, ow.y, ow.z, ow.w}, va[4] = {vw.x, vw.y, vw.z, vw.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sq = fmaf(__uint_as_float(qa[e] << 16), __uint_as_float(ka[e] << 16), sq);
-        sq = fmaf(__uint_as_float(qa[e] & 0xFFFF0000u), __uint_as_float(ka[e] & 0xFFFF0000u), sq);
-        sd = fmaf(__uint_as_float(oa[e] << 16), __uint_as_float(va[e] << 16), sd);
-        sd = fmaf(__uint_as_float(oa[e] & 0xFFFF0000u), __uint_as_float(va[e] & 0xFFFF0000u), sd);
-      }
-    }
-    xs = sb_sum4(sq) * SB_C;
-    dps = sb_sum4(sd);
-  }
   if (MODE == SB_STATS) {
     if (self && lg == 0) {  // one of the row's 4 lanes counts the self key
       const float mx = fmaxf(m, xs), sc = __builtin_amdgcn_exp2f(m - mx), p = __builtin_amdgcn_exp2f(xs - mx);
@@ -589,8 +610,8 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A)
     *(uint4*)(sQ + sb_off(r, 8 * c)) = f.q;
     *(uint4*)(sO + sb_off(r, 8 * c)) = f.o;
     if (c == 0) {
-      sL[r] = f.lse;
-      sD[r] = f.d;
+      sL[r] = -f.lse * (1.0f / SB_C);
+      sD[r] = -f.d;
     }
   };
   // the staged rows against the workgroup's keys; `bias` is this lane's key
@@ -600,11 +621,16 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A)
     const u16* tO = sO;
     const float* tL = sL;
     const float* tD = sD;
+    // lane (key tl, group lg) holds rows 4 lg + r and 16 + 4 lg + r; the
+    // rows' -lse / C and -D are the initial values of the logit and dP
+    // accumulators (rows past the unit's end: -inf and 0, so P = dS = 0)
     f32x4 s[2], dp[2];
+    s[0] = *(const f32x4*)(tL + 4 * lg);
+    s[1] = *(const f32x4*)(tL + 16 + 4 * lg);
+    dp[0] = *(const f32x4*)(tD + 4 * lg);
+    dp[1] = *(const f32x4*)(tD + 16 + 4 * lg);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[hh] = s[hh];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 qa = row_frag(tQ, hh, ks, lane), oa = row_frag(tO, hh, ks, lane);
@@ -616,16 +642,11 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A)
         }
       }
     }
-    // lane (key tl, group lg) holds rows 4 lg + r and 16 + 4 lg + r
-    const float4 l0 = *(const float4*)(tL + 4 * lg), l1 = *(const float4*)(tL + 16 + 4 * lg);
-    const float4 d0 = *(const float4*)(tD + 4 * lg), d1 = *(const float4*)(tD + 16 + 4 * lg);
-    const float lse[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-    const float Dr[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
     float p[8], ds[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(fmaf(s[i >> 2][i & 3], SB_C, bias) - lse[i]);
-      ds[i] = p[i] * (dp[i >> 2][i & 3] - Dr[i]);
+      p[i] = __builtin_amdgcn_exp2f(fmaf(s[i >> 2][i & 3], SB_C, bias));
+      ds[i] = p[i] * dp[i >> 2][i & 3];
     }
     const bf16x8 pb = pack8(p), dsb = pack8(ds);
 #pragma unroll

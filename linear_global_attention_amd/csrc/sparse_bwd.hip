@@ -54,6 +54,36 @@ constexpr int SB_THREADS = 256;                      // 4 waves, 16 rows or keys
 constexpr float SB_C = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
 constexpr int SB_CHUNKS = 8;                         // row chunks of the global-key pass
 
+// Rounds of the query-major passes. Each pass runs as one launch per round
+// of SB_OCC workgroups per compute unit, the workgroups resident at once,
+// so that they start together; special-row units (which walk every key
+// tile in the same order and so stay in step) come first, then the patch
+// units head by head. A patch unit walks its kept tiles in ascending
+// order, and the units of a round drift apart as they go, until an XCD's
+// L2 no longer holds a tile when the next unit reads it: every key tile
+// then crosses the fabric once per unit. So patch units meet at a
+// checkpoint every SB_CK_TILES key tiles. Counters are per XCD group
+// (workgroups are dealt to the XCDs in turn, so the L2 a workgroup shares
+// is that of blockIdx.x % 8); a workgroup goes on once SB_CK_PCT percent of
+// its group's patch units have arrived, or after SB_CK_SPIN polls, so no
+// wait is unbounded. A unit whose kept tiles skip a segment still arrives
+// at the checkpoints in between, and at the remaining ones when its token
+// walk ends, so every checkpoint is reached by every patch unit of the
+// round.
+constexpr int SB_OCC = 4;          // workgroups of the query-major passes per compute unit
+constexpr int SB_XG = 8;           // XCD groups
+constexpr int SB_CK_TILES = 2048;  // key tiles per checkpoint segment
+constexpr int SB_CK_PCT = 85;
+constexpr int SB_CK_SPIN = 1000;
+constexpr int SB_ROUND_MIN = 256;  // smallest round the workspace provides counters for
+
+struct SbRound {
+  int u0;      // first flattened unit of the round
+  int pfirst;  // flattened index of the first patch unit (H x special units per head)
+  int nck;     // checkpoints per walk (segments - 1)
+  int* ck;     // this round's counters [nck][SB_XG], zero at launch
+};
+
 typedef void __attribute__((address_space(3))) sb_lds_void;
 typedef short sb_v4s __attribute__((ext_vector_type(4)));
 typedef void __attribute__((address_space(3))) sb_lds_void;
@@ -175,6 +205,20 @@ __device__ inline const char* lm_kblock(const Geom& g, const u16* LM, int h, int
   return (const char*)LM + (long long)h * g.T_pad * LM_BYTES_PER_TILE + (long long)b * LM_KEY_BLOCK;
 }
 
+// Token of the first key of tile u (row-major within the tile), and u's
+// tile within its frame; no divisions (multiply-high by the frame's and
+// the tile row's reciprocals).
+__device__ inline long long tile_first_token(const Geom& g, int u, int& tl) {
+  const int f = frame_of_tile(g, u);
+  tl = u - f * g.tpf;
+  const int a = g.tc == 1 ? tl : (int)__umulhi((unsigned)tl, g.tc_magic), b = tl - a * g.tc;
+  return (long long)f * g.tok_pf + g.S + (long long)TILE * a * g.C + TILE * b;
+}
+
+// Token offset, from the tile's first token, of its row-major key j (j
+// below the tile's key count) in a tile w tokens wide.
+__device__ inline int in_tile(const Geom& g, int j, int w) { return (j / w) * g.C + j % w; }
+
 // ---------------------------------------------------------------- query-major passes
 
 enum { SB_STATS = 0, SB_DQ = 1 };
@@ -237,10 +281,19 @@ __global__ void __launch_bounds__(256) sbwd_lmparts_kernel(Geom g, SbArgs A, int
 
 // grid (units, H), block 256: one query unit (up to 64 rows, 16 per wave).
 template <int MODE>
-__global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs A) {
+__global__ void __launch_bounds__(SB_THREADS, SB_OCC) sbwd_rows_kernel(Geom g, SbArgs A, SbRound R) {
   __shared__ __attribute__((aligned(16))) u16 sK[64 * D], sV[64 * D], sK2[64 * D], sV2[64 * D];
   __shared__ __attribute__((aligned(16))) float sB[64], sB2[64];
-  const int unit = blockIdx.x, h = blockIdx.y;
+  const int nsu = (g.nspec + 63) / 64;
+  const int uid = R.u0 + blockIdx.x;
+  int unit, h;
+  if (uid < R.pfirst) {
+    h = uid / nsu;
+    unit = g.T + (uid - h * nsu);
+  } else {
+    h = (uid - R.pfirst) / g.T;
+    unit = (uid - R.pfirst) - h * g.T;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lg = lane >> 4, tl = lane & 15;
   const bool patch = unit < g.T;
@@ -391,44 +444,112 @@ __global__ void __launch_bounds__(SB_THREADS, 4) sbwd_rows_kernel(Geom g, SbArgs
   // access names its array and the compiler sees that the fragment reads
   // miss the copies in flight. One barrier per block.
   const int wu = __builtin_amdgcn_readfirstlane(wave);
-  auto block_keys = [&](int kind, int blk) { return kind == 0 ? unit_rows(g, blk) : min(64, g.nspec - 64 * blk); };
-  // (kind, blk) of block i come back to the caller, which hands them to
-  // compute: a second read of the kept-tile list there would be a memory
+  // checkpoints (patch units): the counters of this workgroup's XCD group,
+  // the release target (SB_CK_PCT percent of the group's patch units in the
+  // round: flattened units >= pfirst, so blocks >= bp), and the segment the
+  // walk is in
+  const int xg = blockIdx.x % SB_XG;
+  int* ckg = R.ck + xg;
+  int ck_target = 0;
+  if (patch && R.nck > 0) {
+    const int bp = max(0, R.pfirst - R.u0);
+    auto cnt = [&](int m) { return m > xg ? (m - xg + SB_XG - 1) / SB_XG : 0; };
+    ck_target = ((cnt((int)gridDim.x) - cnt(bp)) * SB_CK_PCT + 99) / 100;
+  }
+  int cseg = 0;
+  // arrive at checkpoints cseg .. c1 - 1 (one arrival per workgroup), then,
+  // if asked, poll until the group's target has arrived at c1 - 1
+  auto cross = [&](int c1, bool wait) __attribute__((always_inline)) {
+    if (threadIdx.x == 0)
+      for (int c = cseg; c < c1; ++c) __hip_atomic_fetch_add(ckg + c * SB_XG, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wait) {
+      int* ctr = ckg + (c1 - 1) * SB_XG;
+#pragma nounroll
+      for (int it = 0; it < SB_CK_SPIN; ++it) {
+        const int v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (v >= ck_target) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    cseg = c1;
+  };
+  // Element offsets, from a token tile's first key row, of this lane's
+  // 16-byte source chunk in each of its two copy rows (16 w + 8 j + lane / 8,
+  // chunk (lane % 8) ^ (row % 8), so that LDS holds the sb_off layout), for
+  // a tile of full width (TILE) and one of the last tile column's width
+  // (computed once: every tile has one of the two widths), and for a row
+  // past the tile's last key, which reads the first key (its bias is -inf,
+  // so it adds exact zeros). The host keeps TILE tile rows of tokens below
+  // 2^31 elements, so the offsets fit 32 bits.
+  const int wlast = g.C - TILE * (g.tc - 1);
+  int cf[2], cl[2], c0[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * wu + 8 * j + (lane >> 3), ch = 8 * ((lane & 7) ^ (r & 7));
+    cf[j] = in_tile(g, r, TILE) * (int)g.in_tok + ch;
+    cl[j] = in_tile(g, r, wlast) * (int)g.in_tok + ch;
+    c0[j] = ch;
+  }
+  // (kind, key count) of block i come back to the caller, which hands them
+  // to compute: a second read of the kept-tile list there would be a memory
   // load issued after the next block's copies, and waiting for it would
   // wait for them too
-  auto issue = [&](int i, u16* bK, u16* bV, float* bB, int& kind, int& blk) __attribute__((always_inline)) {
+  auto issue = [&](int i, u16* bK, u16* bV, float* bB, int& kind, int& nk) __attribute__((always_inline)) {
+    int blk;
     desc(i, kind, blk);
-    const int nk = block_keys(kind, blk);
-    // wave w copies rows 16 w + 8 j + lane / 8, source chunk (lane % 8) ^
-    // (row % 8), so that LDS holds the sb_off layout; rows past the last
-    // key repeat it (their bias is -inf, so they add exact zeros)
+    if (patch && R.nck > 0 && kind == 0) {
+      const int sg = min(blk / SB_CK_TILES, R.nck);
+      if (sg > cseg) cross(sg, true);
+    }
+    // wave w copies rows 16 w + 8 j + lane / 8 (above); rows past a special
+    // block's last key repeat it (bias -inf)
+    if (kind == 0) {
+      // token tile: a uniform base row, per-lane 32-bit offsets
+      int tl;
+      const long long tok0 = tile_first_token(g, blk, tl);
+      nk = tile_n(g, tl);
+      const bool full = tile_w(g, tl) == TILE;
+      const long long base = tok0 * g.in_tok + (long long)h * g.in_head;
+      const u16* kb = A.K + base;
+      const u16* vb = A.V + base;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r0 = 16 * wu + 8 * j, r = r0 + (lane >> 3), rr = min(r, nk - 1);
-      const long long tok = kind == 0 ? unit_token(g, blk, rr) : special_token(g, 64 * blk + rr);
-      const long long src = tok * g.in_tok + (long long)h * g.in_head + 8 * ((lane & 7) ^ (r & 7));
-      __builtin_amdgcn_global_load_lds((const void*)(A.K + src), (sb_lds_void*)(bK + r0 * D), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(A.V + src), (sb_lds_void*)(bV + r0 * D), 16, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        const int r0 = 16 * wu + 8 * j;
+        const unsigned off = (unsigned)(r0 + (lane >> 3) >= nk ? c0[j] : full ? cf[j] : cl[j]);
+        __builtin_amdgcn_global_load_lds((const void*)(kb + off), (sb_lds_void*)(bK + r0 * D), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vb + off), (sb_lds_void*)(bV + r0 * D), 16, 0, 0);
+      }
+    } else {
+      nk = min(64, g.nspec - 64 * blk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r0 = 16 * wu + 8 * j, r = r0 + (lane >> 3);
+        const long long src = special_token(g, 64 * blk + min(r, nk - 1)) * g.in_tok + (long long)h * g.in_head +
+                              8 * ((lane & 7) ^ (r & 7));
+        __builtin_amdgcn_global_load_lds((const void*)(A.K + src), (sb_lds_void*)(bK + r0 * D), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(A.V + src), (sb_lds_void*)(bV + r0 * D), 16, 0, 0);
+      }
     }
     if (threadIdx.x < 64) bB[threadIdx.x] = (int)threadIdx.x < nk ? 0.f : -INFINITY;
   };
-  auto compute = [&](int kind, int blk, const u16* bK, const u16* bV, const float* bB) __attribute__((always_inline)) {
+  auto compute = [&](int kind, int nk, const u16* bK, const u16* bV, const float* bB) __attribute__((always_inline)) {
     block(kind, 0, bK, bV, bB);
-    if (block_keys(kind, blk) > 32) block(kind, 1, bK, bV, bB);
+    if (nk > 32) block(kind, 1, bK, bV, bB);
   };
-  int k0 = 0, b0 = 0, k1 = 0, b1 = 0;  // (kind, blk) of the block in each buffer
-  if (nblk > 0) issue(0, sK, sV, sB, k0, b0);
+  int k0 = 0, n0 = 0, k1 = 0, n1 = 0;  // (kind, key count) of the block in each buffer
+  if (nblk > 0) issue(0, sK, sV, sB, k0, n0);
   for (int i = 0; i < nblk; i += 2) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of block i have landed
     __syncthreads();  // ... in every wave, and block i - 1 is read
-    if (i + 1 < nblk) issue(i + 1, sK2, sV2, sB2, k1, b1);
-    compute(k0, b0, sK, sV, sB);
+    if (i + 1 < nblk) issue(i + 1, sK2, sV2, sB2, k1, n1);
+    compute(k0, n0, sK, sV, sB);
     if (i + 1 >= nblk) break;
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (i + 2 < nblk) issue(i + 2, sK, sV, sB, k0, b0);
-    compute(k1, b1, sK2, sV2, sB2);
+    if (i + 2 < nblk) issue(i + 2, sK, sV, sB, k0, n0);
+    compute(k1, n1, sK2, sV2, sB2);
   }
+  if (patch && cseg < R.nck) cross(R.nck, false);
   // landmark blocks (patch rows): their precomputed bf16 parts copied into
   // the LDS tiles as they are (async 16-byte copies, wave w one part), and
   // the row's biases (log2 n_u; -inf past the last tile or where the row's
@@ -831,19 +952,41 @@ __global__ void __launch_bounds__(128) sbwd_reduce_kernel(Geom g, SbArgs A) {
 
 // ---------------------------------------------------------------- host side
 
+// grid ceil(n / 256), block 256: zero n ints (checkpoint counters)
+__global__ void __launch_bounds__(256) sbwd_zero_kernel(int* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// Checkpoint counters of the query-major passes: [2 passes][rounds][nck][SB_XG],
+// for rounds of at least SB_ROUND_MIN units.
+struct SbCounters {
+  int nck, rounds;
+  size_t ints;
+  explicit SbCounters(const Geom& g) {
+    const int nseg = (g.T + SB_CK_TILES - 1) / SB_CK_TILES;
+    nck = nseg > 1 ? nseg - 1 : 0;
+    const long long units = (long long)g.H * (g.T + (g.nspec + 63) / 64);
+    rounds = (int)((units + SB_ROUND_MIN - 1) / SB_ROUND_MIN);
+    ints = (size_t)2 * rounds * (nck > 0 ? nck : 1) * SB_XG;
+  }
+};
+
 size_t sparse_bwd_workspace_bytes(const Geom& g) {
+  const size_t ck = SbCounters(g).ints * sizeof(int);
   const size_t nw = (size_t)(g.T + 31) / 32;
   const size_t stats = (size_t)2 * g.H * g.N * sizeof(float);
   const size_t selT = (size_t)g.H * g.T * nw * sizeof(unsigned);
   const size_t part = (size_t)SB_CHUNKS * g.H * (g.spec_pad + g.T_pad) * 2 * D * sizeof(float);
   const size_t lgrad = (size_t)g.H * g.T * 2 * D * sizeof(float);
   const size_t lmp = (size_t)g.H * ((g.T + 63) / 64) * 4 * 64 * D * sizeof(u16);
-  return stats + selT + part + lgrad + lmp + 256 * 5;
+  return stats + selT + part + lgrad + lmp + ck + 256 * 6;
 }
 
 // Workspace: lse [H][N], dsum [H][N] fp32; selT [H][T][nw]; the global-key
 // partials [SB_CHUNKS][H][spec_pad + T_pad][2][64] fp32; lgrad [H][T][2][64];
-// the landmark parts [H][ceil(T / 64)][4][64][64] bf16.
+// the landmark parts [H][ceil(T / 64)][4][64][64] bf16; the checkpoint
+// counters of the query-major passes.
 hipError_t launch_sparse_bwd(const Geom& g, int keep, const u16* Q, const u16* K, const u16* V, const u16* dO,
                              long long o_tok, long long o_head, const u16* LM, const double* kbar,
                              const float* vbar, const int* sel,
@@ -871,6 +1014,9 @@ hipError_t launch_sparse_bwd(const Geom& g, int keep, const u16* Q, const u16* K
   A.lgrad = (float*)p;
   p = align((char*)(A.lgrad + (size_t)g.H * g.T * 2 * D));
   A.lmp = (u16*)p;
+  p = align((char*)(A.lmp + (size_t)g.H * ((g.T + 63) / 64) * 4 * 64 * D));
+  const SbCounters ckc(g);
+  int* ck = (int*)p;
   A.dQ = dQ;
   A.dK = dK;
   A.dV = dV;
@@ -878,10 +1024,24 @@ hipError_t launch_sparse_bwd(const Geom& g, int keep, const u16* Q, const u16* K
   A.nw = nw;
   A.o_tok = o_tok;
   A.o_head = o_head;
-  const int nunits = g.T + (g.nspec + 63) / 64;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int rsz = max(SB_OCC * cus, SB_ROUND_MIN);
+  const int total = g.H * (g.T + (g.nspec + 63) / 64);
+  const int ckr = (ckc.nck > 0 ? ckc.nck : 1) * SB_XG;  // counters per round
+  hipLaunchKernelGGL(sbwd_zero_kernel, dim3((unsigned)((ckc.ints + 255) / 256)), dim3(256), 0, s, ck, (int)ckc.ints);
   hipLaunchKernelGGL(sbwd_lmparts_kernel, dim3((g.T + 63) / 64, g.H), dim3(256), 0, s, g, A, (g.T + 63) / 64);
-  hipLaunchKernelGGL(sbwd_rows_kernel<SB_STATS>, dim3(nunits, g.H), dim3(SB_THREADS), 0, s, g, A);
-  hipLaunchKernelGGL(sbwd_rows_kernel<SB_DQ>, dim3(nunits, g.H), dim3(SB_THREADS), 0, s, g, A);
+  for (int pass = 0; pass < 2; ++pass)
+    for (int u0 = 0, r = 0; u0 < total; u0 += rsz, ++r) {
+      const SbRound R{u0, g.H * ((g.nspec + 63) / 64), ckc.nck, ck + ((size_t)pass * ckc.rounds + r) * ckr};
+      const int n = min(rsz, total - u0);
+      if (pass == 0)
+        hipLaunchKernelGGL(sbwd_rows_kernel<SB_STATS>, dim3(n), dim3(SB_THREADS), 0, s, g, A, R);
+      else
+        hipLaunchKernelGGL(sbwd_rows_kernel<SB_DQ>, dim3(n), dim3(SB_THREADS), 0, s, g, A, R);
+    }
   hipLaunchKernelGGL(sbwd_transpose_kernel, dim3((nw + 1) / 2, nw, g.H), dim3(64), 0, s, g, selmask, A.selT, nw);
   if (g.nspec > 0)
     hipLaunchKernelGGL(sbwd_keys_kernel<SB_SPEC>, dim3((g.nspec + 63) / 64, g.H, SB_CHUNKS), dim3(SB_THREADS), 0, s,

@@ -248,3 +248,35 @@ def test_sparse_bwd_32views_rows_and_invariants():
         n = grad_close(got[:, None, :], ref[:, None, :], f"32 views sparse backward dq rows, head {h}",
                        SPARSE_ROW_REL, SPARSE_HEAD_REL)
         assert n == 0
+
+
+def test_sparse_bwd_128views_checkpoints():
+    """128 views of 37x37 patches (3,200 key tiles, so the query-major
+    passes' patch units meet at a checkpoint), 2 heads, y = 0.8: the exact
+    invariants over every key, and sampled dq rows (patch and special rows
+    of both heads) against the oracle's row gradient on the forward's kept
+    tiles."""
+    L = zs.Layout(128, 5, 37, 37, heads=2)
+    y = 0.8
+    q, k, v = zs.stage_inputs(L, seed=43)
+    dy = _dy(L, 43)
+    tm = TileMap(L.frames, L.specials, L.rows, L.cols)
+    assert tm.T > 2048
+    (dq, dk, dv), sel = _sparse_bwd_gpu(L, q, k, v, dy, y)
+    dO = widen(dy)
+    for nm, G, want in (("dv", dv, dO.sum(axis=0)), ("dk", dk, np.zeros((L.heads, 64)))):
+        s = G.sum(axis=0)
+        err = np.abs(s - want).max()
+        scale = np.abs(G).sum(axis=0).max()
+        log(f"128 views sparse backward: sum of {nm} over the keys within {err:.3e} of the invariant "
+            f"(sum of magnitudes {scale:.3e})")
+        assert err <= 2.0 ** -7 * scale
+    Q, K, V = widen(q), widen(k), widen(v)
+    rows = zs.sample_rows(L, 256, seed=43, special_frames=2)
+    for h in range(L.heads):
+        toks = rows[rows[:, 0] == h, 1]
+        ref = obw.sparse_dq_rows(Q[:, h], K[:, h], V[:, h], dO[:, h], tm, y, toks, sel=sel[h])
+        got = dq[toks, h]
+        n = grad_close(got[:, None, :], ref[:, None, :], f"128 views sparse backward dq rows, head {h}",
+                       SPARSE_ROW_REL, SPARSE_HEAD_REL)
+        assert n == 0

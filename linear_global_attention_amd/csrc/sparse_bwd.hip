@@ -215,9 +215,12 @@ __device__ inline long long tile_first_token(const Geom& g, int u, int& tl) {
   return (long long)f * g.tok_pf + g.S + (long long)TILE * a * g.C + TILE * b;
 }
 
-// Token offset, from the tile's first token, of its row-major key j (j
-// below the tile's key count) in a tile w tokens wide.
-__device__ inline int in_tile(const Geom& g, int j, int w) { return (j / w) * g.C + j % w; }
+// Token offset, from the tile's first token, of its row-major key j in a
+// tile w tokens wide (meaningful for j below the tile's key count; callers
+// discard the value otherwise, and unsigned arithmetic keeps it defined).
+__device__ inline unsigned in_tile(const Geom& g, int j, int w) {
+  return (unsigned)(j / w) * (unsigned)g.C + (unsigned)(j % w);
+}
 
 // ---------------------------------------------------------------- query-major passes
 
@@ -482,12 +485,13 @@ __global__ void __launch_bounds__(SB_THREADS, SB_OCC) sbwd_rows_kernel(Geom g, S
   // so it adds exact zeros). The host keeps TILE tile rows of tokens below
   // 2^31 elements, so the offsets fit 32 bits.
   const int wlast = g.C - TILE * (g.tc - 1);
-  int cf[2], cl[2], c0[2];
+  unsigned cf[2], cl[2], c0[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int r = 16 * wu + 8 * j + (lane >> 3), ch = 8 * ((lane & 7) ^ (r & 7));
-    cf[j] = in_tile(g, r, TILE) * (int)g.in_tok + ch;
-    cl[j] = in_tile(g, r, wlast) * (int)g.in_tok + ch;
+    const int r = 16 * wu + 8 * j + (lane >> 3);
+    const unsigned ch = 8u * (unsigned)((lane & 7) ^ (r & 7));
+    cf[j] = in_tile(g, r, TILE) * (unsigned)g.in_tok + ch;
+    cl[j] = in_tile(g, r, wlast) * (unsigned)g.in_tok + ch;
     c0[j] = ch;
   }
   // (kind, key count) of block i come back to the caller, which hands them
@@ -515,7 +519,7 @@ __global__ void __launch_bounds__(SB_THREADS, SB_OCC) sbwd_rows_kernel(Geom g, S
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r0 = 16 * wu + 8 * j;
-        const unsigned off = (unsigned)(r0 + (lane >> 3) >= nk ? c0[j] : full ? cf[j] : cl[j]);
+        const unsigned off = r0 + (lane >> 3) >= nk ? c0[j] : full ? cf[j] : cl[j];
         __builtin_amdgcn_global_load_lds((const void*)(kb + off), (sb_lds_void*)(bK + r0 * D), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(vb + off), (sb_lds_void*)(bV + r0 * D), 16, 0, 0);
       }
@@ -656,6 +660,7 @@ template <int MODE>
 __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A) {
   __shared__ __attribute__((aligned(16))) u16 sQ[32 * D], sO[32 * D];
   __shared__ __attribute__((aligned(16))) float sL[32], sD[32];
+  __shared__ unsigned sT[MODE == SB_TILE ? 1024 : 1];  // TILE: this key tile's transposed-bitmap row (T <= 32,768)
   const int kb = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lg = lane >> 4, tl = lane & 15;
@@ -710,18 +715,48 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A)
     float lse, d;
     unsigned mw;
   };
+  // Token offsets, from a patch tile's first token, of this thread's rows
+  // 32 hb + tid / 8 (hb = 0, 1) in a tile of full width (TILE) and in one
+  // of the last tile column's width, computed once: a patch unit's rows
+  // are then a uniform base plus a per-thread offset, with no division.
+  const int wlast = g.C - TILE * (g.tc - 1);
+  const unsigned tf0 = in_tile(g, threadIdx.x >> 3, TILE), tf1 = in_tile(g, 32 + (threadIdx.x >> 3), TILE);
+  const unsigned tw0 = in_tile(g, threadIdx.x >> 3, wlast), tw1 = in_tile(g, 32 + (threadIdx.x >> 3), wlast);
   auto fetch_rows = [&](int t, int hb, RowFetch& f) {
     const int tid = threadIdx.x, r = tid >> 3, c = tid & 7;
     const int jr = 32 * hb + r;
-    const bool ok = jr < unit_rows(g, t);
-    const long long tk = ok ? unit_token(g, t, jr) : 0;
-    f.q = ld16(A.Q, tk * g.in_tok + (long long)h * g.in_head + 8 * c, ok);
-    f.o = ld16(A.dO, tk * A.o_tok + (long long)h * A.o_head + 8 * c, ok);
+    bool ok;
+    long long tk0;    // uniform: the unit's first token (patch) or 0 (special rows)
+    unsigned toff;    // this thread's row: token tk0 + toff
+    if (t < g.T) {
+      int tl;
+      tk0 = tile_first_token(g, t, tl);
+      ok = jr < tile_n(g, tl);
+      const bool full = tile_w(g, tl) == TILE;
+      toff = !ok ? 0u : full ? (hb ? tf1 : tf0) : (hb ? tw1 : tw0);
+    } else {
+      ok = jr < unit_rows(g, t);
+      tk0 = 0;
+      toff = ok ? (unsigned)unit_token(g, t, jr) : 0u;
+    }
+    // q and dout rows: uniform bases, 32-bit per-thread element offsets
+    // (the host keeps 8 patch rows below 2^31 elements; special rows take
+    // the 64-bit path through a zero base)
+    const u16* qb = A.Q + tk0 * g.in_tok + (long long)h * g.in_head;
+    const u16* ob = A.dO + tk0 * A.o_tok + (long long)h * A.o_head;
+    if (t < g.T) {
+      f.q = ld16(qb, (long long)(toff * (unsigned)g.in_tok + 8u * c), ok);
+      f.o = ld16(ob, (long long)(toff * (unsigned)A.o_tok + 8u * c), ok);
+    } else {
+      f.q = ld16(qb, (long long)toff * g.in_tok + 8 * c, ok);
+      f.o = ld16(ob, (long long)toff * A.o_tok + 8 * c, ok);
+    }
     f.lse = INFINITY;
     f.d = 0.f;
     if (ok && c == 0) {
-      f.lse = A.lse[(long long)h * g.N + tk];
-      f.d = A.dsum[(long long)h * g.N + tk];
+      const long long i = (long long)h * g.N + tk0 + toff;
+      f.lse = A.lse[i];
+      f.d = A.dsum[i];
     }
     f.mw = 0u;
     if (MODE == SB_LMK && kvalid) f.mw = A.selmask[((long long)h * g.T + t) * A.nw + (lmk >> 5)];
@@ -785,7 +820,11 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A)
   unsigned bits = 0u;
   int t0 = 0, t1 = 0;
   if (MODE == SB_TILE) {
-    bits = A.nw > 0 ? (unsigned)__builtin_amdgcn_readfirstlane((int)trow[0]) : 0u;
+    // the bitmap row goes to LDS once: words read in the walk are then LDS
+    // reads, which do not wait for the next step's row loads in flight
+    for (int i = threadIdx.x; i < A.nw; i += SB_THREADS) sT[i] = trow[i];
+    __syncthreads();
+    bits = A.nw > 0 ? (unsigned)__builtin_amdgcn_readfirstlane((int)sT[0]) : 0u;
   } else {
     const int lastu = MODE == SB_LMK ? g.T : nunits;  // special rows see no landmark
     const int c = blockIdx.z;
@@ -799,7 +838,7 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A)
       return tcur + 1 < t1 ? tcur + 1 : -1;
     }
     if (tcur >= g.T) return tcur + 1 < nunits ? tcur + 1 : -1;  // the special-row units
-    while (bits == 0u && w + 1 < A.nw) bits = (unsigned)__builtin_amdgcn_readfirstlane((int)trow[++w]);
+    while (bits == 0u && w + 1 < A.nw) bits = (unsigned)__builtin_amdgcn_readfirstlane((int)sT[++w]);
     if (bits) {
       const int t = 32 * w + __builtin_ctz(bits);
       bits &= bits - 1u;

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -277,6 +278,11 @@ zebra_status validate(const zebra_args* a, int op, Geom& g, int64_t& k) {
       if (k < 0) return fail(ZEBRA_ERR_INVALID_ARG, "y must lie in [0, 1]");
       if (g.T > 32768) return fail(ZEBRA_ERR_UNSUPPORTED, "the sparse backward supports at most 32768 tiles");
       if (g.N >= (1LL << 31)) return fail(ZEBRA_ERR_UNSUPPORTED, "the sparse backward supports fewer than 2^31 tokens");
+      // its kernels address a key tile's rows by 32-bit element offsets
+      // from the tile's first row
+      if ((long long)TILE * g.C * std::max(g.in_tok, g.out_tok) >= (1LL << 31))
+        return fail(ZEBRA_ERR_UNSUPPORTED,
+                    "the sparse backward needs 8 patch rows of q, k, v and dout to span fewer than 2^31 elements");
       NEED(a->q, "q");
       NEED(a->k, "k");
       NEED(a->v, "v");

@@ -657,7 +657,7 @@ enum { SB_TILE = 0, SB_SPEC = 1, SB_LMK = 2 };
 //                                chunk blockIdx.z of the query units
 // Wave w owns keys 16 w .. 16 w + 15 (lane tl: key 16 w + tl).
 template <int MODE>
-__global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A) {
+__global__ void __launch_bounds__(SB_THREADS, 3) sbwd_keys_kernel(Geom g, SbArgs A) {
   __shared__ __attribute__((aligned(16))) u16 sQ[32 * D], sO[32 * D];
   __shared__ __attribute__((aligned(16))) float sL[32], sD[32];
   __shared__ unsigned sT[MODE == SB_TILE ? 1024 : 1];  // TILE: this key tile's transposed-bitmap row (T <= 32,768)
@@ -846,26 +846,45 @@ __global__ void __launch_bounds__(SB_THREADS) sbwd_keys_kernel(Geom g, SbArgs A)
     }
     return g.T < nunits ? g.T : -1;
   };
-  int tn = next_unit(), hn = 0;
-  RowFetch f;
-  if (tn >= 0) fetch_rows(tn, 0, f);
-  while (tn >= 0) {
-    const int t = tn, hb = hn;
-    // the step after (t, hb)
+  // the step after (t, hb), in place (t = -1: none)
+  auto advance = [&](int& t, int& hb) {
+    if (t < 0) return;
     if (hb == 0 && unit_rows(g, t) > 32) {
-      hn = 1;
+      hb = 1;
     } else {
       tcur = t;
-      tn = next_unit();
-      hn = 0;
+      t = next_unit();
+      hb = 0;
     }
+  };
+  // Rows are fetched two steps ahead, into two register sets used in turn:
+  // a step commits its set to LDS, then the same set takes the rows two
+  // steps on, so no set in flight is ever copied.
+  int ta = next_unit(), ha = 0;  // the current step (rows in the set of its turn)
+  int tb = ta, hb2 = ha;         // the next one (rows in the other set)
+  advance(tb, hb2);
+  RowFetch f0, f1;
+  if (ta >= 0) fetch_rows(ta, ha, f0);
+  if (tb >= 0) fetch_rows(tb, hb2, f1);
+  auto step = [&](RowFetch& f) __attribute__((always_inline)) {
     float bias = kbias;
     if (MODE == SB_LMK && ((f.mw >> (lmk & 31)) & 1u)) bias = -INFINITY;
+    int tc = tb, hc = hb2;
+    advance(tc, hc);
     __syncthreads();  // the previous rows' reads are done
     commit_rows(f);
-    if (tn >= 0) fetch_rows(tn, hn, f);
+    if (tc >= 0) fetch_rows(tc, hc, f);
     __syncthreads();
     rows(bias);
+    ta = tb;
+    ha = hb2;
+    tb = tc;
+    hb2 = hc;
+  };
+  while (ta >= 0) {
+    step(f0);
+    if (ta < 0) break;
+    step(f1);
   }
 
   // lane (key tl, group lg) holds channels 16 cb + 4 lg + r of dk (x 1/8 to

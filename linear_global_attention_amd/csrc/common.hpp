@@ -40,7 +40,6 @@ struct Geom {
   int spec_pad;        // nspec rounded up to KBLK
   int T_pad;           // T rounded up to KBLK
   unsigned tpf_magic;  // floor(2^32 / tpf) + 1 (tpf >= 2): u / tpf = umulhi(u, magic) for u*tpf < 2^32
-  unsigned tc_magic;   // floor(2^32 / tc) + 1 (tc >= 2): v / tc = umulhi(v, magic) for v*tc < 2^32
   // element strides: (token n, head h) row of q/k/v at n*in_tok + h*in_head,
   // of the output at n*out_tok + h*out_head
   long long in_tok, in_head, out_tok, out_head;

@@ -199,6 +199,7 @@ struct SbArgs {
   u16* dV;
   int keep, nw;
   long long o_tok, o_head;  // dout strides
+  unsigned tc_magic;        // floor(2^32 / tc) + 1 (tc >= 2): tile row of a frame's tile by multiply-high
 };
 
 __device__ inline const char* lm_kblock(const Geom& g, const u16* LM, int h, int b) {
@@ -208,10 +209,12 @@ __device__ inline const char* lm_kblock(const Geom& g, const u16* LM, int h, int
 // Token of the first key of tile u (row-major within the tile), and u's
 // tile within its frame; no divisions (multiply-high by the frame's and
 // the tile row's reciprocals).
-__device__ inline long long tile_first_token(const Geom& g, int u, int& tl) {
+// tc_magic = floor(2^32 / tc) + 1 (tc >= 2): v / tc = umulhi(v, tc_magic)
+// for v * tc < 2^32.
+__device__ inline long long tile_first_token(const Geom& g, unsigned tc_magic, int u, int& tl) {
   const int f = frame_of_tile(g, u);
   tl = u - f * g.tpf;
-  const int a = g.tc == 1 ? tl : (int)__umulhi((unsigned)tl, g.tc_magic), b = tl - a * g.tc;
+  const int a = g.tc == 1 ? tl : (int)__umulhi((unsigned)tl, tc_magic), b = tl - a * g.tc;
   return (long long)f * g.tok_pf + g.S + (long long)TILE * a * g.C + TILE * b;
 }
 
@@ -510,7 +513,7 @@ __global__ void __launch_bounds__(SB_THREADS, SB_OCC) sbwd_rows_kernel(Geom g, S
     if (kind == 0) {
       // token tile: a uniform base row, per-lane 32-bit offsets
       int tl;
-      const long long tok0 = tile_first_token(g, blk, tl);
+      const long long tok0 = tile_first_token(g, A.tc_magic, blk, tl);
       nk = tile_n(g, tl);
       const bool full = tile_w(g, tl) == TILE;
       const long long base = tok0 * g.in_tok + (long long)h * g.in_head;
@@ -730,7 +733,7 @@ __global__ void __launch_bounds__(SB_THREADS, 3) sbwd_keys_kernel(Geom g, SbArgs
     unsigned toff;    // this thread's row: token tk0 + toff
     if (t < g.T) {
       int tl;
-      tk0 = tile_first_token(g, t, tl);
+      tk0 = tile_first_token(g, A.tc_magic, t, tl);
       ok = jr < tile_n(g, tl);
       const bool full = tile_w(g, tl) == TILE;
       toff = !ok ? 0u : full ? (hb ? tf1 : tf0) : (hb ? tw1 : tw0);
@@ -1082,6 +1085,7 @@ hipError_t launch_sparse_bwd(const Geom& g, int keep, const u16* Q, const u16* K
   A.nw = nw;
   A.o_tok = o_tok;
   A.o_head = o_head;
+  A.tc_magic = g.tc >= 2 ? (unsigned)((1ULL << 32) / (unsigned)g.tc + 1) : 0u;
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

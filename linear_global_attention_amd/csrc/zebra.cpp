@@ -78,7 +78,6 @@ zebra_status make_geom(const zebra_layout* L, Geom& g) {
     return fail(ZEBRA_ERR_UNSUPPORTED, "sequence too long");
   g.T = (int)T;
   g.tpf_magic = g.tpf >= 2 ? (unsigned)((1ULL << 32) / (unsigned)g.tpf + 1) : 0u;
-  g.tc_magic = g.tc >= 2 ? (unsigned)((1ULL << 32) / (unsigned)g.tc + 1) : 0u;
   int off = 0;
   for (int a = 0; a < g.tr; ++a)
     for (int b = 0; b < g.tc; ++b) {

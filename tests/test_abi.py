@@ -163,6 +163,25 @@ def test_strides_and_alignment_checked_on_host():
         assert zb.lib.zebra_buffer_bytes(ctypes.byref(Ls), 0.5, zb.BUF["KT"]) == zb.buffer_bytes(L, 0.5, "KT")
 
 
+def test_sparse_bwd_rejects_wide_row_spans():
+    """The tile-sparse backward addresses a key tile's rows by 32-bit element
+    offsets from its first row, so it rejects layouts whose 8 patch rows of
+    q/k/v (or of dout, which has out's strides) span 2^31 or more elements;
+    the forward entry points accept them (their validation does not touch
+    memory)."""
+    L = zb.Layout(4, 5, 37, 37, 2)
+    a = _full_args(L, 0.5)
+    assert zb.validate(a, "SPARSE_BWD") == 0
+    for field in ("tok_stride", "out_tok_stride"):
+        b = _full_args(L, 0.5)
+        setattr(b.L, field, 1 << 23)  # 8 rows x 37 columns x 2^23 > 2^31
+        assert zb.validate(b, "SPARSE_BWD") == 2 and "2^31" in zb.last_error(), field
+        assert zb.validate(b, "SPARSE") == 0, field
+    b = _full_args(L, 0.5)
+    b.L.tok_stride = (1 << 31) // (8 * 37) // 8 * 8  # just below the bound
+    assert zb.validate(b, "SPARSE_BWD") == 0
+
+
 def test_make_args_rejects_wrong_tensors():
     import torch
     L = zb.Layout(2, 1, 3, 5, 1)

@@ -214,8 +214,10 @@ zebra_status zebra_sparse_attn(const zebra_args* a, zebra_stream stream);
  * the inputs. All four 16-byte aligned. The workspace must hold
  * ZEBRA_BUF_BWD_WORKSPACE bytes (per-row log-sum-exp and D, the transposed
  * kept-tile bitmap, partial gradients of the special keys and landmarks,
- * the landmarks' bf16 high and low parts).
- * At most 32,768 tiles and fewer than 2^31 tokens (ZEBRA_ERR_UNSUPPORTED).
+ * the landmarks' bf16 high and low parts, checkpoint counters that the call
+ * zeroes itself; two calls must not share a workspace at once).
+ * At most 32,768 tiles, fewer than 2^31 tokens, and 8 patch rows of q/k/v
+ * and of dout spanning fewer than 2^31 elements (ZEBRA_ERR_UNSUPPORTED).
  * fp32 arithmetic with bf16 MFMA operands: logits and dP exact products
  * summed in fp32, P and the logit gradients rounded to bf16 for the
  * gradient products; each gradient rounded once to bf16. */
